@@ -1,0 +1,22 @@
+"""fp64 CPU oracle for Fibonacci-offset sparse attention.
+
+Test infrastructure only: imported by tests/, the package smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+"""
+from .fsa_ref import (  # noqa: F401
+    attended_offsets,
+    coprime_layer,
+    dense_forward,
+    dense_forward_rows,
+    fibonacci_base,
+    offset_table,
+    pow2_base,
+    round_half_away,
+    round_half_even,
+    sparse_backward,
+    sparse_backward_rows,
+    sparse_forward,
+    sparse_forward_rows,
+    sparse_probabilities,
+    stagger_alpha,
+)

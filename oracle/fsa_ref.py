@@ -1,0 +1,352 @@
+"""Plain fp64 CPU oracle for Fibonacci-offset sparse attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this
+module; only the test suite, the package smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code, tables or constants with the HIP
+library: it re-derives everything from the pages in the plainest form.
+
+Pages cited (titles as published):
+  [EXPL-pt] "Depth-Staggered Fibonacci Spacing for Sparse Attention: Static
+            Schedules Beat Learned Dilation and Extrapolate Where Dense
+            Attention Fails", gist.science explainer of C. A. Capps' paper,
+            Portuguese edition.
+  [EXPL-fr] the same explainer, French edition (same sections, translated).
+  [SUMM-zh] "深度解读：基于深度交错斐波那契间隔的稀疏注意力机制" (aimsg.uk
+            summary of the same paper), section "核心内容".
+
+What the pages fix:
+  * [EXPL-pt] Metodologia / Arquitetura e Mecanismo de Atenção, item
+    "Conjunto Atendido": query i attends a dense local window of size W plus
+    sparse offsets from the Fibonacci list 1, 2, 3, 5, ..., 987.
+  * same section, item "Escalonamento": every offset f_k is scaled by a
+    per-layer scalar, d_k = alpha * f_k, with alpha restricted to [0.5, 1.5].
+  * [EXPL-pt] Variáveis Experimentais: fixed schedule alpha = 1 for all layers;
+    static linear stagger rising from 0.5 at layer 0 to 1.5 at layer 15.
+  * [EXPL-pt] Controles: a reach-matched power-of-2 (log-sparse) base; a dense
+    baseline with the same architecture.
+  * [EXPL-pt] Principais Contribuições e Resultados, item 2 ("Eficiência"):
+    static schedules execute as a boolean mask, so the offsets are integers and
+    each key is attended at most once.
+
+Readings taken where the pages leave a step open (all switchable here only):
+  * rounding of alpha*F: round half to even on the fp64 product (the half-away
+    variant exists for tests that show which tables the choice moves);
+  * reach R caps the base value (F < R, exclusive), before scaling;
+  * the window holds offsets 0..w-1 (self included); sparse offsets below w
+    merge into it; duplicates collapse (set semantics);
+  * keys before the sequence start are dropped (no padding, no wrap);
+  * one softmax over window and sparse offsets together;
+  * the backward pass is the textbook softmax-attention gradient restricted to
+    the mask.
+
+Floating point: every array is converted to float64 on entry.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Offset tables
+# ----------------------------------------------------------------------------
+
+
+def fibonacci_base(R: int) -> list[int]:
+    """Distinct Fibonacci numbers F < R, starting 1, 2, 3, 5, ...
+
+    [EXPL-pt] Metodologia / Arquitetura, "Conjunto Atendido": the printed list
+    starts 1, 2, 3, 5 (no repeated 1) and ends at 987 when the reach is 1024.
+    Recurrence F_1 = 1, F_2 = 2, F_{k+1} = F_k + F_{k-1}; R is exclusive.
+    """
+    out = []
+    a, b = 1, 2
+    while a < R:
+        out.append(a)
+        a, b = b, a + b
+    return out
+
+
+def pow2_base(R: int) -> list[int]:
+    """Powers of two 2^k < R, k >= 0.
+
+    [EXPL-pt] Controles: a reach-matched power-of-2 (log-sparse) base.
+    """
+    out = []
+    p = 1
+    while p < R:
+        out.append(p)
+        p *= 2
+    return out
+
+
+def round_half_even(x: float) -> int:
+    """Round a finite double to the nearest integer, ties to the even one.
+
+    Written out so that a reader can check it: f = floor(x), r = x - f is exact
+    for doubles of this magnitude; r > 1/2 rounds up, r < 1/2 rounds down, and
+    r == 1/2 picks whichever of f, f+1 is even.
+    """
+    f = math.floor(x)
+    r = x - f
+    if r > 0.5:
+        return int(f) + 1
+    if r < 0.5:
+        return int(f)
+    return int(f) if int(f) % 2 == 0 else int(f) + 1
+
+
+def round_half_away(x: float) -> int:
+    """Alternative reading: ties away from zero (x > 0 here)."""
+    f = math.floor(x)
+    r = x - f
+    return int(f) + 1 if r >= 0.5 else int(f)
+
+
+def offset_table(base: str, alpha: float, w: int, R: int,
+                 rounding: str = "even") -> list[int]:
+    """Sparse offsets T for one layer: sorted unique round(alpha*F) that are >= w.
+
+    [EXPL-pt] Metodologia / Arquitetura, items "Conjunto Atendido" and
+    "Escalonamento": d_k = alpha * f_k over the base list. Values below w fall
+    inside the dense window and are dropped from T; T does not depend on N.
+    """
+    if base == "fib":
+        fs = fibonacci_base(R)
+    elif base == "pow2":
+        fs = pow2_base(R)
+    else:
+        raise ValueError(f"unknown base {base!r}")
+    rnd = round_half_even if rounding == "even" else round_half_away
+    alpha = float(alpha)
+    scaled = [rnd(alpha * float(f)) for f in fs]
+    return sorted({o for o in scaled if o >= w})
+
+
+def attended_offsets(T: list[int], w: int) -> list[int]:
+    """Full offset set O = {0, ..., w-1} union T (sorted, unique)."""
+    return sorted(set(range(w)) | set(int(o) for o in T))
+
+
+def stagger_alpha(layer: int, n_layers: int = 16) -> float:
+    """Static linear stagger: alpha rises linearly from 0.5 at layer 0 to 1.5
+    at the last layer ([EXPL-pt] Variáveis Experimentais, "Escalonado
+    (Linear)"). Computed as 0.5 + layer / (n_layers - 1) in fp64."""
+    return 0.5 + layer / float(n_layers - 1)
+
+
+def coprime_layer(layer: int, n_layers: int = 16) -> int:
+    """Coprime reassignment layer -> 7*layer mod L ([EXPL-pt] Variáveis
+    Experimentais, "Escalonado (Coprimo/HDC)")."""
+    return (7 * layer) % n_layers
+
+
+# ----------------------------------------------------------------------------
+# Attention: forward, backward, dense baseline
+# ----------------------------------------------------------------------------
+
+
+def _scores(q, k, offs, scale):
+    """S[..., i, m] = scale * <q_i, k_{i - offs[m]}>, -inf where i - offs[m] < 0."""
+    N = q.shape[-2]
+    S = np.full(q.shape[:-1] + (len(offs),), -np.inf)
+    for m, o in enumerate(offs):
+        if o < N:
+            S[..., o:, m] = scale * np.sum(q[..., o:, :] * k[..., : N - o, :], axis=-1)
+    return S
+
+
+def _softmax_rows(S):
+    """Two-pass softmax over the last axis; returns P, row max, row sum."""
+    mx = np.max(S, axis=-1, keepdims=True)
+    e = np.exp(S - mx)
+    l = np.sum(e, axis=-1, keepdims=True)
+    return e / l, mx[..., 0], l[..., 0]
+
+
+def sparse_probabilities(q, k, T, w, scale):
+    """P[..., i, m] over the offset list O = {0..w-1} u T, plus row max/sum."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    offs = attended_offsets(T, w)
+    S = _scores(q, k, offs, scale)
+    P, mx, l = _softmax_rows(S)
+    return offs, P, mx, l
+
+
+def sparse_forward(q, k, v, T, w, scale):
+    """o_i = sum_{j in J(i)} P_ij v_j and LSE_i = m_i + ln l_i, where
+    J(i) = {i - o : o in {0..w-1} u T, o <= i}.
+
+    Layout: [..., N, d]; returns (o [..., N, d], lse [..., N]) in float64.
+    [EXPL-pt] Metodologia / Arquitetura, "Conjunto Atendido" (the attended set)
+    and Principais Contribuições §2 (a single boolean mask, so one softmax).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    offs, P, mx, l = sparse_probabilities(q, k, T, w, scale)
+    N = v.shape[-2]
+    o = np.zeros(v.shape)
+    for m, off in enumerate(offs):
+        if off < N:
+            o[..., off:, :] += P[..., off:, m : m + 1] * v[..., : N - off, :]
+    return o, mx + np.log(l)
+
+
+def sparse_backward(q, k, v, dout, T, w, scale):
+    """Gradients of sum(dout * o) with respect to q, k, v.
+
+    Textbook softmax-attention gradient restricted to the mask:
+      D_i = <dO_i, o_i>, dP_ij = <dO_i, v_j>, dS_ij = P_ij (dP_ij - D_i),
+      dQ_i = scale sum_j dS_ij k_j, dK_j = scale sum_i dS_ij q_i,
+      dV_j = sum_i P_ij dO_i, all sums over pairs with j in J(i).
+    The pages describe training through this mask ([EXPL-pt] Metodologia) but
+    print no gradient, so this is the plain derivative of the forward above.
+    Returns (dq, dk, dv) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    offs, P, _, _ = sparse_probabilities(q, k, T, w, scale)
+    o, _ = sparse_forward(q, k, v, T, w, scale)
+    N = q.shape[-2]
+    D = np.sum(dout * o, axis=-1)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for m, off in enumerate(offs):
+        if off >= N:
+            continue
+        qi, doi = q[..., off:, :], dout[..., off:, :]
+        kj, vj = k[..., : N - off, :], v[..., : N - off, :]
+        p = P[..., off:, m]
+        dp = np.sum(doi * vj, axis=-1)
+        ds = p * (dp - D[..., off:])
+        dq[..., off:, :] += scale * ds[..., None] * kj
+        dk[..., : N - off, :] += scale * ds[..., None] * qi
+        dv[..., : N - off, :] += p[..., None] * doi
+    return dq, dk, dv
+
+
+def dense_forward(q, k, v, scale):
+    """Dense causal baseline: o = softmax(scale * q k^T masked to j <= i) v.
+
+    [EXPL-pt] Controles: dense attention with the same architecture.
+    Full N x N matrix; fine for the sizes the tests use.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N = q.shape[-2]
+    S = scale * (q @ np.swapaxes(k, -1, -2))
+    future = np.triu(np.ones((N, N), dtype=bool), k=1)
+    S = np.where(future, -np.inf, S)
+    P, mx, l = _softmax_rows(S)
+    return P @ v, mx + np.log(l)
+
+
+def dense_forward_rows(q, k, v, scale, rows):
+    """Dense causal output for selected query rows only (for large N checks).
+
+    rows: 1-D integer array of query indices. Returns (o [..., len(rows), d],
+    lse [..., len(rows)]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    outs, lses = [], []
+    for i in rows:
+        i = int(i)
+        s = scale * np.sum(q[..., i : i + 1, :] * k[..., : i + 1, :], axis=-1)
+        mx = np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s - mx)
+        l = np.sum(e, axis=-1, keepdims=True)
+        outs.append(np.sum((e / l)[..., None] * v[..., : i + 1, :], axis=-2))
+        lses.append(mx[..., 0] + np.log(l[..., 0]))
+    return np.stack(outs, axis=-2), np.stack(lses, axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Row-sampled forms of the same definitions (for full-size checks)
+# ----------------------------------------------------------------------------
+
+
+def _row_keys(i, offs):
+    """Key indices J(i) = {i - o : o in offs, o <= i} (ascending offset order)."""
+    return [i - o for o in offs if o <= i]
+
+
+def sparse_forward_rows(q, k, v, T, w, scale, rows):
+    """o_i and LSE_i of sparse_forward for the given query rows, one by one.
+
+    q, k, v: [..., N, d]. Returns (o [..., len(rows), d], lse [..., len(rows)]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    offs = attended_offsets(T, w)
+    outs, lses = [], []
+    for i in rows:
+        js = _row_keys(int(i), offs)
+        s = scale * np.sum(q[..., int(i) : int(i) + 1, :] * k[..., js, :], axis=-1)
+        mx = np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s - mx)
+        l = np.sum(e, axis=-1, keepdims=True)
+        outs.append(np.sum((e / l)[..., None] * v[..., js, :], axis=-2))
+        lses.append(mx[..., 0] + np.log(l[..., 0]))
+    return np.stack(outs, axis=-2), np.stack(lses, axis=-1)
+
+
+def sparse_backward_rows(q, k, v, dout, T, w, scale, rows):
+    """dQ_r, dK_r, dV_r of sparse_backward for the given rows r, one by one.
+
+    dQ_r sums over the keys row r attends; dK_r and dV_r sum over the queries
+    i = r + o (o in O, i < N) that attend key r. Each needed P_ij comes from
+    that query's own softmax (its LSE and o_i), recomputed per row.
+    Returns (dq, dk, dv), each [..., len(rows), d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    N = q.shape[-2]
+    offs = attended_offsets(T, w)
+
+    cache = {}
+
+    def row_stats(i):
+        # (keys, P over those keys, D_i) for query row i
+        if i not in cache:
+            js = _row_keys(i, offs)
+            s = scale * np.sum(q[..., i : i + 1, :] * k[..., js, :], axis=-1)
+            mx = np.max(s, axis=-1, keepdims=True)
+            e = np.exp(s - mx)
+            p = e / np.sum(e, axis=-1, keepdims=True)
+            o_i = np.sum(p[..., None] * v[..., js, :], axis=-2)
+            D = np.sum(dout[..., i, :] * o_i, axis=-1)
+            cache[i] = (js, p, D)
+        return cache[i]
+
+    dqs, dks, dvs = [], [], []
+    for r in rows:
+        r = int(r)
+        js, p, D = row_stats(r)
+        dp = np.sum(dout[..., r : r + 1, :] * v[..., js, :], axis=-1)
+        ds = p * (dp - D[..., None])
+        dqs.append(scale * np.sum(ds[..., None] * k[..., js, :], axis=-2))
+        dk_r = np.zeros(q.shape[:-2] + (q.shape[-1],))
+        dv_r = np.zeros(q.shape[:-2] + (q.shape[-1],))
+        for o in offs:
+            i = r + o
+            if i >= N:
+                continue
+            jsi, pi, Di = row_stats(i)
+            col = jsi.index(r)
+            p_ir = pi[..., col]
+            dp_ir = np.sum(dout[..., i, :] * v[..., r, :], axis=-1)
+            ds_ir = p_ir * (dp_ir - Di)
+            dk_r += scale * ds_ir[..., None] * q[..., i, :]
+            dv_r += p_ir[..., None] * dout[..., i, :]
+        dks.append(dk_r)
+        dvs.append(dv_r)
+    return np.stack(dqs, axis=-2), np.stack(dks, axis=-2), np.stack(dvs, axis=-2)
