@@ -1,0 +1,276 @@
+// C-ABI layer of libfsa: argument validation, offset-table construction and
+// kernel launch on the caller's stream. Declarations and contracts: fsa.h.
+//
+// Offset tables follow the explainer page "Depth-Staggered Fibonacci Spacing for
+// Sparse Attention: Static Schedules Beat Learned Dilation and Extrapolate Where
+// Dense Attention Fails" (gist.science), section "Metodologia / Arquitetura e
+// Mecanismo de Atenção", items "Conjunto Atendido" (window plus Fibonacci offsets)
+// and "Escalonamento" (d_k = alpha * f_k), and section "Controles" (power-of-2
+// base). Rounding, reach and deduplication are the library's stated reading:
+// round half to even on the double product, base values F < R, set semantics.
+//
+// This file must be compiled without -ffast-math: the table depends on exact
+// IEEE double rounding of alpha * F.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "fsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fsa_status_t fail(fsa_status_t st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+fsa_status_t fail(fsa_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+fsa_status_t ok() {
+    g_last_error.clear();
+    return FSA_OK;
+}
+
+// Nearest integer to a finite, non-negative double; exact ties go to the even
+// neighbour. x - floor(x) is exact in double arithmetic for these magnitudes.
+int64_t round_half_even(double x) {
+    const double f = std::floor(x);
+    const double r = x - f;
+    int64_t n = static_cast<int64_t>(f);
+    if (r > 0.5 || (r == 0.5 && (n & 1))) ++n;
+    return n;
+}
+
+// Builds T into out[0..FSA_MAX_OFFSETS) and returns |T|, or -1 with the error set.
+int build_table(fsa_base_t base, double alpha, int32_t w, int32_t R, int32_t *out,
+                fsa_status_t *st) {
+    if (base != FSA_BASE_FIB && base != FSA_BASE_POW2) {
+        *st = fail(FSA_E_ARG, "unknown offset base %d", static_cast<int>(base));
+        return -1;
+    }
+    if (!std::isfinite(alpha) || !(alpha > 0.0)) {
+        *st = fail(FSA_E_ARG, "alpha must be finite and > 0 (got %g)", alpha);
+        return -1;
+    }
+    if (w < 1) {
+        *st = fail(FSA_E_ARG, "window w must be >= 1 (got %d)", w);
+        return -1;
+    }
+    if (R < 1) {
+        *st = fail(FSA_E_ARG, "reach R must be >= 1 (got %d)", R);
+        return -1;
+    }
+    int count = 0;
+    int64_t a = 1, b = 2;  // Fibonacci: 1, 2, 3, 5, ...; powers of two: 1, 2, 4, ...
+    while (a < R) {
+        const double x = alpha * static_cast<double>(a);
+        // round(x) <= 2^31 - 1 exactly when x < 2^31 - 1/2 (the tie rounds to even 2^31)
+        if (!(x < 2147483647.5)) {
+            *st = fail(FSA_E_ARG, "alpha * %lld = %.17g does not fit in int32",
+                       static_cast<long long>(a), x);
+            return -1;
+        }
+        const int64_t o = round_half_even(x);
+        if (o >= w) {
+            // insert into the sorted, duplicate-free list
+            int pos = 0;
+            while (pos < count && out[pos] < o) ++pos;
+            if (pos == count || out[pos] != o) {
+                if (count == FSA_MAX_OFFSETS) {
+                    *st = fail(FSA_E_ARG, "offset table exceeds %d entries", FSA_MAX_OFFSETS);
+                    return -1;
+                }
+                for (int t = count; t > pos; --t) out[t] = out[t - 1];
+                out[pos] = static_cast<int32_t>(o);
+                ++count;
+            }
+        }
+        if (base == FSA_BASE_FIB) {
+            const int64_t c = a + b;
+            a = b;
+            b = c;
+        } else {
+            a *= 2;
+        }
+    }
+    return count;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Shape {
+    int32_t B, H, N, d;
+};
+
+// Shape, dtype and scale checks common to every attention call.
+fsa_status_t check_common(fsa_dtype_t dt, const Shape &s, float scale) {
+    if (dt != FSA_F32 && dt != FSA_BF16)
+        return fail(FSA_E_UNSUPPORTED, "unsupported dtype %d", static_cast<int>(dt));
+    if (s.B < 0 || s.H < 0 || s.N < 0)
+        return fail(FSA_E_ARG, "negative size B=%d H=%d N=%d", s.B, s.H, s.N);
+    if (s.d < 1) return fail(FSA_E_ARG, "head size d must be >= 1 (got %d)", s.d);
+    if (s.d != fsa::kHeadDim)
+        return fail(FSA_E_UNSUPPORTED, "head size d=%d (only 64 is implemented)", s.d);
+    if (!std::isfinite(scale)) return fail(FSA_E_ARG, "scale must be finite");
+    const int64_t bh = static_cast<int64_t>(s.B) * s.H;
+    if (bh > INT32_MAX) return fail(FSA_E_ARG, "B*H=%lld too large", static_cast<long long>(bh));
+    const int64_t tiles = (static_cast<int64_t>(s.N) + fsa::kTile - 1) / fsa::kTile;
+    if (bh * tiles > INT32_MAX)
+        return fail(FSA_E_ARG, "B*H*ceil(N/64)=%lld workgroups exceed the grid limit",
+                    static_cast<long long>(bh * tiles));
+    return FSA_OK;
+}
+
+fsa_status_t check_ptrs(const char *const *names, const void *const *ptrs, int n) {
+    for (int i = 0; i < n; ++i) {
+        if (!ptrs[i]) return fail(FSA_E_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ptrs[i])) return fail(FSA_E_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    return FSA_OK;
+}
+
+fsa_status_t check_no_alias(const char *const *names, const void *const *ptrs, int n_in, int n) {
+    for (int i = n_in; i < n; ++i)
+        for (int j = 0; j < n; ++j)
+            if (j != i && ptrs[i] == ptrs[j])
+                return fail(FSA_E_ARG, "%s aliases %s", names[i], names[j]);
+    return FSA_OK;
+}
+
+// Keeps only offsets that reach a key for some row (offset < N); sorted input.
+int trim_offsets(int32_t *off, int count, int32_t N) {
+    int c = 0;
+    while (c < count && off[c] < N) ++c;
+    return c;
+}
+
+fsa_status_t launched(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(FSA_E_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fsa_status_t fsa_build_offsets(fsa_base_t base, double alpha, int32_t w, int32_t R,
+                               int32_t *out, int32_t capacity, int32_t *count) {
+    if (!count) return fail(FSA_E_ARG, "count is NULL");
+    if (capacity < 0) return fail(FSA_E_ARG, "capacity must be >= 0");
+    int32_t tab[FSA_MAX_OFFSETS];
+    fsa_status_t st = FSA_OK;
+    const int n = build_table(base, alpha, w, R, tab, &st);
+    if (n < 0) return st;
+    *count = n;
+    if (n > capacity)
+        return fail(FSA_E_CAPACITY, "offset table has %d entries, capacity is %d", n, capacity);
+    if (n > 0 && !out) return fail(FSA_E_ARG, "out is NULL");
+    if (n > 0) std::memcpy(out, tab, sizeof(int32_t) * static_cast<size_t>(n));
+    return ok();
+}
+
+fsa_status_t fsa_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v, void *o,
+                         float *lse, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                         fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, s, scale);
+    if (st != FSA_OK) return st;
+    fsa::AttnParams p{};
+    const int n_off = build_table(base, alpha, w, R, p.off, &st);
+    if (n_off < 0) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "o", "lse"};
+    const void *ptrs[] = {q, k, v, o, lse};
+    if ((st = check_ptrs(names, ptrs, 5)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 3, 5)) != FSA_OK) return st;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = o;
+    p.lse_out = lse;
+    p.bh = B * H;
+    p.n = N;
+    p.w = w;
+    p.n_off = trim_offsets(p.off, n_off, N);
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_forward(dt, p, static_cast<hipStream_t>(stream)), "forward");
+}
+
+fsa_status_t fsa_backward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
+                          const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                          void *dv, float *delta_ws, int32_t B, int32_t H, int32_t N, int32_t d,
+                          float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                          void *stream) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, s, scale);
+    if (st != FSA_OK) return st;
+    fsa::AttnParams p{};
+    const int n_off = build_table(base, alpha, w, R, p.off, &st);
+    if (n_off < 0) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta_ws"};
+    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta_ws};
+    if ((st = check_ptrs(names, ptrs, 10)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 6, 10)) != FSA_OK) return st;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse_in = lse;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.delta = delta_ws;
+    p.bh = B * H;
+    p.n = N;
+    p.w = w;
+    p.n_off = trim_offsets(p.off, n_off, N);
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_backward(dt, p, static_cast<hipStream_t>(stream)), "backward");
+}
+
+fsa_status_t fsa_dense_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
+                               void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
+                               float scale, void *stream) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, s, scale);
+    if (st != FSA_OK) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "o", "lse"};
+    const void *ptrs[] = {q, k, v, o, lse};
+    if ((st = check_ptrs(names, ptrs, 5)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 3, 5)) != FSA_OK) return st;
+    // Dense causal attention is the window case with w = N and no sparse offsets.
+    fsa::AttnParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = o;
+    p.lse_out = lse;
+    p.bh = B * H;
+    p.n = N;
+    p.w = N;
+    p.n_off = 0;
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_forward(dt, p, static_cast<hipStream_t>(stream)), "dense forward");
+}
+
+const char *fsa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

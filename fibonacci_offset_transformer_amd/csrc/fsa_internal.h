@@ -1,0 +1,39 @@
+// Internal interface between the C-ABI layer (fsa_abi.cpp) and the HIP kernels
+// (fsa_kernels.hip). Not installed; the public interface is include/fsa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fsa.h"
+
+namespace fsa {
+
+constexpr int kHeadDim = 64;   // head size supported by the kernels
+constexpr int kTile = 64;      // query (or key) rows owned by one workgroup
+constexpr int kThreads = 256;  // four wave64 per workgroup, 16 rows each
+
+// Kernel arguments, passed by value. Offsets are the sparse table T after the
+// host dropped entries >= N (they attend nothing); all entries are >= w.
+struct AttnParams {
+    const void *q, *k, *v;   // [BH, N, 64]
+    const void *o;           // forward output (backward input)
+    const void *dout;        // upstream gradient (backward)
+    void *out;               // forward: O
+    void *dq, *dk, *dv;      // backward outputs
+    const float *lse_in;     // backward: forward LSE
+    float *lse_out;          // forward: LSE
+    float *delta;            // backward: D workspace [BH, N]
+    int32_t bh;              // B * H
+    int32_t n;               // sequence length
+    int32_t w;               // window (offsets 0..w-1)
+    int32_t n_off;           // entries used in off[]
+    float scale;             // score scale
+    float scale_log2;        // scale * log2(e)
+    int32_t off[FSA_MAX_OFFSETS];
+};
+
+hipError_t launch_forward(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_backward(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
+
+}  // namespace fsa

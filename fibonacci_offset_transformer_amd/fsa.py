@@ -1,0 +1,145 @@
+"""Python binding of libfsa (ctypes). Argument marshalling only: every step of
+the computation runs in the HIP library; torch supplies device memory and the
+current stream.
+
+Signatures mirror include/fsa.h: tensors are contiguous [B, H, N, 64] in
+float32 or bfloat16 on one GPU; LSE and the backward workspace are float32
+[B, H, N]. There is no CPU fallback: without the built library every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsa.so")
+
+FSA_OK, FSA_E_ARG, FSA_E_UNSUPPORTED, FSA_E_CAPACITY, FSA_E_HIP = range(5)
+STATUS_NAMES = {0: "FSA_OK", 1: "FSA_E_ARG", 2: "FSA_E_UNSUPPORTED", 3: "FSA_E_CAPACITY", 4: "FSA_E_HIP"}
+BASES = {"fib": 0, "pow2": 1}
+DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+MAX_OFFSETS = 48
+
+# Exported symbols, in the order include/fsa.h declares them.
+EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_dense_forward", "fsa_last_error")
+
+
+class FsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library() -> ctypes.CDLL:
+    """Loads libfsa.so from the package directory (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise FsaError(-1, f"{_LIB_PATH} is missing; build it with "
+                                   "`python -m fibonacci_offset_transformer_amd.build`")
+            L = ctypes.CDLL(_LIB_PATH)
+            i32, f32, f64, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+            L.fsa_build_offsets.argtypes = [ctypes.c_int, f64, i32, i32, ctypes.POINTER(i32), i32,
+                                            ctypes.POINTER(i32)]
+            L.fsa_build_offsets.restype = ctypes.c_int
+            L.fsa_forward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                      ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_forward.restype = ctypes.c_int
+            L.fsa_backward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_backward.restype = ctypes.c_int
+            L.fsa_dense_forward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+            L.fsa_dense_forward.restype = ctypes.c_int
+            L.fsa_last_error.argtypes = []
+            L.fsa_last_error.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != FSA_OK:
+        raise FsaError(status, library().fsa_last_error().decode())
+
+
+def build_offsets(alpha: float, w: int, R: int, base: str = "fib") -> list[int]:
+    """Sparse offset table of one layer (host call; see fsa_build_offsets)."""
+    L = library()
+    out = (ctypes.c_int32 * MAX_OFFSETS)()
+    count = ctypes.c_int32(0)
+    _check(L.fsa_build_offsets(BASES[base], float(alpha), int(w), int(R), out, MAX_OFFSETS,
+                               ctypes.byref(count)))
+    return [int(out[t]) for t in range(count.value)]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _shape(q: torch.Tensor, *others: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    if q.dtype not in DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    for t in (q,) + others:
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("all tensors must share shape, dtype and device")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous CUDA/HIP tensors")
+    return q.shape
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def forward(q, k, v, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None,
+            out=None, lse=None):
+    """Sparse forward: returns (o [B,H,N,d] in q.dtype, lse [B,H,N] float32)."""
+    B, H, N, d = _shape(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        _check(library().fsa_forward(DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
+                                     B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
+                                     int(R), _stream(q.device)))
+    return o, l
+
+
+def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
+             scale=None, dq=None, dk=None, dv=None, delta=None):
+    """Sparse backward: returns (dq, dk, dv) in q.dtype."""
+    B, H, N, d = _shape(q, k, v, o, dout)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    with torch.cuda.device(q.device):
+        _check(library().fsa_backward(DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), B, H, N, d,
+                                      _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                                      _stream(q.device)))
+    return dq, dk, dv
+
+
+def dense_forward(q, k, v, *, scale=None, out=None, lse=None):
+    """Dense causal baseline: returns (o, lse)."""
+    B, H, N, d = _shape(q, k, v)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        _check(library().fsa_dense_forward(DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
+                                           B, H, N, d, _scale(scale, d), _stream(q.device)))
+    return o, l

@@ -1,0 +1,142 @@
+/*
+ * fsa.h - C ABI of libfsa, Fibonacci-offset sparse attention for AMD MI355X (gfx950).
+ *
+ * The operation (cited from the explainer page "Depth-Staggered Fibonacci Spacing
+ * for Sparse Attention: Static Schedules Beat Learned Dilation and Extrapolate
+ * Where Dense Attention Fails", gist.science, Portuguese edition, section
+ * "Metodologia / Arquitetura e Mecanismo de Atenção"): causal attention in which
+ * query row i attends a dense local window of w keys (offsets 0..w-1, itself
+ * included) plus the keys i - round(alpha * F) for F in a base list (Fibonacci
+ * numbers 1, 2, 3, 5, ... or, for the power-of-2 control of section "Controles",
+ * 1, 2, 4, 8, ...), with one per-layer scalar alpha (item "Escalonamento").
+ * Static schedules run as one boolean mask (section "Principais Contribuições e
+ * Resultados", item 2), so every key is attended at most once and one softmax
+ * covers window and sparse keys together.
+ *
+ * Conventions shared by every call:
+ *  - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d] in
+ *    device memory, all of the call's dtype, each 16-byte aligned; d must be 64.
+ *  - LSE and the backward workspace are float32 [B, H, N] in device memory; LSE
+ *    is the natural-log row log-sum-exp of the scaled scores.
+ *  - Device buffers are owned by the caller. The library never allocates, frees
+ *    or synchronises; each call enqueues its kernels on `stream` (a hipStream_t,
+ *    NULL for the default stream) and returns without waiting. Faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Outputs are overwritten, never accumulated; outputs must not alias inputs.
+ *  - B, H or N equal to 0 is an empty problem: FSA_OK, nothing is launched.
+ *  - Arguments are validated before any HIP call; on any non-OK status nothing
+ *    has been enqueued and no output has been written. fsa_last_error() then
+ *    returns a text for the calling thread.
+ *  - Offset tables are rebuilt on the host on every call (a few dozen integer
+ *    operations) and passed to the kernels by value; the library keeps no global
+ *    state besides a thread-local error string. All calls are thread-safe.
+ */
+#ifndef FSA_H
+#define FSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FSA_OK = 0,
+    FSA_E_ARG = 1,          /* invalid argument (null pointer, bad size, alpha, w, R, alignment) */
+    FSA_E_UNSUPPORTED = 2,  /* valid but not implemented (head size other than 64, unknown dtype) */
+    FSA_E_CAPACITY = 3,     /* output array too small; *count holds the size needed */
+    FSA_E_HIP = 4           /* the HIP runtime refused a launch; see fsa_last_error() */
+} fsa_status_t;
+
+typedef enum { FSA_BASE_FIB = 0, FSA_BASE_POW2 = 1 } fsa_base_t;
+
+typedef enum { FSA_F32 = 0, FSA_BF16 = 1 } fsa_dtype_t;
+
+/* Largest number of sparse offsets any table can hold (Fibonacci values below 2^31). */
+#define FSA_MAX_OFFSETS 48
+
+/*
+ * fsa_build_offsets - the sparse offset table T of one layer, in host memory.
+ *
+ * T = sorted, duplicate-free { round(alpha * F) : F in base, F < R } restricted
+ * to values >= w (smaller ones already lie in the dense window). Base list:
+ * Fibonacci 1, 2, 3, 5, 8, ... (recurrence F_{k+1} = F_k + F_{k-1}; page section
+ * "Metodologia / Arquitetura e Mecanismo de Atenção", item "Conjunto Atendido")
+ * or powers of two 1, 2, 4, ... (section "Controles"). alpha * F is one IEEE
+ * double product, rounded half to even. R is exclusive and caps the base value
+ * before scaling, so scaled offsets may exceed R. T does not depend on N.
+ *
+ *   base      FSA_BASE_FIB or FSA_BASE_POW2
+ *   alpha     finite, > 0; alpha * F must round to at most 2^31 - 1
+ *   w         window size, >= 1
+ *   R         reach, >= 1
+ *   out       host array receiving T in increasing order (may be NULL if capacity == 0)
+ *   capacity  entries available in out
+ *   count     receives |T| (also on FSA_E_CAPACITY)
+ */
+fsa_status_t fsa_build_offsets(fsa_base_t base, double alpha, int32_t w, int32_t R,
+                               int32_t *out, int32_t capacity, int32_t *count);
+
+/*
+ * fsa_forward - sparse attention forward: O and LSE.
+ *
+ * For every (b, h) and row i < N:
+ *   J(i) = { i - o : o in {0..w-1} u T(base, alpha, w, R), i - o >= 0 }
+ *   s_ij = scale * <q_i, k_j>, P_ij = softmax_j(s_ij) over J(i),
+ *   o_i = sum_j P_ij v_j (written in the input dtype),
+ *   lse_i = ln sum_j exp(s_ij) (float32).
+ * Arithmetic: products and softmax in fp32 (bf16 inputs: bf16 MFMA for the
+ * window, probabilities rounded to bf16 for the window's P.V product).
+ *
+ *   dt              FSA_F32 or FSA_BF16 (dtype of q, k, v, o)
+ *   q, k, v         inputs [B,H,N,d]
+ *   o               output [B,H,N,d]
+ *   lse             output float32 [B,H,N]
+ *   scale           finite score scale (1/sqrt(d) in the usual setting)
+ *   base, alpha, w, R   offset table parameters as in fsa_build_offsets
+ *   stream          hipStream_t to enqueue on
+ */
+fsa_status_t fsa_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
+                         void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
+                         float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                         void *stream);
+
+/*
+ * fsa_backward - gradients of sum(dO * O) with respect to Q, K and V.
+ *
+ * The textbook softmax-attention gradient restricted to the same mask as
+ * fsa_forward (the pages train through this mask, section "Metodologia"):
+ *   D_i = <dO_i, o_i>, P_ij = exp(s_ij - lse_i), dS_ij = P_ij (<dO_i, v_j> - D_i),
+ *   dQ_i = scale sum_j dS_ij k_j, dK_j = scale sum_i dS_ij q_i, dV_j = sum_i P_ij dO_i.
+ * o and lse must be the outputs of fsa_forward for the same inputs and table.
+ * Every output row is written by exactly one workgroup (no atomics), so results
+ * are bitwise reproducible.
+ *
+ *   q, k, v, o, dout    inputs [B,H,N,d] of dtype dt
+ *   lse                 input float32 [B,H,N]
+ *   dq, dk, dv          outputs [B,H,N,d] of dtype dt
+ *   delta_ws            caller-owned float32 [B,H,N] workspace, overwritten with D
+ */
+fsa_status_t fsa_backward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
+                          const void *o, const float *lse, const void *dout,
+                          void *dq, void *dk, void *dv, float *delta_ws,
+                          int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                          fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
+
+/*
+ * fsa_dense_forward - dense causal attention baseline (every j <= i attended),
+ * the same architecture with full attention (page section "Controles").
+ * Arguments as in fsa_forward.
+ */
+fsa_status_t fsa_dense_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
+                               void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
+                               float scale, void *stream);
+
+/* Text describing the calling thread's last non-OK status ("" if none). */
+const char *fsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H */

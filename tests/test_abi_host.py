@@ -1,0 +1,188 @@
+"""Host-side checks of libfsa that need no GPU: the library loads, exports every
+symbol include/fsa.h declares, builds offset tables bit-exactly like the oracle,
+and rejects every invalid argument before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from fibonacci_offset_transformer_amd import fsa, schedules
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fsa.library()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fsa.h")).read()
+    return sorted(set(re.findall(r"\b(fsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_functions():
+    assert header_functions() == sorted(fsa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exported_symbols_are_c_linkage():
+    # nm -D lists the plain (unmangled) names
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", fsa._LIB_PATH], capture_output=True, text=True).stdout
+    names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in header_functions():
+        assert name in names, name
+
+
+def build(lib, base, alpha, w, R, capacity=fsa.MAX_OFFSETS):
+    out = (ctypes.c_int32 * max(capacity, 1))()
+    cnt = ctypes.c_int32(-7)
+    st = lib.fsa_build_offsets(fsa.BASES[base], alpha, w, R, out, capacity, ctypes.byref(cnt))
+    return st, [out[i] for i in range(min(cnt.value, capacity))] if st == 0 else None, cnt.value
+
+
+def alphas():
+    al = [0.5 + l / 15.0 for l in range(16)] + [0.5, 1.0, 1.5]
+    al += list(np.random.default_rng(2024).uniform(0.5, 1.5, 1000))
+    al += [0.25, 2.0, 3.7, 1e-3, 1e3]
+    return [float(a) for a in al]
+
+
+@pytest.mark.parametrize("base", ["fib", "pow2"])
+def test_tables_bit_exact_against_oracle(lib, base):
+    for a in alphas():
+        for w in (1, 6, 8, 10, 12, 16, 64):
+            for R in (1, 2, 256, 1024, 4096):
+                st, got, _ = build(lib, base, a, w, R)
+                assert st == fsa.FSA_OK
+                assert got == oracle.offset_table(base, a, w, R), (base, a, w, R)
+
+
+def test_golden_tables(lib):
+    assert build(lib, "fib", 1.0, 16, 256)[1] == [21, 34, 55, 89, 144, 233]
+    assert build(lib, "fib", 1.0, 64, 1024)[1] == [89, 144, 233, 377, 610, 987]
+    assert build(lib, "pow2", 1.0, 64, 1024)[1] == [64, 128, 256, 512]
+    assert build(lib, "fib", 1.0, 1, 1024)[1][:6] == [1, 2, 3, 5, 8, 13]
+
+
+def test_stagger_alphas_match_oracle_schedule():
+    ours = schedules.linear_stagger(16)
+    assert ours == [oracle.stagger_alpha(l) for l in range(16)]  # bitwise-equal doubles
+    assert schedules.coprime_stagger(16) == [ours[oracle.coprime_layer(l)] for l in range(16)]
+
+
+def test_ties_round_half_even(lib):
+    # alpha = 0.5: 0.5 * 233 = 116.5 -> 116 (even); 0.5 * 377 = 188.5 -> 188
+    assert build(lib, "fib", 0.5, 64, 1024)[1] == [72, 116, 188, 305, 494]
+    # alpha = 1.5: 1.5 * 987 = 1480.5 -> 1480
+    assert build(lib, "fib", 1.5, 64, 1024)[1][-1] == 1480
+
+
+def test_large_reach_and_max_table(lib):
+    st, got, cnt = build(lib, "fib", 1.0, 1, 2**31 - 1)
+    assert st == fsa.FSA_OK and got == oracle.offset_table("fib", 1.0, 1, 2**31 - 1)
+    assert cnt <= fsa.MAX_OFFSETS
+
+
+def test_capacity_error_reports_count(lib):
+    st, _, cnt = build(lib, "fib", 1.0, 64, 1024, capacity=3)
+    assert st == fsa.FSA_E_CAPACITY and cnt == 6
+    assert b"capacity" in lib.fsa_last_error()
+    st, _, cnt = build(lib, "fib", 1.0, 2000, 1024, capacity=0)  # empty table fits
+    assert st == fsa.FSA_OK and cnt == 0
+
+
+@pytest.mark.parametrize("base,alpha,w,R", [
+    (0, 0.0, 64, 1024), (0, -1.0, 64, 1024), (0, float("nan"), 64, 1024), (0, float("inf"), 64, 1024),
+    (0, 1.0, 0, 1024), (0, 1.0, -3, 1024), (0, 1.0, 64, 0), (0, 1.0, 64, -1), (7, 1.0, 64, 1024),
+    (0, 3.0, 1, 2**31 - 1),      # alpha * F overflows int32
+    (1, 1.0, 1, 2**31 - 1),      # fine: 2^30 * 1 fits ...
+])
+def test_build_offsets_argument_errors(lib, base, alpha, w, R):
+    out = (ctypes.c_int32 * 48)()
+    cnt = ctypes.c_int32(0)
+    st = lib.fsa_build_offsets(base, alpha, w, R, out, 48, ctypes.byref(cnt))
+    if (base, alpha, w, R) == (1, 1.0, 1, 2**31 - 1):
+        assert st == fsa.FSA_OK
+    else:
+        assert st == fsa.FSA_E_ARG
+        assert lib.fsa_last_error() != b""
+
+
+def test_build_offsets_null_count(lib):
+    out = (ctypes.c_int32 * 48)()
+    assert lib.fsa_build_offsets(0, 1.0, 64, 1024, out, 48, None) == fsa.FSA_E_ARG
+
+
+# ---- attention entry points: only paths that return before any HIP call ----
+
+P = ctypes.c_void_p
+FAKE = [P(0x10000 * (i + 1)) for i in range(12)]  # distinct, aligned, never dereferenced
+
+
+def fwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256):
+    p = ptrs or FAKE[:5]
+    return lib.fsa_forward(dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+
+
+def bwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256):
+    p = ptrs or FAKE[:10]
+    return lib.fsa_backward(dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+
+
+def dense(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125):
+    p = ptrs or FAKE[:5]
+    return lib.fsa_dense_forward(dt, *p, B, H, N, d, scale, None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, dense])
+def test_shape_and_dtype_errors(lib, call):
+    assert call(lib, d=32) == fsa.FSA_E_UNSUPPORTED
+    assert call(lib, d=0) == fsa.FSA_E_ARG
+    assert call(lib, dt=5) == fsa.FSA_E_UNSUPPORTED
+    assert call(lib, B=-1) == fsa.FSA_E_ARG
+    assert call(lib, N=-5) == fsa.FSA_E_ARG
+    assert call(lib, scale=float("nan")) == fsa.FSA_E_ARG
+    assert call(lib, scale=float("inf")) == fsa.FSA_E_ARG
+    assert call(lib, B=1 << 20, H=1 << 12, N=1 << 16) == fsa.FSA_E_ARG  # grid too large
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_table_errors_on_attention_calls(lib, call):
+    assert call(lib, alpha=0.0) == fsa.FSA_E_ARG
+    assert call(lib, alpha=float("nan")) == fsa.FSA_E_ARG
+    assert call(lib, w=0) == fsa.FSA_E_ARG
+    assert call(lib, R=0) == fsa.FSA_E_ARG
+    assert call(lib, base=9) == fsa.FSA_E_ARG
+
+
+@pytest.mark.parametrize("call,n", [(fwd, 5), (bwd, 10), (dense, 5)])
+def test_null_misaligned_and_aliased_pointers(lib, call, n):
+    for k in range(n):
+        ptrs = list(FAKE[:n])
+        ptrs[k] = P(0)
+        assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG
+        assert b"NULL" in lib.fsa_last_error()
+        ptrs[k] = P(FAKE[k].value + 8)
+        assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG
+        assert b"aligned" in lib.fsa_last_error()
+    ptrs = list(FAKE[:n])
+    ptrs[n - 1] = ptrs[0]  # an output aliasing q
+    assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG
+    assert b"aliases" in lib.fsa_last_error()
+
+
+@pytest.mark.parametrize("call,n", [(fwd, 5), (bwd, 10), (dense, 5)])
+def test_empty_problems_launch_nothing(lib, call, n):
+    nulls = [P(0)] * n
+    for B, H, N in ((0, 1, 64), (1, 0, 64), (1, 1, 0)):
+        assert call(lib, ptrs=nulls, B=B, H=H, N=N) == fsa.FSA_OK
+        assert lib.fsa_last_error() == b""

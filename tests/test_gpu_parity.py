@@ -1,0 +1,237 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: offset tables bit-exact; outputs within max-abs 1e-5 for float32 inputs
+and 1e-2 for bfloat16 inputs (fp32 accumulation), the tolerances the method's
+build target states. Small cases compare every output; full-size workloads
+compare whole sampled heads (the oracle is run on that head alone)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fibonacci_offset_transformer_amd import fsa, schedules, synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 1e-2}
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def inputs(workload, layer, shape, dtype, grad=False):
+    t = synth.layer_inputs(workload, layer, shape, dtype, with_grad=grad)
+    return {k: v.to(dev()) for k, v in t.items()}
+
+
+def maxabs(gpu, ref):
+    return float(np.max(np.abs(synth.as_f64(gpu) - ref))) if ref.size else 0.0
+
+
+def check(name, gpu, ref, tol):
+    err = maxabs(gpu, ref)
+    note(f"  {name}: max|err|={err:.3e} max|ref|={float(np.max(np.abs(ref))) if ref.size else 0:.3f} tol={tol}")
+    assert err <= tol, (name, err)
+
+
+def fwd_case(workload, B, H, N, dtype, base, alpha, w, R, heads=None, layer=0):
+    scale = 1.0 / math.sqrt(64)
+    x = inputs(workload, layer, (B, H, N, 64), dtype)
+    note(f"forward wl={workload} layer={layer} {dtype} B={B} H={H} N={N} base={base} alpha={alpha} w={w} R={R}")
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], alpha=alpha, w=w, R=R, base=base, scale=scale)
+    torch.cuda.synchronize()
+    T = oracle.offset_table(base, alpha, w, R)
+    assert fsa.build_offsets(alpha, w, R, base) == T
+    sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in sel:
+        q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.sparse_forward(q, k, v, T, w, scale)
+        check(f"o[{b},{h}]", o[b, h], ro, TOL[dtype])
+        check(f"lse[{b},{h}]", lse[b, h], rl, 1e-4 if dtype == torch.bfloat16 else 1e-5)
+    return x, o, lse
+
+
+def bwd_case(workload, B, H, N, dtype, base, alpha, w, R, heads=None, layer=0):
+    scale = 1.0 / math.sqrt(64)
+    x = inputs(workload, layer, (B, H, N, 64), dtype, grad=True)
+    note(f"backward wl={workload} layer={layer} {dtype} B={B} H={H} N={N} base={base} alpha={alpha} w={w} R={R}")
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], alpha=alpha, w=w, R=R, base=base, scale=scale)
+    dq, dk, dv = fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], alpha=alpha, w=w, R=R, base=base,
+                              scale=scale)
+    torch.cuda.synchronize()
+    T = oracle.offset_table(base, alpha, w, R)
+    sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in sel:
+        q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
+        rq, rk, rv = oracle.sparse_backward(q, k, v, do, T, w, scale)
+        check(f"dq[{b},{h}]", dq[b, h], rq, TOL[dtype])
+        check(f"dk[{b},{h}]", dk[b, h], rk, TOL[dtype])
+        check(f"dv[{b},{h}]", dv[b, h], rv, TOL[dtype])
+    return x, (o, lse), (dq, dk, dv)
+
+
+# ---------------------------------------------------------------- small, exhaustive
+
+SMALL = [
+    # (N, base, alpha, w, R)
+    (1, "fib", 1.0, 16, 256),
+    (17, "fib", 1.0, 16, 256),
+    (100, "fib", 1.0, 6, 256),
+    (300, "fib", 1.0, 16, 256),
+    (300, "fib", 0.5, 8, 256),
+    (300, "fib", 1.5, 12, 256),
+    (300, "fib", 1.0, 64, 1024),
+    (300, "pow2", 1.0, 10, 1024),
+    (300, "fib", 1.0, 100, 256),     # window wider than a tile
+    (257, "fib", 1.0, 1, 1024),      # no window besides self, every Fibonacci offset
+    (130, "fib", 1.0, 300, 1024),    # window covers the whole sequence (dense)
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N,base,alpha,w,R", SMALL)
+def test_forward_small(dtype, N, base, alpha, w, R):
+    fwd_case(11, 1, 2, N, dtype, base, alpha, w, R)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("N,base,alpha,w,R", SMALL)
+def test_backward_small(dtype, N, base, alpha, w, R):
+    bwd_case(12, 1, 2, N, dtype, base, alpha, w, R)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_window_one_empty_table_returns_v(dtype):
+    x = inputs(13, 0, (2, 3, 150, 64), dtype)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], alpha=1.0, w=1, R=1, scale=0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o, x["v"])
+    ref = 0.125 * (x["q"].double() * x["k"].double()).sum(-1)
+    assert float((lse.double() - ref).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_wide_window_equals_dense_kernel_and_oracle(dtype):
+    x = inputs(14, 0, (1, 2, 200, 64), dtype)
+    o, l = fsa.forward(x["q"], x["k"], x["v"], alpha=1.0, w=200, R=1024, scale=0.125)
+    od, ld = fsa.dense_forward(x["q"], x["k"], x["v"], scale=0.125)
+    torch.cuda.synchronize()
+    for h in range(2):
+        q, k, v = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.dense_forward(q, k, v, 0.125)
+        check(f"dense o[{h}]", od[0, h], ro, TOL[dtype])
+        check(f"dense lse[{h}]", ld[0, h], rl, 1e-4)
+        check(f"wide o[{h}]", o[0, h], ro, TOL[dtype])
+
+
+def test_empty_problem_is_noop():
+    q = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device=dev())
+    o, l = fsa.forward(q, q.clone(), q.clone(), alpha=1.0, w=64, R=1024)
+    assert o.shape == q.shape and l.shape == (2, 3, 0)
+
+
+def test_unsupported_head_size_raises():
+    q = torch.zeros((1, 1, 16, 32), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.forward(q, q.clone(), q.clone(), alpha=1.0, w=64, R=1024)
+    assert e.value.status == fsa.FSA_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+def test_workload1_single_head_fp32():
+    # fp32 [1,1,256,64], w=16, alpha=1, R=256, forward
+    fwd_case(1, 1, 1, 256, torch.float32, "fib", 1.0, 16, 256)
+
+
+def test_workload2_one_layer_bf16():
+    # bf16 [8,8,1024,64], w=64, alpha=1, R=1024, forward; every head compared
+    fwd_case(2, 8, 8, 1024, torch.bfloat16, "fib", 1.0, 64, 1024)
+
+
+def test_workload3_sixteen_layer_stagger_forward():
+    alphas = schedules.linear_stagger(16)
+    rng = np.random.default_rng(3)
+    for l, a in enumerate(alphas):
+        b, h = (int(z) for z in rng.integers(0, 8, 2))
+        fwd_case(3, 8, 8, 1024, torch.bfloat16, "fib", a, 64, 1024, heads=[(b, h)], layer=l)
+
+
+def test_workload4_training_step_at_4096():
+    alphas = schedules.linear_stagger(16)
+    rng = np.random.default_rng(4)
+    for l in range(16):
+        b, h = int(rng.integers(0, 2)), int(rng.integers(0, 8))
+        x, (o, lse), _ = bwd_case(4, 2, 8, 4096, torch.bfloat16, "fib", alphas[l], 64, 1024,
+                                  heads=[(b, h)], layer=l)
+        q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.sparse_forward(q, k, v, oracle.offset_table("fib", alphas[l], 64, 1024), 64, 0.125)
+        check("o", o[b, h], ro, 1e-2)
+
+
+def test_workload4_dense_baseline_sampled_rows():
+    x = inputs(4, 0, (2, 8, 4096, 64), torch.bfloat16)
+    od, ld = fsa.dense_forward(x["q"], x["k"], x["v"], scale=0.125)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 63, 64, 1000, 2047, 4000, 4095])
+    for b, h in ((0, 0), (1, 7)):
+        q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.dense_forward_rows(q, k, v, 0.125, rows)
+        check(f"dense o[{b},{h}] rows", od[b, h][rows], ro, 1e-2)
+        check(f"dense lse[{b},{h}] rows", ld[b, h][rows], rl, 1e-4)
+
+
+def test_workload5_long_context_pow2():
+    bwd_case(5, 1, 8, 32768, torch.bfloat16, "pow2", 1.0, 64, 1024, heads=[(0, 3)])
+
+
+# ---------------------------------------------------------------- properties
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_bitwise_deterministic(dtype):
+    x = inputs(15, 0, (2, 4, 1000, 64), dtype, grad=True)
+    kw = dict(alpha=1.5, w=64, R=1024, scale=0.125)
+    a = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    b = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    ga = fsa.backward(x["q"], x["k"], x["v"], a[0], a[1], x["do"], **kw)
+    gb = fsa.backward(x["q"], x["k"], x["v"], a[0], a[1], x["do"], **kw)
+    torch.cuda.synchronize()
+    for u, v in zip(a + ga, b + gb):
+        assert torch.equal(u, v)
+
+
+def test_prefix_rows_unchanged_when_sequence_grows():
+    # rows < 1024 of an N=4096 run equal an N=1024 run on the prefix (1024 -> 4096 protocol)
+    x = inputs(16, 0, (1, 4, 4096, 64), torch.bfloat16)
+    kw = dict(alpha=1.0, w=64, R=1024, scale=0.125)
+    o, l = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    p = {t: x[t][:, :, :1024].contiguous() for t in ("q", "k", "v")}
+    op, lp = fsa.forward(p["q"], p["k"], p["v"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, :1024], op)
+    assert torch.equal(l[:, :, :1024], lp)
+
+
+def test_outputs_leave_guard_bands_untouched():
+    x = inputs(17, 0, (1, 2, 333, 64), torch.bfloat16, grad=True)
+    n = x["q"].numel()
+    canary = 12345.0
+    big = torch.full((n + 2048,), canary, dtype=torch.bfloat16, device=dev())
+    o = big[1024:1024 + n].view(x["q"].shape)
+    lbig = torch.full((666 + 2048,), canary, dtype=torch.float32, device=dev())
+    lse = lbig[1024:1024 + 666].view(1, 2, 333)
+    fsa.forward(x["q"], x["k"], x["v"], alpha=1.0, w=64, R=1024, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool((big[:1024] == canary).all()) and bool((big[1024 + n:] == canary).all())
+    assert bool((lbig[:1024] == canary).all()) and bool((lbig[1024 + 666:] == canary).all())
