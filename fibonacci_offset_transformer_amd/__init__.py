@@ -7,6 +7,8 @@ from .fsa import (  # noqa: F401
     EXPORTS,
     FsaError,
     backward,
+    backward_delta,
+    backward_grads,
     build_offsets,
     dense_forward,
     forward,

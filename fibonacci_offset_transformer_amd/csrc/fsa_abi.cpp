@@ -114,9 +114,11 @@ struct Shape {
 };
 
 // Shape, dtype and scale checks common to every attention call.
-fsa_status_t check_common(fsa_dtype_t dt, const Shape &s, float scale) {
+fsa_status_t check_common(fsa_dtype_t dt, fsa_dtype_t out_dt, const Shape &s, float scale) {
     if (dt != FSA_F32 && dt != FSA_BF16)
         return fail(FSA_E_UNSUPPORTED, "unsupported dtype %d", static_cast<int>(dt));
+    if (out_dt != FSA_F32 && out_dt != FSA_BF16)
+        return fail(FSA_E_UNSUPPORTED, "unsupported output dtype %d", static_cast<int>(out_dt));
     if (s.B < 0 || s.H < 0 || s.N < 0)
         return fail(FSA_E_ARG, "negative size B=%d H=%d N=%d", s.B, s.H, s.N);
     if (s.d < 1) return fail(FSA_E_ARG, "head size d must be >= 1 (got %d)", s.d);
@@ -181,11 +183,11 @@ fsa_status_t fsa_build_offsets(fsa_base_t base, double alpha, int32_t w, int32_t
     return ok();
 }
 
-fsa_status_t fsa_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v, void *o,
+fsa_status_t fsa_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v, void *o,
                          float *lse, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
                          fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream) {
     const Shape s{B, H, N, d};
-    fsa_status_t st = check_common(dt, s, scale);
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
     if (st != FSA_OK) return st;
     fsa::AttnParams p{};
     const int n_off = build_table(base, alpha, w, R, p.off, &st);
@@ -206,49 +208,109 @@ fsa_status_t fsa_forward(fsa_dtype_t dt, const void *q, const void *k, const voi
     p.n_off = trim_offsets(p.off, n_off, N);
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-    return launched(fsa::launch_forward(dt, p, static_cast<hipStream_t>(stream)), "forward");
+    return launched(fsa::launch_forward(dt, out_dt, p, static_cast<hipStream_t>(stream)), "forward");
 }
 
-fsa_status_t fsa_backward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
-                          const void *o, const float *lse, const void *dout, void *dq, void *dk,
-                          void *dv, float *delta_ws, int32_t B, int32_t H, int32_t N, int32_t d,
-                          float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
-                          void *stream) {
+fsa_status_t fsa_backward_delta(fsa_dtype_t dt, const void *o, const void *dout, float *delta_ws,
+                                int32_t B, int32_t H, int32_t N, int32_t d, void *stream) {
     const Shape s{B, H, N, d};
-    fsa_status_t st = check_common(dt, s, scale);
+    fsa_status_t st = check_common(dt, dt, s, 1.0f);
     if (st != FSA_OK) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"o", "dout", "delta_ws"};
+    const void *ptrs[] = {o, dout, delta_ws};
+    if ((st = check_ptrs(names, ptrs, 3)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 2, 3)) != FSA_OK) return st;
     fsa::AttnParams p{};
+    p.o = o;
+    p.dout = dout;
+    p.delta = delta_ws;
+    p.bh = B * H;
+    p.n = N;
+    return launched(fsa::launch_backward_delta(dt, p, static_cast<hipStream_t>(stream)), "backward delta");
+}
+
+namespace {
+
+// Validates the arguments of the gradient stage and fills its kernel parameters.
+fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
+                           const void *k, const void *v, const float *lse, const void *dout,
+                           const float *delta, void *dq, void *dk, void *dv, int32_t B, int32_t H,
+                           int32_t N, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
+                           int32_t R, bool *empty) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
+    if (st != FSA_OK) return st;
     const int n_off = build_table(base, alpha, w, R, p.off, &st);
     if (n_off < 0) return st;
-    if (static_cast<int64_t>(B) * H * N == 0) return ok();
-    const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta_ws"};
-    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta_ws};
-    if ((st = check_ptrs(names, ptrs, 10)) != FSA_OK) return st;
-    if ((st = check_no_alias(names, ptrs, 6, 10)) != FSA_OK) return st;
+    *empty = static_cast<int64_t>(B) * H * N == 0;
+    if (*empty) return FSA_OK;
+    const char *names[] = {"q", "k", "v", "lse", "dout", "delta", "dq", "dk", "dv"};
+    const void *ptrs[] = {q, k, v, lse, dout, delta, dq, dk, dv};
+    if ((st = check_ptrs(names, ptrs, 9)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 6, 9)) != FSA_OK) return st;
     p.q = q;
     p.k = k;
     p.v = v;
-    p.o = o;
     p.lse_in = lse;
     p.dout = dout;
+    p.delta = const_cast<float *>(delta);
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
-    p.delta = delta_ws;
     p.bh = B * H;
     p.n = N;
     p.w = w;
     p.n_off = trim_offsets(p.off, n_off, N);
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-    return launched(fsa::launch_backward(dt, p, static_cast<hipStream_t>(stream)), "backward");
+    return FSA_OK;
 }
 
-fsa_status_t fsa_dense_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
+}  // namespace
+
+fsa_status_t fsa_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                                const void *v, const float *lse, const void *dout,
+                                const float *delta, void *dq, void *dk, void *dv, int32_t B,
+                                int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base,
+                                double alpha, int32_t w, int32_t R, void *stream) {
+    fsa::AttnParams p{};
+    bool empty = false;
+    fsa_status_t st = prepare_grads(p, dt, out_dt, q, k, v, lse, dout, delta, dq, dk, dv, B, H, N, d,
+                                    scale, base, alpha, w, R, &empty);
+    if (st != FSA_OK) return st;
+    if (empty) return ok();
+    return launched(fsa::launch_backward_grads(dt, out_dt, p, static_cast<hipStream_t>(stream)),
+                    "backward grads");
+}
+
+fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                          const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                          void *dv, float *delta_ws, int32_t B, int32_t H, int32_t N, int32_t d,
+                          float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                          void *stream) {
+    fsa::AttnParams p{};
+    bool empty = false;
+    fsa_status_t st = prepare_grads(p, dt, out_dt, q, k, v, lse, dout, delta_ws, dq, dk, dv, B, H, N,
+                                    d, scale, base, alpha, w, R, &empty);
+    if (st != FSA_OK) return st;
+    if (empty) return ok();
+    // delta_ws is written here, so it must not alias any input either
+    const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta_ws"};
+    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta_ws};
+    if ((st = check_ptrs(names, ptrs, 10)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 6, 10)) != FSA_OK) return st;
+    p.o = o;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if ((st = launched(fsa::launch_backward_delta(dt, p, hs), "backward delta")) != FSA_OK) return st;
+    return launched(fsa::launch_backward_grads(dt, out_dt, p, hs), "backward grads");
+}
+
+fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
                                void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
                                float scale, void *stream) {
     const Shape s{B, H, N, d};
-    fsa_status_t st = check_common(dt, s, scale);
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
     if (st != FSA_OK) return st;
     if (static_cast<int64_t>(B) * H * N == 0) return ok();
     const char *names[] = {"q", "k", "v", "o", "lse"};
@@ -268,7 +330,7 @@ fsa_status_t fsa_dense_forward(fsa_dtype_t dt, const void *q, const void *k, con
     p.n_off = 0;
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-    return launched(fsa::launch_forward(dt, p, static_cast<hipStream_t>(stream)), "dense forward");
+    return launched(fsa::launch_forward(dt, out_dt, p, static_cast<hipStream_t>(stream)), "dense forward");
 }
 
 const char *fsa_last_error(void) { return g_last_error.c_str(); }

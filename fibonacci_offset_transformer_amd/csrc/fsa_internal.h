@@ -33,7 +33,8 @@ struct AttnParams {
     int32_t off[FSA_MAX_OFFSETS];
 };
 
-hipError_t launch_forward(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
-hipError_t launch_backward(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 
 }  // namespace fsa

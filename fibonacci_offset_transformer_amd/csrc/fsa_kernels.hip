@@ -264,9 +264,10 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 // forward
 // ----------------------------------------------------------------------------
 
-template <bool BF16>
+template <bool BF16, bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
+    using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) E vt[64 * kLdsRow];  // V^T of one 64-key chunk
 
     const int n = p.n, w = p.w;
@@ -378,7 +379,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     // ---- epilogue ----
     const float l = group_sum(lsum);
     if (row_ok) {
-        store_row(static_cast<E *>(p.out) + head, i, g, acc, 1.f / l);
+        store_row(static_cast<OE *>(p.out) + head, i, g, acc, 1.f / l);
         if (g == 0) p.lse_out[(int64_t)bh * n + i] = m * kLn2 + logf(l);
     }
 }
@@ -417,9 +418,10 @@ __global__ void __launch_bounds__(kThreads) delta_kernel(const AttnParams p) {
 // backward: dQ (query-owned) then dK, dV (key-owned) of one 64-row tile
 // ----------------------------------------------------------------------------
 
-template <bool BF16>
+template <bool BF16, bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
+    using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) E t0s[64 * kLdsRow];  // transposed tile (K^T, or Q^T)
     __shared__ __attribute__((aligned(16))) E t1s[64 * kLdsRow];  // transposed tile (dO^T)
     __shared__ float lse_s[64], del_s[64];
@@ -498,7 +500,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                 frag_axpy(acc, pv * (dp - di), kf);
             }
         }
-        if (row_ok) store_row(static_cast<E *>(p.dq) + head, i, g, acc, p.scale);
+        if (row_ok) store_row(static_cast<OE *>(p.dq) + head, i, g, acc, p.scale);
     }
 
     // ========================= dK, dV of key rows ==========================
@@ -572,42 +574,57 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
             }
         }
         if (key_ok) {
-            store_row(static_cast<E *>(p.dk) + head, j, g, dk, p.scale);
-            store_row(static_cast<E *>(p.dv) + head, j, g, dv, 1.f);
+            store_row(static_cast<OE *>(p.dk) + head, j, g, dk, p.scale);
+            store_row(static_cast<OE *>(p.dv) + head, j, g, dv, 1.f);
         }
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool OUT_BF16>
 hipError_t launch_forward_t(const AttnParams &p, hipStream_t stream) {
     const int nt = (p.n + 63) / 64;
     const dim3 grid(p.bh * nt), block(kThreads);
     AttnParams a = p;
     void *args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<BF16>), grid, block, args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<BF16, OUT_BF16>), grid, block, args, 0,
+                           stream);
 }
 
 template <bool BF16>
-hipError_t launch_backward_t(const AttnParams &p, hipStream_t stream) {
+hipError_t launch_delta_t(const AttnParams &p, hipStream_t stream) {
     AttnParams a = p;
     void *args[] = {&a};
     const int64_t rows = (int64_t)p.bh * p.n;
-    const dim3 gd((unsigned)((rows + 15) / 16)), block(kThreads);
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&delta_kernel<BF16>), gd, block, args, 0, stream);
-    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((rows + 15) / 16)), block(kThreads);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&delta_kernel<BF16>), grid, block, args, 0, stream);
+}
+
+template <bool BF16, bool OUT_BF16>
+hipError_t launch_grads_t(const AttnParams &p, hipStream_t stream) {
+    AttnParams a = p;
+    void *args[] = {&a};
     const int nt = (p.n + 63) / 64;
-    const dim3 grid(p.bh * nt);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_kernel<BF16>), grid, block, args, 0, stream);
+    const dim3 grid(p.bh * nt), block(kThreads);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_kernel<BF16, OUT_BF16>), grid, block, args, 0,
+                           stream);
 }
 
 }  // namespace
 
-hipError_t launch_forward(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream) {
-    return dt == FSA_BF16 ? launch_forward_t<true>(p, stream) : launch_forward_t<false>(p, stream);
+hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
+    if (dt == FSA_BF16)
+        return out_dt == FSA_BF16 ? launch_forward_t<true, true>(p, stream) : launch_forward_t<true, false>(p, stream);
+    return out_dt == FSA_BF16 ? launch_forward_t<false, true>(p, stream) : launch_forward_t<false, false>(p, stream);
 }
 
-hipError_t launch_backward(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream) {
-    return dt == FSA_BF16 ? launch_backward_t<true>(p, stream) : launch_backward_t<false>(p, stream);
+hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream) {
+    return dt == FSA_BF16 ? launch_delta_t<true>(p, stream) : launch_delta_t<false>(p, stream);
+}
+
+hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
+    if (dt == FSA_BF16)
+        return out_dt == FSA_BF16 ? launch_grads_t<true, true>(p, stream) : launch_grads_t<true, false>(p, stream);
+    return out_dt == FSA_BF16 ? launch_grads_t<false, true>(p, stream) : launch_grads_t<false, false>(p, stream);
 }
 
 }  // namespace fsa

@@ -25,7 +25,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 MAX_OFFSETS = 48
 
 # Exported symbols, in the order include/fsa.h declares them.
-EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_dense_forward", "fsa_last_error")
+EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_delta", "fsa_backward_grads",
+           "fsa_dense_forward", "fsa_last_error")
 
 
 class FsaError(RuntimeError):
@@ -51,13 +52,18 @@ def library() -> ctypes.CDLL:
             L.fsa_build_offsets.argtypes = [ctypes.c_int, f64, i32, i32, ctypes.POINTER(i32), i32,
                                             ctypes.POINTER(i32)]
             L.fsa_build_offsets.restype = ctypes.c_int
-            L.fsa_forward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+            L.fsa_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
                                       ctypes.c_int, f64, i32, i32, vp]
             L.fsa_forward.restype = ctypes.c_int
-            L.fsa_backward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+            L.fsa_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                        i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
             L.fsa_backward.restype = ctypes.c_int
-            L.fsa_dense_forward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
+            L.fsa_backward_delta.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, vp]
+            L.fsa_backward_delta.restype = ctypes.c_int
+            L.fsa_backward_grads.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_backward_grads.restype = ctypes.c_int
+            L.fsa_dense_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
             L.fsa_dense_forward.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
             L.fsa_last_error.restype = ctypes.c_char_p
@@ -105,41 +111,77 @@ def _scale(scale, d):
     return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
 
 
+def _out(like, out, out_dtype):
+    if out is None:
+        return torch.empty_like(like, dtype=out_dtype or like.dtype)
+    if out.shape != like.shape or not out.is_contiguous() or out.device != like.device:
+        raise ValueError("output must be a contiguous tensor of the input shape on the same device")
+    if out_dtype is not None and out.dtype != out_dtype:
+        raise ValueError("output dtype does not match out_dtype")
+    return out
+
+
 def forward(q, k, v, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None,
-            out=None, lse=None):
-    """Sparse forward: returns (o [B,H,N,d] in q.dtype, lse [B,H,N] float32)."""
+            out=None, lse=None, out_dtype=None):
+    """Sparse forward: returns (o [B,H,N,d] in out_dtype (default q.dtype), lse [B,H,N] float32)."""
     B, H, N, d = _shape(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    o = _out(q, out, out_dtype)
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
-        _check(library().fsa_forward(DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
+        _check(library().fsa_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
                                      B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
                                      int(R), _stream(q.device)))
     return o, l
 
 
 def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
-             scale=None, dq=None, dk=None, dv=None, delta=None):
-    """Sparse backward: returns (dq, dk, dv) in q.dtype."""
+             scale=None, dq=None, dk=None, dv=None, delta=None, out_dtype=None):
+    """Sparse backward: returns (dq, dk, dv) in out_dtype (default q.dtype).
+    q, k, v, o and dout share one dtype."""
     B, H, N, d = _shape(q, k, v, o, dout)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    dq = _out(q, dq, out_dtype)
+    dk = _out(q, dk, dq.dtype)
+    dv = _out(q, dv, dq.dtype)
     ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
     with torch.cuda.device(q.device):
-        _check(library().fsa_backward(DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+        _check(library().fsa_backward(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                       _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), B, H, N, d,
                                       _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
                                       _stream(q.device)))
     return dq, dk, dv
 
 
-def dense_forward(q, k, v, *, scale=None, out=None, lse=None):
+def backward_delta(o, dout, *, delta=None):
+    """First backward stage: D = rowsum(dout * o), float32 [B, H, N]."""
+    B, H, N, d = _shape(o, dout)
+    ws = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if delta is None else delta
+    with torch.cuda.device(o.device):
+        _check(library().fsa_backward_delta(DTYPES[o.dtype], _ptr(o), _ptr(dout), _ptr(ws), B, H, N, d,
+                                            _stream(o.device)))
+    return ws
+
+
+def backward_grads(q, k, v, lse, dout, delta, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
+                   scale=None, dq=None, dk=None, dv=None, out_dtype=None):
+    """Second backward stage: (dq, dk, dv) from a D computed by backward_delta."""
+    B, H, N, d = _shape(q, k, v, dout)
+    dq = _out(q, dq, out_dtype)
+    dk = _out(q, dk, dq.dtype)
+    dv = _out(q, dv, dq.dtype)
+    with torch.cuda.device(q.device):
+        _check(library().fsa_backward_grads(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v),
+                                            _ptr(lse), _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                            B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
+                                            int(R), _stream(q.device)))
+    return dq, dk, dv
+
+
+def dense_forward(q, k, v, *, scale=None, out=None, lse=None, out_dtype=None):
     """Dense causal baseline: returns (o, lse)."""
     B, H, N, d = _shape(q, k, v)
-    o = torch.empty_like(q) if out is None else out
+    o = _out(q, out, out_dtype)
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     with torch.cuda.device(q.device):
-        _check(library().fsa_dense_forward(DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
+        _check(library().fsa_dense_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
                                            B, H, N, d, _scale(scale, d), _stream(q.device)))
     return o, l

@@ -15,7 +15,11 @@
  *
  * Conventions shared by every call:
  *  - Tensors Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d] in
- *    device memory, all of the call's dtype, each 16-byte aligned; d must be 64.
+ *    device memory, each 16-byte aligned; d must be 64. Inputs Q, K, V (and, in
+ *    the backward, O and dO) have the input dtype `dt`; the outputs O (forward)
+ *    and dQ, dK, dV (backward) have the output dtype `out_dt`. Arithmetic does
+ *    not depend on out_dt: a bf16 output is the round-to-nearest-even image of
+ *    the float32 output of the same call.
  *  - LSE and the backward workspace are float32 [B, H, N] in device memory; LSE
  *    is the natural-log row log-sum-exp of the scaled scores.
  *  - Device buffers are owned by the caller. The library never allocates, frees
@@ -83,12 +87,13 @@ fsa_status_t fsa_build_offsets(fsa_base_t base, double alpha, int32_t w, int32_t
  * For every (b, h) and row i < N:
  *   J(i) = { i - o : o in {0..w-1} u T(base, alpha, w, R), i - o >= 0 }
  *   s_ij = scale * <q_i, k_j>, P_ij = softmax_j(s_ij) over J(i),
- *   o_i = sum_j P_ij v_j (written in the input dtype),
+ *   o_i = sum_j P_ij v_j (written in out_dt),
  *   lse_i = ln sum_j exp(s_ij) (float32).
  * Arithmetic: products and softmax in fp32 (bf16 inputs: bf16 MFMA for the
  * window, probabilities rounded to bf16 for the window's P.V product).
  *
- *   dt              FSA_F32 or FSA_BF16 (dtype of q, k, v, o)
+ *   dt              FSA_F32 or FSA_BF16: dtype of q, k, v
+ *   out_dt          FSA_F32 or FSA_BF16: dtype of o
  *   q, k, v         inputs [B,H,N,d]
  *   o               output [B,H,N,d]
  *   lse             output float32 [B,H,N]
@@ -96,8 +101,8 @@ fsa_status_t fsa_build_offsets(fsa_base_t base, double alpha, int32_t w, int32_t
  *   base, alpha, w, R   offset table parameters as in fsa_build_offsets
  *   stream          hipStream_t to enqueue on
  */
-fsa_status_t fsa_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
-                         void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
+fsa_status_t fsa_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                         const void *v, void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
                          float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
                          void *stream);
 
@@ -112,24 +117,42 @@ fsa_status_t fsa_forward(fsa_dtype_t dt, const void *q, const void *k, const voi
  * Every output row is written by exactly one workgroup (no atomics), so results
  * are bitwise reproducible.
  *
- *   q, k, v, o, dout    inputs [B,H,N,d] of dtype dt
+ *   dt                  dtype of q, k, v, o, dout
+ *   out_dt              dtype of dq, dk, dv
+ *   q, k, v, o, dout    inputs [B,H,N,d]
  *   lse                 input float32 [B,H,N]
- *   dq, dk, dv          outputs [B,H,N,d] of dtype dt
+ *   dq, dk, dv          outputs [B,H,N,d]
  *   delta_ws            caller-owned float32 [B,H,N] workspace, overwritten with D
  */
-fsa_status_t fsa_backward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
-                          const void *o, const float *lse, const void *dout,
+fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                          const void *v, const void *o, const float *lse, const void *dout,
                           void *dq, void *dk, void *dv, float *delta_ws,
                           int32_t B, int32_t H, int32_t N, int32_t d, float scale,
                           fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
+
+/*
+ * fsa_backward_delta and fsa_backward_grads - the two stages of fsa_backward,
+ * exposed so that a caller can schedule (or time) them separately.
+ * fsa_backward_delta writes D_i = <dO_i, o_i> (float32 [B,H,N]) into delta_ws;
+ * fsa_backward_grads then computes dQ, dK, dV from q, k, v, lse, dout and that
+ * D. fsa_backward(...) is exactly fsa_backward_delta followed by
+ * fsa_backward_grads on the same stream. Arguments as in fsa_backward.
+ */
+fsa_status_t fsa_backward_delta(fsa_dtype_t dt, const void *o, const void *dout, float *delta_ws,
+                                int32_t B, int32_t H, int32_t N, int32_t d, void *stream);
+fsa_status_t fsa_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                                const void *v, const float *lse, const void *dout,
+                                const float *delta, void *dq, void *dk, void *dv, int32_t B,
+                                int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base,
+                                double alpha, int32_t w, int32_t R, void *stream);
 
 /*
  * fsa_dense_forward - dense causal attention baseline (every j <= i attended),
  * the same architecture with full attention (page section "Controles").
  * Arguments as in fsa_forward.
  */
-fsa_status_t fsa_dense_forward(fsa_dtype_t dt, const void *q, const void *k, const void *v,
-                               void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
+fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
+                               const void *k, const void *v, void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
                                float scale, void *stream);
 
 /* Text describing the calling thread's last non-OK status ("" if none). */

@@ -128,19 +128,19 @@ P = ctypes.c_void_p
 FAKE = [P(0x10000 * (i + 1)) for i in range(12)]  # distinct, aligned, never dereferenced
 
 
-def fwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256):
+def fwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256, out_dt=1):
     p = ptrs or FAKE[:5]
-    return lib.fsa_forward(dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+    return lib.fsa_forward(dt, out_dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
 
 
-def bwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256):
+def bwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256, out_dt=1):
     p = ptrs or FAKE[:10]
-    return lib.fsa_backward(dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+    return lib.fsa_backward(dt, out_dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
 
 
-def dense(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125):
+def dense(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, out_dt=1):
     p = ptrs or FAKE[:5]
-    return lib.fsa_dense_forward(dt, *p, B, H, N, d, scale, None)
+    return lib.fsa_dense_forward(dt, out_dt, *p, B, H, N, d, scale, None)
 
 
 @pytest.mark.parametrize("call", [fwd, bwd, dense])
@@ -148,6 +148,7 @@ def test_shape_and_dtype_errors(lib, call):
     assert call(lib, d=32) == fsa.FSA_E_UNSUPPORTED
     assert call(lib, d=0) == fsa.FSA_E_ARG
     assert call(lib, dt=5) == fsa.FSA_E_UNSUPPORTED
+    assert call(lib, out_dt=3) == fsa.FSA_E_UNSUPPORTED
     assert call(lib, B=-1) == fsa.FSA_E_ARG
     assert call(lib, N=-5) == fsa.FSA_E_ARG
     assert call(lib, scale=float("nan")) == fsa.FSA_E_ARG
