@@ -72,40 +72,44 @@ def dense_flops_per_layer():
 
 # ---------------------------------------------------------------- CPU baseline (oracle)
 
-def _oracle_head(args):
-    import numpy as np  # noqa: F401
+_SAMPLE = []  # (q, k, v, dO, table) per sampled head; filled before the worker pool forks
+
+
+def _oracle_head(idx):
     import oracle
-    q, k, v, do, T = args
+    q, k, v, do, T = _SAMPLE[idx]
     oracle.sparse_forward(q, k, v, T, W, 1.0 / math.sqrt(D))
     oracle.sparse_backward(q, k, v, do, T, W, 1.0 / math.sqrt(D))
     return q.shape[0]
 
 
-def cpu_baseline(cpu_inputs, alphas, heads_per_core=2):
+def cpu_baseline(cpu_inputs, alphas, heads_per_core=8):
     """fp64 numpy oracle (sparse forward + backward) on sampled heads, one process per core."""
     import multiprocessing as mp
 
     import numpy as np
+    import torch
+
     import oracle
 
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     n_heads = cores * heads_per_core
     rng = np.random.default_rng(7)
-    tasks = []
+    _SAMPLE.clear()
     for t in range(n_heads):
         l = t % LAYERS
         b, h = int(rng.integers(0, B)), int(rng.integers(0, H))
         x = cpu_inputs[l]
         T = oracle.offset_table(BASE, alphas[l], W, R)
-        tasks.append(tuple(x[n][b, h].to(dtype=__import__("torch").float64).numpy()
-                           for n in ("q", "k", "v", "do")) + (T,))
+        _SAMPLE.append(tuple(x[n][b, h].to(torch.float64).numpy() for n in ("q", "k", "v", "do")) + (T,))
     os.environ["OMP_NUM_THREADS"] = "1"
     ctx = mp.get_context("fork")
     with ctx.Pool(cores) as pool:
-        pool.map(_oracle_head, tasks[:cores], chunksize=1)  # warm the workers (imports, caches)
+        pool.map(_oracle_head, range(cores), chunksize=1)  # warm the workers (imports, caches)
         t0 = time.perf_counter()
-        rows = sum(pool.map(_oracle_head, tasks, chunksize=1))
+        rows = sum(pool.map(_oracle_head, range(n_heads), chunksize=1))
         wall = time.perf_counter() - t0
+    _SAMPLE.clear()
     try:
         model = next(ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name"))
     except Exception:
@@ -117,7 +121,7 @@ def cpu_baseline(cpu_inputs, alphas, heads_per_core=2):
         "kind": "oracle",
         "sample": f"{n_heads} of {LAYERS * B * H} (layer, b, h) heads of the same workload, fp64 numpy "
                   f"sparse forward + backward at N={N}, {cores} single-threaded worker processes, "
-                  f"{wall:.2f} s wall; CPU: {model}",
+                  f"{wall:.2f} s wall ({wall * cores:.1f} core-seconds); CPU: {model}",
     }
 
 

@@ -330,7 +330,7 @@ fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     p.n_off = 0;
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-    return launched(fsa::launch_forward(dt, out_dt, p, static_cast<hipStream_t>(stream)), "dense forward");
+    return launched(fsa::launch_dense_forward(dt, out_dt, p, static_cast<hipStream_t>(stream)), "dense forward");
 }
 
 const char *fsa_last_error(void) { return g_last_error.c_str(); }

@@ -34,6 +34,7 @@ struct AttnParams {
 };
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 

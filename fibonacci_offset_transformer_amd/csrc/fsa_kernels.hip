@@ -52,7 +52,9 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
-constexpr int kLdsRow = 64 + 4;  // padded row of a transposed tile in LDS (elements)
+constexpr int kT64 = 64 + 4;    // padded LDS row (elements) of a transposed 64-row tile
+constexpr int kT128 = 128 + 4;  // padded LDS row (elements) of a transposed 128-row tile
+constexpr int kSlabRegs = 8;    // sparse offsets whose rows are prefetched into registers
 
 // ----------------------------------------------------------------------------
 // element types and row fragments
@@ -69,16 +71,18 @@ struct Elem<false> {
     using T = float;
 };
 
-// 16 elements of one row owned by lane group g: chunk s holds d = 16 s + 4 g + (0..3).
+// The 16 elements of one 64-wide row that lane group g (lanes 16g..16g+15) owns:
+// d = 32 h + 8 g + e for h in 0..1, e in 0..7, i.e. two 16-byte chunks in bf16.
+// Output accumulators use the same ownership: acc[2h + b][r] holds d = 32h + 8g + 4b + r.
 template <bool BF16>
 struct Frag;
 template <>
 struct Frag<true> {
-    u32x2_t c[4];
+    u32x4_t c[2];  // c[h] word w = elements e = 2w (low half), 2w + 1 (high half)
 };
 template <>
 struct Frag<false> {
-    f32x4_t c[4];
+    f32x4_t c[4];  // c[2h + e / 4][e % 4]
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
@@ -91,64 +95,89 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ float frag_elem(const Frag<true> &f, int s, int u) {
-    const uint32_t w = (u < 2) ? f.c[s].x : f.c[s].y;
-    return (u & 1) ? bf16_hi(w) : bf16_lo(w);
+__device__ __forceinline__ float frag_elem(const Frag<true> &f, int h, int e) {
+    const uint32_t w = f.c[h][e >> 1];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
 }
-__device__ __forceinline__ float frag_elem(const Frag<false> &f, int s, int u) { return f.c[s][u]; }
+__device__ __forceinline__ float frag_elem(const Frag<false> &f, int h, int e) { return f.c[2 * h + (e >> 2)][e & 3]; }
 
 // Loads row `row` of a [*, 64] matrix into lane group g's fragment.
 __device__ __forceinline__ void load_frag(Frag<true> &f, const uint16_t *base, int64_t row, int g) {
-    const uint16_t *p = base + row * 64 + 4 * g;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) f.c[s] = *reinterpret_cast<const u32x2_t *>(p + 16 * s);
+    const uint16_t *p = base + row * 64 + 8 * g;
+    f.c[0] = *reinterpret_cast<const u32x4_t *>(p);
+    f.c[1] = *reinterpret_cast<const u32x4_t *>(p + 32);
 }
 __device__ __forceinline__ void load_frag(Frag<false> &f, const float *base, int64_t row, int g) {
-    const float *p = base + row * 64 + 4 * g;
+    const float *p = base + row * 64 + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) f.c[s] = *reinterpret_cast<const f32x4_t *>(p + 16 * s);
+    for (int c = 0; c < 4; ++c) f.c[c] = *reinterpret_cast<const f32x4_t *>(p + 32 * (c >> 1) + 4 * (c & 1));
 }
 
-// Stores 16 fp32 values (chunk s, element u) of row `row`, scaled, in the element type.
-__device__ __forceinline__ void store_row(uint16_t *base, int64_t row, int g, const f32x4_t acc[4],
-                                          float mul) {
-    uint16_t *p = base + row * 64 + 4 * g;
+// Stores this lane's 16 accumulator values of row `row`, times `mul`, in the element type.
+__device__ __forceinline__ void store_row(uint16_t *base, int64_t row, int g, const f32x4_t acc[4], float mul) {
+    uint16_t *p = base + row * 64 + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        u32x2_t x;
-        x.x = pack_bf16(acc[s][0] * mul, acc[s][1] * mul);
-        x.y = pack_bf16(acc[s][2] * mul, acc[s][3] * mul);
-        *reinterpret_cast<u32x2_t *>(p + 16 * s) = x;
+    for (int h = 0; h < 2; ++h) {
+        const f32x4_t a = acc[2 * h] * mul, b = acc[2 * h + 1] * mul;
+        const u32x4_t x = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])};
+        *reinterpret_cast<u32x4_t *>(p + 32 * h) = x;
     }
 }
-__device__ __forceinline__ void store_row(float *base, int64_t row, int g, const f32x4_t acc[4],
-                                          float mul) {
-    float *p = base + row * 64 + 4 * g;
+__device__ __forceinline__ void store_row(float *base, int64_t row, int g, const f32x4_t acc[4], float mul) {
+    float *p = base + row * 64 + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4_t *>(p + 16 * s) = acc[s] * mul;
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<f32x4_t *>(p + 32 * (c >> 1) + 4 * (c & 1)) = acc[c] * mul;
 }
 
 // Partial dot product of two fragments (this lane's 16 of the 64 terms).
-template <bool BF16>
-__device__ __forceinline__ float frag_dot(const Frag<BF16> &a, const Frag<BF16> &b) {
-    float acc = 0.f;
+__device__ __forceinline__ float frag_dot(const Frag<true> &a, const Frag<true> &b) {
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = fmaf(frag_elem(a, s, u), frag_elem(b, s, u), acc);
-    return acc;
+        for (int w = 0; w < 4; w += 2) {
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.c[h][w]),
+                                                 __builtin_bit_cast(bf16x2_t, b.c[h][w]), s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.c[h][w + 1]),
+                                                 __builtin_bit_cast(bf16x2_t, b.c[h][w + 1]), s1, false);
+        }
+    return s0 + s1;
+}
+__device__ __forceinline__ float frag_dot(const Frag<false> &a, const Frag<false> &b) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        s0 = fmaf(a.c[c][0], b.c[c][0], s0);
+        s1 = fmaf(a.c[c][1], b.c[c][1], s1);
+        s0 = fmaf(a.c[c][2], b.c[c][2], s0);
+        s1 = fmaf(a.c[c][3], b.c[c][3], s1);
+    }
+    return s0 + s1;
 }
 
-// acc[s][u] += x * f[s][u]
-template <bool BF16>
-__device__ __forceinline__ void frag_axpy(f32x4_t acc[4], float x, const Frag<BF16> &f) {
+// acc += x * f. For bf16 rows the product runs on the packed bf16 dot unit with x
+// rounded to bf16 (the same rounding the MFMA path applies to probabilities):
+// dot2({f_lo, f_hi}, {x, 0}) = x f_lo and dot2({f_lo, f_hi}, {0, x}) = x f_hi.
+__device__ __forceinline__ void frag_axpy(f32x4_t acc[4], float x, const Frag<true> &f) {
+    const bf16x2_t xl = __builtin_bit_cast(bf16x2_t, pack_bf16(x, 0.f));
+    const bf16x2_t xh = __builtin_bit_cast(bf16x2_t, pack_bf16(0.f, x));
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[s][u] = fmaf(x, frag_elem(f, s, u), acc[s][u]);
+        for (int w = 0; w < 4; ++w) {
+            const bf16x2_t v = __builtin_bit_cast(bf16x2_t, f.c[h][w]);
+            f32x4_t &a = acc[2 * h + (w >> 1)];
+            const int r = 2 * (w & 1);
+            a[r] = __builtin_amdgcn_fdot2_f32_bf16(v, xl, a[r], false);
+            a[r + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, xh, a[r + 1], false);
+        }
+}
+__device__ __forceinline__ void frag_axpy(f32x4_t acc[4], float x, const Frag<false> &f) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += x * f.c[c];
 }
 
-// Sum over the four lane groups (lanes l, l^16, l^32, l^48).
+// Sum / max over the four lane groups (lanes l, l^16, l^32, l^48).
 __device__ __forceinline__ float group_sum(float x) {
     x += __shfl_xor(x, 16);
     x += __shfl_xor(x, 32);
@@ -165,89 +194,121 @@ __device__ __forceinline__ float group_max(float x) {
 // register r holds row 4 g + r)
 // ----------------------------------------------------------------------------
 
-// acc[row][col] += sum_d A_row[d] * B_col[d], where lane (l%16, g) supplies the
-// fragment of A row l%16 and of B row (= output column) l%16.
+// acc[row][col] += sum_d A_row[d] * B_col[d]: lane (l%16, g) supplies the fragment
+// of A row l%16 and of B row (= output column) l%16. Both operands present their
+// 64 terms in the same fragment order, so the contraction covers every d once.
 __device__ __forceinline__ f32x4_t mma_over_d(const Frag<true> &a, const Frag<true> &b, f32x4_t acc) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const u32x4_t av = {a.c[2 * h].x, a.c[2 * h].y, a.c[2 * h + 1].x, a.c[2 * h + 1].y};
-        const u32x4_t bv = {b.c[2 * h].x, b.c[2 * h].y, b.c[2 * h + 1].x, b.c[2 * h + 1].y};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                      __builtin_bit_cast(bf16x8_t, bv), acc, 0, 0, 0);
-    }
+    for (int h = 0; h < 2; ++h)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.c[h]),
+                                                      __builtin_bit_cast(bf16x8_t, b.c[h]), acc, 0, 0, 0);
     return acc;
 }
 __device__ __forceinline__ f32x4_t mma_over_d(const Frag<false> &a, const Frag<false> &b, f32x4_t acc) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.c[s][u], b.c[s][u], acc, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.c[c][r], b.c[c][r], acc, 0, 0, 0);
     return acc;
 }
 
-// acc[db][d][col] += sum_{kk<16} At[16 db + d][kk0 + kk] * Bv[kk][col], for db = 0..3.
-// At is a transposed 64 x 64 tile in LDS ([d][row], padded rows); Bv is given in
-// the C layout of a previous product: lane (col, g) register r holds kk = 4 g + r.
-__device__ __forceinline__ void mma_over_rows(f32x4_t acc[4], const uint16_t *At, int kk0, int c16, int g,
-                                              const float bv[4]) {
-    u32x2_t b;
-    b.x = pack_bf16(bv[0], bv[1]);
-    b.y = pack_bf16(bv[2], bv[3]);
+// Row of a transposed tile that feeds MFMA row m of output block db, chosen so
+// that output register r of lane group g lands on d = 32 (db/2) + 8 g + 4 (db%2) + r.
+__device__ __forceinline__ int acc_row_d(int db, int m) { return 32 * (db >> 1) + 8 * (m >> 2) + 4 * (db & 1) + (m & 3); }
+
+// acc[db] += sum_{kk<16} At[d][kk0 + kk] * Bv[kk][col] for the four output blocks db.
+// At is a transposed tile in LDS ([d][row], row stride `stride`); Bv is given in the
+// C layout of an earlier product: lane (col, g) register r holds kk = 4 g + r.
+__device__ __forceinline__ void mma_over_rows(f32x4_t acc[4], const uint16_t *At, int stride, int kk0, int c16,
+                                              int g, const float bv[4]) {
+    const u32x2_t b = {pack_bf16(bv[0], bv[1]), pack_bf16(bv[2], bv[3])};
     const i16x4_t bb = __builtin_bit_cast(i16x4_t, b);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const u32x2_t a = *reinterpret_cast<const u32x2_t *>(At + (16 * db + c16) * kLdsRow + kk0 + 4 * g);
+        const u32x2_t a = *reinterpret_cast<const u32x2_t *>(At + acc_row_d(db, c16) * stride + kk0 + 4 * g);
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), bb, acc[db], 0, 0, 0);
     }
 }
-__device__ __forceinline__ void mma_over_rows(f32x4_t acc[4], const float *At, int kk0, int c16, int g,
+__device__ __forceinline__ void mma_over_rows(f32x4_t acc[4], const float *At, int stride, int kk0, int c16, int g,
                                               const float bv[4]) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(At + (16 * db + c16) * kLdsRow + kk0 + 4 * g);
+        const f32x4_t a = *reinterpret_cast<const f32x4_t *>(At + acc_row_d(db, c16) * stride + kk0 + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], bv[r], acc[db], 0, 0, 0);
     }
 }
 
 // ----------------------------------------------------------------------------
-// LDS staging
+// LDS staging of transposed tiles: lds[d * stride + (row - row0)] = src[row][d],
+// rows outside [0, n) written as zeros. Split into a load step (global -> registers)
+// and a store step (registers -> LDS) so callers can issue the loads early.
+// A thread covers 4 consecutive rows and 8 consecutive d (four 16-byte row loads in
+// bf16); NR / 4 * 8 threads cover NR rows.
 // ----------------------------------------------------------------------------
 
-// Writes rows [row0, row0 + 64) of a [n, 64] matrix transposed into lds[d][row - row0];
-// rows >= n are written as zeros. All 256 threads take part.
-__device__ __forceinline__ void stage_transposed(uint16_t *lds, const uint16_t *src, int row0, int n, int tid) {
-    const int rg = tid >> 4, dg = tid & 15;
-    u32x2_t x[4];
+template <bool BF16>
+struct StageRegs;
+template <>
+struct StageRegs<true> {
+    u32x4_t x[4];
+};
+template <>
+struct StageRegs<false> {
+    f32x4_t x[4][2];
+};
+
+__device__ __forceinline__ void stage_load(StageRegs<true> &s, const uint16_t *src, int row0, int n, int unit) {
+    const int rg = unit >> 3, dg = unit & 7;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
         const int row = row0 + 4 * rg + rr;
-        x[rr] = (row < n) ? *reinterpret_cast<const u32x2_t *>(src + (int64_t)row * 64 + 4 * dg) : u32x2_t{0u, 0u};
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int sh = (c & 1) * 16;
-        uint32_t e[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) e[rr] = (((c < 2) ? x[rr].x : x[rr].y) >> sh) & 0xffffu;
-        u32x2_t w;
-        w.x = e[0] | (e[1] << 16);
-        w.y = e[2] | (e[3] << 16);
-        *reinterpret_cast<u32x2_t *>(lds + (4 * dg + c) * kLdsRow + 4 * rg) = w;
+        s.x[rr] = (row >= 0 && row < n) ? *reinterpret_cast<const u32x4_t *>(src + (int64_t)row * 64 + 8 * dg)
+                                        : u32x4_t{0u, 0u, 0u, 0u};
     }
 }
-__device__ __forceinline__ void stage_transposed(float *lds, const float *src, int row0, int n, int tid) {
-    const int rg = tid >> 4, dg = tid & 15;
-    f32x4_t x[4];
+__device__ __forceinline__ void stage_load(StageRegs<false> &s, const float *src, int row0, int n, int unit) {
+    const int rg = unit >> 3, dg = unit & 7;
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
         const int row = row0 + 4 * rg + rr;
-        x[rr] = (row < n) ? *reinterpret_cast<const f32x4_t *>(src + (int64_t)row * 64 + 4 * dg) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+        const bool ok = row >= 0 && row < n;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const f32x4_t w = {x[0][c], x[1][c], x[2][c], x[3][c]};
-        *reinterpret_cast<f32x4_t *>(lds + (4 * dg + c) * kLdsRow + 4 * rg) = w;
+        for (int hh = 0; hh < 2; ++hh)
+            s.x[rr][hh] = ok ? *reinterpret_cast<const f32x4_t *>(src + (int64_t)row * 64 + 8 * dg + 4 * hh)
+                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+}
+__device__ __forceinline__ void stage_store(uint16_t *lds, int stride, const StageRegs<true> &s, int unit) {
+    const int rg = unit >> 3, dg = unit & 7;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // d = 8 dg + 2 w (low halves) and 8 dg + 2 w + 1 (high halves) of the four rows
+        const u32x2_t lo = {__builtin_amdgcn_perm(s.x[1][w], s.x[0][w], 0x05040100u),
+                            __builtin_amdgcn_perm(s.x[3][w], s.x[2][w], 0x05040100u)};
+        const u32x2_t hi = {__builtin_amdgcn_perm(s.x[1][w], s.x[0][w], 0x07060302u),
+                            __builtin_amdgcn_perm(s.x[3][w], s.x[2][w], 0x07060302u)};
+        *reinterpret_cast<u32x2_t *>(lds + (8 * dg + 2 * w) * stride + 4 * rg) = lo;
+        *reinterpret_cast<u32x2_t *>(lds + (8 * dg + 2 * w + 1) * stride + 4 * rg) = hi;
+    }
+}
+__device__ __forceinline__ void stage_store(float *lds, int stride, const StageRegs<false> &s, int unit) {
+    const int rg = unit >> 3, dg = unit & 7;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const f32x4_t v = {s.x[0][c >> 2][c & 3], s.x[1][c >> 2][c & 3], s.x[2][c >> 2][c & 3], s.x[3][c >> 2][c & 3]};
+        *reinterpret_cast<f32x4_t *>(lds + (8 * dg + c) * stride + 4 * rg) = v;
+    }
+}
+
+// Stages rows [row0, row0 + NR) with the whole workgroup (NR = 64 or 128).
+template <int NR, bool BF16>
+__device__ __forceinline__ void stage_tile(typename Elem<BF16>::T *lds, int stride, const typename Elem<BF16>::T *src,
+                                           int row0, int n, int tid) {
+    if (tid < NR * 2) {
+        StageRegs<BF16> s;
+        stage_load(s, src, row0, n, tid);
+        stage_store(lds, stride, s, tid);
     }
 }
 
@@ -264,11 +325,59 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 // forward
 // ----------------------------------------------------------------------------
 
-template <bool BF16, bool OUT_BF16>
+enum FwdMode { kWindow = 0, kWide = 1, kDense = 2 };
+
+// Sparse offsets t in [t_begin, n_off), four at a time, each with one online
+// softmax update (used beyond the prefetched offsets and by the wide path).
+template <bool BF16>
+__device__ __forceinline__ void fwd_slabs_loop(const AttnParams &p, int t_begin, const Frag<BF16> &qf,
+                                               const typename Elem<BF16>::T *K, const typename Elem<BF16>::T *V,
+                                               int i, bool row_ok, int r0, int n, int g, f32x4_t acc[4], float &m2,
+                                               float &lsum) {
+    for (int t0 = t_begin; t0 < p.n_off; t0 += 4) {
+        if (r0 + 15 < p.off[t0]) break;  // ascending offsets: no later slab reaches a key
+        Frag<BF16> kf[4], vf[4];
+        bool ok[4];
+        int jc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u;
+            const int j = (t < p.n_off) ? i - p.off[t] : -1;
+            ok[u] = row_ok && j >= 0;
+            jc[u] = min(max(j, 0), n - 1);
+            load_frag(kf[u], K, jc[u], g);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load_frag(vf[u], V, jc[u], g);
+        float sc[4], gm = kNegInf;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            sc[u] = ok[u] ? group_sum(frag_dot(qf, kf[u])) * p.scale_log2 : kNegInf;
+            gm = fmaxf(gm, sc[u]);
+        }
+        const float mn = fmaxf(m2, gm);
+        const float ms = (mn == kNegInf) ? 0.f : mn;
+        const float al = exp2f(m2 - ms);
+        float ps = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] *= al;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float pu = exp2f(sc[u] - ms);
+            ps += pu;
+            frag_axpy(acc, pu, vf[u]);
+        }
+        lsum = lsum * al + (g == 0 ? ps : 0.f);
+        m2 = mn;
+    }
+}
+
+template <bool BF16, bool OUT_BF16, int MODE>
 __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
     using OE = typename Elem<OUT_BF16>::T;
-    __shared__ __attribute__((aligned(16))) E vt[64 * kLdsRow];  // V^T of one 64-key chunk
+    // window mode: V^T of keys [i0 - 64, i0 + 64); wide/dense: V^T of one 64-key chunk
+    __shared__ __attribute__((aligned(16))) E vt[MODE == kWindow ? 64 * kT128 : 64 * kT64];
 
     const int n = p.n, w = p.w;
     const int nt = (n + 63) >> 6;
@@ -277,7 +386,7 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4;
     const int i0 = tile * 64, r0 = i0 + 16 * wave;
-    const int i = r0 + c16;          // this lane's query row
+    const int i = r0 + c16;  // this lane's query row
     const bool row_ok = i < n;
     const int64_t head = (int64_t)bh * n * 64;
     const E *Q = static_cast<const E *>(p.q) + head;
@@ -290,97 +399,146 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
 
     f32x4_t acc[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m = kNegInf;  // running max of log2-scaled scores
-    float lsum = 0.f;   // this lane's share of the running sum
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m2 = kNegInf;  // running max of log2-scaled scores
+    float lsum = 0.f;    // this lane's share of the running sum
 
-    // ---- window band on MFMA ----
-    const int jlo = max(0, i0 - w + 1), jhi = min(n - 1, i0 + 63);
-    const int wlo = r0 - w + 1, whi = min(r0 + 15, n - 1);  // keys this wave needs
-    for (int c0 = jlo & ~63; c0 <= jhi; c0 += 64) {
-        __syncthreads();
-        stage_transposed(vt, V, c0, n, tid);
-        __syncthreads();
-        if (r0 >= n) continue;
+    if constexpr (MODE == kWindow) {
+        // ---------------- window of at most 64 keys: every load issued up front ----------------
+        StageRegs<BF16> vs;
+        stage_load(vs, V, i0 - 64, n, tid);
+        const int qb = r0 >> 4;  // the wave's 16-row block; its keys lie in blocks qb-4 .. qb
+        Frag<BF16> kf[5];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int kb0 = c0 + 16 * kb;
-            if (kb0 + 15 < wlo || kb0 > whi) continue;  // uniform across the wave
-            Frag<BF16> kf;
-            load_frag(kf, K, min(kb0 + c16, n - 1), g);
-            const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            float sv[4], bm = kNegInf;
+        for (int b = 0; b < 5; ++b) load_frag(kf[b], K, min(max(16 * (qb - 4 + b) + c16, 0), n - 1), g);
+        Frag<BF16> sk[kSlabRegs], sv[kSlabRegs];
+        int sj[kSlabRegs];
+        bool sok[kSlabRegs];
+#pragma unroll
+        for (int t = 0; t < kSlabRegs; ++t) {
+            const int j = (t < p.n_off) ? i - p.off[t] : -1;
+            sok[t] = row_ok && j >= 0;
+            sj[t] = min(max(j, 0), n - 1);
+            if (t < p.n_off) load_frag(sk[t], K, sj[t], g);
+        }
+        stage_store(vt, kT128, vs, tid);
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kSlabRegs; ++t)
+            if (t < p.n_off) load_frag(sv[t], V, sj[t], g);
+
+        // window band: all 20 scores of the lane, one max, then P.V on MFMA
+        const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);  // keys the wave needs
+        float sc[5][4];
+        float bm = kNegInf;
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            const int kb0 = 16 * (qb - 4 + b);
+            const bool active = kb0 + 15 >= klo && kb0 <= khi;
+            const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
+            f32x4_t st = {kNegInf, kNegInf, kNegInf, kNegInf};
+            if (active) st = mma_over_d(kf[b], qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = kb0 + 4 * g + r;
-                const bool ok = row_ok && j <= i && j > i - w;
-                sv[r] = ok ? st[r] * sl2 : kNegInf;
-                bm = fmaxf(bm, sv[r]);
+                const bool ok = full || (active && row_ok && j <= i && j > i - w && j >= 0);
+                sc[b][r] = ok ? st[r] : kNegInf;
+                bm = fmaxf(bm, sc[b][r]);
             }
-            bm = group_max(bm);
-            const float mn = fmaxf(m, bm);
-            const float ms = (mn == kNegInf) ? 0.f : mn;
-            const float al = exp2f(m - ms);
-            float pr[4], ps = 0.f;
+        }
+        m2 = group_max(bm);
+        const float ms = row_ok ? m2 : 0.f;
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            const int kb0 = 16 * (qb - 4 + b);
+            const bool active = kb0 + 15 >= klo && kb0 <= khi;
+            float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[r] = exp2f(sv[r] - ms);
-                ps += pr[r];
+                pr[r] = exp2f(sc[b][r] - ms);
+                lsum += pr[r];
             }
-            lsum = lsum * al + ps;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc[s] *= al;
-            m = mn;
-            mma_over_rows(acc, vt, 16 * kb, c16, g, pr);
+            if (active) mma_over_rows(acc, vt, kT128, 16 * (wave + b), c16, g, pr);
         }
-    }
 
-    // ---- sparse offsets on VALU, four slabs at a time ----
-    if (r0 < n) {
-        for (int t0 = 0; t0 < p.n_off; t0 += 4) {
-            if (r0 + 15 < p.off[t0]) break;  // ascending offsets: no later slab reaches a key
-            Frag<BF16> kf[4], vf[4];
-            bool ok[4];
-            int jc[4];
+        // prefetched sparse offsets: scores, one rescale, then the P.V terms
+        float ss[kSlabRegs];
+        float gm = kNegInf;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int t = t0 + u;
-                const int j = (t < p.n_off) ? i - p.off[t] : -1;
-                ok[u] = row_ok && j >= 0;
-                jc[u] = min(max(j, 0), n - 1);
-                load_frag(kf[u], K, jc[u], g);
+        for (int t = 0; t < kSlabRegs; ++t) {
+            ss[t] = kNegInf;
+            if (t < p.n_off) {
+                const float d = group_sum(frag_dot(qf, sk[t]));
+                ss[t] = sok[t] ? d * sl2 : kNegInf;
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) load_frag(vf[u], V, jc[u], g);
-            float sc[4], gm = kNegInf;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                sc[u] = group_sum(frag_dot(qf, kf[u]));
-                sc[u] = ok[u] ? sc[u] * sl2 : kNegInf;
-                gm = fmaxf(gm, sc[u]);
-            }
-            const float mn = fmaxf(m, gm);
-            const float ms = (mn == kNegInf) ? 0.f : mn;
-            const float al = exp2f(m - ms);
-            float ps = 0.f;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) acc[s] *= al;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float pu = exp2f(sc[u] - ms);
-                ps += pu;
-                frag_axpy(acc, pu, vf[u]);
-            }
-            lsum = lsum * al + (g == 0 ? ps : 0.f);
-            m = mn;
+            gm = fmaxf(gm, ss[t]);
         }
+        const float mn = fmaxf(m2, gm);
+        const float ms2 = (mn == kNegInf) ? 0.f : mn;
+        const float al = exp2f(m2 - ms2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] *= al;
+        float ps = 0.f;
+#pragma unroll
+        for (int t = 0; t < kSlabRegs; ++t) {
+            if (t < p.n_off) {
+                const float pt = exp2f(ss[t] - ms2);
+                ps += pt;
+                frag_axpy(acc, pt, sv[t]);
+            }
+        }
+        lsum = lsum * al + (g == 0 ? ps : 0.f);
+        m2 = mn;
+        if (p.n_off > kSlabRegs && r0 < n) fwd_slabs_loop(p, kSlabRegs, qf, K, V, i, row_ok, r0, n, g, acc, m2, lsum);
+    } else {
+        // ---------------- wide window or dense: 64-key chunks with an online softmax ----------------
+        const int jlo = max(0, i0 - w + 1), jhi = min(n - 1, i0 + 63);
+        const int wlo = r0 - w + 1, whi = min(r0 + 15, n - 1);  // keys this wave needs
+        for (int c0 = jlo & ~63; c0 <= jhi; c0 += 64) {
+            __syncthreads();
+            stage_tile<64, BF16>(vt, kT64, V, c0, n, tid);
+            __syncthreads();
+            if (r0 >= n) continue;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int kb0 = c0 + 16 * kb;
+                if (kb0 + 15 < wlo || kb0 > whi) continue;  // uniform across the wave
+                Frag<BF16> kf;
+                load_frag(kf, K, min(kb0 + c16, n - 1), g);
+                const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+                float sv[4], bm = kNegInf;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = kb0 + 4 * g + r;
+                    const bool ok = row_ok && j <= i && j > i - w;
+                    sv[r] = ok ? st[r] : kNegInf;
+                    bm = fmaxf(bm, sv[r]);
+                }
+                bm = group_max(bm);
+                const float mn = fmaxf(m2, bm);
+                const float ms = (mn == kNegInf) ? 0.f : mn;
+                const float al = exp2f(m2 - ms);
+                float pr[4], ps = 0.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    pr[r] = exp2f(sv[r] - ms);
+                    ps += pr[r];
+                }
+                lsum = lsum * al + ps;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] *= al;
+                m2 = mn;
+                mma_over_rows(acc, vt, kT64, 16 * kb, c16, g, pr);
+            }
+        }
+        if (MODE == kWide && r0 < n) fwd_slabs_loop(p, 0, qf, K, V, i, row_ok, r0, n, g, acc, m2, lsum);
     }
 
     // ---- epilogue ----
     const float l = group_sum(lsum);
     if (row_ok) {
         store_row(static_cast<OE *>(p.out) + head, i, g, acc, 1.f / l);
-        if (g == 0) p.lse_out[(int64_t)bh * n + i] = m * kLn2 + logf(l);
+        if (g == 0) p.lse_out[(int64_t)bh * n + i] = m2 * kLn2 + logf(l);
     }
 }
 
@@ -422,8 +580,8 @@ template <bool BF16, bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
     using OE = typename Elem<OUT_BF16>::T;
-    __shared__ __attribute__((aligned(16))) E t0s[64 * kLdsRow];  // transposed tile (K^T, or Q^T)
-    __shared__ __attribute__((aligned(16))) E t1s[64 * kLdsRow];  // transposed tile (dO^T)
+    __shared__ __attribute__((aligned(16))) E t0s[64 * kT64];  // transposed tile (K^T, or Q^T)
+    __shared__ __attribute__((aligned(16))) E t1s[64 * kT64];  // transposed tile (dO^T)
     __shared__ float lse_s[64], del_s[64];
 
     const int n = p.n, w = p.w;
@@ -460,7 +618,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
         const int wlo = r0 - w + 1, whi = min(r0 + 15, n - 1);
         for (int c0 = jlo & ~63; c0 <= jhi; c0 += 64) {
             __syncthreads();
-            stage_transposed(t0s, K, c0, n, tid);
+            stage_tile<64, BF16>(t0s, kT64, K, c0, n, tid);
             __syncthreads();
             if (r0 >= n) continue;
 #pragma unroll
@@ -481,7 +639,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                     const float pv = ok ? exp2f(st[r] * sl2 - lse2) : 0.f;
                     ds[r] = pv * (dpt[r] - di);
                 }
-                mma_over_rows(acc, t0s, 16 * kb, c16, g, ds);
+                mma_over_rows(acc, t0s, kT64, 16 * kb, c16, g, ds);
             }
         }
         if (r0 < n) {
@@ -522,8 +680,8 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
         const int ilo = r0, ihi = (int)min((int64_t)n - 1, (int64_t)r0 + 15 + w - 1);
         for (int c0 = t0; c0 <= ihi_wg; c0 += 64) {
             __syncthreads();
-            stage_transposed(t0s, Q, c0, n, tid);
-            stage_transposed(t1s, DO, c0, n, tid);
+            stage_tile<64, BF16>(t0s, kT64, Q, c0, n, tid);
+            stage_tile<64, BF16>(t1s, kT64, DO, c0, n, tid);
             if (tid < 64) {
                 const int row = c0 + tid;
                 lse_s[tid] = (row < n) ? LSE[row] * kLog2e : 0.f;
@@ -550,8 +708,8 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                     pr[r] = ok ? exp2f(sq[r] * sl2 - lse_s[qi]) : 0.f;
                     ds[r] = pr[r] * (dpq[r] - del_s[qi]);
                 }
-                mma_over_rows(dv, t1s, 16 * qb, c16, g, pr);
-                mma_over_rows(dk, t0s, 16 * qb, c16, g, ds);
+                mma_over_rows(dv, t1s, kT64, 16 * qb, c16, g, pr);
+                mma_over_rows(dk, t0s, kT64, 16 * qb, c16, g, ds);
             }
         }
         // sparse offsets: queries i = j + o
@@ -580,14 +738,23 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
     }
 }
 
-template <bool BF16, bool OUT_BF16>
+template <bool BF16, bool OUT_BF16, int MODE>
 hipError_t launch_forward_t(const AttnParams &p, hipStream_t stream) {
     const int nt = (p.n + 63) / 64;
     const dim3 grid(p.bh * nt), block(kThreads);
     AttnParams a = p;
     void *args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<BF16, OUT_BF16>), grid, block, args, 0,
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<BF16, OUT_BF16, MODE>), grid, block, args, 0,
                            stream);
+}
+
+template <int MODE>
+hipError_t launch_forward_mode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
+    if (dt == FSA_BF16)
+        return out_dt == FSA_BF16 ? launch_forward_t<true, true, MODE>(p, stream)
+                                  : launch_forward_t<true, false, MODE>(p, stream);
+    return out_dt == FSA_BF16 ? launch_forward_t<false, true, MODE>(p, stream)
+                              : launch_forward_t<false, false, MODE>(p, stream);
 }
 
 template <bool BF16>
@@ -612,9 +779,12 @@ hipError_t launch_grads_t(const AttnParams &p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
-    if (dt == FSA_BF16)
-        return out_dt == FSA_BF16 ? launch_forward_t<true, true>(p, stream) : launch_forward_t<true, false>(p, stream);
-    return out_dt == FSA_BF16 ? launch_forward_t<false, true>(p, stream) : launch_forward_t<false, false>(p, stream);
+    return p.w <= 64 ? launch_forward_mode<kWindow>(dt, out_dt, p, stream)
+                     : launch_forward_mode<kWide>(dt, out_dt, p, stream);
+}
+
+hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
+    return launch_forward_mode<kDense>(dt, out_dt, p, stream);
 }
 
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream) {
