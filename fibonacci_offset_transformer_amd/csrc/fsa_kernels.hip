@@ -53,8 +53,6 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
 constexpr int kT64 = 64 + 4;    // padded LDS row (elements) of a transposed 64-row tile
-constexpr int kT128 = 128 + 4;  // padded LDS row (elements) of a transposed 128-row tile
-constexpr int kSlabRegs = 8;    // sparse offsets whose rows are prefetched into registers
 
 // ----------------------------------------------------------------------------
 // element types and row fragments
@@ -95,11 +93,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
-__device__ __forceinline__ float frag_elem(const Frag<true> &f, int h, int e) {
-    const uint32_t w = f.c[h][e >> 1];
-    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+// Reinterprets a 32-bit word as two bf16. The word is taken by value on purpose:
+// hipcc (clang 22, ROCm 7.2) miscompiles __builtin_bit_cast applied directly to an
+// element of an ext_vector_type value, reading element 0 whatever the index.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t w) {
+    bf16x2_t v;
+    __builtin_memcpy(&v, &w, sizeof v);
+    return v;
 }
-__device__ __forceinline__ float frag_elem(const Frag<false> &f, int h, int e) { return f.c[2 * h + (e >> 2)][e & 3]; }
 
 // Loads row `row` of a [*, 64] matrix into lane group g's fragment.
 __device__ __forceinline__ void load_frag(Frag<true> &f, const uint16_t *base, int64_t row, int g) {
@@ -136,10 +137,8 @@ __device__ __forceinline__ float frag_dot(const Frag<true> &a, const Frag<true> 
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int w = 0; w < 4; w += 2) {
-            s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.c[h][w]),
-                                                 __builtin_bit_cast(bf16x2_t, b.c[h][w]), s0, false);
-            s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.c[h][w + 1]),
-                                                 __builtin_bit_cast(bf16x2_t, b.c[h][w + 1]), s1, false);
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.c[h][w]), as_bf16x2(b.c[h][w]), s0, false);
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.c[h][w + 1]), as_bf16x2(b.c[h][w + 1]), s1, false);
         }
     return s0 + s1;
 }
@@ -159,13 +158,13 @@ __device__ __forceinline__ float frag_dot(const Frag<false> &a, const Frag<false
 // rounded to bf16 (the same rounding the MFMA path applies to probabilities):
 // dot2({f_lo, f_hi}, {x, 0}) = x f_lo and dot2({f_lo, f_hi}, {0, x}) = x f_hi.
 __device__ __forceinline__ void frag_axpy(f32x4_t acc[4], float x, const Frag<true> &f) {
-    const bf16x2_t xl = __builtin_bit_cast(bf16x2_t, pack_bf16(x, 0.f));
-    const bf16x2_t xh = __builtin_bit_cast(bf16x2_t, pack_bf16(0.f, x));
+    const bf16x2_t xl = as_bf16x2(pack_bf16(x, 0.f));
+    const bf16x2_t xh = as_bf16x2(pack_bf16(0.f, x));
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const bf16x2_t v = __builtin_bit_cast(bf16x2_t, f.c[h][w]);
+            const bf16x2_t v = as_bf16x2(f.c[h][w]);
             f32x4_t &a = acc[2 * h + (w >> 1)];
             const int r = 2 * (w & 1);
             a[r] = __builtin_amdgcn_fdot2_f32_bf16(v, xl, a[r], false);
@@ -177,17 +176,31 @@ __device__ __forceinline__ void frag_axpy(f32x4_t acc[4], float x, const Frag<fa
     for (int c = 0; c < 4; ++c) acc[c] += x * f.c[c];
 }
 
-// Sum / max over the four lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float group_sum(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+// Sum / max over the four lane groups (lanes l, l^16, l^32, l^48) with the gfx950
+// row-swap permutes: permlane16_swap(x, x) yields x of lane l and of lane l^16,
+// permlane32_swap(x, x) x of lane l and of lane l^32 (both VALU, no LDS trip).
+__device__ __forceinline__ float swap_add16(float x) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
-__device__ __forceinline__ float group_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+__device__ __forceinline__ float swap_add32(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
+__device__ __forceinline__ float swap_max16(float x) {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float swap_max32(float x) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float group_sum(float x) { return swap_add32(swap_add16(x)); }
+__device__ __forceinline__ float group_max(float x) { return swap_max32(swap_max16(x)); }
+
+// 2^x on the hardware exponential unit; results below the normal range flush to
+// zero, which only affects probabilities under 2^-126.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ----------------------------------------------------------------------------
 // MFMA building blocks (16x16 output tiles; C layout: lane (col = l%16, g = l/16),
@@ -322,10 +335,188 @@ __device__ __forceinline__ int xcd_logical_block(int b, int nb) {
 }
 
 // ----------------------------------------------------------------------------
+// Row-major LDS tiles filled by direct global -> LDS loads (bf16 window kernels)
+// ----------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kTileRows = 128;  // rows per LDS tile: the 64-row tile and its 64-row neighbour
+
+// Copies rows [row0, row0 + 128) of a [n, 64] bf16 matrix into a row-major LDS
+// tile (128 bytes per row). Each of the four waves issues four 1 KiB transfers;
+// lane l of a transfer carries the 16 bytes that land at tile offset 16 l. Rows
+// outside [0, n) are read from row 0: finite values that the masks discard.
+// Completion is waited for with wait_vm_all() before the workgroup barrier.
+__device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src, int row0, int n, int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int rb = 8 * (4 * wave + k);  // first of the 8 rows this transfer covers
+        int r = row0 + rb + (lane >> 3);
+        r = (r >= 0 && r < n) ? r : 0;
+        __builtin_amdgcn_global_load_lds(src + (int64_t)r * 64 + 8 * (lane & 7),
+                                         (lds_void_t *)(tile + rb * 64), 16, 0, 0);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Buffer-resource loads (bf16 window kernels): a 32-bit byte offset against a
+// per-head descriptor whose range is the head's rows. Offsets outside the range
+// (rows < 0 or >= n) return zeros without touching memory, so slab rows need no
+// clamping; the masks discard such pairs.
+// ----------------------------------------------------------------------------
+
+constexpr int kBufferConfig = 0x00020000;  // descriptor word 3 for gfx9-family raw buffers
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufferConfig);
+}
+
+// Row fragment of row `row` (lane group g's 16 elements) from a [n, 64] bf16 head.
+__device__ __forceinline__ void buf_frag(Frag<true> &f, __amdgpu_buffer_rsrc_t r, int row, int g) {
+    const int off = row * 128 + 16 * g;
+    f.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    f.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64, 0, 0));
+}
+
+__device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int idx) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, idx * 4, 0, 0));
+}
+
+// Row that sparse offset t pairs with row `row`: row - off[t] (sign -1) or row + off[t]
+// (sign +1); t beyond the table yields an offset of 0. Used as a buffer-load row only
+// (out-of-range rows read as zeros); the caller masks pairs outside the sequence.
+__device__ __forceinline__ int slab_row(const AttnParams &p, int t, int row, int sign) {
+    const int o = p.off[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1];
+    return row + sign * (t < p.n_off ? o : 0);
+}
+
+// Offset t of the table, or a value no row can reach when t is past the table.
+__device__ __forceinline__ int table_off(const AttnParams &p, int t) {
+    return t < p.n_off ? p.off[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1] : 0x3fffffff;
+}
+
+// Waits for every outstanding memory operation of the wave (global -> LDS copies included).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Row fragment (lane group g's 16 elements) of tile row `row`.
+__device__ __forceinline__ void lds_frag(Frag<true> &f, const uint16_t *tile, int row, int g) {
+    const uint16_t *p = tile + row * 64 + 8 * g;
+    f.c[0] = *reinterpret_cast<const u32x4_t *>(p);
+    f.c[1] = *reinterpret_cast<const u32x4_t *>(p + 32);
+}
+
+// acc[db] += sum_{kk<16} Tile[lr + kk][d] * Bv[kk][col] for the four output blocks db,
+// i.e. the product with the transposed rows lr .. lr+15 of a row-major tile. The A
+// operand comes from ds_read_b64_tr_b16: within a 16-lane group, result lane j, slot
+// k receives element j % 4 of the 8 bytes that group lane j / 4 + 4 k addresses. Lane
+// s therefore addresses row lr + 4 g + s / 4 at column 32 (db / 2) + 8 (s % 4) + 4 (db % 2),
+// which hands lane j the column acc_row_d(db, j) of rows lr + 4 g + k.
+__device__ __forceinline__ void mma_over_rows_tr(f32x4_t acc[4], const uint16_t *tile, int lr, int c16, int g,
+                                                 const float bv[4]) {
+    const u32x2_t b = {pack_bf16(bv[0], bv[1]), pack_bf16(bv[2], bv[3])};
+    const i16x4_t bb = __builtin_bit_cast(i16x4_t, b);
+    const uint16_t *rowp = tile + (lr + 4 * g + (c16 >> 2)) * 64 + 8 * (c16 & 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const i16x4_t a =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(rowp + 32 * (db >> 1) + 4 * (db & 1)));
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bb, acc[db], 0, 0, 0);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Slab layout (bf16 window kernels). The sparse-offset rows are streamed in a
+// layout of their own: lane l takes rows l / 8 and 8 + l / 8 of the wave's 16 rows
+// and the 16-byte chunk d = 8 (l % 8) .. 8 (l % 8) + 7 of each, so one load covers
+// eight whole 128-byte rows (the MFMA operand layout touches sixteen half rows per
+// load, which the L2 -> CU path serves about three times slower). Row sums run over
+// eight consecutive lanes with DPP.
+// ----------------------------------------------------------------------------
+
+struct SFrag {
+    u32x4_t r[2];  // bf16 chunk of the lane's first and second row
+};
+
+__device__ __forceinline__ void sfrag_load(SFrag &f, __amdgpu_buffer_rsrc_t rs, int row_a, int row_b, int c8) {
+    f.r[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_a * 128 + 16 * c8, 0, 0));
+    f.r[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_b * 128 + 16 * c8, 0, 0));
+}
+
+// Partial dot product of two 8-element bf16 chunks.
+__device__ __forceinline__ float chunk_dot(const u32x4_t &a, const u32x4_t &b) {
+    float s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[0]), as_bf16x2(b[0]), 0.f, false);
+    float s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[1]), as_bf16x2(b[1]), 0.f, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[2]), as_bf16x2(b[2]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[3]), as_bf16x2(b[3]), s1, false);
+    return s0 + s1;
+}
+
+// acc[0..1] (8 fp32 values of one row) += x * chunk, with x rounded to bf16 (packed dot unit).
+__device__ __forceinline__ void chunk_axpy(f32x4_t acc[2], float x, const u32x4_t &c) {
+    const bf16x2_t xl = as_bf16x2(pack_bf16(x, 0.f));
+    const bf16x2_t xh = as_bf16x2(pack_bf16(0.f, x));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const bf16x2_t v = as_bf16x2(c[w]);
+        f32x4_t &a = acc[w >> 1];
+        const int r = 2 * (w & 1);
+        a[r] = __builtin_amdgcn_fdot2_f32_bf16(v, xl, a[r], false);
+        a[r + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, xh, a[r + 1], false);
+    }
+}
+
+// DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], and the mirror of each half row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+
+__device__ __forceinline__ float row8_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor2, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppHalfMirror, 0xF, 0xF, false));
+    return x;
+}
+__device__ __forceinline__ float row8_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor2, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppHalfMirror, 0xF, 0xF, false)));
+    return x;
+}
+
+// Stores row `row` chunk (8 values, times mul) of a slab-layout accumulator.
+__device__ __forceinline__ void store_chunk(uint16_t *base, int64_t row, int c8, const f32x4_t a[2], float mul) {
+    const f32x4_t x = a[0] * mul, y = a[1] * mul;
+    const u32x4_t v = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+    *reinterpret_cast<u32x4_t *>(base + row * 64 + 8 * c8) = v;
+}
+__device__ __forceinline__ void store_chunk(float *base, int64_t row, int c8, const f32x4_t a[2], float mul) {
+    *reinterpret_cast<f32x4_t *>(base + row * 64 + 8 * c8) = a[0] * mul;
+    *reinterpret_cast<f32x4_t *>(base + row * 64 + 8 * c8 + 4) = a[1] * mul;
+}
+
+// Moves a 16-row accumulator from the MFMA C layout (lane (q = l % 16, g), acc[db][r] =
+// row q, d = acc_row_d(db, 4 g + r)) to the slab layout through a wave-private fp32
+// area of 16 x 64 values; 16-byte units are XOR-swizzled by row to spread LDS banks.
+// The writes and reads come from the same wave and are processed in order.
+__device__ __forceinline__ void c_to_slab(float *area, const f32x4_t acc[4], f32x4_t out[2][2], int c16, int g,
+                                          int s8, int c8) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int unit = 8 * (db >> 1) + 2 * g + (db & 1);
+        *reinterpret_cast<f32x4_t *>(area + c16 * 64 + 4 * (unit ^ c16)) = acc[db];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = s8 + 8 * h;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) out[h][b] = *reinterpret_cast<const f32x4_t *>(area + row * 64 + 4 * ((2 * c8 + b) ^ row));
+    }
+}
+
+// ----------------------------------------------------------------------------
 // forward
 // ----------------------------------------------------------------------------
 
-enum FwdMode { kWindow = 0, kWide = 1, kDense = 2 };
+enum FwdMode { kWide = 1, kDense = 2 };
 
 // Sparse offsets t in [t_begin, n_off), four at a time, each with one online
 // softmax update (used beyond the prefetched offsets and by the wide path).
@@ -357,13 +548,13 @@ __device__ __forceinline__ void fwd_slabs_loop(const AttnParams &p, int t_begin,
         }
         const float mn = fmaxf(m2, gm);
         const float ms = (mn == kNegInf) ? 0.f : mn;
-        const float al = exp2f(m2 - ms);
+        const float al = fast_exp2(m2 - ms);
         float ps = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] *= al;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const float pu = exp2f(sc[u] - ms);
+            const float pu = fast_exp2(sc[u] - ms);
             ps += pu;
             frag_axpy(acc, pu, vf[u]);
         }
@@ -376,8 +567,7 @@ template <bool BF16, bool OUT_BF16, int MODE>
 __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
     using OE = typename Elem<OUT_BF16>::T;
-    // window mode: V^T of keys [i0 - 64, i0 + 64); wide/dense: V^T of one 64-key chunk
-    __shared__ __attribute__((aligned(16))) E vt[MODE == kWindow ? 64 * kT128 : 64 * kT64];
+    __shared__ __attribute__((aligned(16))) E vt[64 * kT64];  // V^T of one 64-key chunk
 
     const int n = p.n, w = p.w;
     const int nt = (n + 63) >> 6;
@@ -403,136 +593,47 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     float m2 = kNegInf;  // running max of log2-scaled scores
     float lsum = 0.f;    // this lane's share of the running sum
 
-    if constexpr (MODE == kWindow) {
-        // ---------------- window of at most 64 keys: every load issued up front ----------------
-        StageRegs<BF16> vs;
-        stage_load(vs, V, i0 - 64, n, tid);
-        const int qb = r0 >> 4;  // the wave's 16-row block; its keys lie in blocks qb-4 .. qb
-        Frag<BF16> kf[5];
-#pragma unroll
-        for (int b = 0; b < 5; ++b) load_frag(kf[b], K, min(max(16 * (qb - 4 + b) + c16, 0), n - 1), g);
-        Frag<BF16> sk[kSlabRegs], sv[kSlabRegs];
-        int sj[kSlabRegs];
-        bool sok[kSlabRegs];
-#pragma unroll
-        for (int t = 0; t < kSlabRegs; ++t) {
-            const int j = (t < p.n_off) ? i - p.off[t] : -1;
-            sok[t] = row_ok && j >= 0;
-            sj[t] = min(max(j, 0), n - 1);
-            if (t < p.n_off) load_frag(sk[t], K, sj[t], g);
-        }
-        stage_store(vt, kT128, vs, tid);
+    // ---------------- wide window or dense: 64-key chunks with an online softmax ----------------
+    const int jlo = max(0, i0 - w + 1), jhi = min(n - 1, i0 + 63);
+    const int wlo = r0 - w + 1, whi = min(r0 + 15, n - 1);  // keys this wave needs
+    for (int c0 = jlo & ~63; c0 <= jhi; c0 += 64) {
         __syncthreads();
+        stage_tile<64, BF16>(vt, kT64, V, c0, n, tid);
+        __syncthreads();
+        if (r0 >= n) continue;
 #pragma unroll
-        for (int t = 0; t < kSlabRegs; ++t)
-            if (t < p.n_off) load_frag(sv[t], V, sj[t], g);
-
-        // window band: all 20 scores of the lane, one max, then P.V on MFMA
-        const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);  // keys the wave needs
-        float sc[5][4];
-        float bm = kNegInf;
-#pragma unroll
-        for (int b = 0; b < 5; ++b) {
-            const int kb0 = 16 * (qb - 4 + b);
-            const bool active = kb0 + 15 >= klo && kb0 <= khi;
-            const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
-            f32x4_t st = {kNegInf, kNegInf, kNegInf, kNegInf};
-            if (active) st = mma_over_d(kf[b], qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+        for (int kb = 0; kb < 4; ++kb) {
+            const int kb0 = c0 + 16 * kb;
+            if (kb0 + 15 < wlo || kb0 > whi) continue;  // uniform across the wave
+            Frag<BF16> kf;
+            load_frag(kf, K, min(kb0 + c16, n - 1), g);
+            const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+            float sv[4], bm = kNegInf;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int j = kb0 + 4 * g + r;
-                const bool ok = full || (active && row_ok && j <= i && j > i - w && j >= 0);
-                sc[b][r] = ok ? st[r] : kNegInf;
-                bm = fmaxf(bm, sc[b][r]);
+                const bool ok = row_ok && j <= i && j > i - w;
+                sv[r] = ok ? st[r] : kNegInf;
+                bm = fmaxf(bm, sv[r]);
             }
-        }
-        m2 = group_max(bm);
-        const float ms = row_ok ? m2 : 0.f;
-#pragma unroll
-        for (int b = 0; b < 5; ++b) {
-            const int kb0 = 16 * (qb - 4 + b);
-            const bool active = kb0 + 15 >= klo && kb0 <= khi;
-            float pr[4];
+            bm = group_max(bm);
+            const float mn = fmaxf(m2, bm);
+            const float ms = (mn == kNegInf) ? 0.f : mn;
+            const float al = fast_exp2(m2 - ms);
+            float pr[4], ps = 0.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                pr[r] = exp2f(sc[b][r] - ms);
-                lsum += pr[r];
+                pr[r] = fast_exp2(sv[r] - ms);
+                ps += pr[r];
             }
-            if (active) mma_over_rows(acc, vt, kT128, 16 * (wave + b), c16, g, pr);
+            lsum = lsum * al + ps;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] *= al;
+            m2 = mn;
+            mma_over_rows(acc, vt, kT64, 16 * kb, c16, g, pr);
         }
-
-        // prefetched sparse offsets: scores, one rescale, then the P.V terms
-        float ss[kSlabRegs];
-        float gm = kNegInf;
-#pragma unroll
-        for (int t = 0; t < kSlabRegs; ++t) {
-            ss[t] = kNegInf;
-            if (t < p.n_off) {
-                const float d = group_sum(frag_dot(qf, sk[t]));
-                ss[t] = sok[t] ? d * sl2 : kNegInf;
-            }
-            gm = fmaxf(gm, ss[t]);
-        }
-        const float mn = fmaxf(m2, gm);
-        const float ms2 = (mn == kNegInf) ? 0.f : mn;
-        const float al = exp2f(m2 - ms2);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] *= al;
-        float ps = 0.f;
-#pragma unroll
-        for (int t = 0; t < kSlabRegs; ++t) {
-            if (t < p.n_off) {
-                const float pt = exp2f(ss[t] - ms2);
-                ps += pt;
-                frag_axpy(acc, pt, sv[t]);
-            }
-        }
-        lsum = lsum * al + (g == 0 ? ps : 0.f);
-        m2 = mn;
-        if (p.n_off > kSlabRegs && r0 < n) fwd_slabs_loop(p, kSlabRegs, qf, K, V, i, row_ok, r0, n, g, acc, m2, lsum);
-    } else {
-        // ---------------- wide window or dense: 64-key chunks with an online softmax ----------------
-        const int jlo = max(0, i0 - w + 1), jhi = min(n - 1, i0 + 63);
-        const int wlo = r0 - w + 1, whi = min(r0 + 15, n - 1);  // keys this wave needs
-        for (int c0 = jlo & ~63; c0 <= jhi; c0 += 64) {
-            __syncthreads();
-            stage_tile<64, BF16>(vt, kT64, V, c0, n, tid);
-            __syncthreads();
-            if (r0 >= n) continue;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int kb0 = c0 + 16 * kb;
-                if (kb0 + 15 < wlo || kb0 > whi) continue;  // uniform across the wave
-                Frag<BF16> kf;
-                load_frag(kf, K, min(kb0 + c16, n - 1), g);
-                const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
-                float sv[4], bm = kNegInf;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = kb0 + 4 * g + r;
-                    const bool ok = row_ok && j <= i && j > i - w;
-                    sv[r] = ok ? st[r] : kNegInf;
-                    bm = fmaxf(bm, sv[r]);
-                }
-                bm = group_max(bm);
-                const float mn = fmaxf(m2, bm);
-                const float ms = (mn == kNegInf) ? 0.f : mn;
-                const float al = exp2f(m2 - ms);
-                float pr[4], ps = 0.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pr[r] = exp2f(sv[r] - ms);
-                    ps += pr[r];
-                }
-                lsum = lsum * al + ps;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc[c] *= al;
-                m2 = mn;
-                mma_over_rows(acc, vt, kT64, 16 * kb, c16, g, pr);
-            }
-        }
-        if (MODE == kWide && r0 < n) fwd_slabs_loop(p, 0, qf, K, V, i, row_ok, r0, n, g, acc, m2, lsum);
     }
+    if (MODE == kWide && r0 < n) fwd_slabs_loop(p, 0, qf, K, V, i, row_ok, r0, n, g, acc, m2, lsum);
 
     // ---- epilogue ----
     const float l = group_sum(lsum);
@@ -542,34 +643,235 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     }
 }
 
+// Forward, bf16 inputs, window w <= 64. The sparse slabs stream first, in the slab
+// layout, through a ring of four row pairs per lane (one online softmax state per
+// row); meanwhile the workgroup's band keys [i0 - 64, i0 + 64) are copied into LDS
+// (K and V row-major). The band then runs on MFMA with its own softmax state, and
+// the two states are merged per row in the slab layout, which also stores O.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p) {
+    using OE = typename Elem<OUT_BF16>::T;
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kTileRows * 64];  // band K rows, then merge areas
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kTileRows * 64];  // band V rows, then band row stats
+
+    const int n = p.n, w = p.w, n_off = p.n_off;
+    const int nt = (n + 63) >> 6;
+    const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
+    const int bh = lb / nt, tile = lb - bh * nt;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15, g = lane >> 4;  // MFMA layout: row c16, lane group g
+    const int s8 = lane >> 3, c8 = lane & 7;   // slab layout: rows s8 and 8 + s8, chunk c8
+    const int i0 = tile * 64, r0 = i0 + 16 * wave;
+    const int row_s[2] = {r0 + s8, r0 + 8 + s8};
+    const int64_t head = (int64_t)bh * n * 64;
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q) + head;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128), rv = head_rsrc(V, n * 128);
+    const float sl2 = p.scale_log2;
+
+    // issue order matters: the slab loads go before the band copies, so waiting for
+    // them does not wait for the copies
+    SFrag qs;
+    sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+    SFrag sk[4], sv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+        sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+    }
+    dma_tile(ks, K, i0 - 64, n, wave, lane);
+    dma_tile(vs, V, i0 - 64, n, wave, lane);
+
+    // ---- sparse slabs: one online softmax state per row (replicated over its 8 lanes) ----
+    float m_s[2] = {kNegInf, kNegInf}, l_s[2] = {0.f, 0.f};
+    f32x4_t acc_s[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) acc_s[h][0] = acc_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t0 = 0; t0 < 8; t0 += 4) {
+        if (t0 >= n_off || r0 + 15 < p.off[t0]) break;  // ascending offsets
+        float ss[4][2], gm[2] = {kNegInf, kNegInf};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int o = table_off(p, t0 + u);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                ss[u][h] = ok ? d * sl2 : kNegInf;
+                gm[h] = fmaxf(gm[h], ss[u][h]);
+            }
+            if (t0 == 0)
+                sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+        }
+        float ms[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float mn = fmaxf(m_s[h], gm[h]);
+            ms[h] = (mn == kNegInf) ? 0.f : mn;
+            const float al = fast_exp2(m_s[h] - ms[h]);
+            acc_s[h][0] *= al;
+            acc_s[h][1] *= al;
+            l_s[h] *= al;
+            m_s[h] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float pt = fast_exp2(ss[u][h] - ms[h]);
+                l_s[h] += pt;
+                chunk_axpy(acc_s[h], pt, sv[u].r[h]);
+            }
+            if (t0 == 0)
+                sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+        }
+    }
+    for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
+        if (r0 + 15 < p.off[t]) break;
+        SFrag kt, vt;
+        sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+        sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
+            const float d = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
+            const float sv1 = ok ? d * sl2 : kNegInf;
+            const float mn = fmaxf(m_s[h], sv1);
+            const float ms = (mn == kNegInf) ? 0.f : mn;
+            const float al = fast_exp2(m_s[h] - ms);
+            const float pt = fast_exp2(sv1 - ms);
+            acc_s[h][0] *= al;
+            acc_s[h][1] *= al;
+            l_s[h] = l_s[h] * al + pt;
+            m_s[h] = mn;
+            chunk_axpy(acc_s[h], pt, vt.r[h]);
+        }
+    }
+
+    // ---- window band on MFMA: rows r0..r0+15 (row c16 of the lane) see key blocks qb-4 .. qb ----
+    const int i = r0 + c16;
+    const bool row_ok = i < n;
+    Frag<true> qf;
+    buf_frag(qf, rq, i, g);
+    wait_vm_all();
+    __syncthreads();
+    const int qb = r0 >> 4;
+    const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
+    float sc[5][4];
+    float bm = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const int kb0 = 16 * (qb - 4 + b);
+        const bool active = kb0 + 15 >= klo && kb0 <= khi;
+        const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
+        f32x4_t st = {kNegInf, kNegInf, kNegInf, kNegInf};
+        if (active) {
+            Frag<true> kf;
+            lds_frag(kf, ks, 16 * (wave + b) + c16, g);
+            st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = kb0 + 4 * g + r;
+            const bool ok = full || (active && row_ok && j <= i && j > i - w && j >= 0);
+            sc[b][r] = ok ? st[r] : kNegInf;
+            bm = fmaxf(bm, sc[b][r]);
+        }
+    }
+    const float m_b = group_max(bm);
+    const float msb = row_ok ? m_b : 0.f;  // a valid row always attends itself
+    f32x4_t acc_b[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc_b[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float lsum_b = 0.f;
+#pragma unroll
+    for (int b = 0; b < 5; ++b) {
+        const int kb0 = 16 * (qb - 4 + b);
+        const bool active = kb0 + 15 >= klo && kb0 <= khi;
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = fast_exp2(sc[b][r] - msb);
+            lsum_b += pr[r];
+        }
+        if (active) mma_over_rows_tr(acc_b, vs, 16 * (wave + b), c16, g, pr);
+    }
+    const float l_b = group_sum(lsum_b);
+
+    // ---- merge the band state into the slab layout, normalise, store ----
+    __syncthreads();  // every wave is done with the band tiles
+    float *area = reinterpret_cast<float *>(ks) + wave * 1024;
+    float *stat = reinterpret_cast<float *>(vs) + wave * 32;
+    if (g == 0) {
+        stat[c16] = m_b;
+        stat[16 + c16] = l_b;
+    }
+    f32x4_t accb[2][2];
+    c_to_slab(area, acc_b, accb, c16, g, s8, c8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rl = s8 + 8 * h;
+        const float mb = stat[rl], lb2 = stat[16 + rl];
+        const float m = fmaxf(m_s[h], mb);
+        const float ms = (m == kNegInf) ? 0.f : m;
+        const float fa = fast_exp2(m_s[h] - ms), fb = fast_exp2(mb - ms);
+        const float l = l_s[h] * fa + lb2 * fb;
+        const f32x4_t o[2] = {acc_s[h][0] * fa + accb[h][0] * fb, acc_s[h][1] * fa + accb[h][1] * fb};
+        if (row_s[h] < n) {
+            store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, o, 1.f / l);
+            if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = m * kLn2 + logf(l);
+        }
+    }
+}
+
 // ----------------------------------------------------------------------------
 // backward: D = rowsum(dO * O)
 // ----------------------------------------------------------------------------
 
+// D = rowsum(dO * O): eight lanes per 64-wide row, 16 bytes each (bf16); a workgroup
+// covers 32 rows per pass and two passes.
 template <bool BF16>
 __global__ void __launch_bounds__(kThreads) delta_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
+    constexpr int kPer = 16 / sizeof(E);  // elements per lane and load
+    constexpr int kLanesPerRow = 64 / kPer;
+    constexpr int kRowsPerPass = kThreads / kLanesPerRow;
     const int64_t rows = (int64_t)p.bh * p.n;
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int part = threadIdx.x & 15;  // 4 elements each
-    float acc = 0.f;
-    if (row < rows) {
-        const E *o = static_cast<const E *>(p.o) + row * 64 + 4 * part;
-        const E *d = static_cast<const E *>(p.dout) + row * 64 + 4 * part;
-        if constexpr (BF16) {
-            const u32x2_t a = *reinterpret_cast<const u32x2_t *>(o);
-            const u32x2_t b = *reinterpret_cast<const u32x2_t *>(d);
-            acc = bf16_lo(a.x) * bf16_lo(b.x) + bf16_hi(a.x) * bf16_hi(b.x) + bf16_lo(a.y) * bf16_lo(b.y) +
-                  bf16_hi(a.y) * bf16_hi(b.y);
-        } else {
-            const f32x4_t a = *reinterpret_cast<const f32x4_t *>(o);
-            const f32x4_t b = *reinterpret_cast<const f32x4_t *>(d);
-            acc = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    const int part = threadIdx.x % kLanesPerRow;
+    float acc[2];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int64_t row = ((int64_t)blockIdx.x * 2 + pass) * kRowsPerPass + threadIdx.x / kLanesPerRow;
+        acc[pass] = 0.f;
+        if (row < rows) {
+            const E *o = static_cast<const E *>(p.o) + row * 64 + kPer * part;
+            const E *d = static_cast<const E *>(p.dout) + row * 64 + kPer * part;
+            if constexpr (BF16) {
+                const u32x4_t a = *reinterpret_cast<const u32x4_t *>(o);
+                const u32x4_t b = *reinterpret_cast<const u32x4_t *>(d);
+                float s = 0.f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[k]), as_bf16x2(b[k]), s, false);
+                acc[pass] = s;
+            } else {
+                const f32x4_t a = *reinterpret_cast<const f32x4_t *>(o);
+                const f32x4_t b = *reinterpret_cast<const f32x4_t *>(d);
+                acc[pass] = a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+            }
         }
     }
 #pragma unroll
-    for (int sh = 1; sh < 16; sh <<= 1) acc += __shfl_xor(acc, sh);
-    if (row < rows && part == 0) p.delta[row] = acc;
+    for (int pass = 0; pass < 2; ++pass) {
+        float s = acc[pass];
+#pragma unroll
+        for (int sh = 1; sh < kLanesPerRow; sh <<= 1) s += __shfl_xor(s, sh);
+        const int64_t row = ((int64_t)blockIdx.x * 2 + pass) * kRowsPerPass + threadIdx.x / kLanesPerRow;
+        if (row < rows && part == 0) p.delta[row] = s;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -577,7 +879,7 @@ __global__ void __launch_bounds__(kThreads) delta_kernel(const AttnParams p) {
 // ----------------------------------------------------------------------------
 
 template <bool BF16, bool OUT_BF16>
-__global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
+__global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) E t0s[64 * kT64];  // transposed tile (K^T, or Q^T)
@@ -636,7 +938,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                 for (int r = 0; r < 4; ++r) {
                     const int j = kb0 + 4 * g + r;
                     const bool ok = row_ok && j <= i && j > i - w;
-                    const float pv = ok ? exp2f(st[r] * sl2 - lse2) : 0.f;
+                    const float pv = ok ? fast_exp2(st[r] * sl2 - lse2) : 0.f;
                     ds[r] = pv * (dpt[r] - di);
                 }
                 mma_over_rows(acc, t0s, kT64, 16 * kb, c16, g, ds);
@@ -654,7 +956,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                 load_frag(vf, V, jc, g);
                 const float s = group_sum(frag_dot(qf, kf));
                 const float dp = group_sum(frag_dot(df, vf));
-                const float pv = ok ? exp2f(s * sl2 - lse2) : 0.f;
+                const float pv = ok ? fast_exp2(s * sl2 - lse2) : 0.f;
                 frag_axpy(acc, pv * (dp - di), kf);
             }
         }
@@ -705,7 +1007,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                     const int qi = 16 * qb + 4 * g + r;  // row within the chunk
                     const int iq = c0 + qi;
                     const bool ok = key_ok && iq < n && iq >= j && iq - j < w;
-                    pr[r] = ok ? exp2f(sq[r] * sl2 - lse_s[qi]) : 0.f;
+                    pr[r] = ok ? fast_exp2(sq[r] * sl2 - lse_s[qi]) : 0.f;
                     ds[r] = pr[r] * (dpq[r] - del_s[qi]);
                 }
                 mma_over_rows(dv, t1s, kT64, 16 * qb, c16, g, pr);
@@ -725,7 +1027,7 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
                 load_frag(df, DO, ic, g);
                 const float s = group_sum(frag_dot(qf, kf));
                 const float dp = group_sum(frag_dot(df, vf));
-                const float pv = ok ? exp2f(s * sl2 - LSE[ic] * kLog2e) : 0.f;
+                const float pv = ok ? fast_exp2(s * sl2 - LSE[ic] * kLog2e) : 0.f;
                 const float dsv = pv * (dp - DEL[ic]);
                 frag_axpy(dv, pv, df);
                 frag_axpy(dk, dsv, qf);
@@ -738,63 +1040,333 @@ __global__ void __launch_bounds__(kThreads) bwd_kernel(const AttnParams p) {
     }
 }
 
-template <bool BF16, bool OUT_BF16, int MODE>
-hipError_t launch_forward_t(const AttnParams &p, hipStream_t stream) {
-    const int nt = (p.n + 63) / 64;
-    const dim3 grid(p.bh * nt), block(kThreads);
+// Backward, bf16 inputs, window w <= 64. One workgroup owns rows [t0, t0 + 64).
+// Phase A forms dQ of those query rows: the slab keys t - o stream in the slab
+// layout while the band keys [t0 - 64, t0 + 64) are copied into LDS (K, V); the band
+// then runs on MFMA and its part of dQ joins the slab part through LDS. Phase B does
+// the same for dK, dV of those key rows with the slab queries t + o and the band
+// queries [t0, t0 + 128) (Q, dO, LSE and D in LDS). Every output row has one writer.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p) {
+    using OE = typename Elem<OUT_BF16>::T;
+    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // K rows, then Q rows; merge areas
+    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // V rows, then dO rows; merge areas
+    __shared__ __attribute__((aligned(16))) float lse_s[kTileRows];       // log2-scaled LSE of band queries
+    __shared__ __attribute__((aligned(16))) float del_s[kTileRows];       // D of band queries
+
+    const int n = p.n, w = p.w, n_off = p.n_off;
+    const int nt = (n + 63) >> 6;
+    const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
+    const int bh = lb / nt, tile = lb - bh * nt;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, g = lane >> 4;  // MFMA layout
+    const int s8 = lane >> 3, c8 = lane & 7;   // slab layout
+    const int t0 = tile * 64, r0 = t0 + 16 * wave;
+    const int row_s[2] = {r0 + s8, r0 + 8 + s8};
+    const int me = r0 + c16;  // MFMA-layout row: query row in phase A, key row in phase B
+    const bool me_ok = me < n;
+    const int64_t head = (int64_t)bh * n * 64;
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q) + head;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
+    const uint16_t *DO = static_cast<const uint16_t *>(p.dout) + head;
+    const float *LSE = p.lse_in + (int64_t)bh * n;
+    const float *DEL = p.delta + (int64_t)bh * n;
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128);
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, n * 128), rdo = head_rsrc(DO, n * 128);
+    const __amdgpu_buffer_rsrc_t rl = head_rsrc(LSE, n * 4), rd = head_rsrc(DEL, n * 4);
+    const float sl2 = p.scale_log2;
+    float *area_a = reinterpret_cast<float *>(ta) + wave * 1024;  // 16 x 64 fp32 per wave
+    float *area_b = reinterpret_cast<float *>(tb) + wave * 1024;
+
+    // =========================== phase A: dQ of query rows ===========================
+    {
+        SFrag qs, dos;
+        sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+        sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
+        float lse2[2], di[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
+            di[h] = buf_f32(rd, row_s[h]);
+        }
+        SFrag sk[4], sv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+            sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+        }
+        dma_tile(ta, K, t0 - 64, n, wave, lane);
+        dma_tile(tb, V, t0 - 64, n, wave, lane);
+
+        f32x4_t dq_s[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) dq_s[h][0] = dq_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < 8; s0 += 4) {
+            if (s0 >= n_off || r0 + 15 < p.off[s0]) break;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int o = table_off(p, s0 + u);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                    const float s = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                    const float dp = row8_sum(chunk_dot(dos.r[h], sv[u].r[h]));
+                    const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                    chunk_axpy(dq_s[h], pv * (dp - di[h]), sk[u].r[h]);
+                }
+                if (s0 == 0) {
+                    sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+                    sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+                }
+            }
+        }
+        for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
+            if (r0 + 15 < p.off[t]) break;
+            SFrag kt, vt;
+            sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+            sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
+                const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
+                const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
+                const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                chunk_axpy(dq_s[h], pv * (dp - di[h]), kt.r[h]);
+            }
+        }
+
+        // band on MFMA: query row me sees key blocks qb-4 .. qb
+        const int i = me;
+        Frag<true> qf, df;
+        buf_frag(qf, rq, i, g);
+        buf_frag(df, rdo, i, g);
+        const float lse2_i = buf_f32(rl, i) * kLog2e;
+        const float di_i = buf_f32(rd, i);
+        wait_vm_all();
+        __syncthreads();
+        f32x4_t acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int qb = r0 >> 4;
+        const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
+#pragma unroll 1
+        for (int b = 0; b < 5; ++b) {
+            const int kb0 = 16 * (qb - 4 + b);
+            if (kb0 + 15 < klo || kb0 > khi) continue;  // uniform across the wave
+            const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
+            const int lr = 16 * (wave + b);
+            Frag<true> kf, vf;
+            lds_frag(kf, ta, lr + c16, g);
+            lds_frag(vf, tb, lr + c16, g);
+            const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            float ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = kb0 + 4 * g + r;
+                const bool ok = full || (me_ok && j <= i && j > i - w && j >= 0);
+                const float pv = ok ? fast_exp2(st[r] * sl2 - lse2_i) : 0.f;
+                ds[r] = pv * (dpt[r] - di_i);
+            }
+            mma_over_rows_tr(acc, ta, lr, c16, g, ds);
+        }
+        __syncthreads();  // every wave is done with the K, V band tiles
+        f32x4_t dq_b[2][2];
+        c_to_slab(area_a, acc, dq_b, c16, g, s8, c8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (row_s[h] < n) {
+                const f32x4_t o[2] = {dq_s[h][0] + dq_b[h][0], dq_s[h][1] + dq_b[h][1]};
+                store_chunk(static_cast<OE *>(p.dq) + head, row_s[h], c8, o, p.scale);
+            }
+        }
+        __syncthreads();  // the merge areas are reused by phase B's copies
+    }
+
+    // ========================= phase B: dK, dV of key rows ==========================
+    {
+        SFrag kS, vS;
+        sfrag_load(kS, rk, row_s[0], row_s[1], c8);
+        sfrag_load(vS, rv, row_s[0], row_s[1], c8);
+        SFrag sq[4], sd[4];
+        float sl[4][2], sdl[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int iq0 = slab_row(p, u, row_s[0], 1), iq1 = slab_row(p, u, row_s[1], 1);
+            sfrag_load(sq[u], rq, iq0, iq1, c8);
+            sfrag_load(sd[u], rdo, iq0, iq1, c8);
+            sl[u][0] = buf_f32(rl, iq0);
+            sl[u][1] = buf_f32(rl, iq1);
+            sdl[u][0] = buf_f32(rd, iq0);
+            sdl[u][1] = buf_f32(rd, iq1);
+        }
+        dma_tile(ta, Q, t0, n, wave, lane);
+        dma_tile(tb, DO, t0, n, wave, lane);
+        if (tid < kTileRows) {
+            const int row = t0 + tid;
+            lse_s[tid] = (row < n) ? LSE[row] * kLog2e : 0.f;
+            del_s[tid] = (row < n) ? DEL[row] : 0.f;
+        }
+
+        f32x4_t dk_s[2][2], dv_s[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            dk_s[h][0] = dk_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dv_s[h][0] = dv_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        // sparse offsets: queries j + o
+#pragma unroll
+        for (int s0 = 0; s0 < 8; s0 += 4) {
+            if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int o = table_off(p, s0 + u);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bool ok = (row_s[h] < n) & (row_s[h] + o < n);
+                    const float s = row8_sum(chunk_dot(sq[u].r[h], kS.r[h]));
+                    const float dp = row8_sum(chunk_dot(sd[u].r[h], vS.r[h]));
+                    const float pv = ok ? fast_exp2(s * sl2 - sl[u][h] * kLog2e) : 0.f;
+                    chunk_axpy(dv_s[h], pv, sd[u].r[h]);
+                    chunk_axpy(dk_s[h], pv * (dp - sdl[u][h]), sq[u].r[h]);
+                }
+                if (s0 == 0) {
+                    const int iq0 = slab_row(p, u + 4, row_s[0], 1), iq1 = slab_row(p, u + 4, row_s[1], 1);
+                    sfrag_load(sq[u], rq, iq0, iq1, c8);
+                    sfrag_load(sd[u], rdo, iq0, iq1, c8);
+                    sl[u][0] = buf_f32(rl, iq0);
+                    sl[u][1] = buf_f32(rl, iq1);
+                    sdl[u][0] = buf_f32(rd, iq0);
+                    sdl[u][1] = buf_f32(rd, iq1);
+                }
+            }
+        }
+        for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
+            if (r0 + p.off[t] >= n) break;
+            const int iq0 = row_s[0] + p.off[t], iq1 = row_s[1] + p.off[t];
+            SFrag qt, dt;
+            sfrag_load(qt, rq, iq0, iq1, c8);
+            sfrag_load(dt, rdo, iq0, iq1, c8);
+            const float lq[2] = {buf_f32(rl, iq0), buf_f32(rl, iq1)};
+            const float dq2[2] = {buf_f32(rd, iq0), buf_f32(rd, iq1)};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] + p.off[t] < n);
+                const float s = row8_sum(chunk_dot(qt.r[h], kS.r[h]));
+                const float dp = row8_sum(chunk_dot(dt.r[h], vS.r[h]));
+                const float pv = ok ? fast_exp2(s * sl2 - lq[h] * kLog2e) : 0.f;
+                chunk_axpy(dv_s[h], pv, dt.r[h]);
+                chunk_axpy(dk_s[h], pv * (dp - dq2[h]), qt.r[h]);
+            }
+        }
+
+        // band on MFMA: key row me sees query blocks r0 + 16 b
+        const int j = me;
+        Frag<true> kf, vf;
+        buf_frag(kf, rk, j, g);
+        buf_frag(vf, rv, j, g);
+        wait_vm_all();
+        __syncthreads();
+        f32x4_t dk[4], dv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            dk[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        const int qhi = min(r0 + 15 + w - 1, n - 1);
+#pragma unroll 1
+        for (int b = 0; b < 5; ++b) {
+            const int qb0 = r0 + 16 * b;
+            if (qb0 > qhi) break;  // uniform across the wave
+            const bool full = qb0 >= r0 + 15 && qb0 + 15 <= r0 + w - 1 && qb0 + 15 < n && r0 + 15 < n;
+            const int lr = 16 * (wave + b);
+            Frag<true> qf, df;
+            lds_frag(qf, ta, lr + c16, g);
+            lds_frag(df, tb, lr + c16, g);
+            const f32x4_t sq4 = mma_over_d(qf, kf, f32x4_t{0.f, 0.f, 0.f, 0.f});  // rows: queries
+            const f32x4_t dp4 = mma_over_d(df, vf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse_s + lr + 4 * g);
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + lr + 4 * g);
+            float pr[4], ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int q = qb0 + 4 * g + r;
+                const bool ok = full || (me_ok && q < n && q >= j && q - j < w);
+                pr[r] = ok ? fast_exp2(sq4[r] * sl2 - l4[r]) : 0.f;
+                ds[r] = pr[r] * (dp4[r] - d4[r]);
+            }
+            mma_over_rows_tr(dv, tb, lr, c16, g, pr);
+            mma_over_rows_tr(dk, ta, lr, c16, g, ds);
+        }
+        __syncthreads();  // every wave is done with the Q, dO band tiles
+        f32x4_t dk_b[2][2], dv_b[2][2];
+        c_to_slab(area_a, dk, dk_b, c16, g, s8, c8);
+        c_to_slab(area_b, dv, dv_b, c16, g, s8, c8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (row_s[h] < n) {
+                const f32x4_t ok_[2] = {dk_s[h][0] + dk_b[h][0], dk_s[h][1] + dk_b[h][1]};
+                const f32x4_t ov_[2] = {dv_s[h][0] + dv_b[h][0], dv_s[h][1] + dv_b[h][1]};
+                store_chunk(static_cast<OE *>(p.dk) + head, row_s[h], c8, ok_, p.scale);
+                store_chunk(static_cast<OE *>(p.dv) + head, row_s[h], c8, ov_, 1.f);
+            }
+        }
+    }
+}
+
+template <typename Kernel>
+hipError_t launch(Kernel *kernel, unsigned grid, const AttnParams &p, hipStream_t stream) {
     AttnParams a = p;
     void *args[] = {&a};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&fwd_kernel<BF16, OUT_BF16, MODE>), grid, block, args, 0,
-                           stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), dim3(grid), dim3(kThreads), args, 0, stream);
 }
+
+unsigned tiles(const AttnParams &p) { return (unsigned)(p.bh * ((p.n + 63) / 64)); }
 
 template <int MODE>
-hipError_t launch_forward_mode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
+hipError_t launch_generic_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (dt == FSA_BF16)
-        return out_dt == FSA_BF16 ? launch_forward_t<true, true, MODE>(p, stream)
-                                  : launch_forward_t<true, false, MODE>(p, stream);
-    return out_dt == FSA_BF16 ? launch_forward_t<false, true, MODE>(p, stream)
-                              : launch_forward_t<false, false, MODE>(p, stream);
-}
-
-template <bool BF16>
-hipError_t launch_delta_t(const AttnParams &p, hipStream_t stream) {
-    AttnParams a = p;
-    void *args[] = {&a};
-    const int64_t rows = (int64_t)p.bh * p.n;
-    const dim3 grid((unsigned)((rows + 15) / 16)), block(kThreads);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&delta_kernel<BF16>), grid, block, args, 0, stream);
-}
-
-template <bool BF16, bool OUT_BF16>
-hipError_t launch_grads_t(const AttnParams &p, hipStream_t stream) {
-    AttnParams a = p;
-    void *args[] = {&a};
-    const int nt = (p.n + 63) / 64;
-    const dim3 grid(p.bh * nt), block(kThreads);
-    return hipLaunchKernel(reinterpret_cast<const void *>(&bwd_kernel<BF16, OUT_BF16>), grid, block, args, 0,
-                           stream);
+        return out_dt == FSA_BF16 ? launch(&fwd_kernel<true, true, MODE>, tiles(p), p, s)
+                                  : launch(&fwd_kernel<true, false, MODE>, tiles(p), p, s);
+    return out_dt == FSA_BF16 ? launch(&fwd_kernel<false, true, MODE>, tiles(p), p, s)
+                              : launch(&fwd_kernel<false, false, MODE>, tiles(p), p, s);
 }
 
 }  // namespace
 
-hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
-    return p.w <= 64 ? launch_forward_mode<kWindow>(dt, out_dt, p, stream)
-                     : launch_forward_mode<kWide>(dt, out_dt, p, stream);
+// The window kernels address a head with 32-bit byte offsets (buffer loads).
+bool window_path(fsa_dtype_t dt, const AttnParams &p) { return dt == FSA_BF16 && p.w <= 64 && p.n <= (1 << 24); }
+
+hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    if (window_path(dt, p))
+        return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true>, tiles(p), p, s)
+                                  : launch(&fwd_window_kernel<false>, tiles(p), p, s);
+    return launch_generic_forward<kWide>(dt, out_dt, p, s);
 }
 
-hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
-    return launch_forward_mode<kDense>(dt, out_dt, p, stream);
+hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    return launch_generic_forward<kDense>(dt, out_dt, p, s);
 }
 
-hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream) {
-    return dt == FSA_BF16 ? launch_delta_t<true>(p, stream) : launch_delta_t<false>(p, stream);
+hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t s) {
+    const int64_t rows = (int64_t)p.bh * p.n;
+    const int64_t per_block = dt == FSA_BF16 ? 64 : 32;  // two passes of 32 (bf16) or 16 (fp32) rows
+    const unsigned grid = (unsigned)((rows + per_block - 1) / per_block);
+    return dt == FSA_BF16 ? launch(&delta_kernel<true>, grid, p, s) : launch(&delta_kernel<false>, grid, p, s);
 }
 
-hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream) {
+hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    if (window_path(dt, p))
+        return out_dt == FSA_BF16 ? launch(&bwd_window_kernel<true>, tiles(p), p, s)
+                                  : launch(&bwd_window_kernel<false>, tiles(p), p, s);
     if (dt == FSA_BF16)
-        return out_dt == FSA_BF16 ? launch_grads_t<true, true>(p, stream) : launch_grads_t<true, false>(p, stream);
-    return out_dt == FSA_BF16 ? launch_grads_t<false, true>(p, stream) : launch_grads_t<false, false>(p, stream);
+        return out_dt == FSA_BF16 ? launch(&bwd_generic_kernel<true, true>, tiles(p), p, s)
+                                  : launch(&bwd_generic_kernel<true, false>, tiles(p), p, s);
+    return out_dt == FSA_BF16 ? launch(&bwd_generic_kernel<false, true>, tiles(p), p, s)
+                              : launch(&bwd_generic_kernel<false, false>, tiles(p), p, s);
 }
 
 }  // namespace fsa
