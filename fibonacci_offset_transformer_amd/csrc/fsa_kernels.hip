@@ -342,6 +342,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kTileRows = 128;  // rows per LDS tile: the 64-row tile and its 64-row neighbour
+constexpr int kRingA = 3;       // slab row pairs in flight per lane: backward phase A (K, V)
+constexpr int kRingB = 3;       // backward phase B (Q, dO, LSE, D)
+
+// Offsets handled by the unrolled, prefetching slab code for a ring of r slots:
+// whole groups of r covering at least the eight offsets of a window-64 table.
+constexpr int unrolled_slabs(int r) { return ((8 + r - 1) / r) * r; }
 
 // Copies rows [row0, row0 + 128) of a [n, 64] bf16 matrix into a row-major LDS
 // tile (128 bytes per row). Each of the four waves issues four 1 KiB transfers;
@@ -1041,11 +1047,12 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
 }
 
 // Backward, bf16 inputs, window w <= 64. One workgroup owns rows [t0, t0 + 64).
-// Phase A forms dQ of those query rows: the slab keys t - o stream in the slab
-// layout while the band keys [t0 - 64, t0 + 64) are copied into LDS (K, V); the band
-// then runs on MFMA and its part of dQ joins the slab part through LDS. Phase B does
-// the same for dK, dV of those key rows with the slab queries t + o and the band
-// queries [t0, t0 + 128) (Q, dO, LSE and D in LDS). Every output row has one writer.
+// Phase A forms dQ of those query rows: the band keys [t0 - 64, t0 + 64) are copied
+// into LDS (K, V) and processed on MFMA first; their part of dQ moves through LDS into
+// the slab layout, where the slab keys t - o stream through a register ring and add
+// their part. Phase B does the same for dK, dV of those key rows with the band queries
+// [t0, t0 + 128) (Q, dO, LSE, D in LDS, copied while phase A's slabs run) and the slab
+// queries t + o. Every output row has one writer; rows are stored whole.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
@@ -1082,63 +1089,8 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
 
     // =========================== phase A: dQ of query rows ===========================
     {
-        SFrag qs, dos;
-        sfrag_load(qs, rq, row_s[0], row_s[1], c8);
-        sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
-        float lse2[2], di[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
-            di[h] = buf_f32(rd, row_s[h]);
-        }
-        SFrag sk[4], sv[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
-            sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
-        }
         dma_tile(ta, K, t0 - 64, n, wave, lane);
         dma_tile(tb, V, t0 - 64, n, wave, lane);
-
-        f32x4_t dq_s[2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) dq_s[h][0] = dq_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s0 = 0; s0 < 8; s0 += 4) {
-            if (s0 >= n_off || r0 + 15 < p.off[s0]) break;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int o = table_off(p, s0 + u);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-                    const float s = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
-                    const float dp = row8_sum(chunk_dot(dos.r[h], sv[u].r[h]));
-                    const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
-                    chunk_axpy(dq_s[h], pv * (dp - di[h]), sk[u].r[h]);
-                }
-                if (s0 == 0) {
-                    sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
-                    sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
-                }
-            }
-        }
-        for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
-            if (r0 + 15 < p.off[t]) break;
-            SFrag kt, vt;
-            sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-            sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
-                const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
-                const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
-                const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
-                chunk_axpy(dq_s[h], pv * (dp - di[h]), kt.r[h]);
-            }
-        }
-
-        // band on MFMA: query row me sees key blocks qb-4 .. qb
         const int i = me;
         Frag<true> qf, df;
         buf_frag(qf, rq, i, g);
@@ -1147,6 +1099,8 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
         const float di_i = buf_f32(rd, i);
         wait_vm_all();
         __syncthreads();
+
+        // band on MFMA: query row i sees key blocks qb-4 .. qb
         f32x4_t acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1174,35 +1128,11 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
             mma_over_rows_tr(acc, ta, lr, c16, g, ds);
         }
         __syncthreads();  // every wave is done with the K, V band tiles
-        f32x4_t dq_b[2][2];
-        c_to_slab(area_a, acc, dq_b, c16, g, s8, c8);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (row_s[h] < n) {
-                const f32x4_t o[2] = {dq_s[h][0] + dq_b[h][0], dq_s[h][1] + dq_b[h][1]};
-                store_chunk(static_cast<OE *>(p.dq) + head, row_s[h], c8, o, p.scale);
-            }
-        }
-        __syncthreads();  // the merge areas are reused by phase B's copies
-    }
+        f32x4_t dq_s[2][2];
+        c_to_slab(area_a, acc, dq_s, c16, g, s8, c8);
+        __syncthreads();  // every wave has read its merge area back
 
-    // ========================= phase B: dK, dV of key rows ==========================
-    {
-        SFrag kS, vS;
-        sfrag_load(kS, rk, row_s[0], row_s[1], c8);
-        sfrag_load(vS, rv, row_s[0], row_s[1], c8);
-        SFrag sq[4], sd[4];
-        float sl[4][2], sdl[4][2];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int iq0 = slab_row(p, u, row_s[0], 1), iq1 = slab_row(p, u, row_s[1], 1);
-            sfrag_load(sq[u], rq, iq0, iq1, c8);
-            sfrag_load(sd[u], rdo, iq0, iq1, c8);
-            sl[u][0] = buf_f32(rl, iq0);
-            sl[u][1] = buf_f32(rl, iq1);
-            sdl[u][0] = buf_f32(rd, iq0);
-            sdl[u][1] = buf_f32(rd, iq1);
-        }
+        // phase B's band queries [t0, t0 + 128): copied while phase A's slabs run
         dma_tile(ta, Q, t0, n, wave, lane);
         dma_tile(tb, DO, t0, n, wave, lane);
         if (tid < kTileRows) {
@@ -1211,65 +1141,72 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
             del_s[tid] = (row < n) ? DEL[row] : 0.f;
         }
 
-        f32x4_t dk_s[2][2], dv_s[2][2];
+        // sparse offsets: keys i - o, in the slab layout
+        SFrag qs, dos;
+        sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+        sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
+        float lse2[2], di[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            dk_s[h][0] = dk_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dv_s[h][0] = dv_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
+            di[h] = buf_f32(rd, row_s[h]);
         }
-        // sparse offsets: queries j + o
+        SFrag sk[kRingA], sv[kRingA];
 #pragma unroll
-        for (int s0 = 0; s0 < 8; s0 += 4) {
-            if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
+        for (int u = 0; u < kRingA; ++u) {
+            sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+            sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+        }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+        for (int s0 = 0; s0 < unrolled_slabs(kRingA); s0 += kRingA) {
+            if (s0 >= n_off || r0 + 15 < p.off[s0]) break;
+#pragma unroll
+            for (int u = 0; u < kRingA; ++u) {
                 const int o = table_off(p, s0 + u);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const bool ok = (row_s[h] < n) & (row_s[h] + o < n);
-                    const float s = row8_sum(chunk_dot(sq[u].r[h], kS.r[h]));
-                    const float dp = row8_sum(chunk_dot(sd[u].r[h], vS.r[h]));
-                    const float pv = ok ? fast_exp2(s * sl2 - sl[u][h] * kLog2e) : 0.f;
-                    chunk_axpy(dv_s[h], pv, sd[u].r[h]);
-                    chunk_axpy(dk_s[h], pv * (dp - sdl[u][h]), sq[u].r[h]);
+                    const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                    const float s = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                    const float dp = row8_sum(chunk_dot(dos.r[h], sv[u].r[h]));
+                    const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                    chunk_axpy(dq_s[h], pv * (dp - di[h]), sk[u].r[h]);
                 }
-                if (s0 == 0) {
-                    const int iq0 = slab_row(p, u + 4, row_s[0], 1), iq1 = slab_row(p, u + 4, row_s[1], 1);
-                    sfrag_load(sq[u], rq, iq0, iq1, c8);
-                    sfrag_load(sd[u], rdo, iq0, iq1, c8);
-                    sl[u][0] = buf_f32(rl, iq0);
-                    sl[u][1] = buf_f32(rl, iq1);
-                    sdl[u][0] = buf_f32(rd, iq0);
-                    sdl[u][1] = buf_f32(rd, iq1);
+                if (s0 + kRingA < unrolled_slabs(kRingA)) {
+                    const int tn = s0 + u + kRingA;
+                    sfrag_load(sk[u], rk, slab_row(p, tn, row_s[0], -1), slab_row(p, tn, row_s[1], -1), c8);
+                    sfrag_load(sv[u], rv, slab_row(p, tn, row_s[0], -1), slab_row(p, tn, row_s[1], -1), c8);
                 }
             }
         }
-        for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
-            if (r0 + p.off[t] >= n) break;
-            const int iq0 = row_s[0] + p.off[t], iq1 = row_s[1] + p.off[t];
-            SFrag qt, dt;
-            sfrag_load(qt, rq, iq0, iq1, c8);
-            sfrag_load(dt, rdo, iq0, iq1, c8);
-            const float lq[2] = {buf_f32(rl, iq0), buf_f32(rl, iq1)};
-            const float dq2[2] = {buf_f32(rd, iq0), buf_f32(rd, iq1)};
+        for (int t = unrolled_slabs(kRingA); t < n_off; ++t) {  // longer tables
+            if (r0 + 15 < p.off[t]) break;
+            SFrag kt, vt;
+            sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+            sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const bool ok = (row_s[h] < n) & (row_s[h] + p.off[t] < n);
-                const float s = row8_sum(chunk_dot(qt.r[h], kS.r[h]));
-                const float dp = row8_sum(chunk_dot(dt.r[h], vS.r[h]));
-                const float pv = ok ? fast_exp2(s * sl2 - lq[h] * kLog2e) : 0.f;
-                chunk_axpy(dv_s[h], pv, dt.r[h]);
-                chunk_axpy(dk_s[h], pv * (dp - dq2[h]), qt.r[h]);
+                const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
+                const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
+                const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
+                const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                chunk_axpy(dq_s[h], pv * (dp - di[h]), kt.r[h]);
             }
         }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (row_s[h] < n) store_chunk(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
+    }
 
-        // band on MFMA: key row me sees query blocks r0 + 16 b
+    // ========================= phase B: dK, dV of key rows ==========================
+    {
         const int j = me;
         Frag<true> kf, vf;
         buf_frag(kf, rk, j, g);
         buf_frag(vf, rv, j, g);
         wait_vm_all();
-        __syncthreads();
+        __syncthreads();  // the Q, dO band copies and the LSE, D rows have landed
+
+        // band on MFMA: key row j sees query blocks r0 + 16 b
         f32x4_t dk[4], dv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1302,16 +1239,76 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
             mma_over_rows_tr(dk, ta, lr, c16, g, ds);
         }
         __syncthreads();  // every wave is done with the Q, dO band tiles
-        f32x4_t dk_b[2][2], dv_b[2][2];
-        c_to_slab(area_a, dk, dk_b, c16, g, s8, c8);
-        c_to_slab(area_b, dv, dv_b, c16, g, s8, c8);
+        f32x4_t dk_s[2][2], dv_s[2][2];
+        c_to_slab(area_a, dk, dk_s, c16, g, s8, c8);
+        c_to_slab(area_b, dv, dv_s, c16, g, s8, c8);
+
+        // sparse offsets: queries j + o, in the slab layout
+        SFrag kS, vS;
+        sfrag_load(kS, rk, row_s[0], row_s[1], c8);
+        sfrag_load(vS, rv, row_s[0], row_s[1], c8);
+        SFrag sq[kRingB], sd[kRingB];
+        float sl[kRingB][2], sdl[kRingB][2];
+#pragma unroll
+        for (int u = 0; u < kRingB; ++u) {
+            const int iq0 = slab_row(p, u, row_s[0], 1), iq1 = slab_row(p, u, row_s[1], 1);
+            sfrag_load(sq[u], rq, iq0, iq1, c8);
+            sfrag_load(sd[u], rdo, iq0, iq1, c8);
+            sl[u][0] = buf_f32(rl, iq0);
+            sl[u][1] = buf_f32(rl, iq1);
+            sdl[u][0] = buf_f32(rd, iq0);
+            sdl[u][1] = buf_f32(rd, iq1);
+        }
+#pragma unroll
+        for (int s0 = 0; s0 < unrolled_slabs(kRingB); s0 += kRingB) {
+            if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
+#pragma unroll
+            for (int u = 0; u < kRingB; ++u) {
+                const int o = table_off(p, s0 + u);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const bool ok = (row_s[h] < n) & (row_s[h] + o < n);
+                    const float s = row8_sum(chunk_dot(sq[u].r[h], kS.r[h]));
+                    const float dp = row8_sum(chunk_dot(sd[u].r[h], vS.r[h]));
+                    const float pv = ok ? fast_exp2(s * sl2 - sl[u][h] * kLog2e) : 0.f;
+                    chunk_axpy(dv_s[h], pv, sd[u].r[h]);
+                    chunk_axpy(dk_s[h], pv * (dp - sdl[u][h]), sq[u].r[h]);
+                }
+                if (s0 + kRingB < unrolled_slabs(kRingB)) {
+                    const int tn = s0 + u + kRingB;
+                    const int iq0 = slab_row(p, tn, row_s[0], 1), iq1 = slab_row(p, tn, row_s[1], 1);
+                    sfrag_load(sq[u], rq, iq0, iq1, c8);
+                    sfrag_load(sd[u], rdo, iq0, iq1, c8);
+                    sl[u][0] = buf_f32(rl, iq0);
+                    sl[u][1] = buf_f32(rl, iq1);
+                    sdl[u][0] = buf_f32(rd, iq0);
+                    sdl[u][1] = buf_f32(rd, iq1);
+                }
+            }
+        }
+        for (int t = unrolled_slabs(kRingB); t < n_off; ++t) {  // longer tables
+            if (r0 + p.off[t] >= n) break;
+            const int iq0 = row_s[0] + p.off[t], iq1 = row_s[1] + p.off[t];
+            SFrag qt, dt;
+            sfrag_load(qt, rq, iq0, iq1, c8);
+            sfrag_load(dt, rdo, iq0, iq1, c8);
+            const float lq[2] = {buf_f32(rl, iq0), buf_f32(rl, iq1)};
+            const float dq2[2] = {buf_f32(rd, iq0), buf_f32(rd, iq1)};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] + p.off[t] < n);
+                const float s = row8_sum(chunk_dot(qt.r[h], kS.r[h]));
+                const float dp = row8_sum(chunk_dot(dt.r[h], vS.r[h]));
+                const float pv = ok ? fast_exp2(s * sl2 - lq[h] * kLog2e) : 0.f;
+                chunk_axpy(dv_s[h], pv, dt.r[h]);
+                chunk_axpy(dk_s[h], pv * (dp - dq2[h]), qt.r[h]);
+            }
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if (row_s[h] < n) {
-                const f32x4_t ok_[2] = {dk_s[h][0] + dk_b[h][0], dk_s[h][1] + dk_b[h][1]};
-                const f32x4_t ov_[2] = {dv_s[h][0] + dv_b[h][0], dv_s[h][1] + dv_b[h][1]};
-                store_chunk(static_cast<OE *>(p.dk) + head, row_s[h], c8, ok_, p.scale);
-                store_chunk(static_cast<OE *>(p.dv) + head, row_s[h], c8, ov_, 1.f);
+                store_chunk(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], p.scale);
+                store_chunk(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
             }
         }
     }
