@@ -717,10 +717,12 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         for (int h = 0; h < 2; ++h) {
             const float mn = fmaxf(m_s[h], gm[h]);
             ms[h] = (mn == kNegInf) ? 0.f : mn;
-            const float al = fast_exp2(m_s[h] - ms[h]);
-            acc_s[h][0] *= al;
-            acc_s[h][1] *= al;
-            l_s[h] *= al;
+            if (t0 > 0) {  // the first group starts from an empty state
+                const float al = fast_exp2(m_s[h] - ms[h]);
+                acc_s[h][0] *= al;
+                acc_s[h][1] *= al;
+                l_s[h] *= al;
+            }
             m_s[h] = mn;
         }
 #pragma unroll
@@ -1119,11 +1121,13 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
             const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
             float ds[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = kb0 + 4 * g + r;
-                const bool ok = full || (me_ok && j <= i && j > i - w && j >= 0);
-                const float pv = ok ? fast_exp2(st[r] * sl2 - lse2_i) : 0.f;
-                ds[r] = pv * (dpt[r] - di_i);
+            for (int r = 0; r < 4; ++r) ds[r] = fast_exp2(st[r] * sl2 - lse2_i) * (dpt[r] - di_i);
+            if (!full) {  // uniform: edge blocks only
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = kb0 + 4 * g + r;
+                    if (!(me_ok && j <= i && j > i - w && j >= 0)) ds[r] = 0.f;
+                }
             }
             mma_over_rows_tr(acc, ta, lr, c16, g, ds);
         }
@@ -1163,13 +1167,15 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
 #pragma unroll
             for (int u = 0; u < kRingA; ++u) {
                 const int o = table_off(p, s0 + u);
+                if (s0 + u < n_off) {  // uniform: slots past the table only refill
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-                    const float s = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
-                    const float dp = row8_sum(chunk_dot(dos.r[h], sv[u].r[h]));
-                    const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
-                    chunk_axpy(dq_s[h], pv * (dp - di[h]), sk[u].r[h]);
+                    for (int h = 0; h < 2; ++h) {
+                        const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                        const float s = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                        const float dp = row8_sum(chunk_dot(dos.r[h], sv[u].r[h]));
+                        const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                        chunk_axpy(dq_s[h], pv * (dp - di[h]), sk[u].r[h]);
+                    }
                 }
                 if (s0 + kRingA < unrolled_slabs(kRingA)) {
                     const int tn = s0 + u + kRingA;
@@ -1229,12 +1235,16 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
             const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + lr + 4 * g);
             float pr[4], ds[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int q = qb0 + 4 * g + r;
-                const bool ok = full || (me_ok && q < n && q >= j && q - j < w);
-                pr[r] = ok ? fast_exp2(sq4[r] * sl2 - l4[r]) : 0.f;
-                ds[r] = pr[r] * (dp4[r] - d4[r]);
+            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sq4[r] * sl2 - l4[r]);
+            if (!full) {  // uniform: edge blocks only
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int q = qb0 + 4 * g + r;
+                    if (!(me_ok && q < n && q >= j && q - j < w)) pr[r] = 0.f;
+                }
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ds[r] = pr[r] * (dp4[r] - d4[r]);
             mma_over_rows_tr(dv, tb, lr, c16, g, pr);
             mma_over_rows_tr(dk, ta, lr, c16, g, ds);
         }
@@ -1265,14 +1275,16 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
 #pragma unroll
             for (int u = 0; u < kRingB; ++u) {
                 const int o = table_off(p, s0 + u);
+                if (s0 + u < n_off) {  // uniform: slots past the table only refill
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const bool ok = (row_s[h] < n) & (row_s[h] + o < n);
-                    const float s = row8_sum(chunk_dot(sq[u].r[h], kS.r[h]));
-                    const float dp = row8_sum(chunk_dot(sd[u].r[h], vS.r[h]));
-                    const float pv = ok ? fast_exp2(s * sl2 - sl[u][h] * kLog2e) : 0.f;
-                    chunk_axpy(dv_s[h], pv, sd[u].r[h]);
-                    chunk_axpy(dk_s[h], pv * (dp - sdl[u][h]), sq[u].r[h]);
+                    for (int h = 0; h < 2; ++h) {
+                        const bool ok = (row_s[h] < n) & (row_s[h] + o < n);
+                        const float s = row8_sum(chunk_dot(sq[u].r[h], kS.r[h]));
+                        const float dp = row8_sum(chunk_dot(sd[u].r[h], vS.r[h]));
+                        const float pv = ok ? fast_exp2(s * sl2 - sl[u][h] * kLog2e) : 0.f;
+                        chunk_axpy(dv_s[h], pv, sd[u].r[h]);
+                        chunk_axpy(dk_s[h], pv * (dp - sdl[u][h]), sq[u].r[h]);
+                    }
                 }
                 if (s0 + kRingB < unrolled_slabs(kRingB)) {
                     const int tn = s0 + u + kRingB;
