@@ -295,8 +295,8 @@ def main():
     qh_per_step = rows * LAYERS
     step_bytes = per_row["step"] * rows * LAYERS
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_names = {"fwd": "fwd_kernel<bf16 in, bf16 out>", "delta": "delta_kernel<bf16>",
-                    "grads": "bwd_kernel<bf16 in, bf16 out>"}
+    kernel_names = {"fwd": "fwd_window_kernel<bf16 out>", "delta": "delta_kernel<bf16>",
+                    "grads": "bwd_window_kernel<bf16 out>"}
     dom = max(avg_us, key=lambda k: avg_us[k])
     achieved = per_row[dom] * rows / (avg_us[dom] * 1e-6) / 1e9
     roof = {
