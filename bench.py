@@ -7,8 +7,8 @@ with the static linear stagger alpha_l = 0.5 + l/15 (Fibonacci base, window
 w = 64, reach R = 1024; tables built at R = 1024 and used unchanged at 4096).
 Inputs are seeded N(0, 1) synthetic tensors resident in HBM before timing.
 
-One step = the 16 layers' fsa_forward, fsa_backward_delta and fsa_backward_grads
-(the whole backward), launched as one HIP graph. Prints one JSON line:
+One step = the 16 layers' fsa_forward and fsa_backward (the whole backward: D,
+dQ and the pair weights, dK and dV), launched as one HIP graph. Prints one JSON line:
 query-heads/s (value), algorithmic HBM GB/s of the step, a roofline entry for
 the dominant kernel, the dense causal baseline, and the fp64 CPU oracle timed
 on a bounded sample of the same workload.
@@ -48,19 +48,18 @@ def rows_per_layer():
 
 
 def alg_bytes_per_row():
-    """Compulsory HBM bytes per (b, h, row) of each kernel and of the whole step.
+    """Compulsory HBM bytes per (b, h, row) of each stage and of the whole step.
 
-    forward: read q, k, v; write o; write lse
-    delta:   read o, dO; write D
-    grads:   read q, k, v, dO, lse, D; write dq, dk, dv
-    step (fwd + bwd, each tensor element once, D scratch excluded):
-             read q, k, v, o, dO, lse; write o, lse, dq, dk, dv
+    fwd:  read q, k, v; write o, lse
+    bwd:  read q, k, v, o, dO, lse; write dq, dk, dv (the D and pair-weight
+          workspaces are the library's scratch and not counted)
+    step (fwd + bwd, each tensor element once):
+          read q, k, v, o, dO, lse; write o, lse, dq, dk, dv
     """
     row = D * ELEM
     return {
         "fwd": 4 * row + 4,
-        "delta": 2 * row + 4,
-        "grads": 7 * row + 8,
+        "bwd": 8 * row + 4,
         "step": 12 * row + 8,
     }
 
@@ -163,7 +162,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the sparse-attention path is not sharded across GPUs in this build.", file=sys.stderr)
+              "this library runs the sparse-attention path on one GPU and does not shard it.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -204,6 +203,9 @@ def main():
     del cpu_inputs
     scale = 1.0 / math.sqrt(D)
     tables = [fsa.build_offsets(a, W, R, BASE) for a in alphas]
+    # one pair workspace serves every layer (the layers run one after another on the stream)
+    pair_bytes = max(fsa.workspace_bytes(torch.bfloat16, B, H, N, D, alpha=a, w=W, R=R, base=BASE) for a in alphas)
+    pair_ws = torch.empty(max(pair_bytes, 16) // 4, dtype=torch.int32, device=dev)
     log("offset tables per layer: " + "; ".join(",".join(map(str, t)) for t in tables))
 
     def layer_fwd(l):
@@ -211,43 +213,49 @@ def main():
         fsa.forward(x["q"], x["k"], x["v"], alpha=alphas[l], w=W, R=R, base=BASE, scale=scale,
                     out=x["o"], lse=x["lse"])
 
-    def layer_delta(l):
+    def layer_bwd(l):
         x = bufs[l]
-        fsa.backward_delta(x["o"], x["do"], delta=x["delta"])
-
-    def layer_grads(l):
-        x = bufs[l]
-        fsa.backward_grads(x["q"], x["k"], x["v"], x["lse"], x["do"], x["delta"], alpha=alphas[l], w=W, R=R,
-                           base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"])
+        fsa.backward(x["q"], x["k"], x["v"], x["o"], x["lse"], x["do"], alpha=alphas[l], w=W, R=R, base=BASE,
+                     scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], delta=x["delta"], pair_ws=pair_ws)
 
     def step():
         for l in range(LAYERS):
             layer_fwd(l)
-            layer_delta(l)
-            layer_grads(l)
+            layer_bwd(l)
 
     # eager reference results
     step()
     torch.cuda.synchronize()
     ref = [tuple(bufs[l][t].clone() for t in ("o", "lse", "dq", "dk", "dv")) for l in range(LAYERS)]
 
-    # per-kernel durations with HIP events on the launch stream (eager launches)
+    # per-kernel durations: each kernel's 16 per-layer launches captured back to back in a
+    # HIP graph of their own, replayed between two HIP events on the launch stream
     stream = torch.cuda.current_stream(dev)
-    per = {"fwd": [], "delta": [], "grads": []}
-    fns = {"fwd": layer_fwd, "delta": layer_delta, "grads": layer_grads}
-    for _ in range(max(3, args.steps // 5)):
-        evs = []
-        for l in range(LAYERS):
-            for key in ("fwd", "delta", "grads"):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fns[key](l)
-                e1.record(stream)
-                evs.append((key, e0, e1))
+    fns = {"fwd": layer_fwd, "bwd": layer_bwd}
+    reps = max(3, args.steps // 5)
+    avg_us = {}
+    for key, fn in fns.items():
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for l in range(LAYERS):
+                fn(l)
+        stream.wait_stream(side)
         torch.cuda.synchronize()
-        for key, e0, e1 in evs:
-            per[key].append(e0.elapsed_time(e1) * 1e3)  # microseconds
-    avg_us = {k: sum(v) / len(v) for k, v in per.items()}
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(LAYERS):
+                fn(l)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg_us[key] = e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
+        del g
     log("average kernel durations (us): " + ", ".join(f"{k}={v:.2f}" for k, v in avg_us.items()))
 
     # capture one step as a HIP graph
@@ -295,9 +303,8 @@ def main():
     qh_per_step = rows * LAYERS
     step_bytes = per_row["step"] * rows * LAYERS
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_names = {"fwd": "fwd_window_kernel<bf16 out>", "delta": "delta_kernel<bf16>",
-                    "grads": "bwd_window_kernel<bf16 out>"}
-    dom = max(avg_us, key=lambda k: avg_us[k])
+    kernel_names = {"fwd": "fwd_window_kernel<bf16 out>"}
+    dom = "fwd"
     achieved = per_row[dom] * rows / (avg_us[dom] * 1e-6) / 1e9
     roof = {
         "bound": "hbm",

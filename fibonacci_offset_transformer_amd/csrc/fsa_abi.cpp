@@ -235,9 +235,9 @@ namespace {
 // Validates the arguments of the gradient stage and fills its kernel parameters.
 fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
                            const void *k, const void *v, const float *lse, const void *dout,
-                           const float *delta, void *dq, void *dk, void *dv, int32_t B, int32_t H,
-                           int32_t N, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
-                           int32_t R, bool *empty) {
+                           const float *delta, void *dq, void *dk, void *dv, void *pair_ws,
+                           uint64_t pair_ws_bytes, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                           fsa_base_t base, double alpha, int32_t w, int32_t R, bool *empty) {
     const Shape s{B, H, N, d};
     fsa_status_t st = check_common(dt, out_dt, s, scale);
     if (st != FSA_OK) return st;
@@ -245,10 +245,16 @@ fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_d
     if (n_off < 0) return st;
     *empty = static_cast<int64_t>(B) * H * N == 0;
     if (*empty) return FSA_OK;
-    const char *names[] = {"q", "k", "v", "lse", "dout", "delta", "dq", "dk", "dv"};
-    const void *ptrs[] = {q, k, v, lse, dout, delta, dq, dk, dv};
-    if ((st = check_ptrs(names, ptrs, 9)) != FSA_OK) return st;
-    if ((st = check_no_alias(names, ptrs, 6, 9)) != FSA_OK) return st;
+    p.n_off = trim_offsets(p.off, n_off, N);
+    const uint64_t need = 4ull * static_cast<uint64_t>(fsa::pair_words(dt, w, N, static_cast<int64_t>(B) * H, p.n_off));
+    const int np = need > 0 ? 10 : 9;  // the pair workspace is checked only when it is used
+    const char *names[] = {"q", "k", "v", "lse", "dout", "delta", "dq", "dk", "dv", "pair_ws"};
+    const void *ptrs[] = {q, k, v, lse, dout, delta, dq, dk, dv, pair_ws};
+    if ((st = check_ptrs(names, ptrs, np)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 6, np)) != FSA_OK) return st;
+    if (pair_ws_bytes < need)
+        return fail(FSA_E_ARG, "pair_ws holds %llu bytes, this problem needs %llu",
+                    static_cast<unsigned long long>(pair_ws_bytes), static_cast<unsigned long long>(need));
     p.q = q;
     p.k = k;
     p.v = v;
@@ -258,10 +264,10 @@ fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_d
     p.dq = dq;
     p.dk = dk;
     p.dv = dv;
+    p.pairs = need > 0 ? static_cast<uint32_t *>(pair_ws) : nullptr;
     p.bh = B * H;
     p.n = N;
     p.w = w;
-    p.n_off = trim_offsets(p.off, n_off, N);
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     return FSA_OK;
@@ -269,41 +275,58 @@ fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_d
 
 }  // namespace
 
+fsa_status_t fsa_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                                          fsa_base_t base, double alpha, int32_t w, int32_t R,
+                                          uint64_t *bytes) {
+    if (!bytes) return fail(FSA_E_ARG, "bytes is NULL");
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, dt, s, 1.0f);
+    if (st != FSA_OK) return st;
+    int32_t tab[FSA_MAX_OFFSETS];
+    const int n_off = build_table(base, alpha, w, R, tab, &st);
+    if (n_off < 0) return st;
+    *bytes = 4ull * static_cast<uint64_t>(
+                        fsa::pair_words(dt, w, N, static_cast<int64_t>(B) * H, trim_offsets(tab, n_off, N)));
+    return ok();
+}
+
 fsa_status_t fsa_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
                                 const void *v, const float *lse, const void *dout,
-                                const float *delta, void *dq, void *dk, void *dv, int32_t B,
-                                int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base,
-                                double alpha, int32_t w, int32_t R, void *stream) {
+                                const float *delta, void *dq, void *dk, void *dv, void *pair_ws,
+                                uint64_t pair_ws_bytes, int32_t B, int32_t H, int32_t N, int32_t d,
+                                float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                                void *stream) {
     fsa::AttnParams p{};
     bool empty = false;
-    fsa_status_t st = prepare_grads(p, dt, out_dt, q, k, v, lse, dout, delta, dq, dk, dv, B, H, N, d,
-                                    scale, base, alpha, w, R, &empty);
+    fsa_status_t st = prepare_grads(p, dt, out_dt, q, k, v, lse, dout, delta, dq, dk, dv, pair_ws,
+                                    pair_ws_bytes, B, H, N, d, scale, base, alpha, w, R, &empty);
     if (st != FSA_OK) return st;
     if (empty) return ok();
-    return launched(fsa::launch_backward_grads(dt, out_dt, p, static_cast<hipStream_t>(stream)),
+    return launched(fsa::launch_backward_grads(dt, out_dt, p, static_cast<hipStream_t>(stream), false),
                     "backward grads");
 }
 
 fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
                           const void *o, const float *lse, const void *dout, void *dq, void *dk,
-                          void *dv, float *delta_ws, int32_t B, int32_t H, int32_t N, int32_t d,
-                          float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
-                          void *stream) {
+                          void *dv, float *delta_ws, void *pair_ws, uint64_t pair_ws_bytes, int32_t B,
+                          int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
+                          int32_t w, int32_t R, void *stream) {
     fsa::AttnParams p{};
     bool empty = false;
-    fsa_status_t st = prepare_grads(p, dt, out_dt, q, k, v, lse, dout, delta_ws, dq, dk, dv, B, H, N,
-                                    d, scale, base, alpha, w, R, &empty);
+    fsa_status_t st = prepare_grads(p, dt, out_dt, q, k, v, lse, dout, delta_ws, dq, dk, dv, pair_ws,
+                                    pair_ws_bytes, B, H, N, d, scale, base, alpha, w, R, &empty);
     if (st != FSA_OK) return st;
     if (empty) return ok();
     // delta_ws is written here, so it must not alias any input either
-    const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta_ws"};
-    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta_ws};
-    if ((st = check_ptrs(names, ptrs, 10)) != FSA_OK) return st;
-    if ((st = check_no_alias(names, ptrs, 6, 10)) != FSA_OK) return st;
+    const bool use_pairs = p.pairs != nullptr;
+    const int np = use_pairs ? 11 : 10;
+    const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "delta_ws", "pair_ws"};
+    const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, delta_ws, pair_ws};
+    if ((st = check_ptrs(names, ptrs, np)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 6, np)) != FSA_OK) return st;
     p.o = o;
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    if ((st = launched(fsa::launch_backward_delta(dt, p, hs), "backward delta")) != FSA_OK) return st;
-    return launched(fsa::launch_backward_grads(dt, out_dt, p, hs), "backward grads");
+    return launched(fsa::launch_backward_grads(dt, out_dt, p, static_cast<hipStream_t>(stream), true),
+                    "backward");
 }
 
 fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,

@@ -24,6 +24,7 @@ struct AttnParams {
     const float *lse_in;     // backward: forward LSE
     float *lse_out;          // forward: LSE
     float *delta;            // backward: D workspace [BH, N]
+    uint32_t *pairs;         // backward: per-pair workspace [n_off, BH, N] (window path)
     int32_t bh;              // B * H
     int32_t n;               // sequence length
     int32_t w;               // window (offsets 0..w-1)
@@ -33,9 +34,23 @@ struct AttnParams {
     int32_t off[FSA_MAX_OFFSETS];
 };
 
+// The bf16 window kernels (w <= 64) address each head with 32-bit byte offsets.
+inline bool window_path(fsa_dtype_t dt, int32_t w, int32_t n) { return dt == FSA_BF16 && w <= 64 && n <= (1 << 24); }
+
+// 32-bit words of the backward pair workspace: one word (bf16 P and bf16 dS of a
+// query row and sparse offset) per (offset, head, row) on the window path, none
+// elsewhere.
+inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
+    return window_path(dt, w, n) ? static_cast<int64_t>(n_off) * bh * n : 0;
+}
+
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
-hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
+// Gradient stage. With `with_delta`, D is formed from p.o and p.dout and written to
+// p.delta on the way (by the dQ kernel on the window path, by the delta kernel
+// elsewhere); otherwise p.delta is read as given.
+hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream,
+                                 bool with_delta);
 
 }  // namespace fsa

@@ -342,28 +342,34 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kTileRows = 128;  // rows per LDS tile: the 64-row tile and its 64-row neighbour
-constexpr int kRingA = 3;       // slab row pairs in flight per lane: backward phase A (K, V)
-constexpr int kRingB = 3;       // backward phase B (Q, dO, LSE, D)
 
 // Offsets handled by the unrolled, prefetching slab code for a ring of r slots:
 // whole groups of r covering at least the eight offsets of a window-64 table.
 constexpr int unrolled_slabs(int r) { return ((8 + r - 1) / r) * r; }
 
-// Copies rows [row0, row0 + 128) of a [n, 64] bf16 matrix into a row-major LDS
-// tile (128 bytes per row). Each of the four waves issues four 1 KiB transfers;
-// lane l of a transfer carries the 16 bytes that land at tile offset 16 l. Rows
-// outside [0, n) are read from row 0: finite values that the masks discard.
-// Completion is waited for with wait_vm_all() before the workgroup barrier.
+// Copies rows [row0, row0 + 128) of a [n, 64] bf16 matrix into an LDS tile of 128
+// rows of 128 bytes. The eight 16-byte chunks of tile row r are stored XOR-swizzled:
+// chunk c sits at position c ^ (r & 7) of the row, so that sixteen consecutive rows
+// read at one chunk (row fragments) or four rows read at four chunks (transposed
+// reads) spread over the LDS banks. Each of the four waves issues four 1 KiB
+// transfers; lane l of a transfer fills tile position 16 l, so it fetches the chunk
+// that belongs there. Rows outside [0, n) are read from row 0: finite values that the
+// masks discard. Completion is waited for with wait_vm_all() before the workgroup
+// barrier.
 __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src, int row0, int n, int wave, int lane) {
+    const int rl = lane >> 3;                 // row within the transfer's 8 rows (= tile row & 7)
+    const int chunk = (lane & 7) ^ rl;        // chunk stored at this lane's position
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const int rb = 8 * (4 * wave + k);  // first of the 8 rows this transfer covers
-        int r = row0 + rb + (lane >> 3);
+        const int rb = 8 * (4 * wave + k);  // first of the 8 tile rows this transfer covers
+        int r = row0 + rb + rl;
         r = (r >= 0 && r < n) ? r : 0;
-        __builtin_amdgcn_global_load_lds(src + (int64_t)r * 64 + 8 * (lane & 7),
-                                         (lds_void_t *)(tile + rb * 64), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + (int64_t)r * 64 + 8 * chunk, (lds_void_t *)(tile + rb * 64), 16, 0, 0);
     }
 }
+
+// Element offset, within a swizzled tile, of the 16-byte chunk c of tile row r.
+__device__ __forceinline__ int tile_chunk(int r, int c) { return r * 64 + 8 * (c ^ (r & 7)); }
 
 // ----------------------------------------------------------------------------
 // Buffer-resource loads (bf16 window kernels): a 32-bit byte offset against a
@@ -405,28 +411,36 @@ __device__ __forceinline__ int table_off(const AttnParams &p, int t) {
 // Waits for every outstanding memory operation of the wave (global -> LDS copies included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
 
-// Row fragment (lane group g's 16 elements) of tile row `row`.
+// Waits until at most `n` vector memory operations of the wave are outstanding
+// (operations complete in issue order); LDS and scalar counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Row fragment (lane group g's 16 elements: chunks g and g + 4) of tile row `row`.
 __device__ __forceinline__ void lds_frag(Frag<true> &f, const uint16_t *tile, int row, int g) {
-    const uint16_t *p = tile + row * 64 + 8 * g;
-    f.c[0] = *reinterpret_cast<const u32x4_t *>(p);
-    f.c[1] = *reinterpret_cast<const u32x4_t *>(p + 32);
+    f.c[0] = *reinterpret_cast<const u32x4_t *>(tile + tile_chunk(row, g));
+    f.c[1] = *reinterpret_cast<const u32x4_t *>(tile + tile_chunk(row, g + 4));
 }
 
 // acc[db] += sum_{kk<16} Tile[lr + kk][d] * Bv[kk][col] for the four output blocks db,
-// i.e. the product with the transposed rows lr .. lr+15 of a row-major tile. The A
-// operand comes from ds_read_b64_tr_b16: within a 16-lane group, result lane j, slot
-// k receives element j % 4 of the 8 bytes that group lane j / 4 + 4 k addresses. Lane
-// s therefore addresses row lr + 4 g + s / 4 at column 32 (db / 2) + 8 (s % 4) + 4 (db % 2),
+// i.e. the product with the transposed rows lr .. lr+15 of a swizzled tile (lr a
+// multiple of 8). The A operand comes from ds_read_b64_tr_b16: within a 16-lane group,
+// result lane j, slot k receives element j % 4 of the 8 bytes that group lane j / 4 + 4 k
+// addresses. Lane s therefore addresses row lr + 4 g + s / 4 at column
+// 32 (db / 2) + 8 (s % 4) + 4 (db % 2), i.e. half db % 2 of chunk 4 (db / 2) + s % 4,
 // which hands lane j the column acc_row_d(db, j) of rows lr + 4 g + k.
 __device__ __forceinline__ void mma_over_rows_tr(f32x4_t acc[4], const uint16_t *tile, int lr, int c16, int g,
                                                  const float bv[4]) {
     const u32x2_t b = {pack_bf16(bv[0], bv[1]), pack_bf16(bv[2], bv[3])};
     const i16x4_t bb = __builtin_bit_cast(i16x4_t, b);
-    const uint16_t *rowp = tile + (lr + 4 * g + (c16 >> 2)) * 64 + 8 * (c16 & 3);
+    const int row = lr + 4 * g + (c16 >> 2);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const i16x4_t a =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(rowp + 32 * (db >> 1) + 4 * (db & 1)));
+        const uint16_t *p = tile + tile_chunk(row, 4 * (db >> 1) + (c16 & 3)) + 4 * (db & 1);
+        const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bb, acc[db], 0, 0, 0);
     }
 }
@@ -458,18 +472,24 @@ __device__ __forceinline__ float chunk_dot(const u32x4_t &a, const u32x4_t &b) {
     return s0 + s1;
 }
 
-// acc[0..1] (8 fp32 values of one row) += x * chunk, with x rounded to bf16 (packed dot unit).
-__device__ __forceinline__ void chunk_axpy(f32x4_t acc[2], float x, const u32x4_t &c) {
-    const bf16x2_t xl = as_bf16x2(pack_bf16(x, 0.f));
-    const bf16x2_t xh = as_bf16x2(pack_bf16(0.f, x));
+// acc[0..1] (8 fp32 values of one row) += x * chunk on the packed dot unit, with the
+// bf16 weight x given as the words {x, 0} (xl) and {0, x} (xh).
+__device__ __forceinline__ void chunk_axpy_words(f32x4_t acc[2], uint32_t xl, uint32_t xh, const u32x4_t &c) {
+    const bf16x2_t bl = as_bf16x2(xl), bh = as_bf16x2(xh);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const bf16x2_t v = as_bf16x2(c[w]);
         f32x4_t &a = acc[w >> 1];
         const int r = 2 * (w & 1);
-        a[r] = __builtin_amdgcn_fdot2_f32_bf16(v, xl, a[r], false);
-        a[r + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, xh, a[r + 1], false);
+        a[r] = __builtin_amdgcn_fdot2_f32_bf16(v, bl, a[r], false);
+        a[r + 1] = __builtin_amdgcn_fdot2_f32_bf16(v, bh, a[r + 1], false);
     }
+}
+
+// acc[0..1] += x * chunk, with x rounded to bf16.
+__device__ __forceinline__ void chunk_axpy(f32x4_t acc[2], float x, const u32x4_t &c) {
+    const uint32_t xb = pack_bf16(x, 0.f);
+    chunk_axpy_words(acc, xb, xb << 16, c);
 }
 
 // DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], and the mirror of each half row.
@@ -502,7 +522,9 @@ __device__ __forceinline__ void store_chunk(float *base, int64_t row, int c8, co
 // Moves a 16-row accumulator from the MFMA C layout (lane (q = l % 16, g), acc[db][r] =
 // row q, d = acc_row_d(db, 4 g + r)) to the slab layout through a wave-private fp32
 // area of 16 x 64 values; 16-byte units are XOR-swizzled by row to spread LDS banks.
-// The writes and reads come from the same wave and are processed in order.
+// The writes and reads come from the same wave and are processed in order. With ADD
+// the moved values are added to `out` instead of replacing it.
+template <bool ADD = false>
 __device__ __forceinline__ void c_to_slab(float *area, const f32x4_t acc[4], f32x4_t out[2][2], int c16, int g,
                                           int s8, int c8) {
 #pragma unroll
@@ -514,7 +536,10 @@ __device__ __forceinline__ void c_to_slab(float *area, const f32x4_t acc[4], f32
     for (int h = 0; h < 2; ++h) {
         const int row = s8 + 8 * h;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) out[h][b] = *reinterpret_cast<const f32x4_t *>(area + row * 64 + 4 * ((2 * c8 + b) ^ row));
+        for (int b = 0; b < 2; ++b) {
+            const f32x4_t x = *reinterpret_cast<const f32x4_t *>(area + row * 64 + 4 * ((2 * c8 + b) ^ row));
+            out[h][b] = ADD ? out[h][b] + x : x;
+        }
     }
 }
 
@@ -649,11 +674,12 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     }
 }
 
-// Forward, bf16 inputs, window w <= 64. The sparse slabs stream first, in the slab
-// layout, through a ring of four row pairs per lane (one online softmax state per
-// row); meanwhile the workgroup's band keys [i0 - 64, i0 + 64) are copied into LDS
-// (K and V row-major). The band then runs on MFMA with its own softmax state, and
-// the two states are merged per row in the slab layout, which also stores O.
+// Forward, bf16 inputs, window w <= 64. The workgroup's band keys [i0 - 64, i0 + 64)
+// are copied into LDS (K and V row-major) first. Once they have landed, the first
+// sparse slabs are requested, in the slab layout, into a ring of four row pairs per
+// lane, and the band runs on MFMA while those loads are in flight; its softmax state
+// then moves into the slab layout and the slabs continue it as an online softmax, one
+// group of four offsets at a time. The slab layout stores O and the LSE.
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
@@ -676,96 +702,25 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
     const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128), rv = head_rsrc(V, n * 128);
     const float sl2 = p.scale_log2;
+    const int i = r0 + c16;  // MFMA-layout query row
+    const bool row_ok = i < n;
 
-    // issue order matters: the slab loads go before the band copies, so waiting for
-    // them does not wait for the copies
-    SFrag qs;
-    sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+    dma_tile(ks, K, i0 - 64, n, wave, lane);
+    dma_tile(vs, V, i0 - 64, n, wave, lane);
+    Frag<true> qf;
+    buf_frag(qf, rq, i, g);
+    wait_vm_all();
+    __syncthreads();
+    // the first slab rows are requested now and land while the band runs; most of them
+    // are rows of neighbouring tiles whose band copies have just passed through L2
     SFrag sk[4], sv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
         sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
     }
-    dma_tile(ks, K, i0 - 64, n, wave, lane);
-    dma_tile(vs, V, i0 - 64, n, wave, lane);
-
-    // ---- sparse slabs: one online softmax state per row (replicated over its 8 lanes) ----
-    float m_s[2] = {kNegInf, kNegInf}, l_s[2] = {0.f, 0.f};
-    f32x4_t acc_s[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) acc_s[h][0] = acc_s[h][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t0 = 0; t0 < 8; t0 += 4) {
-        if (t0 >= n_off || r0 + 15 < p.off[t0]) break;  // ascending offsets
-        float ss[4][2], gm[2] = {kNegInf, kNegInf};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int o = table_off(p, t0 + u);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-                const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
-                ss[u][h] = ok ? d * sl2 : kNegInf;
-                gm[h] = fmaxf(gm[h], ss[u][h]);
-            }
-            if (t0 == 0)
-                sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
-        }
-        float ms[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float mn = fmaxf(m_s[h], gm[h]);
-            ms[h] = (mn == kNegInf) ? 0.f : mn;
-            if (t0 > 0) {  // the first group starts from an empty state
-                const float al = fast_exp2(m_s[h] - ms[h]);
-                acc_s[h][0] *= al;
-                acc_s[h][1] *= al;
-                l_s[h] *= al;
-            }
-            m_s[h] = mn;
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float pt = fast_exp2(ss[u][h] - ms[h]);
-                l_s[h] += pt;
-                chunk_axpy(acc_s[h], pt, sv[u].r[h]);
-            }
-            if (t0 == 0)
-                sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
-        }
-    }
-    for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
-        if (r0 + 15 < p.off[t]) break;
-        SFrag kt, vt;
-        sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-        sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
-            const float d = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
-            const float sv1 = ok ? d * sl2 : kNegInf;
-            const float mn = fmaxf(m_s[h], sv1);
-            const float ms = (mn == kNegInf) ? 0.f : mn;
-            const float al = fast_exp2(m_s[h] - ms);
-            const float pt = fast_exp2(sv1 - ms);
-            acc_s[h][0] *= al;
-            acc_s[h][1] *= al;
-            l_s[h] = l_s[h] * al + pt;
-            m_s[h] = mn;
-            chunk_axpy(acc_s[h], pt, vt.r[h]);
-        }
-    }
 
     // ---- window band on MFMA: rows r0..r0+15 (row c16 of the lane) see key blocks qb-4 .. qb ----
-    const int i = r0 + c16;
-    const bool row_ok = i < n;
-    Frag<true> qf;
-    buf_frag(qf, rq, i, g);
-    wait_vm_all();
-    __syncthreads();
     const int qb = r0 >> 4;
     const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
     float sc[5][4];
@@ -809,7 +764,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     }
     const float l_b = group_sum(lsum_b);
 
-    // ---- merge the band state into the slab layout, normalise, store ----
+    // ---- the band state, moved into the slab layout, starts the slabs' online softmax ----
     __syncthreads();  // every wave is done with the band tiles
     float *area = reinterpret_cast<float *>(ks) + wave * 1024;
     float *stat = reinterpret_cast<float *>(vs) + wave * 32;
@@ -817,20 +772,86 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         stat[c16] = m_b;
         stat[16 + c16] = l_b;
     }
-    f32x4_t accb[2][2];
-    c_to_slab(area, acc_b, accb, c16, g, s8, c8);
+    float m_s[2], l_s[2];
+    f32x4_t acc_s[2][2];
+    c_to_slab(area, acc_b, acc_s, c16, g, s8, c8);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int rl = s8 + 8 * h;
-        const float mb = stat[rl], lb2 = stat[16 + rl];
-        const float m = fmaxf(m_s[h], mb);
-        const float ms = (m == kNegInf) ? 0.f : m;
-        const float fa = fast_exp2(m_s[h] - ms), fb = fast_exp2(mb - ms);
-        const float l = l_s[h] * fa + lb2 * fb;
-        const f32x4_t o[2] = {acc_s[h][0] * fa + accb[h][0] * fb, acc_s[h][1] * fa + accb[h][1] * fb};
+        m_s[h] = stat[s8 + 8 * h];
+        l_s[h] = stat[16 + s8 + 8 * h];
+    }
+
+    // ---- sparse slabs: keys row - off[t], four offsets per online-softmax update ----
+    SFrag qs;
+    sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+#pragma unroll
+    for (int t0 = 0; t0 < 8; t0 += 4) {
+        if (t0 >= n_off || r0 + 15 < p.off[t0]) break;  // ascending offsets
+        float ss[4][2], gm[2] = {kNegInf, kNegInf};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int o = table_off(p, t0 + u);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                ss[u][h] = ok ? d * sl2 : kNegInf;
+                gm[h] = fmaxf(gm[h], ss[u][h]);
+            }
+            if (t0 == 0)
+                sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+        }
+        float ms[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float mn = fmaxf(m_s[h], gm[h]);
+            ms[h] = (mn == kNegInf) ? 0.f : mn;
+            const float al = fast_exp2(m_s[h] - ms[h]);
+            acc_s[h][0] *= al;
+            acc_s[h][1] *= al;
+            l_s[h] *= al;
+            m_s[h] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float pt = fast_exp2(ss[u][h] - ms[h]);
+                l_s[h] += pt;
+                chunk_axpy(acc_s[h], pt, sv[u].r[h]);
+            }
+            if (t0 == 0)
+                sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+        }
+    }
+    for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
+        if (r0 + 15 < p.off[t]) break;
+        SFrag kt, vt;
+        sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+        sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
+            const float d = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
+            const float sv1 = ok ? d * sl2 : kNegInf;
+            const float mn = fmaxf(m_s[h], sv1);
+            const float ms = (mn == kNegInf) ? 0.f : mn;
+            const float al = fast_exp2(m_s[h] - ms);
+            const float pt = fast_exp2(sv1 - ms);
+            acc_s[h][0] *= al;
+            acc_s[h][1] *= al;
+            l_s[h] = l_s[h] * al + pt;
+            m_s[h] = mn;
+            chunk_axpy(acc_s[h], pt, vt.r[h]);
+        }
+    }
+
+    // ---- normalise, store ----
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
         if (row_s[h] < n) {
-            store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, o, 1.f / l);
-            if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = m * kLn2 + logf(l);
+            store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], 1.f / l_s[h]);
+            if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = m_s[h] * kLn2 + logf(l_s[h]);
         }
     }
 }
@@ -1048,18 +1069,182 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
     }
 }
 
-// Backward, bf16 inputs, window w <= 64. One workgroup owns rows [t0, t0 + 64).
-// Phase A forms dQ of those query rows: the band keys [t0 - 64, t0 + 64) are copied
-// into LDS (K, V) and processed on MFMA first; their part of dQ moves through LDS into
-// the slab layout, where the slab keys t - o stream through a register ring and add
-// their part. Phase B does the same for dK, dV of those key rows with the band queries
-// [t0, t0 + 128) (Q, dO, LSE, D in LDS, copied while phase A's slabs run) and the slab
-// queries t + o. Every output row has one writer; rows are stored whole.
-template <bool OUT_BF16>
-__global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p) {
+// Backward on the window path (bf16 inputs, w <= 64) runs as two kernels over 64-row
+// tiles. The first forms dQ of its query rows and, for every sparse pair (query i,
+// key i - off[t]), stores P and dS rounded to bf16 (the weights the gradient products
+// use) in a pair workspace [n_off, BH, N] of 32-bit words (P in the low half). The
+// second forms dK and dV of its key rows from the window band, recomputed on MFMA, and
+// from the stored weights of the sparse pairs (key j, query j + off[t]), so no score is
+// formed twice on the vector units. Each kernel keeps one pair of operands resident
+// (K, V for dQ; Q, dO for dK and dV), which halves the data an XCD's L2 has to hold.
+
+constexpr int kRingQ = 4, kPreQ = 3;    // dQ kernel: slab slots in the ring; slots requested before the band
+constexpr int kRingKV = 3, kPreKV = 1;  // dK/dV kernel
+
+// Descriptor over the pair-workspace words of offset t of head bh: empty (every load
+// reads 0) for t past the table, so ring refills never address beyond the workspace.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int t, int bh) {
+    const bool in = t < p.n_off;
+    const uint32_t *base = p.pairs + ((int64_t)(in ? t : 0) * p.bh + bh) * p.n;
+    return head_rsrc(base, in ? p.n * 4 : 0);
+}
+
+// dQ of query rows [t0, t0 + 64): the band keys [t0 - 64, t0 + 64) (K, V in LDS) on
+// MFMA first, then the slab keys i - off[t] in the slab layout through a register ring,
+// storing each sparse pair's P and dS on the way. With WITH_D the kernel also forms
+// D = rowsum(dO * O) of its rows from O (instead of reading it) and stores it for the
+// dK/dV kernel.
+template <bool OUT_BF16, bool WITH_D>
+__global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
-    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // K rows, then Q rows; merge areas
-    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // V rows, then dO rows; merge areas
+    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // band K rows, then merge areas
+    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // band V rows
+    __shared__ float d_s[64];                                             // D of the tile's rows (WITH_D)
+
+    const int n = p.n, w = p.w, n_off = p.n_off;
+    const int nt = (n + 63) >> 6;
+    const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
+    const int bh = lb / nt, tile = lb - bh * nt;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15, g = lane >> 4;  // MFMA layout
+    const int s8 = lane >> 3, c8 = lane & 7;   // slab layout
+    const int t0 = tile * 64, r0 = t0 + 16 * wave;
+    const int row_s[2] = {r0 + s8, r0 + 8 + s8};
+    const int i = r0 + c16;  // MFMA-layout query row
+    const bool i_ok = i < n;
+    const int64_t head = (int64_t)bh * n * 64;
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q) + head;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
+    const uint16_t *DO = static_cast<const uint16_t *>(p.dout) + head;
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128);
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, n * 128), rdo = head_rsrc(DO, n * 128);
+    const __amdgpu_buffer_rsrc_t rl = head_rsrc(p.lse_in + (int64_t)bh * n, n * 4);
+    const __amdgpu_buffer_rsrc_t rd = head_rsrc(p.delta + (int64_t)bh * n, n * 4);
+    const float sl2 = p.scale_log2;
+
+    dma_tile(ta, K, t0 - 64, n, wave, lane);
+    dma_tile(tb, V, t0 - 64, n, wave, lane);
+    Frag<true> qf, df;
+    buf_frag(qf, rq, i, g);
+    buf_frag(df, rdo, i, g);
+    const float lse2_i = buf_f32(rl, i) * kLog2e;
+    float di[2];  // D of the slab-layout rows
+    if constexpr (WITH_D) {
+        // D from the slab layout (whole rows per load); the band reads it back from LDS
+        SFrag dos, os;
+        sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
+        sfrag_load(os, head_rsrc(static_cast<const uint16_t *>(p.o) + head, n * 128), row_s[0], row_s[1], c8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            di[h] = row8_sum(chunk_dot(dos.r[h], os.r[h]));
+            if (c8 == 0) {
+                d_s[16 * wave + s8 + 8 * h] = di[h];
+                if (row_s[h] < n) p.delta[(int64_t)bh * n + row_s[h]] = di[h];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) di[h] = buf_f32(rd, row_s[h]);
+    }
+    wait_vm_all();
+    __syncthreads();
+    const float di_i = WITH_D ? d_s[16 * wave + c16] : buf_f32(rd, i);
+
+    // the first slab rows land while the band runs
+    SFrag sk[kRingQ], sv[kRingQ];
+    auto fill = [&](int u, int t) {
+        sfrag_load(sk[u], rk, slab_row(p, t, row_s[0], -1), slab_row(p, t, row_s[1], -1), c8);
+        sfrag_load(sv[u], rv, slab_row(p, t, row_s[0], -1), slab_row(p, t, row_s[1], -1), c8);
+    };
+#pragma unroll
+    for (int u = 0; u < kPreQ; ++u) fill(u, u);
+
+    // band on MFMA: query row i sees key blocks qb-4 .. qb
+    f32x4_t acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int qb = r0 >> 4;
+    const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
+#pragma unroll 1
+    for (int b = 0; b < 5; ++b) {
+        const int kb0 = 16 * (qb - 4 + b);
+        if (kb0 + 15 < klo || kb0 > khi) continue;  // uniform across the wave
+        const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
+        const int lr = 16 * (wave + b);
+        Frag<true> kf, vf;
+        lds_frag(kf, ta, lr + c16, g);
+        lds_frag(vf, tb, lr + c16, g);
+        const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        float ds[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[r] = fast_exp2(st[r] * sl2 - lse2_i) * (dpt[r] - di_i);
+        if (!full) {  // uniform: edge blocks only
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = kb0 + 4 * g + r;
+                if (!(i_ok && j <= i && j > i - w && j >= 0)) ds[r] = 0.f;
+            }
+        }
+        mma_over_rows_tr(acc, ta, lr, c16, g, ds);
+    }
+#pragma unroll
+    for (int u = kPreQ; u < kRingQ; ++u) fill(u, u);
+    __syncthreads();  // every wave is done with the band tiles
+    f32x4_t dq_s[2][2];
+    c_to_slab(reinterpret_cast<float *>(ta) + wave * 1024, acc, dq_s, c16, g, s8, c8);
+
+    // sparse offsets: keys i - o, in the slab layout
+    SFrag qs, dos;
+    sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+    sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
+    float lse2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
+    const int64_t pair_stride = (int64_t)p.bh * n;  // words between offsets
+    uint32_t *pairs = p.pairs + (int64_t)bh * n;
+    // one slab: pair weights of the lane's two rows, dQ update, weights stored once per row
+    auto slab = [&](int t, int o, const SFrag &kt, const SFrag &vt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+            const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
+            const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
+            const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+            const uint32_t pw = pack_bf16(pv, pv * (dp - di[h]));
+            if (c8 == 0 && row_s[h] < n) pairs[t * pair_stride + row_s[h]] = pw;
+            chunk_axpy_words(dq_s[h], pw >> 16, pw & 0xffff0000u, kt.r[h]);
+        }
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < unrolled_slabs(kRingQ); s0 += kRingQ) {
+        if (s0 >= n_off || r0 + 15 < p.off[s0]) break;  // ascending offsets: no key left
+#pragma unroll
+        for (int u = 0; u < kRingQ; ++u) {
+            if (s0 + u < n_off) slab(s0 + u, table_off(p, s0 + u), sk[u], sv[u]);  // uniform
+            if (s0 + kRingQ < unrolled_slabs(kRingQ)) fill(u, s0 + u + kRingQ);
+        }
+    }
+    for (int t = unrolled_slabs(kRingQ); t < n_off; ++t) {  // longer tables
+        if (r0 + 15 < p.off[t]) break;
+        fill(0, t);
+        slab(t, p.off[t], sk[0], sv[0]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (row_s[h] < n) store_chunk(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
+}
+
+// dK, dV of key rows [t0, t0 + 64): the band queries [t0, t0 + 128) (Q, dO, LSE, D in
+// LDS) on MFMA first, then the slab queries j + off[t] in the slab layout with the
+// pair weights that bwd_dq_kernel stored.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) {
+    using OE = typename Elem<OUT_BF16>::T;
+    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // band Q rows, then merge areas
+    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // band dO rows, then merge areas
     __shared__ __attribute__((aligned(16))) float lse_s[kTileRows];       // log2-scaled LSE of band queries
     __shared__ __attribute__((aligned(16))) float del_s[kTileRows];       // D of band queries
 
@@ -1073,8 +1258,8 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
     const int s8 = lane >> 3, c8 = lane & 7;   // slab layout
     const int t0 = tile * 64, r0 = t0 + 16 * wave;
     const int row_s[2] = {r0 + s8, r0 + 8 + s8};
-    const int me = r0 + c16;  // MFMA-layout row: query row in phase A, key row in phase B
-    const bool me_ok = me < n;
+    const int j = r0 + c16;  // MFMA-layout key row
+    const bool j_ok = j < n;
     const int64_t head = (int64_t)bh * n * 64;
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + head;
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
@@ -1084,244 +1269,107 @@ __global__ void __launch_bounds__(kThreads) bwd_window_kernel(const AttnParams p
     const float *DEL = p.delta + (int64_t)bh * n;
     const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128);
     const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, n * 128), rdo = head_rsrc(DO, n * 128);
-    const __amdgpu_buffer_rsrc_t rl = head_rsrc(LSE, n * 4), rd = head_rsrc(DEL, n * 4);
     const float sl2 = p.scale_log2;
-    float *area_a = reinterpret_cast<float *>(ta) + wave * 1024;  // 16 x 64 fp32 per wave
-    float *area_b = reinterpret_cast<float *>(tb) + wave * 1024;
 
-    // =========================== phase A: dQ of query rows ===========================
-    {
-        dma_tile(ta, K, t0 - 64, n, wave, lane);
-        dma_tile(tb, V, t0 - 64, n, wave, lane);
-        const int i = me;
-        Frag<true> qf, df;
-        buf_frag(qf, rq, i, g);
-        buf_frag(df, rdo, i, g);
-        const float lse2_i = buf_f32(rl, i) * kLog2e;
-        const float di_i = buf_f32(rd, i);
-        wait_vm_all();
-        __syncthreads();
-
-        // band on MFMA: query row i sees key blocks qb-4 .. qb
-        f32x4_t acc[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int qb = r0 >> 4;
-        const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
-#pragma unroll 1
-        for (int b = 0; b < 5; ++b) {
-            const int kb0 = 16 * (qb - 4 + b);
-            if (kb0 + 15 < klo || kb0 > khi) continue;  // uniform across the wave
-            const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
-            const int lr = 16 * (wave + b);
-            Frag<true> kf, vf;
-            lds_frag(kf, ta, lr + c16, g);
-            lds_frag(vf, tb, lr + c16, g);
-            const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            float ds[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ds[r] = fast_exp2(st[r] * sl2 - lse2_i) * (dpt[r] - di_i);
-            if (!full) {  // uniform: edge blocks only
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = kb0 + 4 * g + r;
-                    if (!(me_ok && j <= i && j > i - w && j >= 0)) ds[r] = 0.f;
-                }
-            }
-            mma_over_rows_tr(acc, ta, lr, c16, g, ds);
-        }
-        __syncthreads();  // every wave is done with the K, V band tiles
-        f32x4_t dq_s[2][2];
-        c_to_slab(area_a, acc, dq_s, c16, g, s8, c8);
-        __syncthreads();  // every wave has read its merge area back
-
-        // phase B's band queries [t0, t0 + 128): copied while phase A's slabs run
-        dma_tile(ta, Q, t0, n, wave, lane);
-        dma_tile(tb, DO, t0, n, wave, lane);
-        if (tid < kTileRows) {
-            const int row = t0 + tid;
-            lse_s[tid] = (row < n) ? LSE[row] * kLog2e : 0.f;
-            del_s[tid] = (row < n) ? DEL[row] : 0.f;
-        }
-
-        // sparse offsets: keys i - o, in the slab layout
-        SFrag qs, dos;
-        sfrag_load(qs, rq, row_s[0], row_s[1], c8);
-        sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
-        float lse2[2], di[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
-            di[h] = buf_f32(rd, row_s[h]);
-        }
-        SFrag sk[kRingA], sv[kRingA];
-#pragma unroll
-        for (int u = 0; u < kRingA; ++u) {
-            sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
-            sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
-        }
-#pragma unroll
-        for (int s0 = 0; s0 < unrolled_slabs(kRingA); s0 += kRingA) {
-            if (s0 >= n_off || r0 + 15 < p.off[s0]) break;
-#pragma unroll
-            for (int u = 0; u < kRingA; ++u) {
-                const int o = table_off(p, s0 + u);
-                if (s0 + u < n_off) {  // uniform: slots past the table only refill
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-                        const float s = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
-                        const float dp = row8_sum(chunk_dot(dos.r[h], sv[u].r[h]));
-                        const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
-                        chunk_axpy(dq_s[h], pv * (dp - di[h]), sk[u].r[h]);
-                    }
-                }
-                if (s0 + kRingA < unrolled_slabs(kRingA)) {
-                    const int tn = s0 + u + kRingA;
-                    sfrag_load(sk[u], rk, slab_row(p, tn, row_s[0], -1), slab_row(p, tn, row_s[1], -1), c8);
-                    sfrag_load(sv[u], rv, slab_row(p, tn, row_s[0], -1), slab_row(p, tn, row_s[1], -1), c8);
-                }
-            }
-        }
-        for (int t = unrolled_slabs(kRingA); t < n_off; ++t) {  // longer tables
-            if (r0 + 15 < p.off[t]) break;
-            SFrag kt, vt;
-            sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-            sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
-                const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
-                const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
-                const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
-                chunk_axpy(dq_s[h], pv * (dp - di[h]), kt.r[h]);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            if (row_s[h] < n) store_chunk(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
+    dma_tile(ta, Q, t0, n, wave, lane);
+    dma_tile(tb, DO, t0, n, wave, lane);
+    if (tid < kTileRows) {
+        const int row = t0 + tid;
+        lse_s[tid] = (row < n) ? LSE[row] * kLog2e : 0.f;
+        del_s[tid] = (row < n) ? DEL[row] : 0.f;
     }
+    Frag<true> kf, vf;
+    buf_frag(kf, rk, j, g);
+    buf_frag(vf, rv, j, g);
+    wait_vm_all();
+    __syncthreads();
 
-    // ========================= phase B: dK, dV of key rows ==========================
-    {
-        const int j = me;
-        Frag<true> kf, vf;
-        buf_frag(kf, rk, j, g);
-        buf_frag(vf, rv, j, g);
-        wait_vm_all();
-        __syncthreads();  // the Q, dO band copies and the LSE, D rows have landed
-
-        // band on MFMA: key row j sees query blocks r0 + 16 b
-        f32x4_t dk[4], dv[4];
+    // slot u: query rows row + off[u] (Q, dO) and their pair weights
+    SFrag sq[kRingKV], sd[kRingKV];
+    uint32_t pw[kRingKV][2];
+    auto fill = [&](int u, int t) {
+        const int iq0 = slab_row(p, t, row_s[0], 1), iq1 = slab_row(p, t, row_s[1], 1);
+        sfrag_load(sq[u], rq, iq0, iq1, c8);
+        sfrag_load(sd[u], rdo, iq0, iq1, c8);
+        const __amdgpu_buffer_rsrc_t rp = pair_rsrc(p, t, bh);
+        pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, iq0 * 4, 0, 0);
+        pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, iq1 * 4, 0, 0);
+    };
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            dk[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        const int qhi = min(r0 + 15 + w - 1, n - 1);
+    for (int u = 0; u < kPreKV; ++u) fill(u, u);
+
+    // band on MFMA: key row j sees query blocks r0 + 16 b
+    f32x4_t dk[4], dv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        dk[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int qhi = min(r0 + 15 + w - 1, n - 1);
 #pragma unroll 1
-        for (int b = 0; b < 5; ++b) {
-            const int qb0 = r0 + 16 * b;
-            if (qb0 > qhi) break;  // uniform across the wave
-            const bool full = qb0 >= r0 + 15 && qb0 + 15 <= r0 + w - 1 && qb0 + 15 < n && r0 + 15 < n;
-            const int lr = 16 * (wave + b);
-            Frag<true> qf, df;
-            lds_frag(qf, ta, lr + c16, g);
-            lds_frag(df, tb, lr + c16, g);
-            const f32x4_t sq4 = mma_over_d(qf, kf, f32x4_t{0.f, 0.f, 0.f, 0.f});  // rows: queries
-            const f32x4_t dp4 = mma_over_d(df, vf, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse_s + lr + 4 * g);
-            const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + lr + 4 * g);
-            float pr[4], ds[4];
+    for (int b = 0; b < 5; ++b) {
+        const int qb0 = r0 + 16 * b;
+        if (qb0 > qhi) break;  // uniform across the wave
+        const bool full = qb0 >= r0 + 15 && qb0 + 15 <= r0 + w - 1 && qb0 + 15 < n && r0 + 15 < n;
+        const int lr = 16 * (wave + b);
+        Frag<true> qf, df;
+        lds_frag(qf, ta, lr + c16, g);
+        lds_frag(df, tb, lr + c16, g);
+        const f32x4_t sq4 = mma_over_d(qf, kf, f32x4_t{0.f, 0.f, 0.f, 0.f});  // rows: queries
+        const f32x4_t dp4 = mma_over_d(df, vf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse_s + lr + 4 * g);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + lr + 4 * g);
+        float pr[4], ds[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sq4[r] * sl2 - l4[r]);
-            if (!full) {  // uniform: edge blocks only
+        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sq4[r] * sl2 - l4[r]);
+        if (!full) {  // uniform: edge blocks only
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int q = qb0 + 4 * g + r;
-                    if (!(me_ok && q < n && q >= j && q - j < w)) pr[r] = 0.f;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int q = qb0 + 4 * g + r;
+                if (!(j_ok && q < n && q >= j && q - j < w)) pr[r] = 0.f;
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ds[r] = pr[r] * (dp4[r] - d4[r]);
-            mma_over_rows_tr(dv, tb, lr, c16, g, pr);
-            mma_over_rows_tr(dk, ta, lr, c16, g, ds);
         }
-        __syncthreads();  // every wave is done with the Q, dO band tiles
-        f32x4_t dk_s[2][2], dv_s[2][2];
-        c_to_slab(area_a, dk, dk_s, c16, g, s8, c8);
-        c_to_slab(area_b, dv, dv_s, c16, g, s8, c8);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ds[r] = pr[r] * (dp4[r] - d4[r]);
+        mma_over_rows_tr(dv, tb, lr, c16, g, pr);
+        mma_over_rows_tr(dk, ta, lr, c16, g, ds);
+    }
+#pragma unroll
+    for (int u = kPreKV; u < kRingKV; ++u) fill(u, u);
+    __syncthreads();  // every wave is done with the band tiles
+    f32x4_t dk_s[2][2], dv_s[2][2];
+    c_to_slab(reinterpret_cast<float *>(ta) + wave * 1024, dk, dk_s, c16, g, s8, c8);
+    c_to_slab(reinterpret_cast<float *>(tb) + wave * 1024, dv, dv_s, c16, g, s8, c8);
 
-        // sparse offsets: queries j + o, in the slab layout
-        SFrag kS, vS;
-        sfrag_load(kS, rk, row_s[0], row_s[1], c8);
-        sfrag_load(vS, rv, row_s[0], row_s[1], c8);
-        SFrag sq[kRingB], sd[kRingB];
-        float sl[kRingB][2], sdl[kRingB][2];
-#pragma unroll
-        for (int u = 0; u < kRingB; ++u) {
-            const int iq0 = slab_row(p, u, row_s[0], 1), iq1 = slab_row(p, u, row_s[1], 1);
-            sfrag_load(sq[u], rq, iq0, iq1, c8);
-            sfrag_load(sd[u], rdo, iq0, iq1, c8);
-            sl[u][0] = buf_f32(rl, iq0);
-            sl[u][1] = buf_f32(rl, iq1);
-            sdl[u][0] = buf_f32(rd, iq0);
-            sdl[u][1] = buf_f32(rd, iq1);
-        }
-#pragma unroll
-        for (int s0 = 0; s0 < unrolled_slabs(kRingB); s0 += kRingB) {
-            if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
-#pragma unroll
-            for (int u = 0; u < kRingB; ++u) {
-                const int o = table_off(p, s0 + u);
-                if (s0 + u < n_off) {  // uniform: slots past the table only refill
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const bool ok = (row_s[h] < n) & (row_s[h] + o < n);
-                        const float s = row8_sum(chunk_dot(sq[u].r[h], kS.r[h]));
-                        const float dp = row8_sum(chunk_dot(sd[u].r[h], vS.r[h]));
-                        const float pv = ok ? fast_exp2(s * sl2 - sl[u][h] * kLog2e) : 0.f;
-                        chunk_axpy(dv_s[h], pv, sd[u].r[h]);
-                        chunk_axpy(dk_s[h], pv * (dp - sdl[u][h]), sq[u].r[h]);
-                    }
-                }
-                if (s0 + kRingB < unrolled_slabs(kRingB)) {
-                    const int tn = s0 + u + kRingB;
-                    const int iq0 = slab_row(p, tn, row_s[0], 1), iq1 = slab_row(p, tn, row_s[1], 1);
-                    sfrag_load(sq[u], rq, iq0, iq1, c8);
-                    sfrag_load(sd[u], rdo, iq0, iq1, c8);
-                    sl[u][0] = buf_f32(rl, iq0);
-                    sl[u][1] = buf_f32(rl, iq1);
-                    sdl[u][0] = buf_f32(rd, iq0);
-                    sdl[u][1] = buf_f32(rd, iq1);
-                }
-            }
-        }
-        for (int t = unrolled_slabs(kRingB); t < n_off; ++t) {  // longer tables
-            if (r0 + p.off[t] >= n) break;
-            const int iq0 = row_s[0] + p.off[t], iq1 = row_s[1] + p.off[t];
-            SFrag qt, dt;
-            sfrag_load(qt, rq, iq0, iq1, c8);
-            sfrag_load(dt, rdo, iq0, iq1, c8);
-            const float lq[2] = {buf_f32(rl, iq0), buf_f32(rl, iq1)};
-            const float dq2[2] = {buf_f32(rd, iq0), buf_f32(rd, iq1)};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bool ok = (row_s[h] < n) & (row_s[h] + p.off[t] < n);
-                const float s = row8_sum(chunk_dot(qt.r[h], kS.r[h]));
-                const float dp = row8_sum(chunk_dot(dt.r[h], vS.r[h]));
-                const float pv = ok ? fast_exp2(s * sl2 - lq[h] * kLog2e) : 0.f;
-                chunk_axpy(dv_s[h], pv, dt.r[h]);
-                chunk_axpy(dk_s[h], pv * (dp - dq2[h]), qt.r[h]);
-            }
-        }
+    // sparse offsets: queries j + o, weights P (low half) and dS (high half) as stored;
+    // pairs past the sequence end read as zero words
+    auto slab = [&](const uint32_t pwt[2], const SFrag &qt, const SFrag &dt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            if (row_s[h] < n) {
-                store_chunk(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], p.scale);
-                store_chunk(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
-            }
+            const uint32_t x = pwt[h];
+            chunk_axpy_words(dv_s[h], x & 0xffffu, x << 16, dt.r[h]);
+            chunk_axpy_words(dk_s[h], x >> 16, x & 0xffff0000u, qt.r[h]);
+        }
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < unrolled_slabs(kRingKV); s0 += kRingKV) {
+        if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
+#pragma unroll
+        for (int u = 0; u < kRingKV; ++u) {
+            if (s0 + u < n_off) slab(pw[u], sq[u], sd[u]);  // uniform
+            if (s0 + kRingKV < unrolled_slabs(kRingKV)) fill(u, s0 + u + kRingKV);
+        }
+    }
+    for (int t = unrolled_slabs(kRingKV); t < n_off; ++t) {  // longer tables
+        if (r0 + p.off[t] >= n) break;
+        fill(0, t);
+        slab(pw[0], sq[0], sd[0]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (row_s[h] < n) {
+            store_chunk(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], p.scale);
+            store_chunk(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
         }
     }
 }
@@ -1346,8 +1394,7 @@ hipError_t launch_generic_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const Attn
 
 }  // namespace
 
-// The window kernels address a head with 32-bit byte offsets (buffer loads).
-bool window_path(fsa_dtype_t dt, const AttnParams &p) { return dt == FSA_BF16 && p.w <= 64 && p.n <= (1 << 24); }
+bool window_path(fsa_dtype_t dt, const AttnParams &p) { return window_path(dt, p.w, p.n); }
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (window_path(dt, p))
@@ -1367,10 +1414,24 @@ hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_
     return dt == FSA_BF16 ? launch(&delta_kernel<true>, grid, p, s) : launch(&delta_kernel<false>, grid, p, s);
 }
 
-hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
-    if (window_path(dt, p))
-        return out_dt == FSA_BF16 ? launch(&bwd_window_kernel<true>, tiles(p), p, s)
-                                  : launch(&bwd_window_kernel<false>, tiles(p), p, s);
+hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s,
+                                 bool with_delta) {
+    if (window_path(dt, p)) {
+        hipError_t e;
+        if (with_delta)
+            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true>, tiles(p), p, s)
+                                   : launch(&bwd_dq_kernel<false, true>, tiles(p), p, s);
+        else
+            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, false>, tiles(p), p, s)
+                                   : launch(&bwd_dq_kernel<false, false>, tiles(p), p, s);
+        if (e != hipSuccess) return e;
+        return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true>, tiles(p), p, s)
+                                  : launch(&bwd_dkdv_kernel<false>, tiles(p), p, s);
+    }
+    if (with_delta) {  // the generic kernel reads D: form it first
+        const hipError_t e = launch_backward_delta(dt, p, s);
+        if (e != hipSuccess) return e;
+    }
     if (dt == FSA_BF16)
         return out_dt == FSA_BF16 ? launch(&bwd_generic_kernel<true, true>, tiles(p), p, s)
                                   : launch(&bwd_generic_kernel<true, false>, tiles(p), p, s);

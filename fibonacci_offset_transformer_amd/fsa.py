@@ -3,9 +3,10 @@ the computation runs in the HIP library; torch supplies device memory and the
 current stream.
 
 Signatures mirror include/fsa.h: tensors are contiguous [B, H, N, 64] in
-float32 or bfloat16 on one GPU; LSE and the backward workspace are float32
-[B, H, N]. There is no CPU fallback: without the built library every call
-raises.
+float32 or bfloat16 on one GPU; LSE and the backward D workspace are float32
+[B, H, N]; the backward pair workspace is a device buffer of
+workspace_bytes(...) bytes (allocated here when the caller passes none). There
+is no CPU fallback: without the built library every call raises.
 """
 from __future__ import annotations
 
@@ -25,8 +26,8 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 MAX_OFFSETS = 48
 
 # Exported symbols, in the order include/fsa.h declares them.
-EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_delta", "fsa_backward_grads",
-           "fsa_dense_forward", "fsa_last_error")
+EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_workspace_bytes",
+           "fsa_backward_delta", "fsa_backward_grads", "fsa_dense_forward", "fsa_last_error")
 
 
 class FsaError(RuntimeError):
@@ -55,12 +56,16 @@ def library() -> ctypes.CDLL:
             L.fsa_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
                                       ctypes.c_int, f64, i32, i32, vp]
             L.fsa_forward.restype = ctypes.c_int
-            L.fsa_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+            u64 = ctypes.c_uint64
+            L.fsa_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64,
                                        i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
             L.fsa_backward.restype = ctypes.c_int
+            L.fsa_backward_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64, i32,
+                                                       i32, ctypes.POINTER(u64)]
+            L.fsa_backward_workspace_bytes.restype = ctypes.c_int
             L.fsa_backward_delta.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, vp]
             L.fsa_backward_delta.restype = ctypes.c_int
-            L.fsa_backward_grads.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+            L.fsa_backward_grads.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64,
                                              i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
             L.fsa_backward_grads.restype = ctypes.c_int
             L.fsa_dense_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
@@ -134,8 +139,30 @@ def forward(q, k, v, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", s
     return o, l
 
 
+def workspace_bytes(dtype, B: int, H: int, N: int, d: int = 64, *, alpha: float = 1.0, w: int, R: int,
+                    base: str = "fib") -> int:
+    """Bytes of pair workspace the backward of this problem needs (see fsa_backward_workspace_bytes)."""
+    out = ctypes.c_uint64(0)
+    _check(library().fsa_backward_workspace_bytes(DTYPES[dtype], int(B), int(H), int(N), int(d), BASES[base],
+                                                  float(alpha), int(w), int(R), ctypes.byref(out)))
+    return int(out.value)
+
+
+def _pair_ws(q, pair_ws, alpha, w, R, base):
+    """(pointer, size) of the pair workspace: the caller's buffer, or a new one of the size needed."""
+    B, H, N, d = q.shape
+    if pair_ws is None:
+        need = workspace_bytes(q.dtype, B, H, N, d, alpha=alpha, w=w, R=R, base=base)
+        if need == 0:
+            return None, 0
+        pair_ws = torch.empty(need // 4, dtype=torch.int32, device=q.device)
+    if not pair_ws.is_cuda or not pair_ws.is_contiguous() or pair_ws.device != q.device:
+        raise ValueError("pair_ws must be a contiguous device tensor on the inputs' device")
+    return pair_ws, pair_ws.numel() * pair_ws.element_size()
+
+
 def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
-             scale=None, dq=None, dk=None, dv=None, delta=None, out_dtype=None):
+             scale=None, dq=None, dk=None, dv=None, delta=None, pair_ws=None, out_dtype=None):
     """Sparse backward: returns (dq, dk, dv) in out_dtype (default q.dtype).
     q, k, v, o and dout share one dtype."""
     B, H, N, d = _shape(q, k, v, o, dout)
@@ -143,10 +170,11 @@ def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base:
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
     ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    pw, pw_bytes = _pair_ws(q, pair_ws, alpha, w, R, base)
     with torch.cuda.device(q.device):
         _check(library().fsa_backward(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), B, H, N, d,
-                                      _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _ptr(pw), pw_bytes,
+                                      B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
                                       _stream(q.device)))
     return dq, dk, dv
 
@@ -162,17 +190,18 @@ def backward_delta(o, dout, *, delta=None):
 
 
 def backward_grads(q, k, v, lse, dout, delta, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
-                   scale=None, dq=None, dk=None, dv=None, out_dtype=None):
+                   scale=None, dq=None, dk=None, dv=None, pair_ws=None, out_dtype=None):
     """Second backward stage: (dq, dk, dv) from a D computed by backward_delta."""
     B, H, N, d = _shape(q, k, v, dout)
     dq = _out(q, dq, out_dtype)
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
+    pw, pw_bytes = _pair_ws(q, pair_ws, alpha, w, R, base)
     with torch.cuda.device(q.device):
         _check(library().fsa_backward_grads(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v),
                                             _ptr(lse), _ptr(dout), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
-                                            B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
-                                            int(R), _stream(q.device)))
+                                            _ptr(pw), pw_bytes, B, H, N, d, _scale(scale, d), BASES[base],
+                                            float(alpha), int(w), int(R), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -123,12 +123,31 @@ fsa_status_t fsa_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, cons
  *   lse                 input float32 [B,H,N]
  *   dq, dk, dv          outputs [B,H,N,d]
  *   delta_ws            caller-owned float32 [B,H,N] workspace, overwritten with D
+ *   pair_ws             caller-owned device workspace of at least
+ *                       fsa_backward_workspace_bytes(...) bytes, 16-byte aligned,
+ *                       overwritten; its contents on entry do not matter. It may
+ *                       be NULL when that size is 0.
+ *   pair_ws_bytes       size of pair_ws in bytes; FSA_E_ARG if smaller than needed
  */
 fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
                           const void *v, const void *o, const float *lse, const void *dout,
-                          void *dq, void *dk, void *dv, float *delta_ws,
-                          int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                          void *dq, void *dk, void *dv, float *delta_ws, void *pair_ws,
+                          uint64_t pair_ws_bytes, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
                           fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
+
+/*
+ * fsa_backward_workspace_bytes - bytes of pair workspace the backward needs.
+ *
+ * On the bf16 window path (dt = FSA_BF16, w <= 64, N <= 2^24) the gradient stage
+ * runs as two kernels: the first stores, for every query row i and sparse offset
+ * o of the table (offsets >= N dropped), the bf16 values of P and dS of the pair
+ * (i, i - o) in one 32-bit word; the second reads them to form dK and dV. The
+ * size is 4 * |T| * B * H * N bytes there and 0 on every other path. Arguments
+ * as in fsa_backward; *bytes receives the size.
+ */
+fsa_status_t fsa_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                                          fsa_base_t base, double alpha, int32_t w, int32_t R,
+                                          uint64_t *bytes);
 
 /*
  * fsa_backward_delta and fsa_backward_grads - the two stages of fsa_backward,
@@ -142,9 +161,10 @@ fsa_status_t fsa_backward_delta(fsa_dtype_t dt, const void *o, const void *dout,
                                 int32_t B, int32_t H, int32_t N, int32_t d, void *stream);
 fsa_status_t fsa_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
                                 const void *v, const float *lse, const void *dout,
-                                const float *delta, void *dq, void *dk, void *dv, int32_t B,
-                                int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base,
-                                double alpha, int32_t w, int32_t R, void *stream);
+                                const float *delta, void *dq, void *dk, void *dv, void *pair_ws,
+                                uint64_t pair_ws_bytes, int32_t B, int32_t H, int32_t N, int32_t d,
+                                float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                                void *stream);
 
 /*
  * fsa_dense_forward - dense causal attention baseline (every j <= i attended),

@@ -133,9 +133,16 @@ def fwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1
     return lib.fsa_forward(dt, out_dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
 
 
-def bwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256, out_dt=1):
-    p = ptrs or FAKE[:10]
-    return lib.fsa_backward(dt, out_dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+def bwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256, out_dt=1,
+        pair_bytes=1 << 40):
+    p = ptrs or FAKE[:11]  # q k v o lse dout dq dk dv delta_ws pair_ws
+    return lib.fsa_backward(dt, out_dt, *p, pair_bytes, B, H, N, d, scale, base, alpha, w, R, None)
+
+
+def grads(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256, out_dt=1,
+          pair_bytes=1 << 40):
+    p = ptrs or FAKE[:10]  # q k v lse dout delta dq dk dv pair_ws
+    return lib.fsa_backward_grads(dt, out_dt, *p, pair_bytes, B, H, N, d, scale, base, alpha, w, R, None)
 
 
 def dense(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, out_dt=1):
@@ -143,7 +150,7 @@ def dense(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, out_dt=1):
     return lib.fsa_dense_forward(dt, out_dt, *p, B, H, N, d, scale, None)
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, dense])
+@pytest.mark.parametrize("call", [fwd, bwd, grads, dense])
 def test_shape_and_dtype_errors(lib, call):
     assert call(lib, d=32) == fsa.FSA_E_UNSUPPORTED
     assert call(lib, d=0) == fsa.FSA_E_ARG
@@ -156,7 +163,7 @@ def test_shape_and_dtype_errors(lib, call):
     assert call(lib, B=1 << 20, H=1 << 12, N=1 << 16) == fsa.FSA_E_ARG  # grid too large
 
 
-@pytest.mark.parametrize("call", [fwd, bwd])
+@pytest.mark.parametrize("call", [fwd, bwd, grads])
 def test_table_errors_on_attention_calls(lib, call):
     assert call(lib, alpha=0.0) == fsa.FSA_E_ARG
     assert call(lib, alpha=float("nan")) == fsa.FSA_E_ARG
@@ -165,7 +172,7 @@ def test_table_errors_on_attention_calls(lib, call):
     assert call(lib, base=9) == fsa.FSA_E_ARG
 
 
-@pytest.mark.parametrize("call,n", [(fwd, 5), (bwd, 10), (dense, 5)])
+@pytest.mark.parametrize("call,n", [(fwd, 5), (bwd, 11), (grads, 10), (dense, 5)])
 def test_null_misaligned_and_aliased_pointers(lib, call, n):
     for k in range(n):
         ptrs = list(FAKE[:n])
@@ -181,9 +188,46 @@ def test_null_misaligned_and_aliased_pointers(lib, call, n):
     assert b"aliases" in lib.fsa_last_error()
 
 
-@pytest.mark.parametrize("call,n", [(fwd, 5), (bwd, 10), (dense, 5)])
+@pytest.mark.parametrize("call,n", [(fwd, 5), (bwd, 11), (grads, 10), (dense, 5)])
 def test_empty_problems_launch_nothing(lib, call, n):
     nulls = [P(0)] * n
     for B, H, N in ((0, 1, 64), (1, 0, 64), (1, 1, 0)):
         assert call(lib, ptrs=nulls, B=B, H=H, N=N) == fsa.FSA_OK
         assert lib.fsa_last_error() == b""
+
+
+def ws_bytes(lib, dt=1, B=2, H=8, N=4096, d=64, base=0, alpha=1.0, w=64, R=1024):
+    out = ctypes.c_uint64(123)
+    st = lib.fsa_backward_workspace_bytes(dt, B, H, N, d, base, alpha, w, R, ctypes.byref(out))
+    return st, out.value
+
+
+def test_backward_workspace_size(lib):
+    # bf16, window 64: one 32-bit word per (offset, head, row); alpha = 1, R = 1024 gives
+    # the offsets 89, 144, 233, 377, 610, 987 (all below N = 4096)
+    assert ws_bytes(lib) == (fsa.FSA_OK, 4 * 6 * 16 * 4096)
+    # offsets >= N are dropped: at N = 600 only 89, 144, 233, 377 remain
+    assert ws_bytes(lib, N=600) == (fsa.FSA_OK, 4 * 4 * 16 * 600)
+    # paths without the pair workspace: fp32 inputs, wide windows
+    assert ws_bytes(lib, dt=0) == (fsa.FSA_OK, 0)
+    assert ws_bytes(lib, w=65) == (fsa.FSA_OK, 0)
+    assert ws_bytes(lib, B=0) == (fsa.FSA_OK, 0)
+    assert ws_bytes(lib, alpha=0.0)[0] == fsa.FSA_E_ARG
+    assert ws_bytes(lib, d=32)[0] == fsa.FSA_E_UNSUPPORTED
+    assert lib.fsa_backward_workspace_bytes(1, 1, 1, 64, 64, 0, 1.0, 64, 1024, None) == fsa.FSA_E_ARG
+
+
+@pytest.mark.parametrize("call", [bwd, grads])
+def test_backward_pair_workspace_checks(lib, call):
+    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 3 * 64 words needed.
+    # Only failing validations are exercised here (the pointers are fake); the calls
+    # that pass NULL for an unneeded workspace run in the GPU tests (fp32 inputs).
+    need = 4 * 3 * 64
+    assert call(lib, pair_bytes=need - 1) == fsa.FSA_E_ARG
+    assert b"pair_ws holds" in lib.fsa_last_error()
+    assert call(lib, pair_bytes=0) == fsa.FSA_E_ARG
+    n = 11 if call is bwd else 10
+    ptrs = list(FAKE[:n])
+    ptrs[n - 1] = P(0)
+    assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG
+    assert b"pair_ws is NULL" in lib.fsa_last_error()

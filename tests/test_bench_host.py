@@ -25,8 +25,8 @@ def test_algorithmic_bytes_match_the_stated_totals():
     bhn = bench.B * bench.H * bench.N
     assert per["step"] * rows == (4 * vt + 4 * bhn) + (8 * vt + 4 * bhn)
     assert per["step"] * rows * bench.LAYERS == 1_619_001_344
-    # the kernels move the step's bytes plus D (written once, read once) and a second dO read
-    assert (per["fwd"] + per["delta"] + per["grads"]) * rows == per["step"] * rows + 8 * bhn + vt
+    # the two stages move exactly the step's bytes: the backward reads back o and lse
+    assert (per["fwd"] + per["bwd"]) * rows == per["step"] * rows
 
 
 def test_dense_flops():

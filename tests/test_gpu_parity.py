@@ -268,17 +268,41 @@ def test_backward_equals_its_two_stages():
     assert float((D.double() - ref).abs().max()) <= 1e-4
 
 
+def test_pair_workspace_contents_do_not_matter():
+    # every word the dK/dV kernel reads was written by the dQ kernel of the same call
+    x = inputs(20, 0, (1, 2, 777, 64), torch.bfloat16, grad=True)
+    kw = dict(alpha=0.75, w=64, R=1024, scale=0.125)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    need = fsa.workspace_bytes(torch.bfloat16, 1, 2, 777, alpha=0.75, w=64, R=1024)
+    assert need > 0
+    runs = []
+    for fill in (0, 0x7FC07FC0, -1):  # zeros, NaN bit patterns, all ones
+        pw = torch.full((need // 4 + 333,), fill, dtype=torch.int32, device=dev())
+        runs.append(fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], pair_ws=pw, out_dtype=torch.float32, **kw))
+    torch.cuda.synchronize()
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            assert torch.equal(a, b)
+    T = oracle.offset_table("fib", 0.75, 64, 1024)
+    for h in range(2):
+        q, k, v, do = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v", "do"))
+        for name, got, want in zip(("dq", "dk", "dv"), runs[0], oracle.sparse_backward(q, k, v, do, T, 64, 0.125)):
+            check(f"{name}[0,{h}]", got[0, h], want, TOL[torch.bfloat16])
+
+
 def test_graph_replays_match_eager():
     x = inputs(19, 0, (2, 4, 700, 64), torch.bfloat16, grad=True)
     kw = dict(alpha=1.2, w=64, R=1024, scale=0.125)
     bufs = {n: torch.empty_like(x["q"]) for n in ("o", "dq", "dk", "dv")}
     lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=x["q"].device)
     D = torch.empty_like(lse)
+    pw = torch.empty(fsa.workspace_bytes(torch.bfloat16, 2, 4, 700, w=64, R=1024, alpha=1.2) // 4,
+                     dtype=torch.int32, device=x["q"].device)
 
     def step():
         fsa.forward(x["q"], x["k"], x["v"], out=bufs["o"], lse=lse, **kw)
         fsa.backward(x["q"], x["k"], x["v"], bufs["o"], lse, x["do"], dq=bufs["dq"], dk=bufs["dk"],
-                     dv=bufs["dv"], delta=D, **kw)
+                     dv=bufs["dv"], delta=D, pair_ws=pw, **kw)
 
     step()
     torch.cuda.synchronize()
