@@ -44,6 +44,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -419,10 +420,28 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Row fragment (lane group g's 16 elements: chunks g and g + 4) of tile row `row`.
-__device__ __forceinline__ void lds_frag(Frag<true> &f, const uint16_t *tile, int row, int g) {
-    f.c[0] = *reinterpret_cast<const u32x4_t *>(tile + tile_chunk(row, g));
-    f.c[1] = *reinterpret_cast<const u32x4_t *>(tile + tile_chunk(row, g + 4));
+// Per-lane element offsets into a swizzled tile, for blocks of 16 rows starting at a
+// multiple of 8 (the swizzle then depends on the lane only, so a block's rows add a
+// constant that the LDS instructions take as an immediate).
+struct TileLanes {
+    int frag[2];  // row fragment of row c16: chunks g and g + 4
+    int tr[4];    // transposed reads, one per output block db
+};
+
+__device__ __forceinline__ TileLanes tile_lanes(int c16, int g) {
+    TileLanes t;
+    t.frag[0] = tile_chunk(c16, g);
+    t.frag[1] = tile_chunk(c16, g + 4);
+    const int row = 4 * g + (c16 >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) t.tr[db] = tile_chunk(row, 4 * (db >> 1) + (c16 & 3)) + 4 * (db & 1);
+    return t;
+}
+
+// Row fragment (lane group g's 16 elements: chunks g and g + 4) of tile row lr + c16.
+__device__ __forceinline__ void lds_frag(Frag<true> &f, const uint16_t *tile, int lr, const TileLanes &tl) {
+    f.c[0] = *reinterpret_cast<const u32x4_t *>(tile + lr * 64 + tl.frag[0]);
+    f.c[1] = *reinterpret_cast<const u32x4_t *>(tile + lr * 64 + tl.frag[1]);
 }
 
 // acc[db] += sum_{kk<16} Tile[lr + kk][d] * Bv[kk][col] for the four output blocks db,
@@ -432,16 +451,31 @@ __device__ __forceinline__ void lds_frag(Frag<true> &f, const uint16_t *tile, in
 // addresses. Lane s therefore addresses row lr + 4 g + s / 4 at column
 // 32 (db / 2) + 8 (s % 4) + 4 (db % 2), i.e. half db % 2 of chunk 4 (db / 2) + s % 4,
 // which hands lane j the column acc_row_d(db, j) of rows lr + 4 g + k.
-__device__ __forceinline__ void mma_over_rows_tr(f32x4_t acc[4], const uint16_t *tile, int lr, int c16, int g,
+__device__ __forceinline__ void mma_over_rows_tr(f32x4_t acc[4], const uint16_t *tile, int lr, const TileLanes &tl,
                                                  const float bv[4]) {
     const u32x2_t b = {pack_bf16(bv[0], bv[1]), pack_bf16(bv[2], bv[3])};
     const i16x4_t bb = __builtin_bit_cast(i16x4_t, b);
-    const int row = lr + 4 * g + (c16 >> 2);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-        const uint16_t *p = tile + tile_chunk(row, 4 * (db >> 1) + (c16 & 3)) + 4 * (db & 1);
-        const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)p);
+        const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr * 64 + tl.tr[db]));
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bb, acc[db], 0, 0, 0);
+    }
+}
+
+// As mma_over_rows_tr for two 16-row blocks at once (rows lr0 .. lr0+15 with weights
+// bv0 and rows lr1 .. lr1+15 with bv1) on the 32-deep MFMA: k-slots 0..3 of lane group
+// g are rows lr0 + 4 g + k and slots 4..7 rows lr1 + 4 g + k, in both operands.
+__device__ __forceinline__ void mma_over_rows_tr2(f32x4_t acc[4], const uint16_t *tile, int lr0, int lr1,
+                                                  const TileLanes &tl, const float bv0[4], const float bv1[4]) {
+    const u32x4_t b = {pack_bf16(bv0[0], bv0[1]), pack_bf16(bv0[2], bv0[3]), pack_bf16(bv1[0], bv1[1]),
+                       pack_bf16(bv1[2], bv1[3])};
+    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr0 * 64 + tl.tr[db]));
+        const i16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr1 * 64 + tl.tr[db]));
+        const i16x8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bb, acc[db], 0, 0, 0);
     }
 }
 
@@ -693,6 +727,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c16 = lane & 15, g = lane >> 4;  // MFMA layout: row c16, lane group g
+    const TileLanes tl = tile_lanes(c16, g);
+    const uint16_t *ks_w = ks + 1024 * wave, *vs_w = vs + 1024 * wave;  // this wave's band rows start here
     const int s8 = lane >> 3, c8 = lane & 7;   // slab layout: rows s8 and 8 + s8, chunk c8
     const int i0 = tile * 64, r0 = i0 + 16 * wave;
     const int row_s[2] = {r0 + s8, r0 + 8 + s8};
@@ -721,27 +757,29 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     }
 
     // ---- window band on MFMA: rows r0..r0+15 (row c16 of the lane) see key blocks qb-4 .. qb ----
+    // Blocks wholly outside the sequence or the window are computed like the others and
+    // masked: their tile rows hold finite values (row 0 stands in for rows outside [0, n)).
     const int qb = r0 >> 4;
-    const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
     float sc[5][4];
     float bm = kNegInf;
 #pragma unroll
     for (int b = 0; b < 5; ++b) {
         const int kb0 = 16 * (qb - 4 + b);
-        const bool active = kb0 + 15 >= klo && kb0 <= khi;
         const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
-        f32x4_t st = {kNegInf, kNegInf, kNegInf, kNegInf};
-        if (active) {
-            Frag<true> kf;
-            lds_frag(kf, ks, 16 * (wave + b) + c16, g);
-            st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+        Frag<true> kf;
+        lds_frag(kf, ks_w, 16 * b, tl);
+        f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+        if (!full) {  // uniform: edge blocks only
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = kb0 + 4 * g + r;
+                if (!(row_ok && j <= i && j > i - w && j >= 0)) st[r] = kNegInf;
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int j = kb0 + 4 * g + r;
-            const bool ok = full || (active && row_ok && j <= i && j > i - w && j >= 0);
-            sc[b][r] = ok ? st[r] : kNegInf;
-            bm = fmaxf(bm, sc[b][r]);
+            sc[b][r] = st[r];
+            bm = fmaxf(bm, st[r]);
         }
     }
     const float m_b = group_max(bm);
@@ -749,19 +787,17 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     f32x4_t acc_b[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc_b[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float lsum_b = 0.f;
+    float pr[5][4], lsum_b = 0.f;
 #pragma unroll
-    for (int b = 0; b < 5; ++b) {
-        const int kb0 = 16 * (qb - 4 + b);
-        const bool active = kb0 + 15 >= klo && kb0 <= khi;
-        float pr[4];
+    for (int b = 0; b < 5; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pr[r] = fast_exp2(sc[b][r] - msb);
-            lsum_b += pr[r];
+            pr[b][r] = fast_exp2(sc[b][r] - msb);
+            lsum_b += pr[b][r];
         }
-        if (active) mma_over_rows_tr(acc_b, vs, 16 * (wave + b), c16, g, pr);
-    }
+    mma_over_rows_tr2(acc_b, vs_w, 0, 16, tl, pr[0], pr[1]);
+    mma_over_rows_tr2(acc_b, vs_w, 32, 48, tl, pr[2], pr[3]);
+    mma_over_rows_tr(acc_b, vs_w, 64, tl, pr[4]);
     const float l_b = group_sum(lsum_b);
 
     // ---- the band state, moved into the slab layout, starts the slabs' online softmax ----
@@ -793,10 +829,13 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             const int o = table_off(p, t0 + u);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-                const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
-                ss[u][h] = ok ? d * sl2 : kNegInf;
-                gm[h] = fmaxf(gm[h], ss[u][h]);
+                ss[u][h] = kNegInf;
+                if (t0 + u < n_off) {  // uniform: slots past the table only refill
+                    const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                    const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                    ss[u][h] = ok ? d * sl2 : kNegInf;
+                    gm[h] = fmaxf(gm[h], ss[u][h]);
+                }
             }
             if (t0 == 0)
                 sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
@@ -814,11 +853,13 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            if (t0 + u < n_off) {  // uniform
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float pt = fast_exp2(ss[u][h] - ms[h]);
-                l_s[h] += pt;
-                chunk_axpy(acc_s[h], pt, sv[u].r[h]);
+                for (int h = 0; h < 2; ++h) {
+                    const float pt = fast_exp2(ss[u][h] - ms[h]);
+                    l_s[h] += pt;
+                    chunk_axpy(acc_s[h], pt, sv[u].r[h]);
+                }
             }
             if (t0 == 0)
                 sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
@@ -1108,6 +1149,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int c16 = lane & 15, g = lane >> 4;  // MFMA layout
+    const TileLanes tl = tile_lanes(c16, g);
+    const uint16_t *ta_w = ta + 1024 * wave, *tb_w = tb + 1024 * wave;  // this wave's band rows start here
     const int s8 = lane >> 3, c8 = lane & 7;   // slab layout
     const int t0 = tile * 64, r0 = t0 + 16 * wave;
     const int row_s[2] = {r0 + s8, r0 + 8 + s8};
@@ -1161,24 +1204,20 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
 #pragma unroll
     for (int u = 0; u < kPreQ; ++u) fill(u, u);
 
-    // band on MFMA: query row i sees key blocks qb-4 .. qb
+    // band on MFMA: query row i sees key blocks qb-4 .. qb (blocks outside the sequence
+    // or the window are masked like edge blocks: their tile rows hold finite values)
     f32x4_t acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int qb = r0 >> 4;
-    const int klo = max(0, r0 - w + 1), khi = min(r0 + 15, n - 1);
-#pragma unroll 1
-    for (int b = 0; b < 5; ++b) {
+    auto block_ds = [&](int b, float ds[4]) {
         const int kb0 = 16 * (qb - 4 + b);
-        if (kb0 + 15 < klo || kb0 > khi) continue;  // uniform across the wave
         const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
-        const int lr = 16 * (wave + b);
         Frag<true> kf, vf;
-        lds_frag(kf, ta, lr + c16, g);
-        lds_frag(vf, tb, lr + c16, g);
+        lds_frag(kf, ta_w, 16 * b, tl);
+        lds_frag(vf, tb_w, 16 * b, tl);
         const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
         const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
-        float ds[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds[r] = fast_exp2(st[r] * sl2 - lse2_i) * (dpt[r] - di_i);
         if (!full) {  // uniform: edge blocks only
@@ -1188,7 +1227,17 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
                 if (!(i_ok && j <= i && j > i - w && j >= 0)) ds[r] = 0.f;
             }
         }
-        mma_over_rows_tr(acc, ta, lr, c16, g, ds);
+    };
+    {
+        float d0[4], d1[4];
+        block_ds(0, d0);
+        block_ds(1, d1);
+        mma_over_rows_tr2(acc, ta_w, 0, 16, tl, d0, d1);
+        block_ds(2, d0);
+        block_ds(3, d1);
+        mma_over_rows_tr2(acc, ta_w, 32, 48, tl, d0, d1);
+        block_ds(4, d0);
+        mma_over_rows_tr(acc, ta_w, 64, tl, d0);
     }
 #pragma unroll
     for (int u = kPreQ; u < kRingQ; ++u) fill(u, u);
@@ -1255,6 +1304,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;  // MFMA layout
+    const TileLanes tl = tile_lanes(c16, g);
+    const uint16_t *ta_w = ta + 1024 * wave, *tb_w = tb + 1024 * wave;  // this wave's band rows start here
     const int s8 = lane >> 3, c8 = lane & 7;   // slab layout
     const int t0 = tile * 64, r0 = t0 + 16 * wave;
     const int row_s[2] = {r0 + s8, r0 + 8 + s8};
@@ -1298,28 +1349,25 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 #pragma unroll
     for (int u = 0; u < kPreKV; ++u) fill(u, u);
 
-    // band on MFMA: key row j sees query blocks r0 + 16 b
+    // band on MFMA: key row j sees query blocks r0 + 16 b (blocks past the sequence or
+    // the window are masked like edge blocks)
     f32x4_t dk[4], dv[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         dk[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         dv[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const int qhi = min(r0 + 15 + w - 1, n - 1);
-#pragma unroll 1
-    for (int b = 0; b < 5; ++b) {
+    auto block_pds = [&](int b, float pr[4], float ds[4]) {
         const int qb0 = r0 + 16 * b;
-        if (qb0 > qhi) break;  // uniform across the wave
         const bool full = qb0 >= r0 + 15 && qb0 + 15 <= r0 + w - 1 && qb0 + 15 < n && r0 + 15 < n;
-        const int lr = 16 * (wave + b);
+        const int lr = 16 * b;  // band rows of this block, relative to the wave's first
         Frag<true> qf, df;
-        lds_frag(qf, ta, lr + c16, g);
-        lds_frag(df, tb, lr + c16, g);
+        lds_frag(qf, ta_w, lr, tl);
+        lds_frag(df, tb_w, lr, tl);
         const f32x4_t sq4 = mma_over_d(qf, kf, f32x4_t{0.f, 0.f, 0.f, 0.f});  // rows: queries
         const f32x4_t dp4 = mma_over_d(df, vf, f32x4_t{0.f, 0.f, 0.f, 0.f});
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse_s + lr + 4 * g);
-        const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + lr + 4 * g);
-        float pr[4], ds[4];
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse_s + 16 * wave + lr + 4 * g);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + 16 * wave + lr + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sq4[r] * sl2 - l4[r]);
         if (!full) {  // uniform: edge blocks only
@@ -1331,8 +1379,20 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) ds[r] = pr[r] * (dp4[r] - d4[r]);
-        mma_over_rows_tr(dv, tb, lr, c16, g, pr);
-        mma_over_rows_tr(dk, ta, lr, c16, g, ds);
+    };
+    {
+        float p0[4], s0[4], p1[4], s1[4];
+        block_pds(0, p0, s0);
+        block_pds(1, p1, s1);
+        mma_over_rows_tr2(dv, tb_w, 0, 16, tl, p0, p1);
+        mma_over_rows_tr2(dk, ta_w, 0, 16, tl, s0, s1);
+        block_pds(2, p0, s0);
+        block_pds(3, p1, s1);
+        mma_over_rows_tr2(dv, tb_w, 32, 48, tl, p0, p1);
+        mma_over_rows_tr2(dk, ta_w, 32, 48, tl, s0, s1);
+        block_pds(4, p0, s0);
+        mma_over_rows_tr(dv, tb_w, 64, tl, p0);
+        mma_over_rows_tr(dk, ta_w, 64, tl, s0);
     }
 #pragma unroll
     for (int u = kPreKV; u < kRingKV; ++u) fill(u, u);
