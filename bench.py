@@ -131,9 +131,15 @@ def kernel_source_sha():
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
 
 
-def measured_traffic(kernel_key, units):
-    """HBM bytes per launch from committed rocprofv3 counter readings, if they were taken
-    on the current kernel source; None otherwise."""
+# Kernels that one launch of each stage runs (bf16, window path), under their short names.
+STAGE_KERNELS = {"fwd": ("fwd",), "bwd": ("dq", "dkdv")}
+KERNEL_NAMES = {"fwd": "fwd_window_kernel<bf16 out>", "dq": "bwd_dq_kernel<bf16 out, D formed>",
+                "dkdv": "bwd_dkdv_kernel<bf16 out>"}
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of a stage (summed over its kernels) from committed rocprofv3
+    counter readings, if they were taken on the current kernel source; None otherwise."""
     p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     try:
         rec = json.load(open(p))
@@ -141,12 +147,14 @@ def measured_traffic(kernel_key, units):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_sha():
         return None
-    k = rec.get("kernels", {}).get(kernel_key)
-    if not k:
-        return None
-    fetch = k["fetch_kib_per_dispatch"] * 1024.0 * rec["copy_scale_fetch"]
-    write = k["write_kib_per_dispatch"] * 1024.0 * rec["copy_scale_write"]
-    return fetch + write
+    total = 0.0
+    for name in STAGE_KERNELS[stage]:
+        k = rec.get("kernels", {}).get(name)
+        if not k:
+            return None
+        total += k["fetch_kib_per_dispatch"] * 1024.0 * rec["copy_scale_fetch"]
+        total += k["write_kib_per_dispatch"] * 1024.0 * rec["copy_scale_write"]
+    return total
 
 
 def main():
@@ -228,7 +236,7 @@ def main():
     torch.cuda.synchronize()
     ref = [tuple(bufs[l][t].clone() for t in ("o", "lse", "dq", "dk", "dv")) for l in range(LAYERS)]
 
-    # per-kernel durations: each kernel's 16 per-layer launches captured back to back in a
+    # per-stage durations: each stage's 16 per-layer launches captured back to back in a
     # HIP graph of their own, replayed between two HIP events on the launch stream
     stream = torch.cuda.current_stream(dev)
     fns = {"fwd": layer_fwd, "bwd": layer_bwd}
@@ -303,8 +311,8 @@ def main():
     qh_per_step = rows * LAYERS
     step_bytes = per_row["step"] * rows * LAYERS
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_names = {"fwd": "fwd_window_kernel<bf16 out>"}
-    dom = "fwd"
+    # dominant stage: the backward's two kernels (one launch of fsa_backward runs both)
+    dom = max(avg_us, key=lambda k: avg_us[k])
     achieved = per_row[dom] * rows / (avg_us[dom] * 1e-6) / 1e9
     roof = {
         "bound": "hbm",
@@ -312,11 +320,15 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(dom, rows),
-        "kernel": kernel_names[dom],
+        "traffic": measured_traffic(dom),
+        "kernel": " + ".join(KERNEL_NAMES[k] for k in STAGE_KERNELS[dom]),
+        "stage": dom,
         "algorithmic_bytes_per_launch": per_row[dom] * rows,
         "avg_launch_us": round(avg_us[dom], 3),
     }
+    stages = {k: {"avg_us": round(v, 3), "algorithmic_bytes": per_row[k] * rows,
+                  "gb_s": round(per_row[k] * rows / (v * 1e-6) / 1e9, 1),
+                  "kernels": [KERNEL_NAMES[n] for n in STAGE_KERNELS[k]]} for k, v in avg_us.items()}
 
     dense = None
     if not args.no_dense:
@@ -370,7 +382,7 @@ def main():
         "algorithmic_bytes_per_step": step_bytes,
         "query_heads_per_step": qh_per_step,
         "eager_ms_per_step": round(eager_ms, 4),
-        "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
+        "stages": stages,
         "roofline": roof,
         "cpu_baseline": cpu,
         "dense_baseline": dense,

@@ -386,10 +386,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, in
 }
 
 // Row fragment of row `row` (lane group g's 16 elements) from a [n, 64] bf16 head.
+// Cache policy of a buffer access: kCacheNT marks data read or written once, so that
+// it does not push the rows other workgroups re-read out of L2.
+constexpr int kCacheNormal = 0, kCacheNT = 2;
+
+template <int POLICY = kCacheNormal>
 __device__ __forceinline__ void buf_frag(Frag<true> &f, __amdgpu_buffer_rsrc_t r, int row, int g) {
     const int off = row * 128 + 16 * g;
-    f.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    f.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64, 0, 0));
+    f.c[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+    f.c[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64, 0, POLICY));
 }
 
 __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int idx) {
@@ -492,9 +497,10 @@ struct SFrag {
     u32x4_t r[2];  // bf16 chunk of the lane's first and second row
 };
 
+template <int POLICY = kCacheNormal>
 __device__ __forceinline__ void sfrag_load(SFrag &f, __amdgpu_buffer_rsrc_t rs, int row_a, int row_b, int c8) {
-    f.r[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_a * 128 + 16 * c8, 0, 0));
-    f.r[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_b * 128 + 16 * c8, 0, 0));
+    f.r[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_a * 128 + 16 * c8, 0, POLICY));
+    f.r[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_b * 128 + 16 * c8, 0, POLICY));
 }
 
 // Partial dot product of two 8-element bf16 chunks.
@@ -543,14 +549,25 @@ __device__ __forceinline__ float row8_max(float x) {
 }
 
 // Stores row `row` chunk (8 values, times mul) of a slab-layout accumulator.
+// (NT: a non-temporal store, for outputs no later workgroup of the kernel reads.)
+template <bool NT = false>
 __device__ __forceinline__ void store_chunk(uint16_t *base, int64_t row, int c8, const f32x4_t a[2], float mul) {
     const f32x4_t x = a[0] * mul, y = a[1] * mul;
     const u32x4_t v = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
-    *reinterpret_cast<u32x4_t *>(base + row * 64 + 8 * c8) = v;
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(base + row * 64 + 8 * c8);
+    if constexpr (NT) __builtin_nontemporal_store(v, dst);
+    else *dst = v;
 }
+template <bool NT = false>
 __device__ __forceinline__ void store_chunk(float *base, int64_t row, int c8, const f32x4_t a[2], float mul) {
-    *reinterpret_cast<f32x4_t *>(base + row * 64 + 8 * c8) = a[0] * mul;
-    *reinterpret_cast<f32x4_t *>(base + row * 64 + 8 * c8 + 4) = a[1] * mul;
+    f32x4_t *dst = reinterpret_cast<f32x4_t *>(base + row * 64 + 8 * c8);
+    if constexpr (NT) {
+        __builtin_nontemporal_store(a[0] * mul, dst);
+        __builtin_nontemporal_store(a[1] * mul, dst + 1);
+    } else {
+        dst[0] = a[0] * mul;
+        dst[1] = a[1] * mul;
+    }
 }
 
 // Moves a 16-row accumulator from the MFMA C layout (lane (q = l % 16, g), acc[db][r] =
@@ -1178,7 +1195,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
         // D from the slab layout (whole rows per load); the band reads it back from LDS
         SFrag dos, os;
         sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
-        sfrag_load(os, head_rsrc(static_cast<const uint16_t *>(p.o) + head, n * 128), row_s[0], row_s[1], c8);
+        sfrag_load<kCacheNT>(os, head_rsrc(static_cast<const uint16_t *>(p.o) + head, n * 128), row_s[0], row_s[1], c8);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             di[h] = row8_sum(chunk_dot(dos.r[h], os.r[h]));
@@ -1247,8 +1264,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
 
     // sparse offsets: keys i - o, in the slab layout
     SFrag qs, dos;
-    sfrag_load(qs, rq, row_s[0], row_s[1], c8);
-    sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
+    sfrag_load<kCacheNT>(qs, rq, row_s[0], row_s[1], c8);  // second and last read of these rows
+    sfrag_load<kCacheNT>(dos, rdo, row_s[0], row_s[1], c8);
     float lse2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
@@ -1283,7 +1300,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-        if (row_s[h] < n) store_chunk(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
+        if (row_s[h] < n) store_chunk<true>(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
 }
 
 // dK, dV of key rows [t0, t0 + 64): the band queries [t0, t0 + 128) (Q, dO, LSE, D in
@@ -1330,8 +1347,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
         del_s[tid] = (row < n) ? DEL[row] : 0.f;
     }
     Frag<true> kf, vf;
-    buf_frag(kf, rk, j, g);
-    buf_frag(vf, rv, j, g);
+    buf_frag<kCacheNT>(kf, rk, j, g);  // read once by this kernel
+    buf_frag<kCacheNT>(vf, rv, j, g);
     wait_vm_all();
     __syncthreads();
 
@@ -1428,8 +1445,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (row_s[h] < n) {
-            store_chunk(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], p.scale);
-            store_chunk(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
+            store_chunk<true>(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], p.scale);
+            store_chunk<true>(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
         }
     }
 }
