@@ -503,13 +503,13 @@ __device__ __forceinline__ void sfrag_load(SFrag &f, __amdgpu_buffer_rsrc_t rs, 
     f.r[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, row_b * 128 + 16 * c8, 0, POLICY));
 }
 
-// Partial dot product of two 8-element bf16 chunks.
+// Partial dot product of two 8-element bf16 chunks, one accumulation chain (the
+// accumulating form of the dot instruction then needs a zero only once).
 __device__ __forceinline__ float chunk_dot(const u32x4_t &a, const u32x4_t &b) {
-    float s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[0]), as_bf16x2(b[0]), 0.f, false);
-    float s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[1]), as_bf16x2(b[1]), 0.f, false);
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[2]), as_bf16x2(b[2]), s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[3]), as_bf16x2(b[3]), s1, false);
-    return s0 + s1;
+    float s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[0]), as_bf16x2(b[0]), 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[1]), as_bf16x2(b[1]), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[2]), as_bf16x2(b[2]), s, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a[3]), as_bf16x2(b[3]), s, false);
 }
 
 // acc[0..1] (8 fp32 values of one row) += x * chunk on the packed dot unit, with the
