@@ -774,8 +774,10 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     }
 
     // ---- window band on MFMA: rows r0..r0+15 (row c16 of the lane) see key blocks qb-4 .. qb ----
-    // Blocks wholly outside the sequence or the window are computed like the others and
-    // masked: their tile rows hold finite values (row 0 stands in for rows outside [0, n)).
+    // Scores stay unscaled (the scale, > 0 on this path, enters each exponent through
+    // one fma). Blocks wholly outside the sequence or the window are computed like the
+    // others and masked: their tile rows hold finite values (row 0 stands in for rows
+    // outside [0, n)).
     const int qb = r0 >> 4;
     float sc[5][4];
     float bm = kNegInf;
@@ -785,7 +787,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         const bool full = kb0 >= 0 && kb0 + 15 <= r0 && kb0 >= r0 + 16 - w && r0 + 15 < n;
         Frag<true> kf;
         lds_frag(kf, ks_w, 16 * b, tl);
-        f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f}) * sl2;
+        f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
         if (!full) {  // uniform: edge blocks only
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -799,8 +801,9 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             bm = fmaxf(bm, st[r]);
         }
     }
-    const float m_b = group_max(bm);
-    const float msb = row_ok ? m_b : 0.f;  // a valid row always attends itself
+    // scaled row maximum; a valid row always attends itself, so it is finite there
+    const float m_b = row_ok ? group_max(bm) * sl2 : kNegInf;
+    const float msb = row_ok ? m_b : 0.f;
     f32x4_t acc_b[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc_b[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -809,7 +812,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     for (int b = 0; b < 5; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            pr[b][r] = fast_exp2(sc[b][r] - msb);
+            pr[b][r] = fast_exp2(__builtin_fmaf(sc[b][r], sl2, -msb));
             lsum_b += pr[b][r];
         }
     mma_over_rows_tr2(acc_b, vs_w, 0, 16, tl, pr[0], pr[1]);
@@ -825,7 +828,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         stat[c16] = m_b;
         stat[16 + c16] = l_b;
     }
-    float m_s[2], l_s[2];
+    float m_s[2], l_s[2];  // scaled running maximum, running sum
     f32x4_t acc_s[2][2];
     c_to_slab(area, acc_b, acc_s, c16, g, s8, c8);
 #pragma unroll
@@ -837,10 +840,24 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     // ---- sparse slabs: keys row - off[t], four offsets per online-softmax update ----
     SFrag qs;
     sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+    // moves the state to a new maximum; skipped (uniformly) when no row's maximum grew,
+    // which the band's 64 keys make the common case
+    auto rescale = [&](const float mn[2]) {
+        if (__builtin_amdgcn_ballot_w64((mn[0] > m_s[0]) | (mn[1] > m_s[1])) != 0) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float al = fast_exp2(m_s[h] - (mn[h] == kNegInf ? 0.f : mn[h]));
+                acc_s[h][0] *= al;
+                acc_s[h][1] *= al;
+                l_s[h] *= al;
+                m_s[h] = mn[h];
+            }
+        }
+    };
 #pragma unroll
     for (int t0 = 0; t0 < 8; t0 += 4) {
         if (t0 >= n_off || r0 + 15 < p.off[t0]) break;  // ascending offsets
-        float ss[4][2], gm[2] = {kNegInf, kNegInf};
+        float ss[4][2], gm[2] = {kNegInf, kNegInf};    // unscaled scores
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int o = table_off(p, t0 + u);
@@ -850,30 +867,22 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                 if (t0 + u < n_off) {  // uniform: slots past the table only refill
                     const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
                     const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
-                    ss[u][h] = ok ? d * sl2 : kNegInf;
+                    ss[u][h] = ok ? d : kNegInf;
                     gm[h] = fmaxf(gm[h], ss[u][h]);
                 }
             }
             if (t0 == 0)
                 sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
         }
-        float ms[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float mn = fmaxf(m_s[h], gm[h]);
-            ms[h] = (mn == kNegInf) ? 0.f : mn;
-            const float al = fast_exp2(m_s[h] - ms[h]);
-            acc_s[h][0] *= al;
-            acc_s[h][1] *= al;
-            l_s[h] *= al;
-            m_s[h] = mn;
-        }
+        const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
+        rescale(mn);
+        const float ms[2] = {m_s[0] == kNegInf ? 0.f : m_s[0], m_s[1] == kNegInf ? 0.f : m_s[1]};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (t0 + u < n_off) {  // uniform
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float pt = fast_exp2(ss[u][h] - ms[h]);
+                    const float pt = fast_exp2(__builtin_fmaf(ss[u][h], sl2, -ms[h]));
                     l_s[h] += pt;
                     chunk_axpy(acc_s[h], pt, sv[u].r[h]);
                 }
@@ -887,19 +896,18 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         SFrag kt, vt;
         sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
         sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+        float sv1[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
-            const float d = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
-            const float sv1 = ok ? d * sl2 : kNegInf;
-            const float mn = fmaxf(m_s[h], sv1);
-            const float ms = (mn == kNegInf) ? 0.f : mn;
-            const float al = fast_exp2(m_s[h] - ms);
-            const float pt = fast_exp2(sv1 - ms);
-            acc_s[h][0] *= al;
-            acc_s[h][1] *= al;
-            l_s[h] = l_s[h] * al + pt;
-            m_s[h] = mn;
+            sv1[h] = ok ? row8_sum(chunk_dot(qs.r[h], kt.r[h])) : kNegInf;
+        }
+        const float mn[2] = {fmaxf(m_s[0], sv1[0] * sl2), fmaxf(m_s[1], sv1[1] * sl2)};
+        rescale(mn);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float pt = fast_exp2(__builtin_fmaf(sv1[h], sl2, -(m_s[h] == kNegInf ? 0.f : m_s[h])));
+            l_s[h] += pt;
             chunk_axpy(acc_s[h], pt, vt.r[h]);
         }
     }
@@ -1474,7 +1482,7 @@ hipError_t launch_generic_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const Attn
 bool window_path(fsa_dtype_t dt, const AttnParams &p) { return window_path(dt, p.w, p.n); }
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
-    if (window_path(dt, p))
+    if (window_path(dt, p) && p.scale_log2 > 0.f)  // the window kernel folds a positive scale into exponents
         return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true>, tiles(p), p, s)
                                   : launch(&fwd_window_kernel<false>, tiles(p), p, s);
     return launch_generic_forward<kWide>(dt, out_dt, p, s);

@@ -268,6 +268,20 @@ def test_backward_equals_its_two_stages():
     assert float((D.double() - ref).abs().max()) <= 1e-4
 
 
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1e-3])
+def test_forward_any_scale(scale):
+    # the window kernel takes positive scales; others run the general kernel
+    x = inputs(21, 0, (1, 2, 300, 64), torch.bfloat16)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], alpha=1.0, w=64, R=1024, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    T = oracle.offset_table("fib", 1.0, 64, 1024)
+    for h in range(2):
+        q, k, v = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.sparse_forward(q, k, v, T, 64, scale)
+        check(f"o[0,{h}] scale={scale}", o[0, h], ro, TOL[torch.bfloat16])
+        check(f"lse[0,{h}] scale={scale}", lse[0, h], rl, TOL[torch.bfloat16])
+
+
 def test_pair_workspace_contents_do_not_matter():
     # every word the dK/dV kernel reads was written by the dQ kernel of the same call
     x = inputs(20, 0, (1, 2, 777, 64), torch.bfloat16, grad=True)
