@@ -8,30 +8,29 @@
 // softmax over the union. Static schedules run as a single boolean mask
 // (section "Principais Contribuições e Resultados", item 2).
 //
-// Work decomposition (one workgroup = 4 wave64 = one 64-row tile of one head):
-//  * Window band: a banded dense block, computed on MFMA. Scores are formed
-//    transposed, S^T = K Q^T, so each lane's four accumulator rows are four keys
-//    of one query; that accumulator layout is exactly the B-operand layout of
-//    the 16x16x16 MFMA, so P^T feeds the P.V product with no data movement. V
-//    (and, in the backward, K, Q and dO) is staged transposed in LDS to serve
-//    as the A operand of those key-contracting products.
+// Work decomposition of the bf16 window kernels (w <= 64; one workgroup = 4 wave64 =
+// one 64-row tile of one head):
+//  * Window band: a banded dense block on MFMA. Its K/V (or Q/dO) rows are copied
+//    into LDS by direct global -> LDS loads in a chunk-swizzled row-major tile.
+//    Scores are formed transposed, S^T = K Q^T, so each lane's four accumulator
+//    rows are four keys of one query: the B-operand layout of the P.V product,
+//    whose A operand (V^T) comes from transposing LDS reads.
 //  * Sparse offsets: each offset o maps the tile's 64 query rows onto one
-//    contiguous 64-row K/V slab. Lanes read their rows with coalesced vector
-//    loads and form the per-row diagonal dot products on VALU, reducing across
-//    the four lane groups with cross-lane shuffles.
-//  * One online (running max / running sum) fp32 softmax covers both parts.
-//  * Lane ownership of a 64-wide row: lane group g = lane / 16 holds the 16
-//    elements d = 16 s + 4 g + u (s, u in 0..3). The d-contracting MFMAs read
-//    their operands in that order (any fixed assignment of d to k-slots that A
-//    and B share gives the same sum), so the band, the sparse slabs and the
-//    output accumulators all use one layout.
+//    contiguous 64-row slab. Slab rows stream through a register ring in a layout
+//    of their own (eight lanes per 128-byte row, so every load covers whole cache
+//    lines); the per-row dot products and weighted sums run on the packed bf16 dot
+//    unit with DPP row reductions.
+//  * Forward: the band's softmax state moves into the slab layout and the slabs
+//    continue it online.
+//  * Backward: two kernels. The first forms dQ of its query rows (and D), storing
+//    the bf16 P and dS of every sparse pair; the second forms dK, dV of its key
+//    rows from the band (recomputed) and those stored weights. Every output row
+//    has one writer and no atomics are used.
 //  * Workgroup ids are remapped so that the tiles of one head run on one XCD in
-//    increasing row order, keeping that head's K/V in the XCD's L2 for the
+//    increasing row order, keeping that head's rows in the XCD's L2 for the
 //    slab re-reads.
-//  * Backward: one kernel computes D = rowsum(dO * O); the main kernel gives
-//    each workgroup dQ of its 64 query rows and dK, dV of the same 64 key rows,
-//    recomputing P on both sides, so every output row has one writer and no
-//    atomics are used.
+// The general kernels (fp32 inputs, wider windows, the dense baseline) loop over
+// 64-key chunks with an online softmax.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
