@@ -368,6 +368,19 @@ __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src, in
     }
 }
 
+// As dma_tile for a 64-row tile [row0, row0 + 64): two 1 KiB transfers per wave.
+__device__ __forceinline__ void dma_tile64(uint16_t *tile, const uint16_t *src, int row0, int n, int wave, int lane) {
+    const int rl = lane >> 3;
+    const int chunk = (lane & 7) ^ rl;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int rb = 8 * (2 * wave + k);
+        int r = row0 + rb + rl;
+        r = (r >= 0 && r < n) ? r : 0;
+        __builtin_amdgcn_global_load_lds(src + (int64_t)r * 64 + 8 * chunk, (lds_void_t *)(tile + rb * 64), 16, 0, 0);
+    }
+}
+
 // Element offset, within a swizzled tile, of the 16-byte chunk c of tile row r.
 __device__ __forceinline__ int tile_chunk(int r, int c) { return r * 64 + 8 * (c ^ (r & 7)); }
 
@@ -918,6 +931,95 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], 1.f / l_s[h]);
             if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = m_s[h] * kLn2 + logf(l_s[h]);
         }
+    }
+}
+
+// Dense causal forward (the baseline), bf16 inputs, positive scale. One workgroup =
+// one 64-row query tile; it walks the key tiles 0 .. tile, each copied into LDS
+// (K and V, swizzled) one step ahead of its use, with an online softmax whose
+// accumulator is rescaled only when a row maximum grows. The tile order pairs light
+// and heavy tiles on a CU: within each head the upper half of the tiles runs in
+// reverse, so the blocks that dispatch places on one CU (32 apart in an XCD's range)
+// hold tiles t and T - 1 - t.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(kThreads) fwd_dense_kernel(const AttnParams p) {
+    using OE = typename Elem<OUT_BF16>::T;
+    __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t vt[2][64 * 64];
+
+    const int n = p.n, nt = (n + 63) >> 6, half = nt >> 1;
+    const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
+    const int bh = lb / nt, u = lb - bh * nt;
+    const int tile = u < half ? u : nt - 1 + half - u;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c16 = lane & 15, g = lane >> 4;
+    const TileLanes tl = tile_lanes(c16, g);
+    const int i0 = tile * 64, i = i0 + 16 * wave + c16;
+    const bool row_ok = i < n;
+    const int64_t head = (int64_t)bh * n * 64;
+    const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
+    const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
+    const float sl2 = p.scale_log2;
+
+    Frag<true> qf;
+    buf_frag(qf, head_rsrc(static_cast<const uint16_t *>(p.q) + head, n * 128), i, g);
+    dma_tile64(kt[0], K, 0, n, wave, lane);
+    dma_tile64(vt[0], V, 0, n, wave, lane);
+
+    float m = kNegInf, lsum = 0.f;  // unscaled running maximum, running sum (lane partial)
+    f32x4_t acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j <= tile; ++j) {
+        const int buf = j & 1;
+        wait_vm_all();
+        __syncthreads();  // key tile j has landed; every wave is done with tile j - 1
+        if (j < tile) {   // uniform: the next tile goes into the buffer tile j - 1 used
+            dma_tile64(kt[buf ^ 1], K, 64 * (j + 1), n, wave, lane);
+            dma_tile64(vt[buf ^ 1], V, 64 * (j + 1), n, wave, lane);
+        }
+        float sc[4][4], bm = kNegInf;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            Frag<true> kf;
+            lds_frag(kf, kt[buf], 16 * b, tl);
+            f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            if (j == tile) {  // uniform: the diagonal tile is causal-masked
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (!(row_ok && 64 * j + 16 * b + 4 * g + r <= i)) st[r] = kNegInf;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[b][r] = st[r];
+                bm = fmaxf(bm, st[r]);
+            }
+        }
+        const float mn = fmaxf(m, group_max(bm));
+        if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {  // some row's maximum grew
+            const float al = fast_exp2(m == kNegInf ? kNegInf : (m - mn) * sl2);  // 0 while m is still -inf
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] *= al;
+            lsum *= al;
+            m = mn;
+        }
+        const float ms = m == kNegInf ? 0.f : m * sl2;
+        float pr[4][4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[b][r] = fast_exp2(__builtin_fmaf(sc[b][r], sl2, -ms));
+                lsum += pr[b][r];
+            }
+        mma_over_rows_tr2(acc, vt[buf], 0, 16, tl, pr[0], pr[1]);
+        mma_over_rows_tr2(acc, vt[buf], 32, 48, tl, pr[2], pr[3]);
+    }
+    const float l = group_sum(lsum);
+    if (row_ok) {
+        store_row(static_cast<OE *>(p.out) + head, i, g, acc, 1.f / l);
+        if (g == 0) p.lse_out[(int64_t)bh * n + i] = m * sl2 * kLn2 + logf(l);
     }
 }
 
@@ -1488,6 +1590,9 @@ hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &
 }
 
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    if (dt == FSA_BF16 && p.n <= (1 << 24) && p.scale_log2 > 0.f)
+        return out_dt == FSA_BF16 ? launch(&fwd_dense_kernel<true>, tiles(p), p, s)
+                                  : launch(&fwd_dense_kernel<false>, tiles(p), p, s);
     return launch_generic_forward<kDense>(dt, out_dt, p, s);
 }
 

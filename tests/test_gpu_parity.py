@@ -154,6 +154,23 @@ def test_wide_window_equals_dense_kernel_and_oracle(dtype):
         check(f"wide o[{h}]", o[0, h], ro, TOL[dtype])
 
 
+@pytest.mark.parametrize("N,scale", [(1, 0.125), (17, 0.125), (64, 0.125), (65, 0.125), (333, 0.125),
+                                     (1000, 0.125), (333, -0.125), (200, 0.0)])
+def test_dense_forward_against_oracle(N, scale):
+    # bf16 with a positive scale takes the dedicated dense kernel; other scales the general one
+    x = inputs(15, 0, (1, 3, N, 64), torch.bfloat16)
+    od, ld = fsa.dense_forward(x["q"], x["k"], x["v"], scale=scale, out_dtype=torch.float32)
+    od_lo, ld_lo = fsa.dense_forward(x["q"], x["k"], x["v"], scale=scale)
+    torch.cuda.synchronize()
+    same_rounding("dense o", od_lo, od)
+    assert torch.equal(ld_lo, ld)
+    for h in range(3):
+        q, k, v = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.dense_forward(q, k, v, scale)
+        check(f"dense o[0,{h}] N={N} scale={scale}", od[0, h], ro, TOL[torch.bfloat16])
+        check(f"dense lse[0,{h}] N={N} scale={scale}", ld[0, h], rl, TOL[torch.bfloat16])
+
+
 def test_empty_problem_is_noop():
     q = torch.empty((2, 3, 0, 64), dtype=torch.bfloat16, device=dev())
     o, l = fsa.forward(q, q.clone(), q.clone(), alpha=1.0, w=64, R=1024)
