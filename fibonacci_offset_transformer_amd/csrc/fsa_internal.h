@@ -24,7 +24,7 @@ struct AttnParams {
     const float *lse_in;     // backward: forward LSE
     float *lse_out;          // forward: LSE
     float *delta;            // backward: D workspace [BH, N]
-    uint32_t *pairs;         // backward: per-pair workspace [n_off, BH, N] (window path)
+    uint32_t *pairs;         // backward: per-pair workspace [BH, N, pair_slots(n_off)] (window path)
     int32_t bh;              // B * H
     int32_t n;               // sequence length
     int32_t w;               // window (offsets 0..w-1)
@@ -37,11 +37,13 @@ struct AttnParams {
 // The bf16 window kernels (w <= 64) address each head with 32-bit byte offsets.
 inline bool window_path(fsa_dtype_t dt, int32_t w, int32_t n) { return dt == FSA_BF16 && w <= 64 && n <= (1 << 24); }
 
-// 32-bit words of the backward pair workspace: one word (bf16 P and bf16 dS of a
-// query row and sparse offset) per (offset, head, row) on the window path, none
-// elsewhere.
+// Backward pair workspace on the window path: [BH, N, pair_slots(n_off)] 32-bit words,
+// word t of a query row holding bf16 P (low half) and bf16 dS (high half) of the
+// pair (row, row - off[t]). Slots come in groups of 8 so that one row's first eight
+// words are written by one 32-byte store. None elsewhere.
+__host__ __device__ inline int32_t pair_slots(int32_t n_off) { return 8 * ((n_off + 7) / 8); }
 inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
-    return window_path(dt, w, n) ? static_cast<int64_t>(n_off) * bh * n : 0;
+    return window_path(dt, w, n) ? static_cast<int64_t>(pair_slots(n_off)) * bh * n : 0;
 }
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);

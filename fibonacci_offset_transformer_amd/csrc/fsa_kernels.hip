@@ -1239,7 +1239,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
 // Backward on the window path (bf16 inputs, w <= 64) runs as two kernels over 64-row
 // tiles. The first forms dQ of its query rows and, for every sparse pair (query i,
 // key i - off[t]), stores P and dS rounded to bf16 (the weights the gradient products
-// use) in a pair workspace [n_off, BH, N] of 32-bit words (P in the low half). The
+// use) in a pair workspace [BH, N, S] of 32-bit words (P in the low half). The
 // second forms dK and dV of its key rows from the window band, recomputed on MFMA, and
 // from the stored weights of the sparse pairs (key j, query j + off[t]), so no score is
 // formed twice on the vector units. Each kernel keeps one pair of operands resident
@@ -1248,12 +1248,11 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
 constexpr int kRingQ = 4, kPreQ = 3;    // dQ kernel: slab slots in the ring; slots requested before the band
 constexpr int kRingKV = 3, kPreKV = 1;  // dK/dV kernel
 
-// Descriptor over the pair-workspace words of offset t of head bh: empty (every load
-// reads 0) for t past the table, so ring refills never address beyond the workspace.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int t, int bh) {
-    const bool in = t < p.n_off;
-    const uint32_t *base = p.pairs + ((int64_t)(in ? t : 0) * p.bh + bh) * p.n;
-    return head_rsrc(base, in ? p.n * 4 : 0);
+// Descriptor over the pair-workspace words of head bh ([N, S] words, S = pair_slots):
+// rows past the sequence end read as zero words.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int bh) {
+    const int slots = pair_slots(p.n_off);
+    return head_rsrc(p.pairs + (int64_t)bh * p.n * slots, p.n * slots * 4);
 }
 
 // dQ of query rows [t0, t0 + 64): the band keys [t0 - 64, t0 + 64) (K, V in LDS) on
@@ -1378,9 +1377,11 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     float lse2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
-    const int64_t pair_stride = (int64_t)p.bh * n;  // words between offsets
-    uint32_t *pairs = p.pairs + (int64_t)bh * n;
-    // one slab: pair weights of the lane's two rows, dQ update, weights stored once per row
+    // pair words of this head's rows: [n, slots]; lane c8 of a row keeps the word of
+    // slot c8 of the unrolled part and the eight lanes store them with one 32-byte write
+    const int slots = pair_slots(n_off);
+    uint32_t *pairs = p.pairs + (int64_t)bh * n * slots;
+    uint32_t keep[2] = {0u, 0u};
     auto slab = [&](int t, int o, const SFrag &kt, const SFrag &vt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -1389,7 +1390,10 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
             const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
             const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
             const uint32_t pw = pack_bf16(pv, pv * (dp - di[h]));
-            if (c8 == 0 && row_s[h] < n) pairs[t * pair_stride + row_s[h]] = pw;
+            if (t < 8)
+                keep[h] = c8 == t ? pw : keep[h];
+            else if (c8 == 0 && row_s[h] < n)
+                pairs[(int64_t)row_s[h] * slots + t] = pw;
             chunk_axpy_words(dq_s[h], pw >> 16, pw & 0xffff0000u, kt.r[h]);
         }
     };
@@ -1401,6 +1405,12 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
             if (s0 + u < n_off) slab(s0 + u, table_off(p, s0 + u), sk[u], sv[u]);  // uniform
             if (s0 + kRingQ < unrolled_slabs(kRingQ)) fill(u, s0 + u + kRingQ);
         }
+    }
+    static_assert(unrolled_slabs(kRingQ) == 8, "the kept pair words cover slots 0..7");
+    if (n_off > 0) {  // uniform
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (row_s[h] < n) pairs[(int64_t)row_s[h] * slots + c8] = keep[h];
     }
     for (int t = unrolled_slabs(kRingQ); t < n_off; ++t) {  // longer tables
         if (r0 + 15 < p.off[t]) break;
@@ -1461,16 +1471,17 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
     wait_vm_all();
     __syncthreads();
 
-    // slot u: query rows row + off[u] (Q, dO) and their pair weights
+    // slot u: query rows row + off[t] (Q, dO) and their pair weights (word t of each row)
     SFrag sq[kRingKV], sd[kRingKV];
     uint32_t pw[kRingKV][2];
+    const __amdgpu_buffer_rsrc_t rp = pair_rsrc(p, bh);
+    const int slots = pair_slots(n_off);
     auto fill = [&](int u, int t) {
         const int iq0 = slab_row(p, t, row_s[0], 1), iq1 = slab_row(p, t, row_s[1], 1);
         sfrag_load(sq[u], rq, iq0, iq1, c8);
         sfrag_load(sd[u], rdo, iq0, iq1, c8);
-        const __amdgpu_buffer_rsrc_t rp = pair_rsrc(p, t, bh);
-        pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, iq0 * 4, 0, 0);
-        pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, iq1 * 4, 0, 0);
+        pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, 0);
+        pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, 0);
     };
 #pragma unroll
     for (int u = 0; u < kPreKV; ++u) fill(u, u);

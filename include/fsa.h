@@ -142,8 +142,9 @@ fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, con
  * runs as two kernels: the first stores, for every query row i and sparse offset
  * o of the table (offsets >= N dropped), the bf16 values of P and dS of the pair
  * (i, i - o) in one 32-bit word; the second reads them to form dK and dV. The
- * size is 4 * |T| * B * H * N bytes there and 0 on every other path. Arguments
- * as in fsa_backward; *bytes receives the size.
+ * size is 4 * S * B * H * N bytes there, S = |T| rounded up to a multiple of 8
+ * (words per query row), and 0 on every other path. Arguments as in
+ * fsa_backward; *bytes receives the size.
  */
 fsa_status_t fsa_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                                           fsa_base_t base, double alpha, int32_t w, int32_t R,

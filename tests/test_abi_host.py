@@ -203,11 +203,15 @@ def ws_bytes(lib, dt=1, B=2, H=8, N=4096, d=64, base=0, alpha=1.0, w=64, R=1024)
 
 
 def test_backward_workspace_size(lib):
-    # bf16, window 64: one 32-bit word per (offset, head, row); alpha = 1, R = 1024 gives
-    # the offsets 89, 144, 233, 377, 610, 987 (all below N = 4096)
-    assert ws_bytes(lib) == (fsa.FSA_OK, 4 * 6 * 16 * 4096)
-    # offsets >= N are dropped: at N = 600 only 89, 144, 233, 377 remain
-    assert ws_bytes(lib, N=600) == (fsa.FSA_OK, 4 * 4 * 16 * 600)
+    # bf16, window 64: one 32-bit word per (head, row, offset slot), slots rounded up to
+    # a multiple of 8; alpha = 1, R = 1024 gives the offsets 89, 144, 233, 377, 610, 987
+    assert ws_bytes(lib) == (fsa.FSA_OK, 4 * 8 * 16 * 4096)
+    # offsets >= N are dropped: at N = 600 only 89, 144, 233, 377 remain (still 8 slots)
+    assert ws_bytes(lib, N=600) == (fsa.FSA_OK, 4 * 8 * 16 * 600)
+    # a table of 9 offsets takes 16 slots: w = 1, alpha = 1, R = 60 gives 1, 2, 3, 5, 8, 13, 21, 34, 55
+    assert ws_bytes(lib, w=1, R=60) == (fsa.FSA_OK, 4 * 16 * 16 * 4096)
+    # no offset below N: no slots
+    assert ws_bytes(lib, N=50, alpha=1.0, w=64) == (fsa.FSA_OK, 0)
     # paths without the pair workspace: fp32 inputs, wide windows
     assert ws_bytes(lib, dt=0) == (fsa.FSA_OK, 0)
     assert ws_bytes(lib, w=65) == (fsa.FSA_OK, 0)
@@ -219,10 +223,10 @@ def test_backward_workspace_size(lib):
 
 @pytest.mark.parametrize("call", [bwd, grads])
 def test_backward_pair_workspace_checks(lib, call):
-    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 3 * 64 words needed.
+    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 8 slots * 64 rows.
     # Only failing validations are exercised here (the pointers are fake); the calls
     # that pass NULL for an unneeded workspace run in the GPU tests (fp32 inputs).
-    need = 4 * 3 * 64
+    need = 4 * 8 * 64
     assert call(lib, pair_bytes=need - 1) == fsa.FSA_E_ARG
     assert b"pair_ws holds" in lib.fsa_last_error()
     assert call(lib, pair_bytes=0) == fsa.FSA_E_ARG

@@ -113,6 +113,7 @@ SMALL = [
     (300, "fib", 1.0, 100, 256),     # window wider than a tile
     (257, "fib", 1.0, 1, 1024),      # no window besides self, every Fibonacci offset
     (130, "fib", 1.0, 300, 1024),    # window covers the whole sequence (dense)
+    (1100, "fib", 1.0, 6, 1024),     # 11 offsets: more than the unrolled slots, 16 pair slots
 ]
 
 
