@@ -157,6 +157,52 @@ def measured_traffic(stage):
     return total
 
 
+# decode: the newest token of each of DEC_B sequences against full caches of DEC_LMAX rows
+DEC_B, DEC_LMAX, DEC_ALPHA = 64, 4096, 1.0
+
+
+def decode_keys(table, w, L):
+    """Keys one decode query attends: the window's min(w, L) plus table entries <= L - 1."""
+    return min(w, L) + sum(1 for o in table if o <= L - 1)
+
+
+def decode_bench(fsa, torch, dev, stream):
+    """Sparse decode (window 64 + Fibonacci offsets) and dense decode (window = cache) at
+    the same shapes: microseconds per step and algorithmic bytes per second."""
+    from fibonacci_offset_transformer_amd import synth
+    x = synth.layer_inputs(6, 0, (DEC_B, H, DEC_LMAX, D), torch.bfloat16, with_grad=True)
+    k, v = x["k"].to(dev), x["v"].to(dev)
+    q = x["q"][:, :, -1].contiguous().to(dev)
+    del x
+    sl = torch.full((DEC_B,), DEC_LMAX, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((DEC_B, H), dtype=torch.float32, device=dev)
+    res = {"config": {"sequences": DEC_B, "heads": H, "cache_rows": DEC_LMAX, "head_dim": D, "dtype": "bf16",
+                      "base": BASE, "alpha": DEC_ALPHA, "R": R}}
+    for name, w in (("sparse", W), ("dense", DEC_LMAX)):
+        table = fsa.build_offsets(DEC_ALPHA, w, R, BASE)
+        keys = decode_keys(table, w, DEC_LMAX)
+        step_bytes = DEC_B * H * (keys * 2 * D * ELEM + 2 * D * ELEM + 4)
+
+        def run():
+            fsa.decode(q, k, v, sl, alpha=DEC_ALPHA, w=w, R=R, base=BASE, out=o, lse=lse)
+
+        run()
+        torch.cuda.synchronize()
+        reps = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"window": w, "keys_per_query": keys, "us_per_step": round(us, 2),
+                     "algorithmic_bytes": step_bytes, "gb_s": round(step_bytes / (us * 1e-6) / 1e9, 1)}
+    res["dense_over_sparse_time"] = round(res["dense"]["us_per_step"] / res["sparse"]["us_per_step"], 2)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +210,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale reference) and exit")
     args = ap.parse_args()
@@ -357,6 +404,10 @@ def main():
             "dense_over_sparse_fwd_time": round(us / sparse_fwd_us, 2),
         }
 
+    decode = None
+    if not args.no_decode:
+        decode = decode_bench(fsa, torch, dev, stream)
+
     out = {
         "metric": METRIC,
         "value": round(qh_per_step / (ms_per_step * 1e-3), 1),
@@ -386,6 +437,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "dense_baseline": dense,
+        "decode": decode,
     }
     if cpu:
         out["gpu_over_cpu"] = round(out["value"] / cpu["value"], 1)

@@ -329,6 +329,43 @@ fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, con
                     "backward");
 }
 
+fsa_status_t fsa_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *seq_lens, void *o, float *lse, int32_t B, int32_t H,
+                        int32_t Lmax, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                        void *stream) {
+    const Shape s{B, H, Lmax, d};
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
+    if (st != FSA_OK) return st;
+    fsa::AttnParams p{};
+    const int n_off = build_table(base, alpha, w, R, p.off, &st);
+    if (n_off < 0) return st;
+    if (static_cast<int64_t>(B) * H == 0) return ok();
+    if (Lmax < 1) return fail(FSA_E_ARG, "Lmax must be >= 1 (the cache holds at least the newest token)");
+    const char *names[] = {"q", "k_cache", "v_cache", "o", "lse"};
+    const void *ptrs[] = {q, k_cache, v_cache, o, lse};
+    if ((st = check_ptrs(names, ptrs, 5)) != FSA_OK) return st;
+    if (!seq_lens) return fail(FSA_E_ARG, "seq_lens is NULL");
+    if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(FSA_E_ARG, "seq_lens is not 4-byte aligned");
+    const char *names6[] = {"q", "k_cache", "v_cache", "seq_lens", "o", "lse"};
+    const void *ptrs6[] = {q, k_cache, v_cache, seq_lens, o, lse};
+    if ((st = check_no_alias(names6, ptrs6, 4, 6)) != FSA_OK) return st;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.out = o;
+    p.lse_out = lse;
+    p.seq_lens = seq_lens;
+    p.bh = B * H;
+    p.heads = H;
+    p.lmax = Lmax;
+    p.n = Lmax;
+    p.w = w;
+    p.n_off = trim_offsets(p.off, n_off, Lmax);
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_decode(dt, out_dt, p, static_cast<hipStream_t>(stream)), "decode");
+}
+
 fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
                                void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
                                float scale, void *stream) {

@@ -32,6 +32,9 @@ struct AttnParams {
     float scale;             // score scale
     float scale_log2;        // scale * log2(e)
     int32_t off[FSA_MAX_OFFSETS];
+    const int32_t *seq_lens;  // decode: cached length of each sequence [B]
+    int32_t heads;            // decode: H (heads per sequence)
+    int32_t lmax;             // decode: rows allocated per cached head
 };
 
 // The bf16 window kernels (w <= 64) address each head with 32-bit byte offsets.
@@ -49,6 +52,7 @@ inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int3
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 // Gradient stage. With `with_delta`, D is formed from p.o and p.dout and written to
 // p.delta on the way (by the dQ kernel on the window path, by the delta kernel
 // elsewhere); otherwise p.delta is read as given.

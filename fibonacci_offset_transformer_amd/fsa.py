@@ -27,7 +27,7 @@ MAX_OFFSETS = 48
 
 # Exported symbols, in the order include/fsa.h declares them.
 EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_workspace_bytes",
-           "fsa_backward_delta", "fsa_backward_grads", "fsa_dense_forward", "fsa_last_error")
+           "fsa_backward_delta", "fsa_backward_grads", "fsa_decode", "fsa_dense_forward", "fsa_last_error")
 
 
 class FsaError(RuntimeError):
@@ -68,6 +68,9 @@ def library() -> ctypes.CDLL:
             L.fsa_backward_grads.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64,
                                              i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
             L.fsa_backward_grads.restype = ctypes.c_int
+            L.fsa_decode.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                     ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_decode.restype = ctypes.c_int
             L.fsa_dense_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
             L.fsa_dense_forward.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
@@ -203,6 +206,31 @@ def backward_grads(q, k, v, lse, dout, delta, *, alpha: float = 1.0, w: int, R: 
                                             _ptr(pw), pw_bytes, B, H, N, d, _scale(scale, d), BASES[base],
                                             float(alpha), int(w), int(R), _stream(q.device)))
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seq_lens, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None,
+           out=None, lse=None, out_dtype=None):
+    """One decoding step: q [B,H,d] (the newest token of each sequence) against
+    k_cache, v_cache [B,H,Lmax,d] with seq_lens int32 [B] on the device. Returns
+    (o [B,H,d] in out_dtype (default q.dtype), lse [B,H] float32)."""
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("expected q [B, H, d] and caches [B, H, Lmax, d]")
+    B, H, d = q.shape
+    Lmax = k_cache.shape[2]
+    for t in (k_cache, v_cache):
+        if t.shape != (B, H, Lmax, d) or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError("caches must be contiguous [B, H, Lmax, d] tensors of q's dtype and device")
+    if q.dtype not in DTYPES or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous float32 or bfloat16 device tensor")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or seq_lens.device != q.device:
+        raise ValueError("seq_lens must be an int32 [B] tensor on q's device")
+    o = torch.empty_like(q, dtype=out_dtype or q.dtype) if out is None else out
+    l = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        _check(library().fsa_decode(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(seq_lens), _ptr(o), _ptr(l), B, H, Lmax, d, _scale(scale, d), BASES[base],
+                                    float(alpha), int(w), int(R), _stream(q.device)))
+    return o, l
 
 
 def dense_forward(q, k, v, *, scale=None, out=None, lse=None, out_dtype=None):

@@ -168,6 +168,35 @@ fsa_status_t fsa_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *
                                 void *stream);
 
 /*
+ * fsa_decode - one decoding step: the newest query of each sequence against a
+ * key/value cache (the inference workload of the method; the same attended set
+ * as fsa_forward's last row).
+ *
+ * For every (b, h), with L = seq_lens[b] clamped into [1, Lmax] and i = L - 1:
+ *   J = { i - o : o in {0..w-1} u T(base, alpha, w, R), i - o >= 0 },
+ *   o[b,h] = sum_{j in J} softmax_j(scale * <q[b,h], k_cache[b,h,j]>) v_cache[b,h,j],
+ *   lse[b,h] = ln sum_{j in J} exp(scale * <q[b,h], k_cache[b,h,j]>).
+ * Arithmetic in fp32 (inputs converted exactly). A window w >= Lmax makes this
+ * dense decoding.
+ *
+ *   dt, out_dt          dtypes as in fsa_forward (q, k_cache, v_cache; o)
+ *   q                   [B,H,d]: the newest token's query
+ *   k_cache, v_cache    [B,H,Lmax,d]: row j of a sequence holds position j; rows
+ *                       0 .. L-1 must be filled, the newest token's key and value
+ *                       included (appending them is the caller's step)
+ *   seq_lens            device int32 [B], 4-byte aligned: L of each sequence;
+ *                       values outside [1, Lmax] are clamped into it
+ *   o                   output [B,H,d] in out_dt
+ *   lse                 output float32 [B,H]
+ *   Lmax                rows allocated per cached head, >= 1
+ *   scale, base, alpha, w, R   as in fsa_forward (table entries >= Lmax dropped)
+ */
+fsa_status_t fsa_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k_cache,
+                        const void *v_cache, const int32_t *seq_lens, void *o, float *lse, int32_t B, int32_t H,
+                        int32_t Lmax, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w, int32_t R,
+                        void *stream);
+
+/*
  * fsa_dense_forward - dense causal attention baseline (every j <= i attended),
  * the same architecture with full attention (page section "Controles").
  * Arguments as in fsa_forward.

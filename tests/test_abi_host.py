@@ -145,12 +145,17 @@ def grads(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha
     return lib.fsa_backward_grads(dt, out_dt, *p, pair_bytes, B, H, N, d, scale, base, alpha, w, R, None)
 
 
+def decode(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256, out_dt=1):
+    p = ptrs or FAKE[:6]  # q k_cache v_cache seq_lens o lse; N is Lmax
+    return lib.fsa_decode(dt, out_dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+
+
 def dense(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, out_dt=1):
     p = ptrs or FAKE[:5]
     return lib.fsa_dense_forward(dt, out_dt, *p, B, H, N, d, scale, None)
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, grads, dense])
+@pytest.mark.parametrize("call", [fwd, bwd, grads, decode, dense])
 def test_shape_and_dtype_errors(lib, call):
     assert call(lib, d=32) == fsa.FSA_E_UNSUPPORTED
     assert call(lib, d=0) == fsa.FSA_E_ARG
@@ -163,7 +168,7 @@ def test_shape_and_dtype_errors(lib, call):
     assert call(lib, B=1 << 20, H=1 << 12, N=1 << 16) == fsa.FSA_E_ARG  # grid too large
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, grads])
+@pytest.mark.parametrize("call", [fwd, bwd, grads, decode])
 def test_table_errors_on_attention_calls(lib, call):
     assert call(lib, alpha=0.0) == fsa.FSA_E_ARG
     assert call(lib, alpha=float("nan")) == fsa.FSA_E_ARG
@@ -235,3 +240,25 @@ def test_backward_pair_workspace_checks(lib, call):
     ptrs[n - 1] = P(0)
     assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG
     assert b"pair_ws is NULL" in lib.fsa_last_error()
+
+
+def test_decode_specific_checks(lib):
+    assert decode(lib, N=0) == fsa.FSA_E_ARG  # the cache holds at least the newest token
+    assert b"Lmax" in lib.fsa_last_error()
+    ptrs = list(FAKE[:6])
+    ptrs[3] = P(0)
+    assert decode(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"seq_lens is NULL" in lib.fsa_last_error()
+    ptrs[3] = P(FAKE[3].value + 2)
+    assert decode(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"4-byte" in lib.fsa_last_error()
+    for k in (0, 1, 2, 4, 5):
+        ptrs = list(FAKE[:6])
+        ptrs[k] = P(0)
+        assert decode(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"NULL" in lib.fsa_last_error()
+        ptrs[k] = P(FAKE[k].value + 8)
+        assert decode(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"aligned" in lib.fsa_last_error()
+    ptrs = list(FAKE[:6])
+    ptrs[4] = ptrs[1]  # o aliases the key cache
+    assert decode(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"aliases" in lib.fsa_last_error()
+    # empty batches launch nothing, whatever the pointers
+    assert decode(lib, ptrs=[P(0)] * 6, B=0) == fsa.FSA_OK
+    assert decode(lib, ptrs=[P(0)] * 6, H=0) == fsa.FSA_OK

@@ -355,3 +355,54 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for n in bufs:
             assert torch.equal(bufs[n], ref[n]), (rep, n)
+
+
+# ---------------------------------------------------------------- decode (one query per sequence)
+
+def decode_case(dtype, base, alpha, w, R, lens, Lmax=700, H=2, scale=0.125, seed=30):
+    """fsa.decode on a ragged batch against the oracle's forward row L - 1 of each cache."""
+    B = len(lens)
+    x = inputs(seed, 0, (B, H, Lmax, 64), dtype, grad=True)  # k, v are the caches; dO rows serve as queries
+    q = x["do"][:, :, 0, :].contiguous()
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    note(f"decode {dtype} base={base} alpha={alpha} w={w} R={R} lens={lens} Lmax={Lmax}")
+    o, lse = fsa.decode(q, x["k"], x["v"], sl, alpha=alpha, w=w, R=R, base=base, scale=scale,
+                        out_dtype=torch.float32)
+    o_lo, lse_lo = fsa.decode(q, x["k"], x["v"], sl, alpha=alpha, w=w, R=R, base=base, scale=scale)
+    torch.cuda.synchronize()
+    same_rounding("decode o", o_lo, o)
+    assert torch.equal(lse_lo, lse)
+    T = oracle.offset_table(base, alpha, w, R)
+    for b, L in enumerate(lens):
+        L = min(max(L, 1), Lmax)
+        for h in range(H):
+            k, v = (synth.as_f64(x[t][b, h, :L]) for t in ("k", "v"))
+            qf = np.zeros_like(k)
+            qf[L - 1] = synth.as_f64(q[b, h])
+            ro, rl = oracle.sparse_forward_rows(qf, k, v, T, w, scale, [L - 1])
+            check(f"decode o[{b},{h}] L={L}", o[b, h][None], ro, TOL[dtype])
+            check(f"decode lse[{b},{h}] L={L}", lse[b, h][None], rl, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("base,alpha,w,R", [("fib", 1.0, 64, 1024), ("fib", 1.5, 16, 1024), ("pow2", 1.0, 64, 1024),
+                                             ("fib", 0.5, 1, 256)])
+def test_decode_against_oracle(dtype, base, alpha, w, R):
+    decode_case(dtype, base, alpha, w, R, [1, 5, 64, 65, 333, 700])
+
+
+def test_decode_dense_window_and_clamped_lengths():
+    # a window covering the cache is dense decoding; lengths outside [1, Lmax] are clamped
+    decode_case(torch.bfloat16, "fib", 1.0, 700, 1024, [700, 1, 250])
+    decode_case(torch.bfloat16, "fib", 1.0, 64, 1024, [0, -3, 9999, 700])
+
+
+def test_decode_matches_forward_last_row():
+    x = inputs(31, 0, (2, 4, 1000, 64), torch.bfloat16)
+    kw = dict(alpha=1.2, w=64, R=1024, scale=0.125)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], out_dtype=torch.float32, **kw)
+    sl = torch.full((2,), 1000, dtype=torch.int32, device=dev())
+    od, ld = fsa.decode(x["q"][:, :, -1].contiguous(), x["k"], x["v"], sl, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert float((od - o[:, :, -1]).abs().max()) <= 1e-2
+    assert float((ld - lse[:, :, -1]).abs().max()) <= 1e-2
