@@ -479,6 +479,46 @@ __device__ __forceinline__ void mma_over_rows_tr(f32x4_t acc[4], const uint16_t 
     }
 }
 
+// Splits fp32 weights into bf16 high parts and bf16 remainders (w = hi + lo to ~2^-17
+// relative), packed as an MFMA B operand of four values each.
+__device__ __forceinline__ void split_bf16(const float bv[4], u32x2_t &hi, u32x2_t &lo) {
+    hi = u32x2_t{pack_bf16(bv[0], bv[1]), pack_bf16(bv[2], bv[3])};
+    lo = u32x2_t{pack_bf16(bv[0] - bf16_lo(hi[0]), bv[1] - bf16_hi(hi[0])),
+                 pack_bf16(bv[2] - bf16_lo(hi[1]), bv[3] - bf16_hi(hi[1]))};
+}
+
+// As mma_over_rows_tr2 and mma_over_rows_tr, with the weights carried as bf16 high
+// part plus remainder (two MFMAs on one A operand): for products whose weights are
+// large and unnormalised, where one bf16 rounding of each weight would add up.
+__device__ __forceinline__ void mma_over_rows_tr2_exact(f32x4_t acc[4], const uint16_t *tile, int lr0, int lr1,
+                                                        const TileLanes &tl, const float bv0[4], const float bv1[4]) {
+    u32x2_t h0, l0, h1, l1;
+    split_bf16(bv0, h0, l0);
+    split_bf16(bv1, h1, l1);
+    const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, u32x4_t{h0[0], h0[1], h1[0], h1[1]});
+    const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, u32x4_t{l0[0], l0[1], l1[0], l1[1]});
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr0 * 64 + tl.tr[db]));
+        const i16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr1 * 64 + tl.tr[db]));
+        const i16x8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bh, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bl, acc[db], 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void mma_over_rows_tr_exact(f32x4_t acc[4], const uint16_t *tile, int lr, const TileLanes &tl,
+                                                       const float bv[4]) {
+    u32x2_t h, l;
+    split_bf16(bv, h, l);
+    const i16x4_t bh = __builtin_bit_cast(i16x4_t, h), bl = __builtin_bit_cast(i16x4_t, l);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr * 64 + tl.tr[db]));
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bh, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bl, acc[db], 0, 0, 0);
+    }
+}
+
 // As mma_over_rows_tr for two 16-row blocks at once (rows lr0 .. lr0+15 with weights
 // bv0 and rows lr1 .. lr1+15 with bv1) on the 32-deep MFMA: k-slots 0..3 of lane group
 // g are rows lr0 + 4 g + k and slots 4..7 rows lr1 + 4 g + k, in both operands.
@@ -1521,14 +1561,16 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
         float p0[4], s0[4], p1[4], s1[4];
         block_pds(0, p0, s0);
         block_pds(1, p1, s1);
-        mma_over_rows_tr2(dv, tb_w, 0, 16, tl, p0, p1);
+        // dV = sum_i P_ij dO_i is unnormalised and reaches several units at early keys,
+        // where the band's P is large: those weights go in as high part plus remainder
+        mma_over_rows_tr2_exact(dv, tb_w, 0, 16, tl, p0, p1);
         mma_over_rows_tr2(dk, ta_w, 0, 16, tl, s0, s1);
         block_pds(2, p0, s0);
         block_pds(3, p1, s1);
-        mma_over_rows_tr2(dv, tb_w, 32, 48, tl, p0, p1);
+        mma_over_rows_tr2_exact(dv, tb_w, 32, 48, tl, p0, p1);
         mma_over_rows_tr2(dk, ta_w, 32, 48, tl, s0, s1);
         block_pds(4, p0, s0);
-        mma_over_rows_tr(dv, tb_w, 64, tl, p0);
+        mma_over_rows_tr_exact(dv, tb_w, 64, tl, p0);
         mma_over_rows_tr(dk, ta_w, 64, tl, s0);
     }
 #pragma unroll

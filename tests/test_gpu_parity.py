@@ -406,3 +406,26 @@ def test_decode_matches_forward_last_row():
     torch.cuda.synchronize()
     assert float((od - o[:, :, -1]).abs().max()) <= 1e-2
     assert float((ld - lse[:, :, -1]).abs().max()) <= 1e-2
+
+
+# ---------------------------------------------------------------- the pages' other schedules
+
+@pytest.mark.parametrize("layer", [0, 5, 11, 15])
+def test_coprime_stagger_layers(layer):
+    # the coprime reassignment gives layer l the linear-stagger alpha of layer 7 l mod 16
+    alpha = schedules.coprime_stagger(16)[layer]
+    assert alpha == schedules.linear_stagger(16)[oracle.coprime_layer(layer)]
+    bwd_case(32, 1, 2, 1500, torch.bfloat16, "fib", alpha, 64, 1024, layer=layer)
+
+
+@pytest.mark.parametrize("layer", [0, 8, 15])
+def test_pow2_base_with_stagger(layer):
+    alpha = schedules.linear_stagger(16)[layer]
+    bwd_case(33, 1, 2, 1200, torch.bfloat16, "pow2", alpha, 64, 1024, layer=layer)
+
+
+@pytest.mark.parametrize("w", [6, 8, 10, 12])
+def test_window_sweep(w):
+    # the pages' window sweep with the Fibonacci table (offsets below w join the window)
+    fwd_case(34, 1, 2, 700, torch.bfloat16, "fib", 1.0, w, 1024)
+    bwd_case(34, 1, 2, 700, torch.bfloat16, "fib", 1.0, w, 1024)
