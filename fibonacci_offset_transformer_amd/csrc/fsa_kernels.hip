@@ -1285,7 +1285,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
 // formed twice on the vector units. Each kernel keeps one pair of operands resident
 // (K, V for dQ; Q, dO for dK and dV), which halves the data an XCD's L2 has to hold.
 
-constexpr int kRingQ = 4, kPreQ = 3;    // dQ kernel: slab slots in the ring; slots requested before the band
+constexpr int kRingQ = 4, kPreQ = 2;    // dQ kernel: slab slots in the ring; slots requested before the band
 constexpr int kRingKV = 3, kPreKV = 1;  // dK/dV kernel
 
 // Descriptor over the pair-workspace words of head bh ([N, S] words, S = pair_slots):
@@ -1395,14 +1395,15 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     };
     {
         float d0[4], d1[4];
+        // the band's dS weights go in as bf16 high part plus remainder (see bwd_dkdv_kernel)
         block_ds(0, d0);
         block_ds(1, d1);
-        mma_over_rows_tr2(acc, ta_w, 0, 16, tl, d0, d1);
+        mma_over_rows_tr2_exact(acc, ta_w, 0, 16, tl, d0, d1);
         block_ds(2, d0);
         block_ds(3, d1);
-        mma_over_rows_tr2(acc, ta_w, 32, 48, tl, d0, d1);
+        mma_over_rows_tr2_exact(acc, ta_w, 32, 48, tl, d0, d1);
         block_ds(4, d0);
-        mma_over_rows_tr(acc, ta_w, 64, tl, d0);
+        mma_over_rows_tr_exact(acc, ta_w, 64, tl, d0);
     }
 #pragma unroll
     for (int u = kPreQ; u < kRingQ; ++u) fill(u, u);
@@ -1561,17 +1562,18 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
         float p0[4], s0[4], p1[4], s1[4];
         block_pds(0, p0, s0);
         block_pds(1, p1, s1);
-        // dV = sum_i P_ij dO_i is unnormalised and reaches several units at early keys,
-        // where the band's P is large: those weights go in as high part plus remainder
+        // dV = sum_i P_ij dO_i and dK = sum_i dS_ij q_i are unnormalised sums that reach
+        // several units at early keys, where the band's weights are large: the weights go
+        // in as bf16 high part plus remainder
         mma_over_rows_tr2_exact(dv, tb_w, 0, 16, tl, p0, p1);
-        mma_over_rows_tr2(dk, ta_w, 0, 16, tl, s0, s1);
+        mma_over_rows_tr2_exact(dk, ta_w, 0, 16, tl, s0, s1);
         block_pds(2, p0, s0);
         block_pds(3, p1, s1);
         mma_over_rows_tr2_exact(dv, tb_w, 32, 48, tl, p0, p1);
-        mma_over_rows_tr2(dk, ta_w, 32, 48, tl, s0, s1);
+        mma_over_rows_tr2_exact(dk, ta_w, 32, 48, tl, s0, s1);
         block_pds(4, p0, s0);
         mma_over_rows_tr_exact(dv, tb_w, 64, tl, p0);
-        mma_over_rows_tr(dk, ta_w, 64, tl, s0);
+        mma_over_rows_tr_exact(dk, ta_w, 64, tl, s0);
     }
 #pragma unroll
     for (int u = kPreKV; u < kRingKV; ++u) fill(u, u);
