@@ -9,6 +9,13 @@ from .fsa_ref import (  # noqa: F401
     dense_forward,
     dense_forward_rows,
     fibonacci_base,
+    frac_alpha_grad,
+    frac_backward,
+    frac_backward_rows,
+    frac_forward,
+    frac_forward_rows,
+    frac_offset_table,
+    frac_probabilities,
     offset_table,
     pow2_base,
     round_half_away,

@@ -350,3 +350,246 @@ def sparse_backward_rows(q, k, v, dout, T, w, scale, rows):
         dks.append(dk_r)
         dvs.append(dv_r)
     return np.stack(dqs, axis=-2), np.stack(dks, axis=-2), np.stack(dvs, axis=-2)
+
+
+# ----------------------------------------------------------------------------
+# Fractional offsets: the learned-alpha variant
+# ----------------------------------------------------------------------------
+#
+# [EXPL-pt] Metodologia / Arquitetura, item "Implementação": when alpha is a
+# learned parameter the targets d_k = alpha * f_k are not integers, and the model
+# interpolates linearly between key/value rows so that a gradient reaches alpha.
+# [EXPL-pt] Variáveis Experimentais, "Aprendido": one free parameter per layer,
+# started at alpha = 1. [EXPL-pt] Principais Contribuições §2 ("Eficiência"):
+# this variant ran as an unfused interpolated gather.
+#
+# Readings taken where the pages leave a step open:
+#   * d_k = alpha * f_k is one fp64 product and is not rounded; the entry is kept
+#     when d_k >= w (the same threshold as the static table);
+#   * the virtual key of query i for entry k sits at position i - d_k: with
+#     a = floor(d_k) and phi = d_k - a it is (1 - phi) * row(i - a) +
+#     phi * row(i - a - 1), for keys and values alike (the two rows around that
+#     position, weighted by closeness);
+#   * the entry exists for query i when i - d_k >= 0 (no row before the start);
+#   * every entry is its own column of the one softmax (distinct f give distinct
+#     d; entries are not merged with the window or with each other);
+#   * at an integer d_k the derivative is the one-sided one of the piece
+#     [a, a + 1), k(i - a - 1) - k(i - a) (what a floor-based interpolation
+#     differentiates to); a query without the row i - a - 1 contributes none;
+#   * d(loss)/d(alpha) = sum_k f_k d(loss)/d(d_k), summed over batch, heads and
+#     rows, since alpha is one scalar per layer.
+
+
+def frac_offset_table(base: str, alpha: float, w: int, R: int) -> list[tuple[float, int]]:
+    """Entries (d_k, f_k) of the learned-alpha variant: d_k = alpha * f_k in fp64,
+    kept when d_k >= w, in increasing order of d_k."""
+    if base == "fib":
+        fs = fibonacci_base(R)
+    elif base == "pow2":
+        fs = pow2_base(R)
+    else:
+        raise ValueError(f"unknown base {base!r}")
+    alpha = float(alpha)
+    return sorted((alpha * float(f), f) for f in fs if alpha * float(f) >= w)
+
+
+def _split(d: float) -> tuple[int, float, int]:
+    """a = floor(d), phi = d - a, and the first query row i0 = ceil(d) that has the entry."""
+    a = math.floor(d)
+    phi = d - a
+    return int(a), phi, int(a) if phi == 0.0 else int(a) + 1
+
+
+def _virtual_rows(x, d: float):
+    """Rows (1 - phi) x[i - a] + phi x[i - a - 1] for i = i0 .. N-1, or None if i0 >= N."""
+    N = x.shape[-2]
+    a, phi, i0 = _split(d)
+    if i0 >= N:
+        return i0, None
+    near = x[..., i0 - a : N - a, :]
+    if phi == 0.0:
+        return i0, near.copy()
+    far = x[..., i0 - a - 1 : N - a - 1, :]
+    return i0, (1.0 - phi) * near + phi * far
+
+
+def frac_probabilities(q, k, entries, w, scale):
+    """P over columns [window offsets 0..w-1, then one column per entry], row max, row sum."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    N = q.shape[-2]
+    S = np.full(q.shape[:-1] + (w + len(entries),), -np.inf)
+    for o in range(min(w, N)):
+        S[..., o:, o] = scale * np.sum(q[..., o:, :] * k[..., : N - o, :], axis=-1)
+    for m, d in enumerate(entries):
+        i0, kt = _virtual_rows(k, d)
+        if kt is not None:
+            S[..., i0:, w + m] = scale * np.sum(q[..., i0:, :] * kt, axis=-1)
+    return _softmax_rows(S)
+
+
+def frac_forward(q, k, v, entries, w, scale):
+    """Forward of the learned-alpha variant: one softmax over the window keys and the
+    interpolated entry keys, output the same mix of window and interpolated values.
+
+    entries: the d_k of frac_offset_table (floats). Returns (o, lse) in float64.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    P, mx, l = frac_probabilities(q, k, entries, w, scale)
+    N = v.shape[-2]
+    o = np.zeros(v.shape)
+    for off in range(min(w, N)):
+        o[..., off:, :] += P[..., off:, off : off + 1] * v[..., : N - off, :]
+    for m, d in enumerate(entries):
+        i0, vt = _virtual_rows(v, d)
+        if vt is not None:
+            o[..., i0:, :] += P[..., i0:, w + m : w + m + 1] * vt
+    return o, mx + np.log(l)
+
+
+def frac_backward(q, k, v, dout, entries, w, scale):
+    """Gradients of sum(dout * o) for the learned-alpha variant.
+
+    Returns (dq, dk, dv, dd) where dd[m] is the derivative with respect to d_m,
+    summed over every leading index and row; d(loss)/d(alpha) is
+    sum_m f_m dd[m]. The score and value paths are the textbook softmax-attention
+    gradient; an interpolated row passes its gradient to its two source rows with
+    the weights (1 - phi) and phi.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    N = q.shape[-2]
+    P, _, _ = frac_probabilities(q, k, entries, w, scale)
+    o, _ = frac_forward(q, k, v, entries, w, scale)
+    D = np.sum(dout * o, axis=-1)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for off in range(min(w, N)):
+        p = P[..., off:, off]
+        dp = np.sum(dout[..., off:, :] * v[..., : N - off, :], axis=-1)
+        ds = p * (dp - D[..., off:])
+        dq[..., off:, :] += scale * ds[..., None] * k[..., : N - off, :]
+        dk[..., : N - off, :] += scale * ds[..., None] * q[..., off:, :]
+        dv[..., : N - off, :] += p[..., None] * dout[..., off:, :]
+    dd = np.zeros(len(entries))
+    for m, d in enumerate(entries):
+        a, phi, i0 = _split(d)
+        if i0 >= N:
+            continue
+        _, kt = _virtual_rows(k, d)
+        _, vt = _virtual_rows(v, d)
+        p = P[..., i0:, w + m]
+        dp = np.sum(dout[..., i0:, :] * vt, axis=-1)
+        ds = p * (dp - D[..., i0:])
+        dq[..., i0:, :] += scale * ds[..., None] * kt
+        gk = scale * ds[..., None] * q[..., i0:, :]  # gradient reaching the virtual key
+        gv = p[..., None] * dout[..., i0:, :]        # and the virtual value
+        dk[..., i0 - a : N - a, :] += (1.0 - phi) * gk
+        dv[..., i0 - a : N - a, :] += (1.0 - phi) * gv
+        if phi != 0.0:
+            dk[..., i0 - a - 1 : N - a - 1, :] += phi * gk
+            dv[..., i0 - a - 1 : N - a - 1, :] += phi * gv
+        # d/d(d_m) of the virtual rows: row(i - a - 1) - row(i - a), rows i >= a + 1
+        s0 = max(i0, a + 1)
+        if s0 < N:
+            c = s0 - i0
+            dkr = k[..., s0 - a - 1 : N - a - 1, :] - k[..., s0 - a : N - a, :]
+            dvr = v[..., s0 - a - 1 : N - a - 1, :] - v[..., s0 - a : N - a, :]
+            dd[m] = np.sum(np.sum(gk[..., c:, :] * dkr, axis=-1)) + np.sum(np.sum(gv[..., c:, :] * dvr, axis=-1))
+    return dq, dk, dv, dd
+
+
+def frac_alpha_grad(dd, fs) -> float:
+    """d(loss)/d(alpha) = sum_m f_m dd[m] (alpha scales every d_m = alpha f_m)."""
+    return float(sum(float(f) * float(x) for f, x in zip(fs, dd)))
+
+
+def _frac_row_sources(i: int, entries, w: int):
+    """Attended columns of query row i as lists of (key row, weight) pairs:
+    window keys first, then one virtual key per entry present at row i."""
+    cols = [[(i - o, 1.0)] for o in range(w) if o <= i]
+    for d in entries:
+        a, phi, i0 = _split(d)
+        if i < i0:
+            continue
+        cols.append([(i - a, 1.0)] if phi == 0.0 else [(i - a, 1.0 - phi), (i - a - 1, phi)])
+    return cols
+
+
+def frac_forward_rows(q, k, v, entries, w, scale, rows):
+    """o_i and LSE_i of frac_forward for the given query rows, one by one."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    outs, lses = [], []
+    for i in rows:
+        i = int(i)
+        cols = _frac_row_sources(i, entries, w)
+        kt = np.stack([sum(c * k[..., j, :] for j, c in col) for col in cols], axis=-2)
+        vt = np.stack([sum(c * v[..., j, :] for j, c in col) for col in cols], axis=-2)
+        s = scale * np.sum(q[..., i : i + 1, :] * kt, axis=-1)
+        mx = np.max(s, axis=-1, keepdims=True)
+        e = np.exp(s - mx)
+        lsum = np.sum(e, axis=-1, keepdims=True)
+        outs.append(np.sum((e / lsum)[..., None] * vt, axis=-2))
+        lses.append(mx[..., 0] + np.log(lsum[..., 0]))
+    return np.stack(outs, axis=-2), np.stack(lses, axis=-1)
+
+
+def frac_backward_rows(q, k, v, dout, entries, w, scale, rows):
+    """dQ_r, dK_r, dV_r of frac_backward for the given rows r, one by one.
+
+    dK_r and dV_r collect, from every query i and column whose key mixes row r,
+    that column's gradient times row r's weight in the mix. Returns (dq, dk, dv),
+    each [..., len(rows), d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    N = q.shape[-2]
+    cache = {}
+
+    def row_stats(i):
+        # (columns, virtual keys, virtual values, P, dS) of query row i
+        if i not in cache:
+            cols = _frac_row_sources(i, entries, w)
+            kt = np.stack([sum(c * k[..., j, :] for j, c in col) for col in cols], axis=-2)
+            vt = np.stack([sum(c * v[..., j, :] for j, c in col) for col in cols], axis=-2)
+            s = scale * np.sum(q[..., i : i + 1, :] * kt, axis=-1)
+            e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+            p = e / np.sum(e, axis=-1, keepdims=True)
+            o_i = np.sum(p[..., None] * vt, axis=-2)
+            D = np.sum(dout[..., i, :] * o_i, axis=-1)
+            dp = np.sum(dout[..., i : i + 1, :] * vt, axis=-1)
+            cache[i] = (cols, kt, p, p * (dp - D[..., None]))
+        return cache[i]
+
+    # queries whose columns can mix key row r: r + o (window), r + a and r + a + 1
+    reach = set(range(w))
+    for d in entries:
+        a, _, _ = _split(d)
+        reach.update((a, a + 1))
+    dqs, dks, dvs = [], [], []
+    for r in rows:
+        r = int(r)
+        _, kt, _, ds = row_stats(r)
+        dqs.append(scale * np.sum(ds[..., None] * kt, axis=-2))
+        dk_r = np.zeros(q.shape[:-2] + (q.shape[-1],))
+        dv_r = np.zeros(q.shape[:-2] + (q.shape[-1],))
+        for off in sorted(reach):
+            i = r + off
+            if i >= N:
+                continue
+            cols, _, p, dsi = row_stats(i)
+            for m, col in enumerate(cols):
+                for j, c in col:
+                    if j == r:
+                        dk_r += c * scale * dsi[..., m : m + 1] * q[..., i, :]
+                        dv_r += c * p[..., m : m + 1] * dout[..., i, :]
+        dks.append(dk_r)
+        dvs.append(dv_r)
+    return np.stack(dqs, axis=-2), np.stack(dks, axis=-2), np.stack(dvs, axis=-2)
