@@ -13,8 +13,11 @@ query-heads/s (value), algorithmic HBM GB/s of the step, a roofline entry for
 the dominant kernel, the dense causal baseline, and the fp64 CPU oracle timed
 on a bounded sample of the same workload.
 
+The learned-alpha variant (fractional targets, interpolated K/V rows) is timed on
+the same layers next to the static path.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-dense] [--copy-probe]
+                       [--no-dense] [--no-decode] [--no-frac] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -203,6 +206,70 @@ def decode_bench(fsa, torch, dev, stream):
     return res
 
 
+def stage_us(torch, dev, stream, fn, reps):
+    """Average duration (us) of one layer's launches of fn: the 16 layers captured back to
+    back in a HIP graph, replayed `reps` times between two HIP events on the stream."""
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for l in range(LAYERS):
+            fn(l)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(LAYERS):
+            fn(l)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
+
+
+def frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
+    """The learned-alpha variant on the same 16 layers: the stagger alphas taken as learned
+    values, so every target alpha*F stays unrounded and each entry reads interpolated
+    K/V rows. Per-layer forward and backward (dQ, dK/dV, alpha gradient) durations next
+    to the static path's."""
+    ws_bytes = max(fsa.frac_workspace_bytes(torch.bfloat16, B, H, N, D, alpha=a, w=W, R=R, base=BASE)
+                   for a in alphas)
+    ws = torch.empty(ws_bytes // 4 + 1, dtype=torch.int32, device=dev)
+    dalpha = torch.empty((LAYERS, 1), dtype=torch.float32, device=dev)
+    doffs = torch.empty((LAYERS, 48), dtype=torch.float32, device=dev)
+
+    def fwd(l):
+        x = bufs[l]
+        fsa.frac_forward(x["q"], x["k"], x["v"], alpha=alphas[l], w=W, R=R, base=BASE, scale=scale,
+                         out=x["o"], lse=x["lse"])
+
+    def bwd(l):
+        x = bufs[l]
+        fsa.frac_backward(x["q"], x["k"], x["v"], x["o"], x["lse"], x["do"], alpha=alphas[l], w=W, R=R,
+                          base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], dalpha=dalpha[l],
+                          doffs=doffs[l], ws=ws)
+
+    fwd_us = stage_us(torch, dev, stream, fwd, reps)
+    bwd_us = stage_us(torch, dev, stream, bwd, reps)
+    entries = [len(fsa.frac_offsets(a, W, R, BASE)) for a in alphas]
+    return {
+        "what": "learned-alpha variant: fractional targets alpha*F (stagger alphas taken unrounded), "
+                "keys/values interpolated between the two rows around each target, fused in the "
+                "window kernels; dK/dV/dQ plus d(loss)/d(alpha)",
+        "entries_per_layer": entries,
+        "fwd_us_per_layer": round(fwd_us, 3),
+        "bwd_us_per_layer": round(bwd_us, 3),
+        "static_fwd_us_per_layer": round(static_us["fwd"], 3),
+        "static_bwd_us_per_layer": round(static_us["bwd"], 3),
+        "fwd_over_static": round(fwd_us / static_us["fwd"], 3),
+        "step_over_static": round((fwd_us + bwd_us) / (static_us["fwd"] + static_us["bwd"]), 3),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +278,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-frac", action="store_true", help="skip the learned-alpha (fractional) variant")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale reference) and exit")
     args = ap.parse_args()
@@ -286,31 +354,9 @@ def main():
     # per-stage durations: each stage's 16 per-layer launches captured back to back in a
     # HIP graph of their own, replayed between two HIP events on the launch stream
     stream = torch.cuda.current_stream(dev)
-    fns = {"fwd": layer_fwd, "bwd": layer_bwd}
     reps = max(3, args.steps // 5)
-    avg_us = {}
-    for key, fn in fns.items():
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for l in range(LAYERS):
-                fn(l)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for l in range(LAYERS):
-                fn(l)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        avg_us[key] = e0.elapsed_time(e1) * 1e3 / (reps * LAYERS)
-        del g
+    avg_us = {key: stage_us(torch, dev, stream, fn, reps)
+              for key, fn in (("fwd", layer_fwd), ("bwd", layer_bwd))}
     log("average kernel durations (us): " + ", ".join(f"{k}={v:.2f}" for k, v in avg_us.items()))
 
     # capture one step as a HIP graph
@@ -408,6 +454,10 @@ def main():
     if not args.no_decode:
         decode = decode_bench(fsa, torch, dev, stream)
 
+    learned = None
+    if not args.no_frac:
+        learned = frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, avg_us, max(3, args.steps // 5))
+
     out = {
         "metric": METRIC,
         "value": round(qh_per_step / (ms_per_step * 1e-3), 1),
@@ -438,6 +488,7 @@ def main():
         "cpu_baseline": cpu,
         "dense_baseline": dense,
         "decode": decode,
+        "learned_alpha": learned,
     }
     if cpu:
         out["gpu_over_cpu"] = round(out["value"] / cpu["value"], 1)

@@ -107,6 +107,44 @@ int build_table(fsa_base_t base, double alpha, int32_t w, int32_t R, int32_t *ou
     return count;
 }
 
+// Fractional table of the learned-alpha variant: d = alpha * F (one double product,
+// not rounded) for F in the base list below R, kept when d >= w, increasing. Entry t
+// gets whole[t] = floor(d), frac[t] = d - floor(d) rounded to float, fb[t] = F.
+// Returns the count, or -1 with the error set.
+int build_frac_table(fsa_base_t base, double alpha, int32_t w, int32_t R, int32_t *whole, float *frac,
+                     int32_t *fb, fsa_status_t *st) {
+    int32_t tmp[FSA_MAX_OFFSETS];
+    if (build_table(base, alpha, w, R, tmp, st) < 0) return -1;  // the same argument checks
+    int count = 0;
+    int64_t a = 1, b = 2;
+    while (a < R) {
+        const double x = alpha * static_cast<double>(a);
+        if (!(x < 2147483647.0)) {
+            *st = fail(FSA_E_ARG, "alpha * %lld = %.17g does not fit in int32", static_cast<long long>(a), x);
+            return -1;
+        }
+        if (x >= static_cast<double>(w)) {
+            if (count == FSA_MAX_OFFSETS) {
+                *st = fail(FSA_E_ARG, "fractional table exceeds %d entries", FSA_MAX_OFFSETS);
+                return -1;
+            }
+            const double f = std::floor(x);
+            whole[count] = static_cast<int32_t>(f);
+            frac[count] = static_cast<float>(x - f);
+            fb[count] = static_cast<int32_t>(a);
+            ++count;
+        }
+        if (base == FSA_BASE_FIB) {
+            const int64_t c = a + b;
+            a = b;
+            b = c;
+        } else {
+            a *= 2;
+        }
+    }
+    return count;  // base values increase and alpha > 0, so d increases
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Shape {
@@ -391,6 +429,139 @@ fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     return launched(fsa::launch_dense_forward(dt, out_dt, p, static_cast<hipStream_t>(stream)), "dense forward");
+}
+
+fsa_status_t fsa_frac_offsets(fsa_base_t base, double alpha, int32_t w, int32_t R, int32_t *whole,
+                              float *frac, int32_t *base_value, int32_t capacity, int32_t *count) {
+    if (!count) return fail(FSA_E_ARG, "count is NULL");
+    if (capacity < 0) return fail(FSA_E_ARG, "capacity must be >= 0");
+    int32_t wh[FSA_MAX_OFFSETS], fb[FSA_MAX_OFFSETS];
+    float fr[FSA_MAX_OFFSETS];
+    fsa_status_t st = FSA_OK;
+    const int n = build_frac_table(base, alpha, w, R, wh, fr, fb, &st);
+    if (n < 0) return st;
+    *count = n;
+    if (n > capacity)
+        return fail(FSA_E_CAPACITY, "fractional table has %d entries, capacity is %d", n, capacity);
+    if (n > 0 && (!whole || !frac || !base_value)) return fail(FSA_E_ARG, "an output array is NULL");
+    for (int t = 0; t < n; ++t) {
+        whole[t] = wh[t];
+        frac[t] = fr[t];
+        base_value[t] = fb[t];
+    }
+    return ok();
+}
+
+namespace {
+
+// Checks shared by the fractional calls and their table, trimmed to the entries some
+// row of length N reaches (first row floor(d) + (frac != 0) < N).
+fsa_status_t prepare_frac(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_dt, int32_t B, int32_t H, int32_t N,
+                          int32_t d, float scale, fsa_base_t base, double alpha, int32_t w, int32_t R) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
+    if (st != FSA_OK) return st;
+    int32_t fb[FSA_MAX_OFFSETS];
+    const int n = build_frac_table(base, alpha, w, R, p.off, p.phi, fb, &st);
+    if (n < 0) return st;
+    if (dt != FSA_BF16) return fail(FSA_E_UNSUPPORTED, "fractional entries are implemented for bf16 inputs only");
+    if (w > 64) return fail(FSA_E_UNSUPPORTED, "fractional entries need a window w <= 64 (got %d)", w);
+    if (N > (1 << 24)) return fail(FSA_E_UNSUPPORTED, "fractional entries need N <= 2^24 (got %d)", N);
+    if (!(scale > 0.f)) return fail(FSA_E_UNSUPPORTED, "fractional entries need a positive scale");
+    int used = 0;
+    while (used < n && p.off[used] + (p.phi[used] != 0.f ? 1 : 0) < N) ++used;
+    for (int t = 0; t < n; ++t) p.fbase[t] = static_cast<float>(fb[t]);
+    p.n_entries = n;
+    p.n_off = used;
+    p.bh = B * H;
+    p.n = N;
+    p.w = w;
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return FSA_OK;
+}
+
+}  // namespace
+
+fsa_status_t fsa_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                              void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                              fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream) {
+    fsa::AttnParams p{};
+    fsa_status_t st = prepare_frac(p, dt, out_dt, B, H, N, d, scale, base, alpha, w, R);
+    if (st != FSA_OK) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "o", "lse"};
+    const void *ptrs[] = {q, k, v, o, lse};
+    if ((st = check_ptrs(names, ptrs, 5)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 3, 5)) != FSA_OK) return st;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = o;
+    p.lse_out = lse;
+    return launched(fsa::launch_frac_forward(out_dt, p, static_cast<hipStream_t>(stream)), "fractional forward");
+}
+
+fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                                               fsa_base_t base, double alpha, int32_t w, int32_t R,
+                                               uint64_t *bytes) {
+    if (!bytes) return fail(FSA_E_ARG, "bytes is NULL");
+    fsa::AttnParams p{};
+    const fsa_status_t st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R);
+    if (st != FSA_OK) return st;
+    *bytes = fsa::frac_workspace(static_cast<int64_t>(B) * H, N, p.n_off).total;
+    return ok();
+}
+
+fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                               const void *o, const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                               float *dalpha, float *doffs, void *ws, uint64_t ws_bytes, int32_t B, int32_t H,
+                               int32_t N, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
+                               int32_t R, void *stream) {
+    fsa::AttnParams p{};
+    fsa_status_t st = prepare_frac(p, dt, out_dt, B, H, N, d, scale, base, alpha, w, R);
+    if (st != FSA_OK) return st;
+    if (!dalpha) return fail(FSA_E_ARG, "dalpha is NULL");
+    if (reinterpret_cast<uintptr_t>(dalpha) & 3u) return fail(FSA_E_ARG, "dalpha is not 4-byte aligned");
+    if (doffs && (reinterpret_cast<uintptr_t>(doffs) & 3u)) return fail(FSA_E_ARG, "doffs is not 4-byte aligned");
+    const bool empty = static_cast<int64_t>(B) * H * N == 0;
+    if (!empty) {
+        const uint64_t need = fsa::frac_workspace(static_cast<int64_t>(B) * H, N, p.n_off).total;
+        const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"};
+        const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, ws};
+        if ((st = check_ptrs(names, ptrs, 10)) != FSA_OK) return st;
+        if ((st = check_no_alias(names, ptrs, 6, 10)) != FSA_OK) return st;
+        if (ws_bytes < need)
+            return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
+                        static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(need));
+    }
+    // the gradient outputs are written by the kernels, so they must not alias each other or inputs
+    const void *outs[] = {dalpha, doffs, dq, dk, dv, ws, q, k, v, o, lse, dout};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 12; ++j)
+            if (j != i && outs[i] && outs[i] == outs[j])
+                return fail(FSA_E_ARG, "%s aliases another argument", i == 0 ? "dalpha" : "doffs");
+    p.dalpha = dalpha;
+    p.doffs = doffs;
+    if (!empty) {
+        const fsa::FracWorkspace lay = fsa::frac_workspace(p.bh, N, p.n_off);
+        char *base_ws = static_cast<char *>(ws);
+        p.q = q;
+        p.k = k;
+        p.v = v;
+        p.o = o;
+        p.lse_in = lse;
+        p.dout = dout;
+        p.dq = dq;
+        p.dk = dk;
+        p.dv = dv;
+        p.delta = reinterpret_cast<float *>(base_ws + lay.delta);
+        p.pairs = reinterpret_cast<uint32_t *>(base_ws + lay.pairs);
+        p.dd_part = reinterpret_cast<float *>(base_ws + lay.partials);
+    } else {
+        p.bh = 0;  // no tiles: only the alpha reduction runs, writing zeros
+    }
+    return launched(fsa::launch_frac_backward(out_dt, p, static_cast<hipStream_t>(stream)), "fractional backward");
 }
 
 const char *fsa_last_error(void) { return g_last_error.c_str(); }

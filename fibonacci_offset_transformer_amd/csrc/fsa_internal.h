@@ -35,6 +35,14 @@ struct AttnParams {
     const int32_t *seq_lens;  // decode: cached length of each sequence [B]
     int32_t heads;            // decode: H (heads per sequence)
     int32_t lmax;             // decode: rows allocated per cached head
+    // Fractional entries (learned-alpha variant): entry t targets distance
+    // off[t] + phi[t] (off = floor, phi in [0, 1)) and scales base value fbase[t].
+    float phi[FSA_MAX_OFFSETS];
+    float fbase[FSA_MAX_OFFSETS];
+    float *dd_part;           // backward: per-tile partials of d(loss)/d(d_t) [tiles, n_off]
+    float *dalpha;            // backward: d(loss)/d(alpha), one float
+    float *doffs;             // backward: d(loss)/d(d_t) per table entry, or null
+    int32_t n_entries;        // table entries before trimming (length of doffs)
 };
 
 // The bf16 window kernels (w <= 64) address each head with 32-bit byte offsets.
@@ -49,6 +57,23 @@ inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int3
     return window_path(dt, w, n) ? static_cast<int64_t>(pair_slots(n_off)) * bh * n : 0;
 }
 
+// Fractional-entry backward workspace on the window path: D [BH, N] floats, then the
+// pair words [BH, N, pair_slots(n_off), 2] (the near and far weights of every
+// entry), then the per-tile partials [tiles, n_off]; each part 256-byte aligned.
+struct FracWorkspace {
+    uint64_t delta, pairs, partials, total;  // byte offsets of the parts, total size
+};
+inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
+    FracWorkspace w;
+    const uint64_t tiles = static_cast<uint64_t>(bh) * ((n + 63) / 64);
+    w.delta = 0;
+    w.pairs = align256(4ull * bh * n);
+    w.partials = w.pairs + align256(8ull * pair_slots(n_off) * bh * n);
+    w.total = w.partials + align256(4ull * tiles * n_off);
+    return w;
+}
+
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
@@ -58,5 +83,9 @@ hipError_t launch_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p
 // elsewhere); otherwise p.delta is read as given.
 hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream,
                                  bool with_delta);
+// Fractional entries (bf16 window path, positive scale): the forward, and the
+// backward (dQ with D, dK/dV, then the reduction of the alpha gradient).
+hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 
 }  // namespace fsa

@@ -426,6 +426,17 @@ __device__ __forceinline__ int table_off(const AttnParams &p, int t) {
     return t < p.n_off ? p.off[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1] : 0x3fffffff;
 }
 
+// Fractional entries: the weight phi[t] of the far row (row - off[t] - 1), 0 past the
+// table, and the first query row that has entry t (off[t] + (phi[t] != 0): the target
+// position row - off[t] - phi[t] must not lie before the sequence start).
+__device__ __forceinline__ float table_phi(const AttnParams &p, int t) {
+    return t < p.n_off ? p.phi[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1] : 0.f;
+}
+__device__ __forceinline__ int table_first(const AttnParams &p, int t) {
+    const int c = t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1;
+    return t < p.n_off ? p.off[c] + (p.phi[c] != 0.f ? 1 : 0) : 0x3fffffff;
+}
+
 // Waits for every outstanding memory operation of the wave (global -> LDS copies included).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0); }
 
@@ -598,6 +609,20 @@ __device__ __forceinline__ float row8_max(float x) {
     x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppXor2, 0xF, 0xF, false)));
     x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppHalfMirror, 0xF, 0xF, false)));
     return x;
+}
+
+// Sum over lanes l and l ^ 8 (DPP rotation by 8 within each 16-lane row), and over the
+// two halves of a 16-lane row (DPP row mirror).
+constexpr int kDppRowRor8 = 0x128, kDppRowMirror = 0x140;
+__device__ __forceinline__ float xor8_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowRor8, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor8_max(float x) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowRor8, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x = row8_sum(x);
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowMirror, 0xF, 0xF, false));
 }
 
 // Stores row `row` chunk (8 values, times mul) of a slab-layout accumulator.
@@ -783,7 +808,10 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
 // lane, and the band runs on MFMA while those loads are in flight; its softmax state
 // then moves into the slab layout and the slabs continue it as an online softmax, one
 // group of four offsets at a time. The slab layout stores O and the LSE.
-template <bool OUT_BF16>
+// With FRAC the table holds fractional entries (learned-alpha variant): entry t's key
+// and value for row i are (1 - phi) row(i - off[t]) + phi row(i - off[t] - 1), so each
+// entry reads two adjacent slabs (near and far); entries go two per softmax update.
+template <bool OUT_BF16, bool FRAC>
 __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ks[kTileRows * 64];  // band K rows, then merge areas
@@ -818,11 +846,24 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     __syncthreads();
     // the first slab rows are requested now and land while the band runs; most of them
     // are rows of neighbouring tiles whose band copies have just passed through L2
-    SFrag sk[4], sv[4];
+    SFrag sk[4], sv[4];  // FRAC: slot u of entries holds near rows in [2u], far rows in [2u + 1]
+    auto frac_fill = [&](SFrag *f, __amdgpu_buffer_rsrc_t r, int u, int t) {
+        const int n0 = slab_row(p, t, row_s[0], -1), n1 = slab_row(p, t, row_s[1], -1);
+        sfrag_load(f[2 * u], r, n0, n1, c8);
+        sfrag_load(f[2 * u + 1], r, n0 - 1, n1 - 1, c8);
+    };
+    if constexpr (FRAC) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
-        sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+        for (int u = 0; u < 2; ++u) {
+            frac_fill(sk, rk, u, u);
+            frac_fill(sv, rv, u, u);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+            sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+        }
     }
 
     // ---- window band on MFMA: rows r0..r0+15 (row c16 of the lane) see key blocks qb-4 .. qb ----
@@ -906,64 +947,105 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             }
         }
     };
+    if constexpr (FRAC) {
+        // entries two at a time; the ring slot of an entry is refilled with the entry
+        // two further on as soon as its rows have been used
+        for (int t0 = 0; t0 < n_off; t0 += 2) {
+            if (r0 + 15 < p.off[t0]) break;  // ascending entries: no row of the wave has one
+            float ss[2][2], ph[2], gm[2] = {kNegInf, kNegInf};
 #pragma unroll
-    for (int t0 = 0; t0 < 8; t0 += 4) {
-        if (t0 >= n_off || r0 + 15 < p.off[t0]) break;  // ascending offsets
-        float ss[4][2], gm[2] = {kNegInf, kNegInf};    // unscaled scores
+            for (int u = 0; u < 2; ++u) {
+                const int t = t0 + u, first = table_first(p, t);
+                ph[u] = table_phi(p, t);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int o = table_off(p, t0 + u);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                ss[u][h] = kNegInf;
-                if (t0 + u < n_off) {  // uniform: slots past the table only refill
-                    const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-                    const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                for (int h = 0; h < 2; ++h) {
+                    const bool ok = (row_s[h] < n) & (row_s[h] >= first);
+                    const float dn = chunk_dot(qs.r[h], sk[2 * u].r[h]);
+                    const float df = chunk_dot(qs.r[h], sk[2 * u + 1].r[h]);
+                    const float d = row8_sum(__builtin_fmaf(ph[u], df - dn, dn));
                     ss[u][h] = ok ? d : kNegInf;
                     gm[h] = fmaxf(gm[h], ss[u][h]);
                 }
+                if (t + 2 < n_off) frac_fill(sk, rk, u, t + 2);  // uniform
             }
-            if (t0 == 0)
-                sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
-        }
-        const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
-        rescale(mn);
-        const float ms[2] = {m_s[0] == kNegInf ? 0.f : m_s[0], m_s[1] == kNegInf ? 0.f : m_s[1]};
+            const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
+            rescale(mn);
+            const float ms[2] = {m_s[0] == kNegInf ? 0.f : m_s[0], m_s[1] == kNegInf ? 0.f : m_s[1]};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t0 + u < n_off) {  // uniform
+            for (int u = 0; u < 2; ++u) {
+                if (t0 + u < n_off) {  // uniform
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const float pt = fast_exp2(__builtin_fmaf(ss[u][h], sl2, -ms[h]));
+                        const float pf = pt * ph[u];
+                        l_s[h] += pt;
+                        chunk_axpy(acc_s[h], pt - pf, sv[2 * u].r[h]);
+                        chunk_axpy(acc_s[h], pf, sv[2 * u + 1].r[h]);
+                    }
+                }
+                if (t0 + u + 2 < n_off) frac_fill(sv, rv, u, t0 + u + 2);  // uniform
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t0 = 0; t0 < 8; t0 += 4) {
+            if (t0 >= n_off || r0 + 15 < p.off[t0]) break;  // ascending offsets
+            float ss[4][2], gm[2] = {kNegInf, kNegInf};    // unscaled scores
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int o = table_off(p, t0 + u);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const float pt = fast_exp2(__builtin_fmaf(ss[u][h], sl2, -ms[h]));
-                    l_s[h] += pt;
-                    chunk_axpy(acc_s[h], pt, sv[u].r[h]);
+                    ss[u][h] = kNegInf;
+                    if (t0 + u < n_off) {  // uniform: slots past the table only refill
+                        const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                        const float d = row8_sum(chunk_dot(qs.r[h], sk[u].r[h]));
+                        ss[u][h] = ok ? d : kNegInf;
+                        gm[h] = fmaxf(gm[h], ss[u][h]);
+                    }
                 }
+                if (t0 == 0)
+                    sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
             }
-            if (t0 == 0)
-                sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
-        }
-    }
-    for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
-        if (r0 + 15 < p.off[t]) break;
-        SFrag kt, vt;
-        sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-        sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
-        float sv1[2];
+            const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
+            rescale(mn);
+            const float ms[2] = {m_s[0] == kNegInf ? 0.f : m_s[0], m_s[1] == kNegInf ? 0.f : m_s[1]};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
-            sv1[h] = ok ? row8_sum(chunk_dot(qs.r[h], kt.r[h])) : kNegInf;
-        }
-        const float mn[2] = {fmaxf(m_s[0], sv1[0] * sl2), fmaxf(m_s[1], sv1[1] * sl2)};
-        rescale(mn);
+            for (int u = 0; u < 4; ++u) {
+                if (t0 + u < n_off) {  // uniform
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float pt = fast_exp2(__builtin_fmaf(sv1[h], sl2, -(m_s[h] == kNegInf ? 0.f : m_s[h])));
-            l_s[h] += pt;
-            chunk_axpy(acc_s[h], pt, vt.r[h]);
+                    for (int h = 0; h < 2; ++h) {
+                        const float pt = fast_exp2(__builtin_fmaf(ss[u][h], sl2, -ms[h]));
+                        l_s[h] += pt;
+                        chunk_axpy(acc_s[h], pt, sv[u].r[h]);
+                    }
+                }
+                if (t0 == 0)
+                    sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+            }
         }
-    }
+        for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
+            if (r0 + 15 < p.off[t]) break;
+            SFrag kt, vt;
+            sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+            sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+            float sv1[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] - p.off[t] >= 0);
+                sv1[h] = ok ? row8_sum(chunk_dot(qs.r[h], kt.r[h])) : kNegInf;
+            }
+            const float mn[2] = {fmaxf(m_s[0], sv1[0] * sl2), fmaxf(m_s[1], sv1[1] * sl2)};
+            rescale(mn);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float pt = fast_exp2(__builtin_fmaf(sv1[h], sl2, -(m_s[h] == kNegInf ? 0.f : m_s[h])));
+                l_s[h] += pt;
+                chunk_axpy(acc_s[h], pt, vt.r[h]);
+            }
+        }
 
+    }
     // ---- normalise, store ----
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1300,12 +1382,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p,
 // storing each sparse pair's P and dS on the way. With WITH_D the kernel also forms
 // D = rowsum(dO * O) of its rows from O (instead of reading it) and stores it for the
 // dK/dV kernel.
-template <bool OUT_BF16, bool WITH_D>
+//
+// With FRAC (fractional entries, WITH_D) each entry's key and value mix the near row
+// i - off[t] and the far row i - off[t] - 1 with weights 1 - phi and phi. The kernel
+// stores two words per pair, the near and the far share of P and dS, and adds up, per
+// entry, the derivative of the loss with respect to the entry's distance over its rows
+// (one partial per workgroup and entry; see reduce_alpha_grad).
+template <bool OUT_BF16, bool WITH_D, bool FRAC>
 __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
+    static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // band K rows, then merge areas
     __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // band V rows
     __shared__ float d_s[64];                                             // D of the tile's rows (WITH_D)
+    __shared__ float dd_s[FRAC ? 4 * FSA_MAX_OFFSETS : 1];                // per wave and entry (FRAC)
 
     const int n = p.n, w = p.w, n_off = p.n_off;
     const int nt = (n + 63) >> 6;
@@ -1361,13 +1451,32 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     const float di_i = WITH_D ? d_s[16 * wave + c16] : buf_f32(rd, i);
 
     // the first slab rows land while the band runs
-    SFrag sk[kRingQ], sv[kRingQ];
+    SFrag sk[kRingQ], sv[kRingQ];  // FRAC: entry slot u holds near rows in [2u], far rows in [2u + 1]
     auto fill = [&](int u, int t) {
         sfrag_load(sk[u], rk, slab_row(p, t, row_s[0], -1), slab_row(p, t, row_s[1], -1), c8);
         sfrag_load(sv[u], rv, slab_row(p, t, row_s[0], -1), slab_row(p, t, row_s[1], -1), c8);
     };
+    // FRAC: K rows of two entries in flight (slot u: near rows in sk[2u], far rows in
+    // sk[2u + 1]), V rows of one (sv[0] near, sv[1] far), requested as soon as the
+    // previous entry's V rows have been used
+    auto frac_load_k = [&](int u, int t) {
+        const int n0 = slab_row(p, t, row_s[0], -1), n1 = slab_row(p, t, row_s[1], -1);
+        sfrag_load(sk[2 * u], rk, n0, n1, c8);
+        sfrag_load(sk[2 * u + 1], rk, n0 - 1, n1 - 1, c8);
+    };
+    auto frac_load_v = [&](int t) {
+        const int n0 = slab_row(p, t, row_s[0], -1), n1 = slab_row(p, t, row_s[1], -1);
+        sfrag_load(sv[0], rv, n0, n1, c8);
+        sfrag_load(sv[1], rv, n0 - 1, n1 - 1, c8);
+    };
+    if constexpr (FRAC) {
+        frac_load_k(0, 0);
+        frac_load_v(0);
+        if (threadIdx.x < 4 * FSA_MAX_OFFSETS) dd_s[threadIdx.x] = 0.f;  // read after the last barrier
+    } else {
 #pragma unroll
-    for (int u = 0; u < kPreQ; ++u) fill(u, u);
+        for (int u = 0; u < kPreQ; ++u) fill(u, u);
+    }
 
     // band on MFMA: query row i sees key blocks qb-4 .. qb (blocks outside the sequence
     // or the window are masked like edge blocks: their tile rows hold finite values)
@@ -1405,8 +1514,12 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
         block_ds(4, d0);
         mma_over_rows_tr_exact(acc, ta_w, 64, tl, d0);
     }
+    if constexpr (FRAC) {
+        frac_load_k(1, 1);
+    } else {
 #pragma unroll
-    for (int u = kPreQ; u < kRingQ; ++u) fill(u, u);
+        for (int u = kPreQ; u < kRingQ; ++u) fill(u, u);
+    }
     __syncthreads();  // every wave is done with the band tiles
     f32x4_t dq_s[2][2];
     c_to_slab(reinterpret_cast<float *>(ta) + wave * 1024, acc, dq_s, c16, g, s8, c8);
@@ -1422,51 +1535,139 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     // slot c8 of the unrolled part and the eight lanes store them with one 32-byte write
     const int slots = pair_slots(n_off);
     uint32_t *pairs = p.pairs + (int64_t)bh * n * slots;
-    uint32_t keep[2] = {0u, 0u};
-    auto slab = [&](int t, int o, const SFrag &kt, const SFrag &vt) {
+    if constexpr (FRAC) {
+        // pair words [n, slots, 2]: the near word {(1 - phi) P, (1 - phi) dS} and the far
+        // word {phi P, phi dS} of every entry, each rounded once to bf16, stored by the lane
+        // c8 = t mod 8 of each row
+        uint2 *pairs2 = reinterpret_cast<uint2 *>(p.pairs) + (int64_t)bh * n * slots;
+        auto entry = [&](int t, const SFrag &kn, const SFrag &kf) {
+            const int a = p.off[t], first = table_first(p, t);
+            const float ph = table_phi(p, t);
+            float pn[2], pd[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
-            const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
-            const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
-            const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
-            const uint32_t pw = pack_bf16(pv, pv * (dp - di[h]));
-            if (t < 8)
-                keep[h] = c8 == t ? pw : keep[h];
-            else if (c8 == 0 && row_s[h] < n)
-                pairs[(int64_t)row_s[h] * slots + t] = pw;
-            chunk_axpy_words(dq_s[h], pw >> 16, pw & 0xffff0000u, kt.r[h]);
+            for (int h = 0; h < 2; ++h) {
+                pn[h] = row8_sum(chunk_dot(dos.r[h], sv[0].r[h]));
+                pd[h] = row8_sum(chunk_dot(dos.r[h], sv[1].r[h])) - pn[h];
+            }
+            if (t + 1 < n_off) frac_load_v(t + 1);  // uniform
+            float ddl = 0.f;  // this lane's rows' share of d(loss)/d(d_t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int row = row_s[h];
+                const bool ok = (row < n) & (row >= first);
+                const float sn = row8_sum(chunk_dot(qs.r[h], kn.r[h]));
+                const float sd = row8_sum(chunk_dot(qs.r[h], kf.r[h])) - sn;
+                const float sc = __builtin_fmaf(ph, sd, sn), dp = __builtin_fmaf(ph, pd[h], pn[h]);
+                const float pv = ok ? fast_exp2(sc * sl2 - lse2[h]) : 0.f;
+                const float ds = pv * (dp - di[h]);
+                const float pf = pv * ph, dsf = ds * ph;
+                const uint2 pw = {pack_bf16(pv - pf, ds - dsf), pack_bf16(pf, dsf)};
+                if (c8 == (t & 7) && row < n) pairs2[(int64_t)row * slots + t] = pw;
+                chunk_axpy_words(dq_s[h], pw.x >> 16, pw.x & 0xffff0000u, kn.r[h]);
+                chunk_axpy_words(dq_s[h], pw.y >> 16, pw.y & 0xffff0000u, kf.r[h]);
+                // moving the target distance moves the key and value along far - near
+                // (the piece [a, a + 1)); rows without the far row contribute nothing
+                if (ok & (row - a - 1 >= 0)) ddl += __builtin_fmaf(p.scale * ds, sd, pv * pd[h]);
+            }
+            // wave total: the eight lanes of a row hold the same value, so sum over rows
+            const float tot = group_sum(xor8_add(ddl));
+            if (lane == 0) dd_s[wave * FSA_MAX_OFFSETS + t] = tot;
+        };
+        for (int t0 = 0; t0 < n_off; t0 += 2) {
+            if (r0 + 15 < p.off[t0]) break;  // ascending entries: no row of the wave has one
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (t0 + u < n_off) entry(t0 + u, sk[2 * u], sk[2 * u + 1]);  // uniform
+                if (t0 + u + 2 < n_off) frac_load_k(u, t0 + u + 2);         // uniform
+            }
         }
-    };
+    } else {
+        uint32_t keep[2] = {0u, 0u};
+        auto slab = [&](int t, int o, const SFrag &kt, const SFrag &vt) {
 #pragma unroll
-    for (int s0 = 0; s0 < unrolled_slabs(kRingQ); s0 += kRingQ) {
-        if (s0 >= n_off || r0 + 15 < p.off[s0]) break;  // ascending offsets: no key left
+            for (int h = 0; h < 2; ++h) {
+                const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
+                const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
+                const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
+                const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                const uint32_t pw = pack_bf16(pv, pv * (dp - di[h]));
+                if (t < 8)
+                    keep[h] = c8 == t ? pw : keep[h];
+                else if (c8 == 0 && row_s[h] < n)
+                    pairs[(int64_t)row_s[h] * slots + t] = pw;
+                chunk_axpy_words(dq_s[h], pw >> 16, pw & 0xffff0000u, kt.r[h]);
+            }
+        };
 #pragma unroll
-        for (int u = 0; u < kRingQ; ++u) {
-            if (s0 + u < n_off) slab(s0 + u, table_off(p, s0 + u), sk[u], sv[u]);  // uniform
-            if (s0 + kRingQ < unrolled_slabs(kRingQ)) fill(u, s0 + u + kRingQ);
+        for (int s0 = 0; s0 < unrolled_slabs(kRingQ); s0 += kRingQ) {
+            if (s0 >= n_off || r0 + 15 < p.off[s0]) break;  // ascending offsets: no key left
+#pragma unroll
+            for (int u = 0; u < kRingQ; ++u) {
+                if (s0 + u < n_off) slab(s0 + u, table_off(p, s0 + u), sk[u], sv[u]);  // uniform
+                if (s0 + kRingQ < unrolled_slabs(kRingQ)) fill(u, s0 + u + kRingQ);
+            }
         }
-    }
-    static_assert(unrolled_slabs(kRingQ) == 8, "the kept pair words cover slots 0..7");
-    if (n_off > 0) {  // uniform
+        static_assert(unrolled_slabs(kRingQ) == 8, "the kept pair words cover slots 0..7");
+        if (n_off > 0) {  // uniform
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            if (row_s[h] < n) pairs[(int64_t)row_s[h] * slots + c8] = keep[h];
-    }
-    for (int t = unrolled_slabs(kRingQ); t < n_off; ++t) {  // longer tables
-        if (r0 + 15 < p.off[t]) break;
-        fill(0, t);
-        slab(t, p.off[t], sk[0], sv[0]);
+            for (int h = 0; h < 2; ++h)
+                if (row_s[h] < n) pairs[(int64_t)row_s[h] * slots + c8] = keep[h];
+        }
+        for (int t = unrolled_slabs(kRingQ); t < n_off; ++t) {  // longer tables
+            if (r0 + 15 < p.off[t]) break;
+            fill(0, t);
+            slab(t, p.off[t], sk[0], sv[0]);
+        }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
         if (row_s[h] < n) store_chunk<true>(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
+    if constexpr (FRAC) {  // partials [n_off, tiles]: entry t's partials are contiguous
+        __syncthreads();
+        const int t = threadIdx.x;
+        if (t < n_off)
+            p.dd_part[(int64_t)t * (p.bh * nt) + lb] = (dd_s[t] + dd_s[FSA_MAX_OFFSETS + t]) +
+                                                       (dd_s[2 * FSA_MAX_OFFSETS + t] + dd_s[3 * FSA_MAX_OFFSETS + t]);
+    }
+}
+
+// Alpha gradient of the fractional backward, run by one whole workgroup: d(loss)/d(d_t)
+// is the sum of the dQ kernel's per-tile partials of entry t, and d(loss)/d(alpha) =
+// sum_t fbase[t] * d(loss)/d(d_t), since every target distance is alpha times its base
+// value. Wave v sums entries v, v + 4, ... (lanes stride over the tiles, fp64), then one
+// thread forms the outputs in entry order: a fixed order, so the result is reproducible.
+// Entries that no row reaches (trimmed from the table) get 0. `red` holds 48 doubles.
+__device__ void reduce_alpha_grad(const AttnParams &p, double *red) {
+    const int n_tiles = p.bh * ((p.n + 63) >> 6);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int t = wave; t < p.n_off; t += kThreads / 64) {
+        const float *part = p.dd_part + (int64_t)t * n_tiles;
+        double x = 0.0;
+        for (int i = lane; i < n_tiles; i += 64) x += part[i];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+        if (lane == 0) red[t] = x;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double ga = 0.0;
+        for (int t = 0; t < p.n_entries; ++t) {
+            const double tot = t < p.n_off ? red[t] : 0.0;
+            if (p.doffs) p.doffs[t] = static_cast<float>(tot);
+            ga += static_cast<double>(p.fbase[t]) * tot;
+        }
+        p.dalpha[0] = static_cast<float>(ga);
+    }
 }
 
 // dK, dV of key rows [t0, t0 + 64): the band queries [t0, t0 + 128) (Q, dO, LSE, D in
 // LDS) on MFMA first, then the slab queries j + off[t] in the slab layout with the
 // pair weights that bwd_dq_kernel stored.
-template <bool OUT_BF16>
+//
+// With FRAC, key row j receives entry t from two queries: j + off[t], whose key mixes
+// row j with weight 1 - phi (its near word), and j + off[t] + 1, whose key mixes row j
+// with weight phi (its far word).
+template <bool OUT_BF16, bool FRAC>
 __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // band Q rows, then merge areas
@@ -1513,16 +1714,26 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
     __syncthreads();
 
     // slot u: query rows row + off[t] (Q, dO) and their pair weights (word t of each row)
+    // slot u of the ring. FRAC: the ring runs over half entries, 2t (the near queries
+    // j + off[t] with their near words) and 2t + 1 (the far queries j + off[t] + 1 with
+    // their far words)
     SFrag sq[kRingKV], sd[kRingKV];
     uint32_t pw[kRingKV][2];
-    const __amdgpu_buffer_rsrc_t rp = pair_rsrc(p, bh);
     const int slots = pair_slots(n_off);
-    auto fill = [&](int u, int t) {
-        const int iq0 = slab_row(p, t, row_s[0], 1), iq1 = slab_row(p, t, row_s[1], 1);
+    const __amdgpu_buffer_rsrc_t rp =
+        FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, n * slots * 8) : pair_rsrc(p, bh);
+    auto fill = [&](int u, int x) {
+        const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
+        const int iq0 = slab_row(p, t, row_s[0], 1) + far, iq1 = slab_row(p, t, row_s[1], 1) + far;
         sfrag_load(sq[u], rq, iq0, iq1, c8);
         sfrag_load(sd[u], rdo, iq0, iq1, c8);
-        pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, 0);
-        pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, 0);
+        if constexpr (FRAC) {
+            pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq0 * slots + t) * 2 + far) * 4, 0, 0);
+            pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0, 0);
+        } else {
+            pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, 0);
+            pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, 0);
+        }
     };
 #pragma unroll
     for (int u = 0; u < kPreKV; ++u) fill(u, u);
@@ -1592,19 +1803,31 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
             chunk_axpy_words(dk_s[h], x >> 16, x & 0xffff0000u, qt.r[h]);
         }
     };
+    if constexpr (FRAC) {
+        const int n_half = 2 * n_off;
+        for (int x0 = 0; x0 < n_half; x0 += kRingKV) {
+            if (r0 + p.off[x0 >> 1] >= n) break;  // ascending entries: no query row left
 #pragma unroll
-    for (int s0 = 0; s0 < unrolled_slabs(kRingKV); s0 += kRingKV) {
-        if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
-#pragma unroll
-        for (int u = 0; u < kRingKV; ++u) {
-            if (s0 + u < n_off) slab(pw[u], sq[u], sd[u]);  // uniform
-            if (s0 + kRingKV < unrolled_slabs(kRingKV)) fill(u, s0 + u + kRingKV);
+            for (int u = 0; u < kRingKV; ++u) {
+                if (x0 + u < n_half) slab(pw[u], sq[u], sd[u]);          // uniform
+                if (x0 + u + kRingKV < n_half) fill(u, x0 + u + kRingKV);  // uniform
+            }
         }
-    }
-    for (int t = unrolled_slabs(kRingKV); t < n_off; ++t) {  // longer tables
-        if (r0 + p.off[t] >= n) break;
-        fill(0, t);
-        slab(pw[0], sq[0], sd[0]);
+    } else {
+#pragma unroll
+        for (int s0 = 0; s0 < unrolled_slabs(kRingKV); s0 += kRingKV) {
+            if (s0 >= n_off || r0 + p.off[s0] >= n) break;  // ascending offsets: no query row left
+#pragma unroll
+            for (int u = 0; u < kRingKV; ++u) {
+                if (s0 + u < n_off) slab(pw[u], sq[u], sd[u]);  // uniform
+                if (s0 + kRingKV < unrolled_slabs(kRingKV)) fill(u, s0 + u + kRingKV);
+            }
+        }
+        for (int t = unrolled_slabs(kRingKV); t < n_off; ++t) {  // longer tables
+            if (r0 + p.off[t] >= n) break;
+            fill(0, t);
+            slab(pw[0], sq[0], sd[0]);
+        }
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -1613,25 +1836,26 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
             store_chunk<true>(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
         }
     }
+    // FRAC: the dQ kernel, which ran before this one on the stream, left the alpha
+    // gradient's partials; the last tile of head 0, whose keys no later query reaches
+    // through the sparse entries, has the least work and reduces them
+    if constexpr (FRAC) {
+        if (bh == 0 && tile == nt - 1) {  // uniform over the workgroup
+            __syncthreads();              // the LDS tiles are free again
+            reduce_alpha_grad(p, reinterpret_cast<double *>(ta));
+        }
+    }
+}
+
+// The alpha-gradient reduction on its own (an empty problem: writes the zeros).
+__global__ void __launch_bounds__(kThreads) frac_alpha_kernel(const AttnParams p) {
+    __shared__ double red[FSA_MAX_OFFSETS];
+    reduce_alpha_grad(p, red);
 }
 
 // ----------------------------------------------------------------------------
 // decode: the newest query of each sequence against a key/value cache
 // ----------------------------------------------------------------------------
-
-// Sum over lanes l and l ^ 8 (DPP rotation by 8 within each 16-lane row), and over the
-// two halves of a 16-lane row (DPP row mirror).
-constexpr int kDppRowRor8 = 0x128, kDppRowMirror = 0x140;
-__device__ __forceinline__ float xor8_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowRor8, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float xor8_max(float x) {
-    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowRor8, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float row16_sum(float x) {
-    x = row8_sum(x);
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kDppRowMirror, 0xF, 0xF, false));
-}
 
 // One workgroup per (b, h). The newest token of sequence b, at position i = L_b - 1
 // (L_b clamped into [1, lmax]), attends the cached keys i - o for o in {0 .. w-1} and
@@ -1809,8 +2033,8 @@ bool window_path(fsa_dtype_t dt, const AttnParams &p) { return window_path(dt, p
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (window_path(dt, p) && p.scale_log2 > 0.f)  // the window kernel folds a positive scale into exponents
-        return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true>, tiles(p), p, s)
-                                  : launch(&fwd_window_kernel<false>, tiles(p), p, s);
+        return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false>, tiles(p), p, s)
+                                  : launch(&fwd_window_kernel<false, false>, tiles(p), p, s);
     return launch_generic_forward<kWide>(dt, out_dt, p, s);
 }
 
@@ -1842,14 +2066,14 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
     if (window_path(dt, p)) {
         hipError_t e;
         if (with_delta)
-            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true>, tiles(p), p, s)
-                                   : launch(&bwd_dq_kernel<false, true>, tiles(p), p, s);
+            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, false>, tiles(p), p, s)
+                                   : launch(&bwd_dq_kernel<false, true, false>, tiles(p), p, s);
         else
-            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, false>, tiles(p), p, s)
-                                   : launch(&bwd_dq_kernel<false, false>, tiles(p), p, s);
+            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, false, false>, tiles(p), p, s)
+                                   : launch(&bwd_dq_kernel<false, false, false>, tiles(p), p, s);
         if (e != hipSuccess) return e;
-        return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true>, tiles(p), p, s)
-                                  : launch(&bwd_dkdv_kernel<false>, tiles(p), p, s);
+        return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true, false>, tiles(p), p, s)
+                                  : launch(&bwd_dkdv_kernel<false, false>, tiles(p), p, s);
     }
     if (with_delta) {  // the generic kernel reads D: form it first
         const hipError_t e = launch_backward_delta(dt, p, s);
@@ -1860,6 +2084,21 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
                                   : launch(&bwd_generic_kernel<true, false>, tiles(p), p, s);
     return out_dt == FSA_BF16 ? launch(&bwd_generic_kernel<false, true>, tiles(p), p, s)
                               : launch(&bwd_generic_kernel<false, false>, tiles(p), p, s);
+}
+
+hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, true>, tiles(p), p, s)
+                              : launch(&fwd_window_kernel<false, true>, tiles(p), p, s);
+}
+
+hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    if (tiles(p) == 0) return launch(&frac_alpha_kernel, 1, p, s);  // writes the zeros of an empty problem
+    const hipError_t e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, true>, tiles(p), p, s)
+                                            : launch(&bwd_dq_kernel<false, true, true>, tiles(p), p, s);
+    if (e != hipSuccess) return e;
+    // the dK/dV kernel also reduces the alpha gradient
+    return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true, true>, tiles(p), p, s)
+                              : launch(&bwd_dkdv_kernel<false, true>, tiles(p), p, s);
 }
 
 }  // namespace fsa

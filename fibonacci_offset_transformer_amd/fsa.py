@@ -27,7 +27,9 @@ MAX_OFFSETS = 48
 
 # Exported symbols, in the order include/fsa.h declares them.
 EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_workspace_bytes",
-           "fsa_backward_delta", "fsa_backward_grads", "fsa_decode", "fsa_dense_forward", "fsa_last_error")
+           "fsa_backward_delta", "fsa_backward_grads", "fsa_decode", "fsa_dense_forward",
+           "fsa_frac_offsets", "fsa_frac_forward", "fsa_frac_backward", "fsa_frac_backward_workspace_bytes",
+           "fsa_last_error")
 
 
 class FsaError(RuntimeError):
@@ -73,6 +75,18 @@ def library() -> ctypes.CDLL:
             L.fsa_decode.restype = ctypes.c_int
             L.fsa_dense_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp]
             L.fsa_dense_forward.restype = ctypes.c_int
+            L.fsa_frac_offsets.argtypes = [ctypes.c_int, f64, i32, i32, ctypes.POINTER(i32),
+                                           ctypes.POINTER(f32), ctypes.POINTER(i32), i32, ctypes.POINTER(i32)]
+            L.fsa_frac_offsets.restype = ctypes.c_int
+            L.fsa_frac_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                           f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_frac_forward.restype = ctypes.c_int
+            L.fsa_frac_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, u64, i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_frac_backward.restype = ctypes.c_int
+            L.fsa_frac_backward_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64,
+                                                            i32, i32, ctypes.POINTER(u64)]
+            L.fsa_frac_backward_workspace_bytes.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
             L.fsa_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -242,3 +256,73 @@ def dense_forward(q, k, v, *, scale=None, out=None, lse=None, out_dtype=None):
         _check(library().fsa_dense_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
                                            B, H, N, d, _scale(scale, d), _stream(q.device)))
     return o, l
+
+
+# ----------------------------------------------------------------------------
+# learned-alpha variant: fractional entries
+# ----------------------------------------------------------------------------
+
+
+def frac_offsets(alpha: float, w: int, R: int, base: str = "fib") -> list[tuple[int, float, int]]:
+    """Fractional table of one layer: [(floor(d), d - floor(d) as float, F)] (see fsa_frac_offsets)."""
+    L = library()
+    whole = (ctypes.c_int32 * MAX_OFFSETS)()
+    frac = (ctypes.c_float * MAX_OFFSETS)()
+    fb = (ctypes.c_int32 * MAX_OFFSETS)()
+    count = ctypes.c_int32(0)
+    _check(L.fsa_frac_offsets(BASES[base], float(alpha), int(w), int(R), whole, frac, fb, MAX_OFFSETS,
+                              ctypes.byref(count)))
+    return [(int(whole[t]), float(frac[t]), int(fb[t])) for t in range(count.value)]
+
+
+def frac_forward(q, k, v, *, alpha: float, w: int, R: int, base: str = "fib", scale=None, out=None, lse=None,
+                 out_dtype=None):
+    """Learned-alpha forward (interpolated entries): returns (o, lse) like forward()."""
+    B, H, N, d = _shape(q, k, v)
+    o = _out(q, out, out_dtype)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    with torch.cuda.device(q.device):
+        _check(library().fsa_frac_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                          _ptr(l), B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
+                                          int(R), _stream(q.device)))
+    return o, l
+
+
+def frac_workspace_bytes(dtype, B: int, H: int, N: int, d: int = 64, *, alpha: float, w: int, R: int,
+                         base: str = "fib") -> int:
+    """Bytes of workspace fsa_frac_backward needs for this problem."""
+    out = ctypes.c_uint64(0)
+    _check(library().fsa_frac_backward_workspace_bytes(DTYPES[dtype], int(B), int(H), int(N), int(d),
+                                                       BASES[base], float(alpha), int(w), int(R),
+                                                       ctypes.byref(out)))
+    return int(out.value)
+
+
+def frac_backward(q, k, v, o, lse, dout, *, alpha: float, w: int, R: int, base: str = "fib", scale=None,
+                  dq=None, dk=None, dv=None, dalpha=None, doffs=None, ws=None, out_dtype=None):
+    """Learned-alpha backward: returns (dq, dk, dv, dalpha float32 [1], doffs float32 [entries]).
+    ws is the device workspace (allocated here when not given)."""
+    B, H, N, d = _shape(q, k, v, o, dout)
+    dq = _out(q, dq, out_dtype)
+    dk = _out(q, dk, dq.dtype)
+    dv = _out(q, dv, dq.dtype)
+    n_entries = len(frac_offsets(alpha, w, R, base))
+    if dalpha is None:
+        dalpha = torch.empty(1, dtype=torch.float32, device=q.device)
+    if doffs is None:
+        doffs = torch.empty(max(n_entries, 1), dtype=torch.float32, device=q.device)
+    for t, n in ((dalpha, 1), (doffs, n_entries)):
+        if t.dtype != torch.float32 or t.device != q.device or not t.is_contiguous() or t.numel() < n:
+            raise ValueError("dalpha and doffs must be contiguous float32 device tensors of sufficient size")
+    if ws is None:
+        need = frac_workspace_bytes(q.dtype, B, H, N, d, alpha=alpha, w=w, R=R, base=base)
+        ws = torch.empty(max(need // 4, 1), dtype=torch.int32, device=q.device)
+    if not ws.is_cuda or not ws.is_contiguous() or ws.device != q.device:
+        raise ValueError("ws must be a contiguous device tensor on the inputs' device")
+    with torch.cuda.device(q.device):
+        _check(library().fsa_frac_backward(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                           _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dalpha),
+                                           _ptr(doffs), _ptr(ws), ws.numel() * ws.element_size(), B, H, N, d,
+                                           _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                                           _stream(q.device)))
+    return dq, dk, dv, dalpha, doffs[:n_entries]

@@ -205,6 +205,99 @@ fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
                                const void *k, const void *v, void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
                                float scale, void *stream);
 
+/*
+ * Learned-alpha variant: fractional entries.
+ *
+ * With a learned per-layer alpha (page section "Variáveis Experimentais", item
+ * "Aprendido") the targets d = alpha * F are not integers; the model then reads
+ * keys and values linearly interpolated between the two rows around the target
+ * position, so that a gradient reaches alpha (section "Metodologia / Arquitetura",
+ * item "Implementação"). The library's reading of that sentence:
+ *   - d = alpha * F is one IEEE double product, not rounded; entries with d >= w
+ *     are kept (the same threshold as the static table), one per base value, in
+ *     increasing d. Entry t has a = floor(d), phi = d - a.
+ *   - Query row i has entry t when i - d >= 0. Its key is
+ *     (1 - phi) k_{i-a} + phi k_{i-a-1}, its value the same mix of v; every entry
+ *     is one more column of the row's single softmax over window and entries.
+ *   - At alpha * F integral (phi = 0) the entry is the static key i - d, so alpha
+ *     values with integral products reproduce fsa_forward exactly in exact
+ *     arithmetic.
+ *   - The derivative with respect to d is that of the piece [a, a + 1):
+ *     k_{i-a-1} - k_{i-a} (and the same for v); rows without row i - a - 1
+ *     contribute none. d(loss)/d(alpha) = sum_t F_t d(loss)/d(d_t).
+ * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64; other valid
+ * arguments return FSA_E_UNSUPPORTED.
+ */
+
+/*
+ * fsa_frac_offsets - the fractional table of one layer, in host memory.
+ *
+ *   base, alpha, w, R   as in fsa_build_offsets
+ *   whole               receives floor(d) of each entry (int32)
+ *   frac                receives d - floor(d), rounded to float
+ *   base_value          receives the base value F of each entry
+ *   capacity            entries available in each of the three arrays
+ *   count               receives the number of entries (also on FSA_E_CAPACITY)
+ */
+fsa_status_t fsa_frac_offsets(fsa_base_t base, double alpha, int32_t w, int32_t R, int32_t *whole,
+                              float *frac, int32_t *base_value, int32_t capacity, int32_t *count);
+
+/*
+ * fsa_frac_forward - forward of the learned-alpha variant: O and LSE.
+ *
+ * For every (b, h) and row i < N, the columns of row i are the window keys
+ * k_{i-o} (o in 0..w-1, o <= i) and, for each entry t with d_t <= i, the
+ * interpolated key above; s = scale * <q_i, key>, P = softmax over the columns,
+ * o_i = sum P * value (interpolated for the entries), lse_i = ln sum exp(s).
+ * Arithmetic as in fsa_forward (bf16 MFMA window, fp32 dot products for the
+ * entries, each entry's two value weights rounded to bf16). Arguments as in
+ * fsa_forward.
+ */
+fsa_status_t fsa_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                              const void *v, void *o, float *lse, int32_t B, int32_t H, int32_t N, int32_t d,
+                              float scale, fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
+
+/*
+ * fsa_frac_backward - gradients of sum(dO * O) of fsa_frac_forward with respect to
+ * Q, K, V and alpha.
+ *
+ * dQ, dK, dV: the softmax-attention gradient through the interpolation (an entry
+ * column's key and value gradients reach row i - a with weight 1 - phi and row
+ * i - a - 1 with weight phi). dalpha: d(loss)/d(alpha) summed over b, h and rows
+ * (alpha is one scalar per layer), reduced in a fixed order (reproducible).
+ * o and lse must be the outputs of fsa_frac_forward for the same inputs and table.
+ *
+ *   dt, out_dt, q, k, v, o, lse, dout, dq, dk, dv, scale, base, alpha, w, R, stream
+ *                       as in fsa_backward
+ *   dalpha              device float32 [1], 4-byte aligned: receives d(loss)/d(alpha);
+ *                       written also for an empty problem (0)
+ *   doffs               device float32 [count of fsa_frac_offsets], 4-byte aligned,
+ *                       or NULL: receives d(loss)/d(d_t) per entry (0 for entries
+ *                       no row reaches)
+ *   ws                  caller-owned device workspace of at least
+ *                       fsa_frac_backward_workspace_bytes(...) bytes, 16-byte aligned,
+ *                       overwritten; its contents on entry do not matter (it holds D,
+ *                       the near and far bf16 weights of every pair and the per-tile
+ *                       partials of the alpha gradient). May be NULL for an empty problem.
+ *   ws_bytes            size of ws; FSA_E_ARG if smaller than needed
+ */
+fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                               const void *v, const void *o, const float *lse, const void *dout, void *dq,
+                               void *dk, void *dv, float *dalpha, float *doffs, void *ws, uint64_t ws_bytes,
+                               int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base,
+                               double alpha, int32_t w, int32_t R, void *stream);
+
+/*
+ * fsa_frac_backward_workspace_bytes - bytes of ws fsa_frac_backward needs:
+ * 4 B H N (D) + 8 S B H N (two words per pair, S = number of entries some row
+ * reaches, rounded up to a multiple of 8) + 4 B H ceil(N/64) S' (partials, S' the
+ * unrounded count), each part rounded up to 256 bytes. Arguments as in
+ * fsa_frac_backward; *bytes receives the size.
+ */
+fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                                               fsa_base_t base, double alpha, int32_t w, int32_t R,
+                                               uint64_t *bytes);
+
 /* Text describing the calling thread's last non-OK status ("" if none). */
 const char *fsa_last_error(void);
 

@@ -413,8 +413,8 @@ def _virtual_rows(x, d: float):
     return i0, (1.0 - phi) * near + phi * far
 
 
-def frac_probabilities(q, k, entries, w, scale):
-    """P over columns [window offsets 0..w-1, then one column per entry], row max, row sum."""
+def _frac_scores(q, k, entries, w, scale):
+    """Scores over columns [window offsets 0..w-1, then one column per entry], -inf where absent."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     N = q.shape[-2]
@@ -425,7 +425,12 @@ def frac_probabilities(q, k, entries, w, scale):
         i0, kt = _virtual_rows(k, d)
         if kt is not None:
             S[..., i0:, w + m] = scale * np.sum(q[..., i0:, :] * kt, axis=-1)
-    return _softmax_rows(S)
+    return S
+
+
+def frac_probabilities(q, k, entries, w, scale):
+    """P over columns [window offsets 0..w-1, then one column per entry], row max, row sum."""
+    return _softmax_rows(_frac_scores(q, k, entries, w, scale))
 
 
 def frac_forward(q, k, v, entries, w, scale):
@@ -447,7 +452,7 @@ def frac_forward(q, k, v, entries, w, scale):
     return o, mx + np.log(l)
 
 
-def frac_backward(q, k, v, dout, entries, w, scale):
+def frac_backward(q, k, v, dout, entries, w, scale, o=None, lse=None):
     """Gradients of sum(dout * o) for the learned-alpha variant.
 
     Returns (dq, dk, dv, dd) where dd[m] is the derivative with respect to d_m,
@@ -455,15 +460,24 @@ def frac_backward(q, k, v, dout, entries, w, scale):
     sum_m f_m dd[m]. The score and value paths are the textbook softmax-attention
     gradient; an interpolated row passes its gradient to its two source rows with
     the weights (1 - phi) and phi.
+
+    o and lse, when given, are the forward outputs the backward is handed (for
+    instance rounded to a storage type): then P_ij = exp(s_ij - lse_i) and
+    D_i = <dout_i, o_i>, the same formula with those inputs. Otherwise both
+    come from this module's exact forward.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
     N = q.shape[-2]
-    P, _, _ = frac_probabilities(q, k, entries, w, scale)
-    o, _ = frac_forward(q, k, v, entries, w, scale)
-    D = np.sum(dout * o, axis=-1)
+    if lse is None:
+        P, _, _ = frac_probabilities(q, k, entries, w, scale)
+    else:
+        P = np.exp(_frac_scores(q, k, entries, w, scale) - np.asarray(lse, dtype=np.float64)[..., None])
+    if o is None:
+        o, _ = frac_forward(q, k, v, entries, w, scale)
+    D = np.sum(dout * np.asarray(o, dtype=np.float64), axis=-1)
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)

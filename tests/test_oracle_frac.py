@@ -304,3 +304,49 @@ def test_planted_interpolation_mistakes_are_caught(monkeypatch, bad):
     o0, _ = oracle.frac_forward(q, k, v, entries("fib", 1.0, w, R), w, 0.5)
     oe, _ = oracle.frac_forward(q, k, v, entries("fib", 1.0 - 1e-9, w, R), w, 0.5)
     assert np.max(np.abs(oe[:, rows] - o0[:, rows])) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# the backward handed its forward outputs (o, lse)
+# ----------------------------------------------------------------------------
+
+
+def _small_case(seed=50, N=90, alpha=1.27, w=5, R=64):
+    q, k, v, do = (rand((2, N, 8), seed + s) for s in range(4))
+    ds = entries("fib", alpha, w, R)
+    return q, k, v, do, ds, w
+
+
+def test_given_exact_outputs_reproduce_the_backward():
+    q, k, v, do, ds, w = _small_case()
+    o, lse = oracle.frac_forward(q, k, v, ds, w, 0.4)
+    a = oracle.frac_backward(q, k, v, do, ds, w, 0.4)
+    b = oracle.frac_backward(q, k, v, do, ds, w, 0.4, o=o, lse=lse)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) <= 1e-12
+
+
+def test_given_lse_scales_every_gradient():
+    # P = exp(s - lse): adding c to lse multiplies every P and dS, hence every gradient, by exp(-c)
+    q, k, v, do, ds, w = _small_case(60)
+    o, lse = oracle.frac_forward(q, k, v, ds, w, 0.4)
+    a = oracle.frac_backward(q, k, v, do, ds, w, 0.4, o=o, lse=lse)
+    b = oracle.frac_backward(q, k, v, do, ds, w, 0.4, o=o, lse=lse + 0.7)
+    for x, y in zip(a, b):
+        assert np.allclose(y, math.exp(-0.7) * x, rtol=1e-12, atol=1e-13)
+
+
+def test_given_o_enters_through_d_only_and_affinely():
+    # D = <dout, o> enters dS = P (dP - D) linearly: the gradients are affine in o, and move
+    q, k, v, do, ds, w = _small_case(70)
+    o, lse = oracle.frac_forward(q, k, v, ds, w, 0.4)
+    delta = 1e-3 * rand(o.shape, 77)
+    g0 = oracle.frac_backward(q, k, v, do, ds, w, 0.4, o=o, lse=lse)
+    g1 = oracle.frac_backward(q, k, v, do, ds, w, 0.4, o=o + delta, lse=lse)
+    g2 = oracle.frac_backward(q, k, v, do, ds, w, 0.4, o=o + 2 * delta, lse=lse)
+    for n, (a, b, c) in enumerate(zip(g0, g1, g2)):
+        if n != 2:
+            assert np.max(np.abs(b - a)) > 1e-8
+        assert np.allclose(c - a, 2 * (b - a), rtol=1e-7, atol=1e-12)
+    # dV does not involve D
+    assert np.max(np.abs(g1[2] - g0[2])) <= 1e-13
