@@ -13,11 +13,12 @@ query-heads/s (value), algorithmic HBM GB/s of the step, a roofline entry for
 the dominant kernel, the dense causal baseline, and the fp64 CPU oracle timed
 on a bounded sample of the same workload.
 
-The learned-alpha variant (fractional targets, interpolated K/V rows) is timed on
-the same layers next to the static path.
+The learned-alpha variant (fractional targets, interpolated K/V rows) and the
+rotary-embedding variant (unrotated Q, K in) are timed on the same layers next to
+the static path.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-dense] [--no-decode] [--no-frac] [--copy-probe]
+                       [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -253,8 +254,13 @@ def frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
                           base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], dalpha=dalpha[l],
                           doffs=doffs[l], ws=ws)
 
+    def step(l):
+        fwd(l)
+        bwd(l)
+
     fwd_us = stage_us(torch, dev, stream, fwd, reps)
     bwd_us = stage_us(torch, dev, stream, bwd, reps)
+    step_us = stage_us(torch, dev, stream, step, reps)
     entries = [len(fsa.frac_offsets(a, W, R, BASE)) for a in alphas]
     return {
         "what": "learned-alpha variant: fractional targets alpha*F (stagger alphas taken unrounded), "
@@ -266,7 +272,63 @@ def frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
         "static_fwd_us_per_layer": round(static_us["fwd"], 3),
         "static_bwd_us_per_layer": round(static_us["bwd"], 3),
         "fwd_over_static": round(fwd_us / static_us["fwd"], 3),
-        "step_over_static": round((fwd_us + bwd_us) / (static_us["fwd"] + static_us["bwd"]), 3),
+        "bwd_over_static": round(bwd_us / static_us["bwd"], 3),
+        "step_us_per_layer": round(step_us, 3),
+        "static_step_us_per_layer": round(static_us["step"], 3),
+        "step_over_static": round(step_us / static_us["step"], 3),
+    }
+
+
+def rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
+    """Rotary embedding before the attention on the same 16 layers (unrotated Q, K in,
+    gradients with respect to them out): per-layer forward and backward durations
+    next to the static path's, and the rotation pass alone."""
+    table = fsa.rope_table(N, D, device=dev)
+    f_bytes, b_bytes = zip(*(fsa.rope_workspace_bytes(torch.bfloat16, B, H, N, D, alpha=a, w=W, R=R, base=BASE)
+                             for a in alphas))
+    ws = torch.empty(max(b_bytes) // 4 + 1, dtype=torch.int32, device=dev)
+
+    def fwd(l):
+        x = bufs[l]
+        fsa.rope_forward(x["q"], x["k"], x["v"], table, alpha=alphas[l], w=W, R=R, base=BASE, scale=scale,
+                         out=x["o"], lse=x["lse"], ws=ws)
+
+    def bwd(l):
+        x = bufs[l]
+        fsa.rope_backward(x["q"], x["k"], x["v"], table, x["o"], x["lse"], x["do"], alpha=alphas[l], w=W, R=R,
+                          base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], ws=ws)
+
+    def step(l):  # a training step keeps the forward's rotated rows for its backward
+        fwd(l)
+        x = bufs[l]
+        fsa.rope_backward(x["q"], x["k"], x["v"], table, x["o"], x["lse"], x["do"], alpha=alphas[l], w=W, R=R,
+                          base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], ws=ws, reuse_rotated=True)
+
+    def rot(l):
+        x = bufs[l]
+        fsa.rope_rotate(x["q"], table, out=x["dq"])
+
+    fwd_us = stage_us(torch, dev, stream, fwd, reps)
+    bwd_us = stage_us(torch, dev, stream, bwd, reps)
+    step_us = stage_us(torch, dev, stream, step, reps)
+    rot_us = stage_us(torch, dev, stream, rot, reps)
+    rot_bytes = B * H * N * (2 * D * ELEM)  # one tensor: read and write each row (the table stays in L2)
+    return {
+        "what": "rotary embedding before the attention: Q and K rotated once per row into a workspace "
+                "(bf16, as a separate rotation step stores them), the static attention kernels on the "
+                "rotated rows, dQ and dK rotated back in the backward's store",
+        "fwd_us_per_layer": round(fwd_us, 3),
+        "bwd_us_per_layer": round(bwd_us, 3),
+        "static_fwd_us_per_layer": round(static_us["fwd"], 3),
+        "static_bwd_us_per_layer": round(static_us["bwd"], 3),
+        "fwd_over_static": round(fwd_us / static_us["fwd"], 3),
+        "bwd_over_static": round(bwd_us / static_us["bwd"], 3),
+        "step_us_per_layer": round(step_us, 3),
+        "step_note": "forward, then the backward reusing the forward's rotated rows",
+        "static_step_us_per_layer": round(static_us["step"], 3),
+        "step_over_static": round(step_us / static_us["step"], 3),
+        "rotation_us_per_tensor": round(rot_us, 3),
+        "rotation_gb_s": round(rot_bytes / (rot_us * 1e-6) / 1e9, 1),
     }
 
 
@@ -279,6 +341,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frac", action="store_true", help="skip the learned-alpha (fractional) variant")
+    ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding variant")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale reference) and exit")
     args = ap.parse_args()
@@ -358,6 +421,14 @@ def main():
     avg_us = {key: stage_us(torch, dev, stream, fn, reps)
               for key, fn in (("fwd", layer_fwd), ("bwd", layer_bwd))}
     log("average kernel durations (us): " + ", ".join(f"{k}={v:.2f}" for k, v in avg_us.items()))
+
+    def layer_step(l):
+        layer_fwd(l)
+        layer_bwd(l)
+
+    # forward + backward of one layer back to back (the order of a training step, which
+    # finds the layer's rows still in cache): the reference for the variants' steps
+    static_step_us = stage_us(torch, dev, stream, layer_step, reps)
 
     # capture one step as a HIP graph
     side = torch.cuda.Stream(device=dev)
@@ -456,7 +527,13 @@ def main():
 
     learned = None
     if not args.no_frac:
-        learned = frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, avg_us, max(3, args.steps // 5))
+        learned = frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, dict(avg_us, step=static_step_us),
+                             max(3, args.steps // 5))
+
+    rope = None
+    if not args.no_rope:
+        rope = rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, dict(avg_us, step=static_step_us),
+                          max(3, args.steps // 5))
 
     out = {
         "metric": METRIC,
@@ -489,6 +566,7 @@ def main():
         "dense_baseline": dense,
         "decode": decode,
         "learned_alpha": learned,
+        "rope": rope,
     }
     if cpu:
         out["gpu_over_cpu"] = round(out["value"] / cpu["value"], 1)

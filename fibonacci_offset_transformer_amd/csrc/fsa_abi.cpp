@@ -564,6 +564,195 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     return launched(fsa::launch_frac_backward(out_dt, p, static_cast<hipStream_t>(stream)), "fractional backward");
 }
 
+fsa_status_t fsa_rope_table(int32_t n_pos, int32_t d, double rope_base, float *table) {
+    if (n_pos < 0) return fail(FSA_E_ARG, "n_pos must be >= 0 (got %d)", n_pos);
+    if (d < 2 || (d & 1)) return fail(FSA_E_ARG, "d must be even and >= 2 (got %d)", d);
+    if (!std::isfinite(rope_base) || !(rope_base > 0.0))
+        return fail(FSA_E_ARG, "rope_base must be finite and > 0 (got %g)", rope_base);
+    if (n_pos > 0 && !table) return fail(FSA_E_ARG, "table is NULL");
+    const int half = d / 2;
+    for (int m = 0; m < half; ++m) {
+        const double theta = std::pow(rope_base, -2.0 * m / d);
+        for (int32_t pos = 0; pos < n_pos; ++pos) {
+            const double a = pos * theta;
+            table[(static_cast<int64_t>(pos) * half + m) * 2] = static_cast<float>(std::cos(a));
+            table[(static_cast<int64_t>(pos) * half + m) * 2 + 1] = static_cast<float>(std::sin(a));
+        }
+    }
+    return ok();
+}
+
+namespace {
+
+// Rotates `count` bf16 tensors [B*H*N, 64] on the stream (x[t] -> out[t]).
+hipError_t rotate_rows(const void *const *x, void *const *out, int count, const float *rope, int64_t rows,
+                       int32_t n, hipStream_t stream) {
+    fsa::RopeParams rp{};
+    for (int t = 0; t < count; ++t) {
+        rp.x[t] = static_cast<const uint16_t *>(x[t]);
+        rp.out[t] = static_cast<uint16_t *>(out[t]);
+    }
+    rp.table = rope;
+    rp.rows = rows;
+    rp.n = n;
+    rp.count = count;
+    return fsa::launch_rope(rp, stream);
+}
+
+
+// Path checks shared by the fused rotary calls.
+fsa_status_t check_rope_path(fsa_dtype_t dt, int32_t w, int32_t N, float scale, int32_t n_pos) {
+    if (dt != FSA_BF16) return fail(FSA_E_UNSUPPORTED, "the rotary path stores rotated rows in bf16: bf16 inputs only");
+    if (w > 64) return fail(FSA_E_UNSUPPORTED, "the rotary path needs a window w <= 64 (got %d)", w);
+    if (N > (1 << 24)) return fail(FSA_E_UNSUPPORTED, "the rotary path needs N <= 2^24 (got %d)", N);
+    if (!(scale > 0.f)) return fail(FSA_E_UNSUPPORTED, "the rotary path needs a positive scale");
+    if (n_pos < N) return fail(FSA_E_ARG, "the rotary table has %d positions, the sequence %d", n_pos, N);
+    return FSA_OK;
+}
+
+struct RopeLayout {
+    uint64_t qhat, khat, delta, pairs, fwd, bwd;  // byte offsets into ws and the two sizes
+};
+
+RopeLayout rope_layout(int64_t bh, int32_t n, int32_t n_off) {
+    RopeLayout l;
+    const uint64_t rows = static_cast<uint64_t>(bh) * n;
+    l.qhat = 0;
+    l.khat = fsa::align256(rows * 128);
+    l.fwd = l.khat + fsa::align256(rows * 128);
+    l.delta = l.fwd;
+    l.pairs = l.delta + fsa::align256(rows * 4);
+    l.bwd = l.pairs + fsa::align256(4ull * fsa::pair_words(FSA_BF16, 64, n, bh, n_off));
+    return l;
+}
+
+}  // namespace
+
+fsa_status_t fsa_rope_rotate(fsa_dtype_t dt, const void *x, const float *rope, int32_t n_pos, void *out, int32_t B,
+                             int32_t H, int32_t N, int32_t d, void *stream) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, dt, s, 1.0f);
+    if (st != FSA_OK) return st;
+    if (dt != FSA_BF16) return fail(FSA_E_UNSUPPORTED, "rotation is implemented for bf16 rows only");
+    if (N > (1 << 24)) return fail(FSA_E_UNSUPPORTED, "rotation needs N <= 2^24 (got %d)", N);
+    if (n_pos < N) return fail(FSA_E_ARG, "the rotary table has %d positions, the sequence %d", n_pos, N);
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"x", "rope", "out"};
+    const void *ptrs[] = {x, rope, out};
+    if ((st = check_ptrs(names, ptrs, 3)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 2, 3)) != FSA_OK) return st;
+    const void *xs[] = {x};
+    void *outs[] = {out};
+    return launched(rotate_rows(xs, outs, 1, rope, static_cast<int64_t>(B) * H * N, N, static_cast<hipStream_t>(stream)),
+                    "rotary rotation");
+}
+
+fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d, fsa_base_t base,
+                                      double alpha, int32_t w, int32_t R, uint64_t *fwd_bytes, uint64_t *bwd_bytes) {
+    if (!fwd_bytes || !bwd_bytes) return fail(FSA_E_ARG, "fwd_bytes or bwd_bytes is NULL");
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, dt, s, 1.0f);
+    if (st != FSA_OK) return st;
+    int32_t tab[FSA_MAX_OFFSETS];
+    const int n_off = build_table(base, alpha, w, R, tab, &st);
+    if (n_off < 0) return st;
+    if ((st = check_rope_path(dt, w, N, 1.0f, N)) != FSA_OK) return st;
+    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, trim_offsets(tab, n_off, N));
+    *fwd_bytes = static_cast<int64_t>(B) * H * N == 0 ? 0 : l.fwd;
+    *bwd_bytes = static_cast<int64_t>(B) * H * N == 0 ? 0 : l.bwd;
+    return ok();
+}
+
+fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                              const float *rope, int32_t n_pos, void *o, float *lse, void *ws, uint64_t ws_bytes,
+                              int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
+                              int32_t w, int32_t R, void *stream) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
+    if (st != FSA_OK) return st;
+    fsa::AttnParams p{};
+    const int n_off = build_table(base, alpha, w, R, p.off, &st);
+    if (n_off < 0) return st;
+    if ((st = check_rope_path(dt, w, N, scale, n_pos)) != FSA_OK) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "rope", "o", "lse", "ws"};
+    const void *ptrs[] = {q, k, v, rope, o, lse, ws};
+    if ((st = check_ptrs(names, ptrs, 7)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 4, 7)) != FSA_OK) return st;
+    p.n_off = trim_offsets(p.off, n_off, N);
+    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, p.n_off);
+    if (ws_bytes < l.fwd)
+        return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
+                    static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.fwd));
+    char *wsb = static_cast<char *>(ws);
+    const void *xs[] = {q, k};
+    void *hats[] = {wsb + l.qhat, wsb + l.khat};
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = rotate_rows(xs, hats, 2, rope, static_cast<int64_t>(B) * H * N, N, hs);
+    if (e != hipSuccess) return launched(e, "rotary rotation");
+    p.q = hats[0];
+    p.k = hats[1];
+    p.v = v;
+    p.out = o;
+    p.lse_out = lse;
+    p.bh = B * H;
+    p.n = N;
+    p.w = w;
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_forward(dt, out_dt, p, hs), "rotary forward");
+}
+
+fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                               const float *rope, int32_t n_pos, const void *o, const float *lse, const void *dout,
+                               void *dq, void *dk, void *dv, void *ws, uint64_t ws_bytes, int32_t reuse_rotated,
+                               int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
+                               int32_t w, int32_t R, void *stream) {
+    const Shape s{B, H, N, d};
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
+    if (st != FSA_OK) return st;
+    fsa::AttnParams p{};
+    const int n_off = build_table(base, alpha, w, R, p.off, &st);
+    if (n_off < 0) return st;
+    if ((st = check_rope_path(dt, w, N, scale, n_pos)) != FSA_OK) return st;
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "rope", "o", "lse", "dout", "dq", "dk", "dv", "ws"};
+    const void *ptrs[] = {q, k, v, rope, o, lse, dout, dq, dk, dv, ws};
+    if ((st = check_ptrs(names, ptrs, 11)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 7, 11)) != FSA_OK) return st;
+    p.n_off = trim_offsets(p.off, n_off, N);
+    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, p.n_off);
+    if (ws_bytes < l.bwd)
+        return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
+                    static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.bwd));
+    char *wsb = static_cast<char *>(ws);
+    const void *xs[] = {q, k};
+    void *hats[] = {wsb + l.qhat, wsb + l.khat};
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!reuse_rotated) {  // otherwise ws already holds the forward's rotated rows of these q, k
+        const hipError_t e = rotate_rows(xs, hats, 2, rope, static_cast<int64_t>(B) * H * N, N, hs);
+        if (e != hipSuccess) return launched(e, "rotary rotation");
+    }
+    p.q = hats[0];
+    p.k = hats[1];
+    p.v = v;
+    p.o = o;
+    p.lse_in = lse;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.delta = reinterpret_cast<float *>(wsb + l.delta);
+    p.pairs = p.n_off > 0 ? reinterpret_cast<uint32_t *>(wsb + l.pairs) : nullptr;
+    p.rope = rope;
+    p.bh = B * H;
+    p.n = N;
+    p.w = w;
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_backward_grads(dt, out_dt, p, hs, true), "rotary backward");
+}
+
 const char *fsa_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

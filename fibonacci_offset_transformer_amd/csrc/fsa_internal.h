@@ -43,6 +43,22 @@ struct AttnParams {
     float *dalpha;            // backward: d(loss)/d(alpha), one float
     float *doffs;             // backward: d(loss)/d(d_t) per table entry, or null
     int32_t n_entries;        // table entries before trimming (length of doffs)
+    // Rotary embedding: when set, the backward kernels rotate dQ and dK of row r back by
+    // its position's angles before storing them (table [n_pos, 32, 2] of cos, sin).
+    const float *rope;
+};
+
+// Rotary embedding of up to two [rows, 64] bf16 tensors (x[t] -> out[t]); rows come in
+// heads of n, row r sits at position r mod n. table: [n_pos, 32, 2] float32 (cos, sin),
+// n_pos >= n.
+struct RopeParams {
+    const uint16_t *x[2];
+    uint16_t *out[2];
+    const float *table;
+    int64_t rows;
+    int64_t head0;  // first head of the launch (set by the launcher)
+    int32_t n;
+    int32_t count;  // tensors to rotate: 1 or 2
 };
 
 // The bf16 window kernels (w <= 64) address each head with 32-bit byte offsets.
@@ -86,6 +102,7 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
 // Fractional entries (bf16 window path, positive scale): the forward, and the
 // backward (dQ with D, dK/dV, then the reduction of the alpha gradient).
 hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_rope(const RopeParams &p, hipStream_t stream);
 hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 
 }  // namespace fsa

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fsa_internal.h"
 
 namespace fsa {
@@ -667,6 +669,71 @@ __device__ __forceinline__ void c_to_slab(float *area, const f32x4_t acc[4], f32
         for (int b = 0; b < 2; ++b) {
             const f32x4_t x = *reinterpret_cast<const f32x4_t *>(area + row * 64 + 4 * ((2 * c8 + b) ^ row));
             out[h][b] = ADD ? out[h][b] + x : x;
+        }
+    }
+}
+
+// ----------------------------------------------------------------------------
+// rotary position embedding
+// ----------------------------------------------------------------------------
+
+// Channel pair (xe, xo) rotated by the angle whose cosine and sine are (c, s): the
+// even channel becomes fl(c xe - fl(s xo)), the odd one fl(s xe + fl(c xo)) (one fp32
+// product, then one fused multiply-add; fixed so that the stored bf16 values are
+// reproducible).
+__device__ __forceinline__ void rope_pair(float c, float s, float xe, float xo, float &re, float &ro) {
+#pragma clang fp contract(off)
+    const float sx = s * xo, cx = c * xo;
+    re = __builtin_fmaf(c, xe, -sx);
+    ro = __builtin_fmaf(s, xe, cx);
+}
+
+// Rotates bf16 rows into bf16 rows: one thread per 16-byte chunk (channel pairs
+// 4c .. 4c + 3 of one row, eight threads per row), the same chunk of every tensor, so
+// that each table entry is read once. Rows are addressed as (head, position) with
+// blockIdx.y the head, so positions need no division.
+__global__ void __launch_bounds__(kThreads) rope_kernel(const RopeParams p) {
+    const int idx = blockIdx.x * kThreads + threadIdx.x;  // chunk within the head
+    const int pos = idx >> 3, c = idx & 7;
+    if (pos >= p.n) return;
+    const int64_t row = ((int64_t)p.head0 + blockIdx.y) * p.n + pos;
+    const f32x4_t *tab = reinterpret_cast<const f32x4_t *>(p.table + ((int64_t)pos * 32 + 4 * c) * 2);
+    const f32x4_t t01 = tab[0], t23 = tab[1];  // (cos, sin) of pairs 4c, 4c + 1, then 4c + 2, 4c + 3
+    u32x4_t xv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        if (t < p.count)
+            xv[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p.x[t] + row * 64 + 8 * c));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        if (t < p.count) {
+            u32x4_t ov;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const f32x4_t &tt = k < 2 ? t01 : t23;
+                const int j = 2 * (k & 1);
+                float re, ro;
+                rope_pair(tt[j], tt[j + 1], bf16_lo(xv[t][k]), bf16_hi(xv[t][k]), re, ro);
+                ov[k] = pack_bf16(re, ro);
+            }
+            *reinterpret_cast<u32x4_t *>(p.out[t] + row * 64 + 8 * c) = ov;
+        }
+    }
+}
+
+// Rotates a slab-layout gradient chunk (channels 8 c8 .. 8 c8 + 7 of row `row`) back by
+// the row's angles: the transpose of the forward rotation, (e, o) -> (c e + s o, c o - s e).
+__device__ __forceinline__ void rope_back_chunk(const float *table, int row, int c8, f32x4_t a[2]) {
+    const f32x4_t *tab = reinterpret_cast<const f32x4_t *>(table + ((int64_t)row * 32 + 4 * c8) * 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const f32x4_t tt = tab[h];  // pairs 4 c8 + 2h and 4 c8 + 2h + 1
+        f32x4_t &x = a[h];
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            const float c = tt[j], sn = tt[j + 1], e = x[j], o = x[j + 1];
+            x[j] = __builtin_fmaf(c, e, sn * o);
+            x[j + 1] = __builtin_fmaf(c, o, -(sn * e));
         }
     }
 }
@@ -1619,6 +1686,11 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
             slab(t, p.off[t], sk[0], sv[0]);
         }
     }
+    if (p.rope) {  // uniform: gradients with respect to the unrotated rows
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (row_s[h] < n) rope_back_chunk(p.rope, row_s[h], c8, dq_s[h]);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
         if (row_s[h] < n) store_chunk<true>(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
@@ -1828,6 +1900,11 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
             fill(0, t);
             slab(pw[0], sq[0], sd[0]);
         }
+    }
+    if (p.rope) {  // uniform: gradients with respect to the unrotated rows
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if (row_s[h] < n) rope_back_chunk(p.rope, row_s[h], c8, dk_s[h]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -2084,6 +2161,22 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
                                   : launch(&bwd_generic_kernel<true, false>, tiles(p), p, s);
     return out_dt == FSA_BF16 ? launch(&bwd_generic_kernel<false, true>, tiles(p), p, s)
                               : launch(&bwd_generic_kernel<false, false>, tiles(p), p, s);
+}
+
+hipError_t launch_rope(const RopeParams &p, hipStream_t s) {
+    const int64_t chunks = (int64_t)p.n * 8;  // per head
+    const int64_t heads = p.rows / p.n;
+    constexpr int64_t kMaxY = 65535;  // heads per launch (grid y)
+    for (int64_t h0 = 0; h0 < heads; h0 += kMaxY) {
+        const dim3 grid((unsigned)((chunks + kThreads - 1) / kThreads), (unsigned)std::min(kMaxY, heads - h0));
+        RopeParams a = p;
+        a.head0 = h0;
+        void *args[] = {&a};
+        const hipError_t e =
+            hipLaunchKernel(reinterpret_cast<const void *>(&rope_kernel), grid, dim3(kThreads), args, 0, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {

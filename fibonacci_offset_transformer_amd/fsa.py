@@ -29,6 +29,7 @@ MAX_OFFSETS = 48
 EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_workspace_bytes",
            "fsa_backward_delta", "fsa_backward_grads", "fsa_decode", "fsa_dense_forward",
            "fsa_frac_offsets", "fsa_frac_forward", "fsa_frac_backward", "fsa_frac_backward_workspace_bytes",
+           "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
            "fsa_last_error")
 
 
@@ -87,6 +88,19 @@ def library() -> ctypes.CDLL:
             L.fsa_frac_backward_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64,
                                                             i32, i32, ctypes.POINTER(u64)]
             L.fsa_frac_backward_workspace_bytes.restype = ctypes.c_int
+            L.fsa_rope_table.argtypes = [i32, i32, f64, ctypes.POINTER(f32)]
+            L.fsa_rope_table.restype = ctypes.c_int
+            L.fsa_rope_rotate.argtypes = [ctypes.c_int, vp, vp, i32, vp, i32, i32, i32, i32, vp]
+            L.fsa_rope_rotate.restype = ctypes.c_int
+            L.fsa_rope_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64, i32, i32,
+                                                   ctypes.POINTER(u64), ctypes.POINTER(u64)]
+            L.fsa_rope_workspace_bytes.restype = ctypes.c_int
+            L.fsa_rope_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, u64, i32, i32,
+                                           i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_rope_forward.restype = ctypes.c_int
+            L.fsa_rope_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                            u64, i32, i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_rope_backward.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
             L.fsa_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -326,3 +340,88 @@ def frac_backward(q, k, v, o, lse, dout, *, alpha: float, w: int, R: int, base: 
                                            _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
                                            _stream(q.device)))
     return dq, dk, dv, dalpha, doffs[:n_entries]
+
+
+# ----------------------------------------------------------------------------
+# rotary position embedding before the attention
+# ----------------------------------------------------------------------------
+
+
+def rope_table(n_pos: int, d: int = 64, rope_base: float = 10000.0, device=None) -> torch.Tensor:
+    """Rotary table [n_pos, d/2, 2] float32 (cos, sin) built on the host by fsa_rope_table;
+    returned on `device` (host when None)."""
+    host = torch.empty((max(int(n_pos), 0), int(d) // 2, 2), dtype=torch.float32)
+    ptr = ctypes.cast(host.data_ptr(), ctypes.POINTER(ctypes.c_float)) if host.numel() else None
+    _check(library().fsa_rope_table(int(n_pos), int(d), float(rope_base), ptr))
+    return host if device is None else host.to(device)
+
+
+def _table(table, N):
+    if table.dtype != torch.float32 or not table.is_cuda or not table.is_contiguous() or table.dim() != 3:
+        raise ValueError("the rotary table must be a contiguous float32 [n_pos, d/2, 2] device tensor")
+    return int(table.shape[0])
+
+
+def rope_rotate(x, table, *, out=None):
+    """The rotation step alone: bf16 [B,H,N,d] -> bf16 rotated rows."""
+    B, H, N, d = _shape(x)
+    y = _out(x, out, x.dtype)
+    n_pos = _table(table, N)
+    with torch.cuda.device(x.device):
+        _check(library().fsa_rope_rotate(DTYPES[x.dtype], _ptr(x), _ptr(table), n_pos, _ptr(y), B, H, N, d,
+                                         _stream(x.device)))
+    return y
+
+
+def rope_workspace_bytes(dtype, B: int, H: int, N: int, d: int = 64, *, alpha: float = 1.0, w: int, R: int,
+                         base: str = "fib") -> tuple[int, int]:
+    """(forward, backward) workspace bytes of the rotary calls."""
+    f, b = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(library().fsa_rope_workspace_bytes(DTYPES[dtype], int(B), int(H), int(N), int(d), BASES[base],
+                                              float(alpha), int(w), int(R), ctypes.byref(f), ctypes.byref(b)))
+    return int(f.value), int(b.value)
+
+
+def _rope_ws(q, ws, which, alpha, w, R, base):
+    B, H, N, d = q.shape
+    need = rope_workspace_bytes(q.dtype, B, H, N, d, alpha=alpha, w=w, R=R, base=base)[which]
+    if ws is None:
+        ws = torch.empty(max(need // 4, 4), dtype=torch.int32, device=q.device)
+    if not ws.is_cuda or not ws.is_contiguous() or ws.device != q.device:
+        raise ValueError("ws must be a contiguous device tensor on the inputs' device")
+    return ws, ws.numel() * ws.element_size()
+
+
+def rope_forward(q, k, v, table, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None, out=None,
+                 lse=None, out_dtype=None, ws=None):
+    """Forward on rotated Q, K (unrotated inputs, rotary table on the device): (o, lse)."""
+    B, H, N, d = _shape(q, k, v)
+    o = _out(q, out, out_dtype)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    n_pos = _table(table, N)
+    ws, ws_bytes = _rope_ws(q, ws, 0, alpha, w, R, base)
+    with torch.cuda.device(q.device):
+        _check(library().fsa_rope_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(table),
+                                          n_pos, _ptr(o), _ptr(l), _ptr(ws), ws_bytes, B, H, N, d, _scale(scale, d),
+                                          BASES[base], float(alpha), int(w), int(R), _stream(q.device)))
+    return o, l
+
+
+def rope_backward(q, k, v, table, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
+                  scale=None, dq=None, dk=None, dv=None, out_dtype=None, ws=None, reuse_rotated: bool = False):
+    """Backward of rope_forward: (dq, dk, dv) with respect to the unrotated inputs. With
+    reuse_rotated, ws must still hold the rotated rows rope_forward wrote for these q, k."""
+    if reuse_rotated and ws is None:
+        raise ValueError("reuse_rotated needs the forward's workspace")
+    B, H, N, d = _shape(q, k, v, o, dout)
+    dq = _out(q, dq, out_dtype)
+    dk = _out(q, dk, dq.dtype)
+    dv = _out(q, dv, dq.dtype)
+    n_pos = _table(table, N)
+    ws, ws_bytes = _rope_ws(q, ws, 1, alpha, w, R, base)
+    with torch.cuda.device(q.device):
+        _check(library().fsa_rope_backward(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(table),
+                                           n_pos, _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                           _ptr(ws), ws_bytes, int(bool(reuse_rotated)), B, H, N, d, _scale(scale, d),
+                                           BASES[base], float(alpha), int(w), int(R), _stream(q.device)))
+    return dq, dk, dv

@@ -298,6 +298,108 @@ fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_
                                                fsa_base_t base, double alpha, int32_t w, int32_t R,
                                                uint64_t *bytes);
 
+/*
+ * Rotary position embedding before the attention.
+ *
+ * The pages rotate queries and keys with rotary position embeddings before the
+ * rows are gathered, vanilla RoPE without scaling (section "Metodologia /
+ * Arquitetura", item "Implementação", and the limitations paragraph). The
+ * library's reading: channel pairs (2m, 2m + 1) of a row at position p (the row
+ * index) are rotated by the angle p * theta_m, theta_m = rope_base^(-2m/d) (10000
+ * for vanilla RoPE); values are not rotated.
+ *
+ * The rotated rows enter the attention in bf16, as a separate rotation step would
+ * store them. Each rotated value is fixed exactly: with (c, s) the table entries,
+ * channel 2m becomes fma(c, x_2m, -(s * x_2m+1)) and channel 2m + 1 becomes
+ * fma(s, x_2m, c * x_2m+1) in float32, then each is rounded to bf16 (nearest, ties
+ * to even). The attention over the rotated rows is fsa_forward / fsa_backward's.
+ * The backward returns gradients with respect to the unrotated Q and K: the
+ * rotated-row gradients rotated back by each row's angles (the transpose), with the
+ * bf16 rounding passing gradients unchanged.
+ *
+ * Each key row is gathered by about |T| + 2 query tiles, so the calls rotate Q and
+ * K once per row into a workspace (one memory-bound pass) instead of once per
+ * gather; the backward's inverse rotation is fused into the store of dQ and dK.
+ * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64; other valid
+ * arguments return FSA_E_UNSUPPORTED.
+ */
+
+/*
+ * fsa_rope_table - the rotary table, in host memory: table[(p * d/2 + m) * 2] =
+ * cos(p * theta_m) and table[... + 1] = sin(p * theta_m), each computed in double
+ * precision with the C library's cos and sin and rounded once to float32, for
+ * p = 0 .. n_pos - 1 and m = 0 .. d/2 - 1. Copy it to the device for the calls below.
+ *
+ *   n_pos       positions, >= 0 (at least N of the calls that use the table)
+ *   d           head size, even, >= 2
+ *   rope_base   frequency base, finite, > 0 (10000: vanilla RoPE)
+ *   table       host float32 array of n_pos * d floats (NULL allowed when n_pos = 0)
+ */
+fsa_status_t fsa_rope_table(int32_t n_pos, int32_t d, double rope_base, float *table);
+
+/*
+ * fsa_rope_rotate - the rotation step on its own: out = the rotated rows of x,
+ * bf16 [B,H,N,d] -> bf16 [B,H,N,d] (exactly as described above; row i of each head
+ * at position i).
+ *
+ *   dt          FSA_BF16 (FSA_F32 returns FSA_E_UNSUPPORTED)
+ *   x, out      device [B,H,N,d], 16-byte aligned, out must not alias x
+ *   rope        device copy of fsa_rope_table(n_pos, d, ...), 16-byte aligned
+ *   n_pos       positions in the table, >= N
+ *   N           <= 2^24 (larger returns FSA_E_UNSUPPORTED)
+ */
+fsa_status_t fsa_rope_rotate(fsa_dtype_t dt, const void *x, const float *rope, int32_t n_pos, void *out, int32_t B,
+                             int32_t H, int32_t N, int32_t d, void *stream);
+
+/*
+ * fsa_rope_workspace_bytes - bytes of ws the rotary forward and backward need:
+ * forward 2 B H N d * 2 (the rotated Q and K, each part rounded up to 256 bytes);
+ * backward that plus 4 B H N (D) plus fsa_backward_workspace_bytes' pair words.
+ * Arguments as in fsa_rope_forward; 0 and 0 for an empty problem.
+ */
+fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d, fsa_base_t base,
+                                      double alpha, int32_t w, int32_t R, uint64_t *fwd_bytes, uint64_t *bwd_bytes);
+
+/*
+ * fsa_rope_forward - fsa_forward on the rotated Q and K: O and LSE.
+ *
+ *   q, k, v         unrotated inputs [B,H,N,d] (bf16)
+ *   rope, n_pos     device rotary table (fsa_rope_table) and its positions, n_pos >= N
+ *   o, lse          outputs as in fsa_forward
+ *   ws, ws_bytes    caller-owned device workspace of at least the forward size of
+ *                   fsa_rope_workspace_bytes, 16-byte aligned, overwritten (holds
+ *                   the rotated Q and K)
+ *   other arguments as in fsa_forward
+ */
+fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                              const float *rope, int32_t n_pos, void *o, float *lse, void *ws, uint64_t ws_bytes,
+                              int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
+                              int32_t w, int32_t R, void *stream);
+
+/*
+ * fsa_rope_backward - gradients of sum(dO * O) of fsa_rope_forward with respect to
+ * the unrotated Q and K, and V. o and lse must be fsa_rope_forward's outputs for
+ * the same inputs, table and offsets.
+ *
+ *   q, k, v, rope, n_pos   as in fsa_rope_forward
+ *   o, lse, dout           as in fsa_backward
+ *   dq, dk, dv             outputs [B,H,N,d] in out_dt
+ *   ws, ws_bytes           caller-owned device workspace of at least the backward size
+ *                          of fsa_rope_workspace_bytes, 16-byte aligned, overwritten
+ *   reuse_rotated          0: the call rotates q and k itself, and the contents of ws on
+ *                          entry do not matter. Nonzero: ws's first forward-size bytes
+ *                          still hold the rotated rows fsa_rope_forward wrote there for
+ *                          these same q, k and table (the activations a training step
+ *                          keeps for its backward); the rotation is skipped. Nothing
+ *                          checks this: other contents give wrong gradients.
+ *   other arguments as in fsa_backward
+ */
+fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                               const float *rope, int32_t n_pos, const void *o, const float *lse, const void *dout,
+                               void *dq, void *dk, void *dv, void *ws, uint64_t ws_bytes, int32_t reuse_rotated,
+                               int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
+                               int32_t w, int32_t R, void *stream);
+
 /* Text describing the calling thread's last non-OK status ("" if none). */
 const char *fsa_last_error(void);
 

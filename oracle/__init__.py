@@ -18,6 +18,14 @@ from .fsa_ref import (  # noqa: F401
     frac_probabilities,
     offset_table,
     pow2_base,
+    rope_angles,
+    rope_rotate,
+    rope_sparse_backward,
+    rope_sparse_backward_rows,
+    rope_sparse_forward,
+    rope_sparse_forward_rows,
+    rope_store_bf16,
+    rope_table_f32,
     round_half_away,
     round_half_even,
     sparse_backward,

@@ -192,7 +192,7 @@ def sparse_forward(q, k, v, T, w, scale):
     return o, mx + np.log(l)
 
 
-def sparse_backward(q, k, v, dout, T, w, scale):
+def sparse_backward(q, k, v, dout, T, w, scale, o=None, lse=None):
     """Gradients of sum(dout * o) with respect to q, k, v.
 
     Textbook softmax-attention gradient restricted to the mask:
@@ -201,6 +201,10 @@ def sparse_backward(q, k, v, dout, T, w, scale):
       dV_j = sum_i P_ij dO_i, all sums over pairs with j in J(i).
     The pages describe training through this mask ([EXPL-pt] Metodologia) but
     print no gradient, so this is the plain derivative of the forward above.
+    o and lse, when given, are the forward outputs the backward is handed (for
+    instance rounded to a storage type): then P_ij = exp(s_ij - lse_i) and
+    D_i = <dout_i, o_i>, the same formula with those inputs. Otherwise both come
+    from this module's exact forward.
     Returns (dq, dk, dv) in float64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -208,9 +212,12 @@ def sparse_backward(q, k, v, dout, T, w, scale):
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
     offs, P, _, _ = sparse_probabilities(q, k, T, w, scale)
-    o, _ = sparse_forward(q, k, v, T, w, scale)
+    if lse is not None:
+        P = np.exp(_scores(q, k, offs, scale) - np.asarray(lse, dtype=np.float64)[..., None])
+    if o is None:
+        o, _ = sparse_forward(q, k, v, T, w, scale)
     N = q.shape[-2]
-    D = np.sum(dout * o, axis=-1)
+    D = np.sum(dout * np.asarray(o, dtype=np.float64), axis=-1)
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
@@ -607,3 +614,134 @@ def frac_backward_rows(q, k, v, dout, entries, w, scale, rows):
         dks.append(dk_r)
         dvs.append(dv_r)
     return np.stack(dqs, axis=-2), np.stack(dks, axis=-2), np.stack(dvs, axis=-2)
+
+
+# ----------------------------------------------------------------------------
+# Rotary position embedding applied before the attention
+# ----------------------------------------------------------------------------
+#
+# [EXPL-pt] Metodologia / Arquitetura, item "Implementação": rotary position
+# embeddings are applied to queries and keys before the rows are gathered;
+# [EXPL-pt] Limitações: the models use vanilla RoPE without scaling. The pages give
+# no formula; the readings here are the original rotary formulation:
+#   * channel pairs (2m, 2m + 1), m = 0 .. d/2 - 1, with frequency
+#     theta_m = base^(-2m/d), base = 10000 (no scaling);
+#   * the position of row i is i, for queries and keys alike;
+#   * pair m of a row at position p is rotated by the angle p * theta_m;
+#   * values are not rotated; the backward returns gradients with respect to the
+#     unrotated Q and K.
+# The rotated rows are handed to the attention in the input's storage type, as a
+# separate rotation step would store them (rope_store_bf16): that rounding is a
+# decision of the method's data path, so the oracle takes it in the same precision
+# as the library (an fp32 table of cos/sin, two fp32 operations per channel, round
+# to nearest even).
+
+
+def rope_angles(n_pos: int, d: int, base: float = 10000.0):
+    """angle[p, m] = p * base^(-2m/d) in fp64, shape [n_pos, d/2]."""
+    m = np.arange(d // 2, dtype=np.float64)
+    theta = base ** (-2.0 * m / d)
+    return np.arange(n_pos, dtype=np.float64)[:, None] * theta[None, :]
+
+
+def rope_rotate(x, base: float = 10000.0, inverse: bool = False):
+    """Rotates pair m of row p of x [..., N, d] by p * theta_m (by the negative angle
+    when inverse, which is the transpose of the rotation), exactly in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    N, d = x.shape[-2], x.shape[-1]
+    ang = rope_angles(N, d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    if inverse:
+        s = -s
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = xe * c - xo * s
+    out[..., 1::2] = xe * s + xo * c
+    return out
+
+
+def rope_table_f32(n_pos: int, d: int, base: float = 10000.0):
+    """[n_pos, d/2, 2] float32 table of (cos, sin) of p * theta_m: each value computed
+    in fp64 with the C library's cos and sin (Python's math module) and rounded once."""
+    out = np.empty((n_pos, d // 2, 2), dtype=np.float32)
+    for m in range(d // 2):
+        theta = base ** (-2.0 * m / d)
+        for pos in range(n_pos):
+            a = pos * theta
+            out[pos, m, 0] = math.cos(a)
+            out[pos, m, 1] = math.sin(a)
+    return out
+
+
+def rope_store_bf16(x, base: float = 10000.0, table=None):
+    """Rotated rows of x [..., N, d] as a rotation step that stores bf16 produces them:
+    with c, s the float32 table entries, channel 2m becomes fl(c x_2m - fl(s x_2m+1))
+    and channel 2m + 1 becomes fl(s x_2m + fl(c x_2m+1)) (fl = float32 rounding), then
+    each value is rounded to bfloat16 (nearest, ties to even; torch's conversion).
+    Every product of a float32 and a bf16 value and every difference here is exact in
+    fp64 before its single rounding, so fp64 arithmetic with explicit float32 casts
+    reproduces the float32 steps. Returns the bf16 values as float64."""
+    import torch
+
+    x = np.asarray(x, dtype=np.float64)
+    N, d = x.shape[-2], x.shape[-1]
+    tab = rope_table_f32(N, d, base) if table is None else table[:N]
+    c = tab[..., 0].astype(np.float64)
+    s = tab[..., 1].astype(np.float64)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    f32 = lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)
+    re = f32(c * xe - f32(s * xo))
+    ro = f32(s * xe + f32(c * xo))
+    out = np.empty_like(x)
+    out[..., 0::2] = re
+    out[..., 1::2] = ro
+    return torch.from_numpy(out.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def rope_sparse_forward(q, k, v, T, w, scale, base: float = 10000.0, stored: bool = False, table=None):
+    """sparse_forward on rotated queries and keys (rounded to bf16 as stored when
+    `stored`, exact otherwise)."""
+    if stored:
+        return sparse_forward(rope_store_bf16(q, base, table), rope_store_bf16(k, base, table), v, T, w, scale)
+    return sparse_forward(rope_rotate(q, base), rope_rotate(k, base), v, T, w, scale)
+
+
+def rope_sparse_backward(q, k, v, dout, T, w, scale, base: float = 10000.0, stored: bool = False, table=None,
+                         o=None, lse=None):
+    """Gradients of sum(dout * o) of rope_sparse_forward with respect to the unrotated
+    q, k and v: the rotated-input gradients carried back through the transposed
+    rotation (chain rule through a linear map; the storage rounding, when `stored`,
+    passes gradients unchanged, as a separate rotation step's backward would).
+    o and lse, when given, are the forward outputs handed to the backward (see
+    sparse_backward)."""
+    if stored:
+        qr, kr = rope_store_bf16(q, base, table), rope_store_bf16(k, base, table)
+    else:
+        qr, kr = rope_rotate(q, base), rope_rotate(k, base)
+    dq, dk, dv = sparse_backward(qr, kr, v, dout, T, w, scale, o=o, lse=lse)
+    return rope_rotate(dq, base, inverse=True), rope_rotate(dk, base, inverse=True), dv
+
+
+def _rotate_rows_back(x, rows, N, d, base):
+    ang = rope_angles(N, d, base)[np.asarray(rows)]
+    c, s = np.cos(ang), -np.sin(ang)
+    out = np.empty_like(x)
+    out[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    out[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return out
+
+
+def rope_sparse_forward_rows(q, k, v, T, w, scale, rows, base: float = 10000.0, stored: bool = False,
+                             table=None):
+    """Rows of rope_sparse_forward."""
+    rot = (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
+    return sparse_forward_rows(rot(q), rot(k), v, T, w, scale, rows)
+
+
+def rope_sparse_backward_rows(q, k, v, dout, T, w, scale, rows, base: float = 10000.0, stored: bool = False,
+                              table=None):
+    """Rows of rope_sparse_backward."""
+    N, d = np.asarray(q).shape[-2], np.asarray(q).shape[-1]
+    rot = (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
+    dq, dk, dv = sparse_backward_rows(rot(q), rot(k), v, dout, T, w, scale, rows)
+    return _rotate_rows_back(dq, rows, N, d, base), _rotate_rows_back(dk, rows, N, d, base), dv

@@ -1,0 +1,192 @@
+"""GPU parity of the rotary path (Q and K rotated before the attention) through the
+C ABI, against the fp64 oracle.
+
+Bars: the rotation step bit-exact (it is a rounding to bf16 that both sides take
+in the same float32 steps from the same table); O, LSE, dQ, dK, dV within max-abs
+1e-2 of the oracle's attention over the same stored rotated rows, with gradients
+carried back to the unrotated rows.
+
+The backward is a function of (q, k, v, o, lse, dO). The exhaustive small cases
+hand it the oracle's own O (rounded to bf16) and LSE (rounded to fp32) and compare
+with the oracle's backward of those same inputs (P = exp(s - lse), D = <dO, o>).
+The full-size layers run end to end (the GPU forward's O and LSE feed the GPU
+backward): there D also carries the rounding of O to bf16, which at w = 64 stays
+well inside the bar (at w = 1, where a row mixes only a few values, it reaches
+about 0.012 on dQ by itself)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fibonacci_offset_transformer_amd import fsa, schedules, synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def inputs(workload, layer, shape, grad=False):
+    t = synth.layer_inputs(workload, layer, shape, torch.bfloat16, with_grad=grad)
+    return {k: v.to(dev()) for k, v in t.items()}
+
+
+def check(name, gpu, ref, tol=TOL):
+    err = float(np.max(np.abs(synth.as_f64(gpu) - ref))) if ref.size else 0.0
+    note(f"  {name}: max|err|={err:.3e} max|ref|={float(np.max(np.abs(ref))) if ref.size else 0:.3f} tol={tol}")
+    assert err <= tol, (name, err)
+
+
+@pytest.mark.parametrize("B,H,N,n_pos", [(1, 1, 1, 1), (2, 3, 77, 100), (1, 2, 4096, 4096), (2, 1, 1000, 5000)])
+def test_rotation_bit_exact(B, H, N, n_pos):
+    x = inputs(60, 0, (B, H, N, 64))["q"]
+    table = fsa.rope_table(n_pos, device=dev())
+    y = fsa.rope_rotate(x, table)
+    torch.cuda.synchronize()
+    want = oracle.rope_store_bf16(synth.as_f64(x), table=oracle.rope_table_f32(n_pos, 64))
+    got = synth.as_f64(y)
+    bad = int(np.sum(got != want))
+    note(f"rotation B={B} H={H} N={N}: {bad} of {got.size} values differ")
+    assert bad == 0
+
+
+def rope_fwd_case(workload, B, H, N, base, alpha, w, R, heads=None, layer=0, scale=0.125, n_pos=None):
+    x = inputs(workload, layer, (B, H, N, 64))
+    table = fsa.rope_table(n_pos or N, device=dev())
+    note(f"rope forward wl={workload} layer={layer} B={B} H={H} N={N} base={base} alpha={alpha} w={w} R={R}")
+    kw = dict(alpha=alpha, w=w, R=R, base=base, scale=scale)
+    o, lse = fsa.rope_forward(x["q"], x["k"], x["v"], table, out_dtype=torch.float32, **kw)
+    o_lo, lse_lo = fsa.rope_forward(x["q"], x["k"], x["v"], table, out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lo, o.to(torch.bfloat16)) and torch.equal(lse_lo, lse)
+    T = oracle.offset_table(base, alpha, w, R)
+    sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in sel:
+        q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.rope_sparse_forward(q, k, v, T, w, scale, stored=True)
+        check(f"o[{b},{h}]", o[b, h], ro)
+        check(f"lse[{b},{h}]", lse[b, h], rl)
+    return x, table, o_lo, lse
+
+
+def rope_bwd_case(workload, B, H, N, base, alpha, w, R, heads=None, layer=0, scale=0.125, given=True):
+    """given: the backward gets the oracle's O (bf16) and LSE (fp32); otherwise the GPU forward's."""
+    x = inputs(workload, layer, (B, H, N, 64), grad=True)
+    table = fsa.rope_table(N, device=dev())
+    note(f"rope backward ({'oracle-made O/LSE' if given else 'end to end'}) wl={workload} layer={layer} "
+         f"B={B} H={H} N={N} base={base} alpha={alpha} w={w} R={R}")
+    kw = dict(alpha=alpha, w=w, R=R, base=base, scale=scale)
+    T = oracle.offset_table(base, alpha, w, R)
+    if given:
+        o_ref, lse_ref = np.zeros((B, H, N, 64)), np.zeros((B, H, N))
+        for b in range(B):
+            for h in range(H):
+                q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
+                o_ref[b, h], lse_ref[b, h] = oracle.rope_sparse_forward(q, k, v, T, w, scale, stored=True)
+        o_c = torch.from_numpy(o_ref).to(torch.bfloat16)
+        lse_c = torch.from_numpy(lse_ref).to(torch.float32)
+        o, lse = o_c.to(dev()), lse_c.to(dev())
+        o_g, lse_g = synth.as_f64(o_c), synth.as_f64(lse_c)
+    else:
+        o, lse = fsa.rope_forward(x["q"], x["k"], x["v"], table, **kw)
+    g = fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], out_dtype=torch.float32, **kw)
+    g_lo = fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], out_dtype=torch.bfloat16, **kw)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), g_lo, g):
+        assert torch.equal(a, b.to(torch.bfloat16)), name
+    sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in sel:
+        q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
+        extra = dict(o=o_g[b, h], lse=lse_g[b, h]) if given else {}
+        rq, rk, rv = oracle.rope_sparse_backward(q, k, v, do, T, w, scale, stored=True, **extra)
+        check(f"dq[{b},{h}]", g[0][b, h], rq)
+        check(f"dk[{b},{h}]", g[1][b, h], rk)
+        check(f"dv[{b},{h}]", g[2][b, h], rv)
+
+
+SMALL = [
+    (1, "fib", 1.0, 16, 256),
+    (17, "fib", 1.0, 16, 256),
+    (100, "fib", 1.0, 6, 256),
+    (300, "fib", 1.5, 12, 256),
+    (300, "fib", 1.0, 64, 1024),
+    (300, "pow2", 1.0, 10, 1024),
+    (257, "fib", 1.0, 1, 1024),
+    (1100, "fib", 1.0, 6, 1024),
+]
+
+
+@pytest.mark.parametrize("N,base,alpha,w,R", SMALL)
+def test_rope_forward_small(N, base, alpha, w, R):
+    rope_fwd_case(61, 2, 2, N, base, alpha, w, R)
+
+
+@pytest.mark.parametrize("N,base,alpha,w,R", SMALL)
+def test_rope_backward_small(N, base, alpha, w, R):
+    rope_bwd_case(62, 2, 2, N, base, alpha, w, R)
+
+
+def test_rope_full_size_stagger_layers():
+    alphas = schedules.linear_stagger(16)
+    rng = np.random.default_rng(63)
+    for l in (0, 7, 15):
+        b, h = int(rng.integers(0, 2)), int(rng.integers(0, 8))
+        rope_fwd_case(63, 2, 8, 4096, "fib", alphas[l], 64, 1024, heads=[(b, h)], layer=l, n_pos=8192)
+        rope_bwd_case(63, 2, 8, 4096, "fib", alphas[l], 64, 1024, heads=[(b, h)], layer=l, given=False)
+
+
+def test_fused_forward_equals_rotate_then_forward():
+    # the rotated rows the fused call hands to the attention are the rotation step's
+    x = inputs(64, 0, (2, 4, 900, 64), grad=True)
+    table = fsa.rope_table(900, device=dev())
+    kw = dict(alpha=1.3, w=64, R=1024, scale=0.125)
+    o1, l1 = fsa.rope_forward(x["q"], x["k"], x["v"], table, **kw)
+    qr, kr = fsa.rope_rotate(x["q"], table), fsa.rope_rotate(x["k"], table)
+    o2, l2 = fsa.forward(qr, kr, x["v"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_rope_workspace_contents_do_not_matter_and_deterministic():
+    x = inputs(65, 0, (1, 2, 777, 64), grad=True)
+    table = fsa.rope_table(777, device=dev())
+    kw = dict(alpha=0.75, w=64, R=1024, scale=0.125)
+    o, lse = fsa.rope_forward(x["q"], x["k"], x["v"], table, **kw)
+    need = fsa.rope_workspace_bytes(torch.bfloat16, 1, 2, 777, alpha=0.75, w=64, R=1024)[1]
+    runs = []
+    for fill in (0, 0x7FC07FC0, -1):
+        ws = torch.full((need // 4 + 64,), fill, dtype=torch.int32, device=dev())
+        runs.append(fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], ws=ws,
+                                      out_dtype=torch.float32, **kw))
+    torch.cuda.synchronize()
+    for other in runs[1:]:
+        for a, b in zip(runs[0], other):
+            assert torch.equal(a, b)
+    assert all(bool(torch.isfinite(t).all()) for t in runs[0])
+
+
+def test_backward_reusing_the_forward_rotation_is_identical():
+    x = inputs(66, 0, (2, 3, 1234, 64), grad=True)
+    table = fsa.rope_table(1234, device=dev())
+    kw = dict(alpha=1.17, w=64, R=1024, scale=0.125)
+    need = fsa.rope_workspace_bytes(torch.bfloat16, 2, 3, 1234, alpha=1.17, w=64, R=1024)[1]
+    ws = torch.empty(need // 4 + 1, dtype=torch.int32, device=dev())
+    o, lse = fsa.rope_forward(x["q"], x["k"], x["v"], table, ws=ws, **kw)
+    g1 = fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], ws=ws, reuse_rotated=True, **kw)
+    g2 = fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], **kw)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

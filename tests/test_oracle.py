@@ -414,3 +414,42 @@ def test_planted_rounding_mistake_is_caught():
         if floor_table != independent_table("fib", a, 64, 1024):
             return
     pytest.fail("floor rounding was never distinguished")
+
+
+# ----------------------------------------------------------------------------
+# the backward handed its forward outputs (o, lse)
+# ----------------------------------------------------------------------------
+
+
+def test_given_exact_outputs_reproduce_the_backward():
+    N, d, T, w = 90, 8, [8, 13, 21, 34], 5
+    q, k, v, do = (rand((2, N, d), s) for s in (80, 81, 82, 83))
+    o, lse = oracle.sparse_forward(q, k, v, T, w, 0.4)
+    a = oracle.sparse_backward(q, k, v, do, T, w, 0.4)
+    b = oracle.sparse_backward(q, k, v, do, T, w, 0.4, o=o, lse=lse)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) <= 1e-12
+
+
+def test_given_lse_scales_every_gradient():
+    # P = exp(s - lse): adding c to lse multiplies every P and dS, hence every gradient, by exp(-c)
+    N, d, T, w = 70, 8, [8, 13, 21], 4
+    q, k, v, do = (rand((2, N, d), s) for s in (84, 85, 86, 87))
+    o, lse = oracle.sparse_forward(q, k, v, T, w, 0.4)
+    a = oracle.sparse_backward(q, k, v, do, T, w, 0.4, o=o, lse=lse)
+    b = oracle.sparse_backward(q, k, v, do, T, w, 0.4, o=o, lse=lse - 0.3)
+    for x, y in zip(a, b):
+        assert np.allclose(y, math.exp(0.3) * x, rtol=1e-12, atol=1e-13)
+
+
+def test_given_o_enters_through_d_only_and_affinely():
+    N, d, T, w = 70, 8, [8, 13, 21], 4
+    q, k, v, do = (rand((2, N, d), s) for s in (88, 89, 90, 91))
+    o, lse = oracle.sparse_forward(q, k, v, T, w, 0.4)
+    delta = 1e-3 * rand(o.shape, 92)
+    g0, g1, g2 = (oracle.sparse_backward(q, k, v, do, T, w, 0.4, o=o + c * delta, lse=lse) for c in (0, 1, 2))
+    for n, (a, b, c) in enumerate(zip(g0, g1, g2)):
+        if n != 2:
+            assert np.max(np.abs(b - a)) > 1e-8
+        assert np.allclose(c - a, 2 * (b - a), rtol=1e-7, atol=1e-12)
+    assert np.max(np.abs(g1[2] - g0[2])) <= 1e-13  # dV does not involve D
