@@ -18,7 +18,8 @@ rotary-embedding variant (unrotated Q, K in) are timed on the same layers next t
 the static path.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--copy-probe]
+                       [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--no-literal]
+                       [--cold] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -66,6 +67,18 @@ def alg_bytes_per_row():
         "bwd": 8 * row + 4,
         "step": 12 * row + 8,
     }
+
+
+def band_keys_per_head():
+    """Sum over rows of the window keys a row attends, min(i + 1, w)."""
+    return sum(min(i + 1, W) for i in range(N))
+
+
+def band_flops_per_layer():
+    """Useful window-band flops per layer: forward 2 products (scores, P.V), backward 5
+    (scores, dP, dV, dQ, dK), 2 d flops each per (query, key) pair."""
+    pairs = B * H * band_keys_per_head()
+    return {"fwd": 4 * D * pairs, "bwd": 10 * D * pairs}
 
 
 def dense_flops_per_layer():
@@ -200,8 +213,28 @@ def decode_bench(fsa, torch, dev, stream):
             run()
         e1.record(stream)
         torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / reps
+        # device time: the steps captured back to back in a HIP graph (no host launch gaps)
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                run()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
+        del g
         res[name] = {"window": w, "keys_per_query": keys, "us_per_step": round(us, 2),
+                     "us_per_step_eager": round(eager_us, 2),
                      "algorithmic_bytes": step_bytes, "gb_s": round(step_bytes / (us * 1e-6) / 1e9, 1)}
     res["dense_over_sparse_time"] = round(res["dense"]["us_per_step"] / res["sparse"]["us_per_step"], 2)
     return res
@@ -342,6 +375,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frac", action="store_true", help="skip the learned-alpha (fractional) variant")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding variant")
+    ap.add_argument("--no-literal", action="store_true",
+                    help="skip the run with the literal stagger formula 0.5 + l*(1.5/15)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time single steps after writing 1 GiB of scratch (cold caches); median reported")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale reference) and exit")
     args = ap.parse_args()
@@ -470,6 +507,82 @@ def main():
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / max(3, args.steps // 5)
 
+    cold = None
+    if args.cold:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        times = []
+        for _ in range(max(5, min(args.steps, 20))):
+            scratch.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        del scratch
+        times.sort()
+        cold = {"ms_per_step_median": round(times[len(times) // 2], 5), "steps": len(times),
+                "what": "one graph step after writing 1 GiB of scratch, per step"}
+
+    # device-copy bandwidth at the size of one layer's step traffic, for reference
+    cbytes = 128 << 20
+    src = torch.ones(cbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * cbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    literal = None
+    if not args.no_literal:
+        lit_alphas = schedules.literal_stagger(LAYERS)
+
+        def lit_step():
+            for l in range(LAYERS):
+                x = bufs[l]
+                fsa.forward(x["q"], x["k"], x["v"], alpha=lit_alphas[l], w=W, R=R, base=BASE, scale=scale,
+                            out=x["o"], lse=x["lse"])
+                fsa.backward(x["q"], x["k"], x["v"], x["o"], x["lse"], x["do"], alpha=lit_alphas[l], w=W, R=R,
+                             base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], delta=x["delta"],
+                             pair_ws=lit_ws)
+
+        lit_bytes = max(fsa.workspace_bytes(torch.bfloat16, B, H, N, D, alpha=a, w=W, R=R, base=BASE)
+                        for a in lit_alphas)
+        lit_ws = torch.empty(max(lit_bytes, 16) // 4, dtype=torch.int32, device=dev)
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            lit_step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        lg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(lg):
+            lit_step()
+        lg.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(max(3, args.steps // 5)):
+            lg.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lit_ms = e0.elapsed_time(e1) / max(3, args.steps // 5)
+        del lg
+        literal = {
+            "what": "the same 16-layer step with alpha_l = 0.5 + l*(1.5/15) as one workload description writes "
+                    "it (reaches 2.0 at layer 15; the main run uses the pages' ramp 0.5 + l/15)",
+            "tables_per_layer": [len(fsa.build_offsets(a, W, R, BASE)) for a in lit_alphas],
+            "max_offset": max(max(fsa.build_offsets(a, W, R, BASE) or [0]) for a in lit_alphas),
+            "ms_per_step": round(lit_ms, 5),
+            "query_heads_per_s": round(rows_per_layer() * LAYERS / (lit_ms * 1e-3), 1),
+        }
+
     per_row = alg_bytes_per_row()
     rows = rows_per_layer()
     qh_per_step = rows * LAYERS
@@ -490,6 +603,14 @@ def main():
         "algorithmic_bytes_per_launch": per_row[dom] * rows,
         "avg_launch_us": round(avg_us[dom], 3),
     }
+    band = band_flops_per_layer()
+    band_mfma = {k: {"useful_gflop_per_layer": round(band[k] / 1e9, 4),
+                     "tflops": round(band[k] / (avg_us[k] * 1e-6) / 1e12, 1),
+                     "frac_of_bf16_peak": round(band[k] / (avg_us[k] * 1e-6) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+                 for k in ("fwd", "bwd")}
+    band_mfma["note"] = ("useful window-band flops (2 products forward, 5 backward, 2 d flops per pair) over the "
+                         "stage time; the kernels issue 80 keys per 16-row block (about 1.25x the forward's "
+                         "useful flops, and the backward recomputes scores and dP in both kernels)")
     stages = {k: {"avg_us": round(v, 3), "algorithmic_bytes": per_row[k] * rows,
                   "gb_s": round(per_row[k] * rows / (v * 1e-6) / 1e9, 1),
                   "kernels": [KERNEL_NAMES[n] for n in STAGE_KERNELS[k]]} for k, v in avg_us.items()}
@@ -557,16 +678,21 @@ def main():
         },
         "hbm_gb_s": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "copy_gb_s": round(copy_gbs, 1),
+        "hbm_frac_of_copy": round(gbs / copy_gbs, 4),
         "algorithmic_bytes_per_step": step_bytes,
         "query_heads_per_step": qh_per_step,
         "eager_ms_per_step": round(eager_ms, 4),
         "stages": stages,
+        "band_mfma": band_mfma,
         "roofline": roof,
         "cpu_baseline": cpu,
         "dense_baseline": dense,
         "decode": decode,
         "learned_alpha": learned,
         "rope": rope,
+        "literal_stagger": literal,
+        "cold": cold,
     }
     if cpu:
         out["gpu_over_cpu"] = round(out["value"] / cpu["value"], 1)

@@ -21,6 +21,13 @@ def linear_stagger(n_layers: int = 16, lo: float = 0.5, hi: float = 1.5) -> list
     return [lo + (l * (hi - lo)) / (n_layers - 1) for l in range(n_layers)]
 
 
+def literal_stagger(n_layers: int = 16) -> list[float]:
+    """The stagger formula as one workload description writes it, alpha_l = 0.5 +
+    l * (1.5 / 15) (fp64, in that order). It reaches 2.0 at layer 15, outside the
+    pages' alpha range [0.5, 1.5]; it is run once beside the ramp, not instead of it."""
+    return [0.5 + l * (1.5 / 15) for l in range(n_layers)]
+
+
 def coprime_stagger(n_layers: int = 16, step: int = 7, lo: float = 0.5, hi: float = 1.5) -> list[float]:
     """Layer l takes the linear-stagger alpha of layer step * l mod L."""
     lin = linear_stagger(n_layers, lo, hi)

@@ -262,3 +262,12 @@ def test_decode_specific_checks(lib):
     # empty batches launch nothing, whatever the pointers
     assert decode(lib, ptrs=[P(0)] * 6, B=0) == fsa.FSA_OK
     assert decode(lib, ptrs=[P(0)] * 6, H=0) == fsa.FSA_OK
+
+
+def test_literal_stagger_tables(lib):
+    # the literal formula reaches alpha = 2.0: eight offsets at the last two layers, the largest 1974
+    al = schedules.literal_stagger(16)
+    assert al[0] == 0.5 and al[15] == 2.0
+    tabs = [build(lib, "fib", a, 64, 1024)[1] for a in al]
+    assert tabs == [oracle.offset_table("fib", a, 64, 1024) for a in al]
+    assert [len(t) for t in tabs][-2:] == [8, 8] and max(max(t) for t in tabs) == 1974

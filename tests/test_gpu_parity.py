@@ -429,3 +429,16 @@ def test_window_sweep(w):
     # the pages' window sweep with the Fibonacci table (offsets below w join the window)
     fwd_case(34, 1, 2, 700, torch.bfloat16, "fib", 1.0, w, 1024)
     bwd_case(34, 1, 2, 700, torch.bfloat16, "fib", 1.0, w, 1024)
+
+
+@pytest.mark.parametrize("layer", [3, 14, 15])
+def test_literal_stagger_formula_layers(layer):
+    # alpha_l = 0.5 + l*(1.5/15) as one workload description writes it: up to 8 offsets
+    # (the largest 1974) at the training-step shape
+    a = schedules.literal_stagger(16)[layer]
+    T = oracle.offset_table("fib", a, 64, 1024)
+    assert fsa.build_offsets(a, 64, 1024) == T
+    rng = np.random.default_rng(70 + layer)
+    b, h = int(rng.integers(0, 2)), int(rng.integers(0, 8))
+    fwd_case(7, 2, 8, 4096, torch.bfloat16, "fib", a, 64, 1024, heads=[(b, h)], layer=layer)
+    bwd_case(7, 2, 8, 4096, torch.bfloat16, "fib", a, 64, 1024, heads=[(b, h)], layer=layer)
