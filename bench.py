@@ -242,7 +242,8 @@ def decode_bench(fsa, torch, dev, stream):
 
 def stage_us(torch, dev, stream, fn, reps):
     """Average duration (us) of one layer's launches of fn: the 16 layers captured back to
-    back in a HIP graph, replayed `reps` times between two HIP events on the stream."""
+    back in a HIP graph, replayed `reps` times (after ten untimed replays) between two
+    HIP events on the stream."""
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(stream)
     with torch.cuda.stream(side):
@@ -254,7 +255,9 @@ def stage_us(torch, dev, stream, fn, reps):
     with torch.cuda.graph(g):
         for l in range(LAYERS):
             fn(l)
-    g.replay()
+    # a freshly instantiated graph runs its first replays slower: leave ten untimed
+    for _ in range(10):
+        g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -451,21 +454,7 @@ def main():
     torch.cuda.synchronize()
     ref = [tuple(bufs[l][t].clone() for t in ("o", "lse", "dq", "dk", "dv")) for l in range(LAYERS)]
 
-    # per-stage durations: each stage's 16 per-layer launches captured back to back in a
-    # HIP graph of their own, replayed between two HIP events on the launch stream
     stream = torch.cuda.current_stream(dev)
-    reps = max(3, args.steps // 5)
-    avg_us = {key: stage_us(torch, dev, stream, fn, reps)
-              for key, fn in (("fwd", layer_fwd), ("bwd", layer_bwd))}
-    log("average kernel durations (us): " + ", ".join(f"{k}={v:.2f}" for k, v in avg_us.items()))
-
-    def layer_step(l):
-        layer_fwd(l)
-        layer_bwd(l)
-
-    # forward + backward of one layer back to back (the order of a training step, which
-    # finds the layer's rows still in cache): the reference for the variants' steps
-    static_step_us = stage_us(torch, dev, stream, layer_step, reps)
 
     # capture one step as a HIP graph
     side = torch.cuda.Stream(device=dev)
@@ -479,6 +468,13 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # bring the GPU to steady clocks before anything is timed (untimed replays for at
+    # least half a second), then the requested warmup steps
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < 0.5:
+        for _ in range(20):
+            graph.replay()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -495,6 +491,22 @@ def main():
         for name, a in zip(("o", "lse", "dq", "dk", "dv"), ref[l]):
             if not torch.equal(bufs[l][name], a):
                 raise SystemExit(f"graph replay differs from eager result: layer {l} {name}")
+
+    # per-stage durations (at steady clocks, after the timed steps): each stage's 16
+    # per-layer launches captured back to back in a HIP graph of their own, replayed
+    # between two HIP events on the launch stream
+    reps = max(20, args.steps // 5)
+    avg_us = {key: stage_us(torch, dev, stream, fn, reps)
+              for key, fn in (("fwd", layer_fwd), ("bwd", layer_bwd))}
+    log("average kernel durations (us): " + ", ".join(f"{k}={v:.2f}" for k, v in avg_us.items()))
+
+    def layer_step(l):
+        layer_fwd(l)
+        layer_bwd(l)
+
+    # forward + backward of one layer back to back (the order of a training step, which
+    # finds the layer's rows still in cache): the reference for the variants' steps
+    static_step_us = stage_us(torch, dev, stream, layer_step, reps)
 
     # eager step time for context
     step()
