@@ -176,6 +176,7 @@ def measured_traffic(stage):
 
 # decode: the newest token of each of DEC_B sequences against full caches of DEC_LMAX rows
 DEC_B, DEC_LMAX, DEC_ALPHA = 64, 4096, 1.0
+DEC_FRAC_ALPHA = 1.0 + 1.0 / 15  # a learned value near the learned variant's start (alpha = 1): unrounded targets
 
 
 def decode_keys(table, w, L):
@@ -184,8 +185,9 @@ def decode_keys(table, w, L):
 
 
 def decode_bench(fsa, torch, dev, stream):
-    """Sparse decode (window 64 + Fibonacci offsets) and dense decode (window = cache) at
-    the same shapes: microseconds per step and algorithmic bytes per second."""
+    """Sparse decode (window 64 + Fibonacci offsets), dense decode (window = cache) and the
+    learned-alpha variant's decode (fractional targets, two cached rows per entry) at the
+    same shapes: microseconds per step and algorithmic bytes per second."""
     from fibonacci_offset_transformer_amd import synth
     x = synth.layer_inputs(6, 0, (DEC_B, H, DEC_LMAX, D), torch.bfloat16, with_grad=True)
     k, v = x["k"].to(dev), x["v"].to(dev)
@@ -196,13 +198,21 @@ def decode_bench(fsa, torch, dev, stream):
     lse = torch.empty((DEC_B, H), dtype=torch.float32, device=dev)
     res = {"config": {"sequences": DEC_B, "heads": H, "cache_rows": DEC_LMAX, "head_dim": D, "dtype": "bf16",
                       "base": BASE, "alpha": DEC_ALPHA, "R": R}}
-    for name, w in (("sparse", W), ("dense", DEC_LMAX)):
-        table = fsa.build_offsets(DEC_ALPHA, w, R, BASE)
-        keys = decode_keys(table, w, DEC_LMAX)
-        step_bytes = DEC_B * H * (keys * 2 * D * ELEM + 2 * D * ELEM + 4)
+    for name, w, alpha, frac in (("sparse", W, DEC_ALPHA, False), ("dense", DEC_LMAX, DEC_ALPHA, False),
+                                 ("learned_alpha", W, DEC_FRAC_ALPHA, True)):
+        if frac:  # each entry reads two cached rows
+            ents = [(a, ph) for a, ph, _ in fsa.frac_offsets(alpha, w, R, BASE)]
+            n_ent = sum(1 for a, ph in ents if a + (ph != 0.0) <= DEC_LMAX - 1)
+            keys = min(w, DEC_LMAX) + n_ent
+            rows_read = min(w, DEC_LMAX) + 2 * n_ent
+        else:
+            table = fsa.build_offsets(alpha, w, R, BASE)
+            keys = decode_keys(table, w, DEC_LMAX)
+            rows_read = keys
+        step_bytes = DEC_B * H * (rows_read * 2 * D * ELEM + 2 * D * ELEM + 4)
 
         def run():
-            fsa.decode(q, k, v, sl, alpha=DEC_ALPHA, w=w, R=R, base=BASE, out=o, lse=lse)
+            fsa.decode(q, k, v, sl, alpha=alpha, w=w, R=R, base=BASE, out=o, lse=lse, fractional=frac)
 
         run()
         torch.cuda.synchronize()
@@ -233,10 +243,11 @@ def decode_bench(fsa, torch, dev, stream):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         del g
-        res[name] = {"window": w, "keys_per_query": keys, "us_per_step": round(us, 2),
+        res[name] = {"window": w, "alpha": alpha, "keys_per_query": keys, "us_per_step": round(us, 2),
                      "us_per_step_eager": round(eager_us, 2),
                      "algorithmic_bytes": step_bytes, "gb_s": round(step_bytes / (us * 1e-6) / 1e9, 1)}
     res["dense_over_sparse_time"] = round(res["dense"]["us_per_step"] / res["sparse"]["us_per_step"], 2)
+    res["learned_alpha_over_sparse_time"] = round(res["learned_alpha"]["us_per_step"] / res["sparse"]["us_per_step"], 3)
     return res
 
 

@@ -753,6 +753,47 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     return launched(fsa::launch_backward_grads(dt, out_dt, p, hs, true), "rotary backward");
 }
 
+fsa_status_t fsa_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *seq_lens, void *o, float *lse, int32_t B, int32_t H,
+                             int32_t Lmax, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
+                             int32_t R, void *stream) {
+    const Shape s{B, H, Lmax, d};
+    fsa_status_t st = check_common(dt, out_dt, s, scale);
+    if (st != FSA_OK) return st;
+    fsa::AttnParams p{};
+    int32_t fb[FSA_MAX_OFFSETS];
+    const int n = build_frac_table(base, alpha, w, R, p.off, p.phi, fb, &st);
+    if (n < 0) return st;
+    if (static_cast<int64_t>(B) * H == 0) return ok();
+    if (Lmax < 1) return fail(FSA_E_ARG, "Lmax must be >= 1 (the cache holds at least the newest token)");
+    const char *names[] = {"q", "k_cache", "v_cache", "o", "lse"};
+    const void *ptrs[] = {q, k_cache, v_cache, o, lse};
+    if ((st = check_ptrs(names, ptrs, 5)) != FSA_OK) return st;
+    if (!seq_lens) return fail(FSA_E_ARG, "seq_lens is NULL");
+    if (reinterpret_cast<uintptr_t>(seq_lens) & 3u) return fail(FSA_E_ARG, "seq_lens is not 4-byte aligned");
+    const char *names6[] = {"q", "k_cache", "v_cache", "seq_lens", "o", "lse"};
+    const void *ptrs6[] = {q, k_cache, v_cache, seq_lens, o, lse};
+    if ((st = check_no_alias(names6, ptrs6, 4, 6)) != FSA_OK) return st;
+    int used = 0;  // entries some cached position reaches: first row floor(d) + (frac != 0) < Lmax
+    while (used < n && p.off[used] + (p.phi[used] != 0.f ? 1 : 0) < Lmax) ++used;
+    p.q = q;
+    p.k = k_cache;
+    p.v = v_cache;
+    p.out = o;
+    p.lse_out = lse;
+    p.seq_lens = seq_lens;
+    p.bh = B * H;
+    p.heads = H;
+    p.lmax = Lmax;
+    p.n = Lmax;
+    p.w = w;
+    p.n_off = used;
+    p.n_entries = n;
+    p.scale = scale;
+    p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    return launched(fsa::launch_frac_decode(dt, out_dt, p, static_cast<hipStream_t>(stream)), "fractional decode");
+}
+
 const char *fsa_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -94,6 +94,7 @@ hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
+hipError_t launch_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 // Gradient stage. With `with_delta`, D is formed from p.o and p.dout and written to
 // p.delta on the way (by the dQ kernel on the window path, by the delta kernel
 // elsewhere); otherwise p.delta is read as given.

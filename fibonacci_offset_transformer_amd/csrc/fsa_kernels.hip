@@ -1942,7 +1942,11 @@ __global__ void __launch_bounds__(kThreads) frac_alpha_kernel(const AttnParams p
 // flight per wave. Every group of kLanes lanes keeps an online softmax over the keys
 // it takes (log2 domain, scale applied: any finite scale); the groups of a wave merge
 // through lane exchanges and the four waves through LDS.
-template <bool BF16, bool OUT_BF16>
+//
+// With FRAC the table holds fractional entries (learned-alpha variant): entry t is
+// present when i >= off[t] + (phi[t] != 0), and its key and value are the fp32 mix
+// (1 - phi) row(i - off[t]) + phi row(i - off[t] - 1) of the two cached rows.
+template <bool BF16, bool OUT_BF16, bool FRAC>
 __global__ void __launch_bounds__(kThreads) decode_kernel(const AttnParams p) {
     using E = typename Elem<BF16>::T;
     using OE = typename Elem<OUT_BF16>::T;
@@ -1961,7 +1965,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const AttnParams p) {
     const E *V = static_cast<const E *>(p.v) + hid * p.lmax * 64 + kPer * c;
     const int wl = min(p.w, L);
     int nt = 0;  // table entries that reach a key (the table is sorted)
-    while (nt < p.n_off && p.off[nt] <= i) ++nt;
+    while (nt < p.n_off && (FRAC ? table_first(p, nt) : p.off[nt]) <= i) ++nt;
     const int nkeys = wl + nt;
     const int n_iter = (nkeys + 4 * kRows - 1) / (4 * kRows);  // loads per wave
     const float sl2 = p.scale_log2;
@@ -1981,19 +1985,28 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const AttnParams p) {
     float qv[kPer];
     to_f32(*reinterpret_cast<const u32x4_t *>(static_cast<const E *>(p.q) + hid * 64 + kPer * c), qv);
 
-    // key of load `it` for this lane's row group: index (4 it + wave) kRows + kg
-    auto key_row = [&](int it, bool &valid) {
+    // key of load `it` for this lane's row group: index (4 it + wave) kRows + kg; `ph` is
+    // the weight of the row below it (fractional entries only, else 0)
+    auto key_row = [&](int it, bool &valid, float &ph) {
         const int idx = (4 * it + wave) * kRows + kg;
         valid = idx < nkeys;
         const int t = min(max(idx - wl, 0), FSA_MAX_OFFSETS - 1);
+        ph = (FRAC && valid && idx >= wl) ? p.phi[t] : 0.f;
         return valid ? i - (idx < wl ? idx : p.off[t]) : i;  // a valid key lies in [0, i]
     };
     u32x4_t kr[kDepth], vr[kDepth];
+    u32x4_t kr2[FRAC ? kDepth : 1], vr2[FRAC ? kDepth : 1];  // FRAC: the rows below
     auto issue = [&](int u, int it) {
         bool valid;
-        const int j = key_row(it, valid);
+        float ph;
+        const int j = key_row(it, valid, ph);
         kr[u] = *reinterpret_cast<const u32x4_t *>(K + (int64_t)j * 64);
         vr[u] = *reinterpret_cast<const u32x4_t *>(V + (int64_t)j * 64);
+        if constexpr (FRAC) {
+            const int j2 = ph != 0.f ? j - 1 : j;  // a present entry with phi > 0 has j >= 1
+            kr2[u] = *reinterpret_cast<const u32x4_t *>(K + (int64_t)j2 * 64);
+            vr2[u] = *reinterpret_cast<const u32x4_t *>(V + (int64_t)j2 * 64);
+        }
     };
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) issue(u, u);  // rows of loads past the keys are row i: in bounds
@@ -2007,10 +2020,21 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const AttnParams p) {
             const int it = it0 + u;
             if (it < n_iter) {  // uniform
                 bool valid;
-                key_row(it, valid);
+                float ph;
+                key_row(it, valid, ph);
                 float kv[kPer], vv[kPer];
                 to_f32(kr[u], kv);
                 to_f32(vr[u], vv);
+                if constexpr (FRAC) {
+                    float k2[kPer], v2[kPer];
+                    to_f32(kr2[u], k2);
+                    to_f32(vr2[u], v2);
+#pragma unroll
+                    for (int e = 0; e < kPer; ++e) {
+                        kv[e] = __builtin_fmaf(ph, k2[e] - kv[e], kv[e]);
+                        vv[e] = __builtin_fmaf(ph, v2[e] - vv[e], vv[e]);
+                    }
+                }
                 float d = 0.f;
 #pragma unroll
                 for (int e = 0; e < kPer; ++e) d = __builtin_fmaf(qv[e], kv[e], d);
@@ -2132,10 +2156,19 @@ hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_
 hipError_t launch_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     const unsigned grid = (unsigned)p.bh;  // one workgroup per (b, h)
     if (dt == FSA_BF16)
-        return out_dt == FSA_BF16 ? launch(&decode_kernel<true, true>, grid, p, s)
-                                  : launch(&decode_kernel<true, false>, grid, p, s);
-    return out_dt == FSA_BF16 ? launch(&decode_kernel<false, true>, grid, p, s)
-                              : launch(&decode_kernel<false, false>, grid, p, s);
+        return out_dt == FSA_BF16 ? launch(&decode_kernel<true, true, false>, grid, p, s)
+                                  : launch(&decode_kernel<true, false, false>, grid, p, s);
+    return out_dt == FSA_BF16 ? launch(&decode_kernel<false, true, false>, grid, p, s)
+                              : launch(&decode_kernel<false, false, false>, grid, p, s);
+}
+
+hipError_t launch_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    const unsigned grid = (unsigned)p.bh;  // one workgroup per (b, h)
+    if (dt == FSA_BF16)
+        return out_dt == FSA_BF16 ? launch(&decode_kernel<true, true, true>, grid, p, s)
+                                  : launch(&decode_kernel<true, false, true>, grid, p, s);
+    return out_dt == FSA_BF16 ? launch(&decode_kernel<false, true, true>, grid, p, s)
+                              : launch(&decode_kernel<false, false, true>, grid, p, s);
 }
 
 hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s,

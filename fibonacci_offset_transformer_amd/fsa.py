@@ -29,6 +29,7 @@ MAX_OFFSETS = 48
 EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_workspace_bytes",
            "fsa_backward_delta", "fsa_backward_grads", "fsa_decode", "fsa_dense_forward",
            "fsa_frac_offsets", "fsa_frac_forward", "fsa_frac_backward", "fsa_frac_backward_workspace_bytes",
+           "fsa_frac_decode",
            "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
            "fsa_last_error")
 
@@ -88,6 +89,9 @@ def library() -> ctypes.CDLL:
             L.fsa_frac_backward_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64,
                                                             i32, i32, ctypes.POINTER(u64)]
             L.fsa_frac_backward_workspace_bytes.restype = ctypes.c_int
+            L.fsa_frac_decode.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                          f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_frac_decode.restype = ctypes.c_int
             L.fsa_rope_table.argtypes = [i32, i32, f64, ctypes.POINTER(f32)]
             L.fsa_rope_table.restype = ctypes.c_int
             L.fsa_rope_rotate.argtypes = [ctypes.c_int, vp, vp, i32, vp, i32, i32, i32, i32, vp]
@@ -237,10 +241,11 @@ def backward_grads(q, k, v, lse, dout, delta, *, alpha: float = 1.0, w: int, R: 
 
 
 def decode(q, k_cache, v_cache, seq_lens, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None,
-           out=None, lse=None, out_dtype=None):
+           out=None, lse=None, out_dtype=None, fractional: bool = False):
     """One decoding step: q [B,H,d] (the newest token of each sequence) against
     k_cache, v_cache [B,H,Lmax,d] with seq_lens int32 [B] on the device. Returns
-    (o [B,H,d] in out_dtype (default q.dtype), lse [B,H] float32)."""
+    (o [B,H,d] in out_dtype (default q.dtype), lse [B,H] float32). With fractional,
+    the learned-alpha variant's interpolated entries (fsa_frac_decode)."""
     if q.dim() != 3 or k_cache.dim() != 4:
         raise ValueError("expected q [B, H, d] and caches [B, H, Lmax, d]")
     B, H, d = q.shape
@@ -254,10 +259,11 @@ def decode(q, k_cache, v_cache, seq_lens, *, alpha: float = 1.0, w: int, R: int,
         raise ValueError("seq_lens must be an int32 [B] tensor on q's device")
     o = torch.empty_like(q, dtype=out_dtype or q.dtype) if out is None else out
     l = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    fn = library().fsa_frac_decode if fractional else library().fsa_decode
     with torch.cuda.device(q.device):
-        _check(library().fsa_decode(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                    _ptr(seq_lens), _ptr(o), _ptr(l), B, H, Lmax, d, _scale(scale, d), BASES[base],
-                                    float(alpha), int(w), int(R), _stream(q.device)))
+        _check(fn(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(o),
+                  _ptr(l), B, H, Lmax, d, _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                  _stream(q.device)))
     return o, l
 
 

@@ -299,6 +299,19 @@ fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_
                                                uint64_t *bytes);
 
 /*
+ * fsa_frac_decode - one decoding step of the learned-alpha variant: as fsa_decode,
+ * with the fractional entries of fsa_frac_offsets in place of the static table. For
+ * the newest position i = L - 1, entry t is present when i - d_t >= 0, and its key
+ * and value are (1 - phi_t) row(i - a_t) + phi_t row(i - a_t - 1) of the caches,
+ * mixed in fp32. Any scale, bf16 or float32 inputs; arguments as in fsa_decode
+ * (entries no cached position reaches are dropped).
+ */
+fsa_status_t fsa_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k_cache,
+                             const void *v_cache, const int32_t *seq_lens, void *o, float *lse, int32_t B, int32_t H,
+                             int32_t Lmax, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
+                             int32_t R, void *stream);
+
+/*
  * Rotary position embedding before the attention.
  *
  * The pages rotate queries and keys with rotary position embeddings before the

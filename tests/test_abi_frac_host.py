@@ -167,3 +167,27 @@ def test_frac_backward_workspace_too_small(lib):
     st, need = frac_ws(lib, B=1, H=1, N=64, alpha=1.3, w=16, R=256)
     assert st == fsa.FSA_OK and need > 0
     assert fbwd(lib, ws_bytes=need - 1) == fsa.FSA_E_ARG and b"ws holds" in lib.fsa_last_error()
+
+
+def fdec(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.3, w=16, R=256, out_dt=1):
+    p = ptrs or FAKE[:6]  # q k_cache v_cache seq_lens o lse; N is Lmax
+    return lib.fsa_frac_decode(dt, out_dt, *p, B, H, N, d, scale, base, alpha, w, R, None)
+
+
+def test_frac_decode_checks(lib):
+    assert fdec(lib, d=32) == fsa.FSA_E_UNSUPPORTED
+    assert fdec(lib, alpha=0.0) == fsa.FSA_E_ARG
+    assert fdec(lib, N=0) == fsa.FSA_E_ARG and b"Lmax" in lib.fsa_last_error()
+    ptrs = list(FAKE[:6])
+    ptrs[3] = P(0)
+    assert fdec(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"seq_lens is NULL" in lib.fsa_last_error()
+    ptrs[3] = P(FAKE[3].value + 2)
+    assert fdec(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"4-byte" in lib.fsa_last_error()
+    for k in (0, 1, 2, 4, 5):
+        ptrs = list(FAKE[:6])
+        ptrs[k] = P(0)
+        assert fdec(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"NULL" in lib.fsa_last_error()
+    ptrs = list(FAKE[:6])
+    ptrs[5] = ptrs[2]
+    assert fdec(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"aliases" in lib.fsa_last_error()
+    assert fdec(lib, ptrs=[P(0)] * 6, B=0) == fsa.FSA_OK

@@ -303,3 +303,50 @@ def test_frac_alpha_gradient_given_outputs_small(N, base, alpha, w, R):
 
 def test_frac_alpha_gradient_given_outputs_full_size():
     frac_given_case(46, 2, 8, 4096, "fib", schedules.linear_stagger(16)[9], 64, 1024, layer=9)
+
+
+# ---------------------------------------------------------------- decode (inference)
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("alpha,w,R,lens", [(1.3, 64, 1024, [1, 5, 64, 65, 80, 333, 700]),
+                                            (0.53, 1, 300, [1, 2, 3, 4, 60, 299]),
+                                            (1.0, 16, 256, [1, 17, 200]),
+                                            (1.37, 8, 1024, [0, -2, 9999, 11])])
+def test_frac_decode_against_oracle(dtype, alpha, w, R, lens):
+    """fsa_frac_decode on a ragged batch against the oracle's learned-alpha forward row L - 1
+    of each cache (lengths outside [1, Lmax] are clamped)."""
+    Lmax, H, scale = 700, 2, 0.125
+    B = len(lens)
+    t = synth.layer_inputs(47, 0, (B, H, Lmax, 64), dtype, with_grad=True)
+    x = {k: v.to(dev()) for k, v in t.items()}
+    q = x["do"][:, :, 0, :].contiguous()
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev())
+    note(f"frac decode {dtype} alpha={alpha} w={w} R={R} lens={lens}")
+    o, lse = fsa.decode(q, x["k"], x["v"], sl, alpha=alpha, w=w, R=R, scale=scale, out_dtype=torch.float32,
+                        fractional=True)
+    o_lo, lse_lo = fsa.decode(q, x["k"], x["v"], sl, alpha=alpha, w=w, R=R, scale=scale, fractional=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lo, o.to(o_lo.dtype)) and torch.equal(lse_lo, lse)
+    ds = [d for d, _ in oracle.frac_offset_table("fib", alpha, w, R)]
+    tol = 1e-5 if dtype == torch.float32 else TOL
+    for b, L in enumerate(lens):
+        L = min(max(L, 1), Lmax)
+        for h in range(H):
+            k, v = (synth.as_f64(x[n][b, h, :L]) for n in ("k", "v"))
+            qf = np.zeros_like(k)
+            qf[L - 1] = synth.as_f64(q[b, h])
+            ro, rl = oracle.frac_forward_rows(qf, k, v, ds, w, scale, [L - 1])
+            check(f"decode o[{b},{h}] L={L}", o[b, h][None], ro, tol)
+            check(f"decode lse[{b},{h}] L={L}", lse[b, h][None], rl, tol)
+
+
+def test_frac_decode_matches_frac_forward_last_row():
+    x = inputs(48, 0, (1, 4, 999, 64))
+    kw = dict(alpha=1.21, w=64, R=1024, scale=0.125)
+    o, lse = fsa.frac_forward(x["q"], x["k"], x["v"], out_dtype=torch.float32, **kw)
+    sl = torch.tensor([999], dtype=torch.int32, device=dev())
+    od, ld = fsa.decode(x["q"][:, :, -1].contiguous(), x["k"], x["v"], sl, out_dtype=torch.float32, fractional=True,
+                        **kw)
+    torch.cuda.synchronize()
+    assert float((od - o[:, :, -1]).abs().max()) <= 2e-3
+    assert float((ld - lse[:, :, -1]).abs().max()) <= 1e-5
