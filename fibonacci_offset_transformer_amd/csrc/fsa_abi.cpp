@@ -794,6 +794,134 @@ fsa_status_t fsa_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, 
     return launched(fsa::launch_frac_decode(dt, out_dt, p, static_cast<hipStream_t>(stream)), "fractional decode");
 }
 
+// ---- RoPE before the gather, then the learned-alpha variant's interpolated entries ----
+
+namespace {
+
+struct RopeFracLayout {
+    uint64_t qhat, khat, frac, fwd, bwd;  // byte offsets into ws (frac: the fractional workspace) and sizes
+};
+
+RopeFracLayout rope_frac_layout(int64_t bh, int32_t n, int32_t n_off) {
+    RopeFracLayout l;
+    const uint64_t rows = static_cast<uint64_t>(bh) * n;
+    l.qhat = 0;
+    l.khat = fsa::align256(rows * 128);
+    l.fwd = l.khat + fsa::align256(rows * 128);
+    l.frac = l.fwd;
+    l.bwd = l.frac + fsa::frac_workspace(bh, n, n_off).total;
+    return l;
+}
+
+}  // namespace
+
+fsa_status_t fsa_rope_frac_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                                           fsa_base_t base, double alpha, int32_t w, int32_t R, uint64_t *fwd_bytes,
+                                           uint64_t *bwd_bytes) {
+    if (!fwd_bytes || !bwd_bytes) return fail(FSA_E_ARG, "fwd_bytes or bwd_bytes is NULL");
+    fsa::AttnParams p{};
+    const fsa_status_t st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R);
+    if (st != FSA_OK) return st;
+    const bool empty = static_cast<int64_t>(B) * H * N == 0;
+    const RopeFracLayout l = rope_frac_layout(static_cast<int64_t>(B) * H, N, p.n_off);
+    *fwd_bytes = empty ? 0 : l.fwd;
+    *bwd_bytes = empty ? 0 : l.bwd;
+    return ok();
+}
+
+fsa_status_t fsa_rope_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                                   const float *rope, int32_t n_pos, void *o, float *lse, void *ws,
+                                   uint64_t ws_bytes, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                                   fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream) {
+    fsa::AttnParams p{};
+    fsa_status_t st = prepare_frac(p, dt, out_dt, B, H, N, d, scale, base, alpha, w, R);
+    if (st != FSA_OK) return st;
+    if (n_pos < N) return fail(FSA_E_ARG, "the rotary table has %d positions, the sequence %d", n_pos, N);
+    if (static_cast<int64_t>(B) * H * N == 0) return ok();
+    const char *names[] = {"q", "k", "v", "rope", "o", "lse", "ws"};
+    const void *ptrs[] = {q, k, v, rope, o, lse, ws};
+    if ((st = check_ptrs(names, ptrs, 7)) != FSA_OK) return st;
+    if ((st = check_no_alias(names, ptrs, 4, 7)) != FSA_OK) return st;
+    const RopeFracLayout l = rope_frac_layout(p.bh, N, p.n_off);
+    if (ws_bytes < l.fwd)
+        return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
+                    static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.fwd));
+    char *wsb = static_cast<char *>(ws);
+    const void *xs[] = {q, k};
+    void *hats[] = {wsb + l.qhat, wsb + l.khat};
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = rotate_rows(xs, hats, 2, rope, static_cast<int64_t>(B) * H * N, N, hs);
+    if (e != hipSuccess) return launched(e, "rotary rotation");
+    p.q = hats[0];
+    p.k = hats[1];
+    p.v = v;
+    p.out = o;
+    p.lse_out = lse;
+    return launched(fsa::launch_frac_forward(out_dt, p, hs), "rotary fractional forward");
+}
+
+fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                                    const void *v, const float *rope, int32_t n_pos, const void *o, const float *lse,
+                                    const void *dout, void *dq, void *dk, void *dv, float *dalpha, float *doffs,
+                                    void *ws, uint64_t ws_bytes, int32_t reuse_rotated, int32_t B, int32_t H,
+                                    int32_t N, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
+                                    int32_t R, void *stream) {
+    fsa::AttnParams p{};
+    fsa_status_t st = prepare_frac(p, dt, out_dt, B, H, N, d, scale, base, alpha, w, R);
+    if (st != FSA_OK) return st;
+    if (n_pos < N) return fail(FSA_E_ARG, "the rotary table has %d positions, the sequence %d", n_pos, N);
+    if (!dalpha) return fail(FSA_E_ARG, "dalpha is NULL");
+    if (reinterpret_cast<uintptr_t>(dalpha) & 3u) return fail(FSA_E_ARG, "dalpha is not 4-byte aligned");
+    if (doffs && (reinterpret_cast<uintptr_t>(doffs) & 3u)) return fail(FSA_E_ARG, "doffs is not 4-byte aligned");
+    const bool empty = static_cast<int64_t>(B) * H * N == 0;
+    RopeFracLayout l{};
+    if (!empty) {
+        l = rope_frac_layout(p.bh, N, p.n_off);
+        const char *names[] = {"q", "k", "v", "rope", "o", "lse", "dout", "dq", "dk", "dv", "ws"};
+        const void *ptrs[] = {q, k, v, rope, o, lse, dout, dq, dk, dv, ws};
+        if ((st = check_ptrs(names, ptrs, 11)) != FSA_OK) return st;
+        if ((st = check_no_alias(names, ptrs, 7, 11)) != FSA_OK) return st;
+        if (ws_bytes < l.bwd)
+            return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
+                        static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.bwd));
+    }
+    const void *outs[] = {dalpha, doffs, dq, dk, dv, ws, q, k, v, o, lse, dout, rope};
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 13; ++j)
+            if (j != i && outs[i] && outs[i] == outs[j])
+                return fail(FSA_E_ARG, "%s aliases another argument", i == 0 ? "dalpha" : "doffs");
+    p.dalpha = dalpha;
+    p.doffs = doffs;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (empty) {
+        p.bh = 0;
+        return launched(fsa::launch_frac_backward(out_dt, p, hs), "rotary fractional backward");
+    }
+    char *wsb = static_cast<char *>(ws);
+    const void *xs[] = {q, k};
+    void *hats[] = {wsb + l.qhat, wsb + l.khat};
+    if (!reuse_rotated) {
+        const hipError_t e = rotate_rows(xs, hats, 2, rope, static_cast<int64_t>(B) * H * N, N, hs);
+        if (e != hipSuccess) return launched(e, "rotary rotation");
+    }
+    const fsa::FracWorkspace fl = fsa::frac_workspace(p.bh, N, p.n_off);
+    char *fw = wsb + l.frac;
+    p.q = hats[0];
+    p.k = hats[1];
+    p.v = v;
+    p.o = o;
+    p.lse_in = lse;
+    p.dout = dout;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.delta = reinterpret_cast<float *>(fw + fl.delta);
+    p.pairs = reinterpret_cast<uint32_t *>(fw + fl.pairs);
+    p.dd_part = reinterpret_cast<float *>(fw + fl.partials);
+    p.rope = rope;
+    return launched(fsa::launch_frac_backward(out_dt, p, hs), "rotary fractional backward");
+}
+
 const char *fsa_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

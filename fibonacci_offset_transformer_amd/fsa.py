@@ -31,7 +31,7 @@ EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_wor
            "fsa_frac_offsets", "fsa_frac_forward", "fsa_frac_backward", "fsa_frac_backward_workspace_bytes",
            "fsa_frac_decode",
            "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
-           "fsa_last_error")
+           "fsa_rope_frac_workspace_bytes", "fsa_rope_frac_forward", "fsa_rope_frac_backward", "fsa_last_error")
 
 
 class FsaError(RuntimeError):
@@ -105,6 +105,16 @@ def library() -> ctypes.CDLL:
             L.fsa_rope_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                             u64, i32, i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
             L.fsa_rope_backward.restype = ctypes.c_int
+            L.fsa_rope_frac_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64, i32,
+                                                        i32, ctypes.POINTER(u64), ctypes.POINTER(u64)]
+            L.fsa_rope_frac_workspace_bytes.restype = ctypes.c_int
+            L.fsa_rope_frac_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, u64, i32,
+                                                i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_rope_frac_forward.restype = ctypes.c_int
+            L.fsa_rope_frac_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                                 vp, vp, vp, vp, u64, i32, i32, i32, i32, i32, f32, ctypes.c_int, f64,
+                                                 i32, i32, vp]
+            L.fsa_rope_frac_backward.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
             L.fsa_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -431,3 +441,60 @@ def rope_backward(q, k, v, table, o, lse, dout, *, alpha: float = 1.0, w: int, R
                                            _ptr(ws), ws_bytes, int(bool(reuse_rotated)), B, H, N, d, _scale(scale, d),
                                            BASES[base], float(alpha), int(w), int(R), _stream(q.device)))
     return dq, dk, dv
+
+
+# ---- RoPE before the gather, then the learned-alpha variant ----
+
+
+def rope_frac_workspace_bytes(dtype, B: int, H: int, N: int, d: int = 64, *, alpha: float, w: int, R: int,
+                              base: str = "fib") -> tuple[int, int]:
+    """(forward, backward) workspace bytes of the rotary learned-alpha calls."""
+    f, b = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    _check(library().fsa_rope_frac_workspace_bytes(DTYPES[dtype], int(B), int(H), int(N), int(d), BASES[base],
+                                                   float(alpha), int(w), int(R), ctypes.byref(f), ctypes.byref(b)))
+    return int(f.value), int(b.value)
+
+
+def rope_frac_forward(q, k, v, table, *, alpha: float, w: int, R: int, base: str = "fib", scale=None, out=None,
+                      lse=None, out_dtype=None, ws=None):
+    """Learned-alpha forward over rotated Q, K (unrotated inputs): (o, lse)."""
+    B, H, N, d = _shape(q, k, v)
+    o = _out(q, out, out_dtype)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    n_pos = _table(table, N)
+    if ws is None:
+        need = rope_frac_workspace_bytes(q.dtype, B, H, N, d, alpha=alpha, w=w, R=R, base=base)[0]
+        ws = torch.empty(max(need // 4, 4), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(library().fsa_rope_frac_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(table), n_pos, _ptr(o), _ptr(l), _ptr(ws),
+                                               ws.numel() * ws.element_size(), B, H, N, d, _scale(scale, d),
+                                               BASES[base], float(alpha), int(w), int(R), _stream(q.device)))
+    return o, l
+
+
+def rope_frac_backward(q, k, v, table, o, lse, dout, *, alpha: float, w: int, R: int, base: str = "fib",
+                       scale=None, dq=None, dk=None, dv=None, dalpha=None, doffs=None, out_dtype=None, ws=None,
+                       reuse_rotated: bool = False):
+    """Backward of rope_frac_forward: (dq, dk, dv, dalpha [1], doffs [entries])."""
+    B, H, N, d = _shape(q, k, v, o, dout)
+    dq = _out(q, dq, out_dtype)
+    dk = _out(q, dk, dq.dtype)
+    dv = _out(q, dv, dq.dtype)
+    n_pos = _table(table, N)
+    n_entries = len(frac_offsets(alpha, w, R, base))
+    dalpha = torch.empty(1, dtype=torch.float32, device=q.device) if dalpha is None else dalpha
+    doffs = torch.empty(max(n_entries, 1), dtype=torch.float32, device=q.device) if doffs is None else doffs
+    if reuse_rotated and ws is None:
+        raise ValueError("reuse_rotated needs the forward's workspace")
+    if ws is None:
+        need = rope_frac_workspace_bytes(q.dtype, B, H, N, d, alpha=alpha, w=w, R=R, base=base)[1]
+        ws = torch.empty(max(need // 4, 4), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(library().fsa_rope_frac_backward(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(table), n_pos, _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                                _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(doffs), _ptr(ws),
+                                                ws.numel() * ws.element_size(), int(bool(reuse_rotated)), B, H, N, d,
+                                                _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                                                _stream(q.device)))
+    return dq, dk, dv, dalpha, doffs[:n_entries]

@@ -413,6 +413,34 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
                                int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
                                int32_t w, int32_t R, void *stream);
 
+/*
+ * The learned-alpha variant with rotary embedding, as the pages describe it: Q and K
+ * are rotated (as in fsa_rope_forward, stored in bf16), then the attention of
+ * fsa_frac_forward runs over the rotated rows, so each fractional entry interpolates
+ * rotated key rows (and unrotated value rows). The backward returns dQ, dK with
+ * respect to the unrotated rows, dV, dalpha and doffs (as fsa_frac_backward).
+ *
+ * fsa_rope_frac_workspace_bytes: forward 2 B H N d * 2 (rotated Q and K); backward
+ * that plus fsa_frac_backward_workspace_bytes (each part rounded up to 256 bytes).
+ * fsa_rope_frac_forward / fsa_rope_frac_backward: arguments as in fsa_rope_forward /
+ * fsa_rope_backward, plus dalpha and doffs as in fsa_frac_backward; reuse_rotated as
+ * in fsa_rope_backward (ws then holds fsa_rope_frac_forward's rotated rows). Supported
+ * for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64.
+ */
+fsa_status_t fsa_rope_frac_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                                           fsa_base_t base, double alpha, int32_t w, int32_t R, uint64_t *fwd_bytes,
+                                           uint64_t *bwd_bytes);
+fsa_status_t fsa_rope_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
+                                   const float *rope, int32_t n_pos, void *o, float *lse, void *ws,
+                                   uint64_t ws_bytes, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                                   fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
+fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                                    const void *v, const float *rope, int32_t n_pos, const void *o, const float *lse,
+                                    const void *dout, void *dq, void *dk, void *dv, float *dalpha, float *doffs,
+                                    void *ws, uint64_t ws_bytes, int32_t reuse_rotated, int32_t B, int32_t H,
+                                    int32_t N, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
+                                    int32_t R, void *stream);
+
 /* Text describing the calling thread's last non-OK status ("" if none). */
 const char *fsa_last_error(void);
 

@@ -19,6 +19,8 @@ from .fsa_ref import (  # noqa: F401
     offset_table,
     pow2_base,
     rope_angles,
+    rope_frac_backward,
+    rope_frac_forward,
     rope_rotate,
     rope_sparse_backward,
     rope_sparse_backward_rows,

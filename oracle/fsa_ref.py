@@ -745,3 +745,24 @@ def rope_sparse_backward_rows(q, k, v, dout, T, w, scale, rows, base: float = 10
     rot = (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
     dq, dk, dv = sparse_backward_rows(rot(q), rot(k), v, dout, T, w, scale, rows)
     return _rotate_rows_back(dq, rows, N, d, base), _rotate_rows_back(dk, rows, N, d, base), dv
+
+
+def _rope_rot(base, stored, table):
+    return (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
+
+
+def rope_frac_forward(q, k, v, entries, w, scale, base: float = 10000.0, stored: bool = False, table=None):
+    """The learned-alpha variant as the pages run it: queries and keys rotated first
+    ([EXPL-pt] Metodologia / Arquitetura, item "Implementação"), then frac_forward, so
+    each entry interpolates rotated key rows (values are not rotated)."""
+    rot = _rope_rot(base, stored, table)
+    return frac_forward(rot(q), rot(k), v, entries, w, scale)
+
+
+def rope_frac_backward(q, k, v, dout, entries, w, scale, base: float = 10000.0, stored: bool = False, table=None,
+                       o=None, lse=None):
+    """Gradients of rope_frac_forward: frac_backward on the rotated rows, dq and dk
+    rotated back (the transpose), dv and the per-entry derivative unchanged."""
+    rot = _rope_rot(base, stored, table)
+    dq, dk, dv, dd = frac_backward(rot(q), rot(k), v, dout, entries, w, scale, o=o, lse=lse)
+    return rope_rotate(dq, base, inverse=True), rope_rotate(dk, base, inverse=True), dv, dd

@@ -110,3 +110,49 @@ def test_rope_workspace_sizes(lib):
     assert lib.fsa_rope_workspace_bytes(0, 1, 1, 64, 64, 0, 1.0, 64, 1024, ctypes.byref(f), ctypes.byref(b)) \
         == fsa.FSA_E_UNSUPPORTED
     assert lib.fsa_rope_workspace_bytes(1, 1, 1, 64, 64, 0, 1.0, 64, 1024, None, ctypes.byref(b)) == fsa.FSA_E_ARG
+
+
+def rfrac_fwd(lib, ptrs=None, n_pos=64, N=64, dt=1, w=16, scale=0.125, ws_bytes=1 << 40):
+    p = ptrs or FAKE[:7]  # q k v rope o lse ws
+    return lib.fsa_rope_frac_forward(dt, 1, p[0], p[1], p[2], p[3], n_pos, p[4], p[5], p[6], ws_bytes,
+                                     1, 1, N, 64, scale, 0, 1.3, w, 256, None)
+
+
+def rfrac_bwd(lib, ptrs=None, n_pos=64, N=64, dt=1, w=16, scale=0.125, ws_bytes=1 << 40, B=1):
+    p = ptrs or FAKE[:13]  # q k v rope o lse dout dq dk dv dalpha doffs ws
+    return lib.fsa_rope_frac_backward(dt, 1, p[0], p[1], p[2], p[3], n_pos, *p[4:12], p[12], ws_bytes, 0,
+                                      B, 1, N, 64, scale, 0, 1.3, w, 256, None)
+
+
+@pytest.mark.parametrize("call,n", [(rfrac_fwd, 7), (rfrac_bwd, 13)])
+def test_rope_frac_checks(lib, call, n):
+    assert call(lib, dt=0) == fsa.FSA_E_UNSUPPORTED
+    assert call(lib, w=65) == fsa.FSA_E_UNSUPPORTED
+    assert call(lib, scale=0.0) == fsa.FSA_E_UNSUPPORTED
+    assert call(lib, n_pos=63) == fsa.FSA_E_ARG and b"positions" in lib.fsa_last_error()
+    assert call(lib, ws_bytes=0) == fsa.FSA_E_ARG and b"ws holds" in lib.fsa_last_error()
+    skip = {10, 11} if n == 13 else set()  # dalpha and doffs have their own checks
+    for k in range(n):
+        if k in skip:
+            continue
+        ptrs = list(FAKE[:n])
+        ptrs[k] = P(0)
+        assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"NULL" in lib.fsa_last_error()
+        ptrs[k] = P(FAKE[k].value + 8)
+        assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"aligned" in lib.fsa_last_error()
+    if n == 13:
+        ptrs = list(FAKE[:13])
+        ptrs[10] = P(0)
+        assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"dalpha is NULL" in lib.fsa_last_error()
+        ptrs[10] = ptrs[0]
+        assert call(lib, ptrs=ptrs) == fsa.FSA_E_ARG and b"aliases" in lib.fsa_last_error()
+
+
+def test_rope_frac_workspace_sizes(lib):
+    f, b = ctypes.c_uint64(1), ctypes.c_uint64(1)
+    assert lib.fsa_rope_frac_workspace_bytes(1, 2, 8, 4096, 64, 0, 1.3, 64, 1024, ctypes.byref(f),
+                                             ctypes.byref(b)) == 0
+    rows = 2 * 8 * 4096
+    fr = ctypes.c_uint64(0)
+    assert lib.fsa_frac_backward_workspace_bytes(1, 2, 8, 4096, 64, 0, 1.3, 64, 1024, ctypes.byref(fr)) == 0
+    assert f.value == 2 * a256(rows * 128) and b.value == f.value + fr.value

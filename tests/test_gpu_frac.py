@@ -350,3 +350,49 @@ def test_frac_decode_matches_frac_forward_last_row():
     torch.cuda.synchronize()
     assert float((od - o[:, :, -1]).abs().max()) <= 2e-3
     assert float((ld - lse[:, :, -1]).abs().max()) <= 1e-5
+
+
+def test_frac_graph_replays_match_eager():
+    # forward + backward (with the alpha reduction inside the dK/dV kernel) and a decode step
+    # captured in one HIP graph; every replay, with eager work and a clear in between,
+    # reproduces the eager results bit for bit
+    x = inputs(49, 0, (2, 3, 700, 64), grad=True)
+    kw = dict(alpha=1.13, w=64, R=1024, scale=0.125)
+    bufs = {n: torch.empty_like(x["q"]) for n in ("o", "dq", "dk", "dv")}
+    lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev())
+    da = torch.empty(1, dtype=torch.float32, device=dev())
+    dd = torch.empty(len(fsa.frac_offsets(1.13, 64, 1024)), dtype=torch.float32, device=dev())  # one per entry
+    ws = torch.empty(fsa.frac_workspace_bytes(torch.bfloat16, 2, 3, 700, alpha=1.13, w=64, R=1024) // 4 + 1,
+                     dtype=torch.int32, device=dev())
+    qd = x["q"][:, :, -1].contiguous()
+    sl = torch.tensor([700, 333], dtype=torch.int32, device=dev())
+    od = torch.empty_like(qd)
+    ld = torch.empty(qd.shape[:2], dtype=torch.float32, device=dev())
+
+    def step():
+        fsa.frac_forward(x["q"], x["k"], x["v"], out=bufs["o"], lse=lse, **kw)
+        fsa.frac_backward(x["q"], x["k"], x["v"], bufs["o"], lse, x["do"], dq=bufs["dq"], dk=bufs["dk"],
+                          dv=bufs["dv"], dalpha=da, doffs=dd, ws=ws, **kw)
+        fsa.decode(qd, x["k"], x["v"], sl, out=od, lse=ld, fractional=True, **kw)
+
+    outs = dict(bufs, lse=lse, da=da, dd=dd, od=od, ld=ld)
+    step()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in outs.values():
+            t.zero_()
+        fsa.frac_forward(x["k"], x["q"], x["v"], **kw)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(outs[n], ref[n]), (rep, n)

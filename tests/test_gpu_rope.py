@@ -190,3 +190,139 @@ def test_backward_reusing_the_forward_rotation_is_identical():
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_rope_graph_replays_match_eager():
+    x = inputs(67, 0, (2, 3, 700, 64), grad=True)
+    table = fsa.rope_table(700, device=dev())
+    kw = dict(alpha=1.2, w=64, R=1024, scale=0.125)
+    bufs = {n: torch.empty_like(x["q"]) for n in ("o", "dq", "dk", "dv")}
+    lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev())
+    ws = torch.empty(fsa.rope_workspace_bytes(torch.bfloat16, 2, 3, 700, alpha=1.2, w=64, R=1024)[1] // 4 + 1,
+                     dtype=torch.int32, device=dev())
+
+    def step():
+        fsa.rope_forward(x["q"], x["k"], x["v"], table, out=bufs["o"], lse=lse, ws=ws, **kw)
+        fsa.rope_backward(x["q"], x["k"], x["v"], table, bufs["o"], lse, x["do"], dq=bufs["dq"], dk=bufs["dk"],
+                          dv=bufs["dv"], ws=ws, reuse_rotated=True, **kw)
+
+    outs = dict(bufs, lse=lse)
+    step()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in outs.values():
+            t.zero_()
+        ws.fill_(-1)  # the workspace's contents on entry must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in outs:
+            assert torch.equal(outs[n], ref[n]), (rep, n)
+
+
+# ---------------------------------------------------------------- learned-alpha variant over rotated rows
+
+def _entry_l1(q, k, v, do, o_given, tab, w, scale):
+    """Per entry: sum over rows of |scale dS ds_raw| + |P ddp| (the alpha-gradient terms' absolute
+    values, D from o_given) for one head of rotated rows q, k."""
+    N = q.shape[0]
+    ds = [d for d, _ in tab]
+    P, _, _ = oracle.frac_probabilities(q, k, ds, w, scale)
+    D = np.sum(do * o_given, -1)
+    out = np.zeros(len(tab))
+    for m, (d, _) in enumerate(tab):
+        a = math.floor(d)
+        phi = d - a
+        if a + 1 >= N:
+            continue
+        r = np.arange(a + 1, N)
+        kn, kf, vn, vf = k[r - a], k[r - a - 1], v[r - a], v[r - a - 1]
+        p = P[r, w + m]
+        ds_raw = np.sum(q[r] * (kf - kn), -1)
+        dS = p * (np.sum(do[r] * ((1 - phi) * vn + phi * vf), -1) - D[r])
+        out[m] = np.sum(np.abs(scale * dS * ds_raw) + np.abs(p * np.sum(do[r] * (vf - vn), -1)))
+    return out
+
+
+@pytest.mark.parametrize("N,alpha,w,R", [(300, 1.3, 16, 256), (257, 1.1, 1, 1024), (1100, 1.21, 6, 1024),
+                                         (300, 1.0, 64, 1024)])
+def test_rope_frac_against_oracle(N, alpha, w, R):
+    """Forward against the oracle over the stored rotated rows; backward handed the oracle's
+    O (bf16) and LSE (fp32), dQ/dK/dV at 1e-2 and the alpha gradient within 1e-5 of its
+    terms' absolute sum (as in the unrotated learned-alpha tests)."""
+    B, H, scale = 2, 2, 0.125
+    x = inputs(68, 0, (B, H, N, 64), grad=True)
+    table = fsa.rope_table(N, device=dev())
+    kw = dict(alpha=alpha, w=w, R=R, scale=scale)
+    note(f"rope + learned alpha N={N} alpha={alpha} w={w} R={R}")
+    tab = oracle.frac_offset_table("fib", alpha, w, R)
+    ds = [d for d, _ in tab]
+    o, lse = fsa.rope_frac_forward(x["q"], x["k"], x["v"], table, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = np.zeros((B, H, N, 64)), np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
+            o_ref[b, h], lse_ref[b, h] = oracle.rope_frac_forward(q, k, v, ds, w, scale, stored=True)
+            check(f"o[{b},{h}]", o[b, h], o_ref[b, h])
+            check(f"lse[{b},{h}]", lse[b, h], lse_ref[b, h])
+    o_c = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse_c = torch.from_numpy(lse_ref).to(torch.float32)
+    g = fsa.rope_frac_backward(x["q"], x["k"], x["v"], table, o_c.to(dev()), lse_c.to(dev()), x["do"],
+                               out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    o_g, lse_g = synth.as_f64(o_c), synth.as_f64(lse_c)
+    dd = np.zeros(len(tab))
+    l1 = np.zeros(len(tab))
+    for b in range(B):
+        for h in range(H):
+            q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
+            rq, rk, rv, rdd = oracle.rope_frac_backward(q, k, v, do, ds, w, scale, stored=True,
+                                                        o=o_g[b, h], lse=lse_g[b, h])
+            check(f"dq[{b},{h}]", g[0][b, h], rq)
+            check(f"dk[{b},{h}]", g[1][b, h], rk)
+            check(f"dv[{b},{h}]", g[2][b, h], rv)
+            dd += rdd
+            l1 += _entry_l1(oracle.rope_store_bf16(q), oracle.rope_store_bf16(k), v, do, o_g[b, h], tab, w, scale)
+    tol = 1e-5 * l1 + 1e-6
+    err = np.abs(synth.as_f64(g[4]) - dd)
+    note(f"  doffs: max|err|/tol={float(np.max(err / tol)) if len(tab) else 0:.4f}")
+    assert np.all(err <= tol)
+    fs = np.array([f for _, f in tab], dtype=np.float64)
+    ga = oracle.frac_alpha_grad(dd, fs)
+    assert abs(float(g[3].item()) - ga) <= float(np.sum(fs * tol))
+
+
+def test_rope_frac_reuse_and_full_size():
+    # the training-step shape, end to end, with the backward reusing the forward's rotation
+    a = schedules.linear_stagger(16)[11]
+    x = inputs(69, 11, (2, 8, 4096, 64), grad=True)
+    table = fsa.rope_table(4096, device=dev())
+    kw = dict(alpha=a, w=64, R=1024, scale=0.125)
+    ws = torch.empty(fsa.rope_frac_workspace_bytes(torch.bfloat16, 2, 8, 4096, alpha=a, w=64, R=1024)[1] // 4 + 1,
+                     dtype=torch.int32, device=dev())
+    o, lse = fsa.rope_frac_forward(x["q"], x["k"], x["v"], table, ws=ws, **kw)
+    g1 = fsa.rope_frac_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], ws=ws, reuse_rotated=True,
+                                out_dtype=torch.float32, **kw)
+    g2 = fsa.rope_frac_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    for u, v_ in zip(g1, g2):
+        assert torch.equal(u, v_)
+    ds = [d for d, _ in oracle.frac_offset_table("fib", a, 64, 1024)]
+    b, h = 1, 6
+    q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
+    ro, rl = oracle.rope_frac_forward(q, k, v, ds, 64, 0.125, stored=True)
+    check("o[1,6]", o[b, h].float(), ro)
+    rq, rk, rv, _ = oracle.rope_frac_backward(q, k, v, do, ds, 64, 0.125, stored=True)
+    check("dq[1,6]", g1[0][b, h], rq)
+    check("dk[1,6]", g1[1][b, h], rk)
+    check("dv[1,6]", g1[2][b, h], rv)

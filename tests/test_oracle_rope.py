@@ -214,3 +214,47 @@ def test_stored_forward_and_backward_close_to_exact():
     g2 = oracle.rope_sparse_backward(q, k, v, do, T, w, 0.125, stored=True)
     for a, b in zip(g1, g2):
         assert np.max(np.abs(a - b)) <= 3e-2
+
+
+# ---- rotary embedding before the learned-alpha variant's interpolated gather ----
+
+def test_rope_frac_integer_targets_equal_static_rope():
+    N, w, R = 150, 6, 128
+    q, k, v, do = (rand((2, N, 64), s) for s in (30, 31, 32, 33))
+    ds = [d for d, _ in oracle.frac_offset_table("fib", 1.0, w, R)]
+    T = oracle.offset_table("fib", 1.0, w, R)
+    o1, l1 = oracle.rope_frac_forward(q, k, v, ds, w, 0.125)
+    o2, l2 = oracle.rope_sparse_forward(q, k, v, T, w, 0.125)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12 and np.max(np.abs(l1 - l2)) <= 1e-12
+    g1 = oracle.rope_frac_backward(q, k, v, do, ds, w, 0.125)
+    g2 = oracle.rope_sparse_backward(q, k, v, do, T, w, 0.125)
+    for a, b in zip(g1[:3], g2):
+        assert np.max(np.abs(a - b)) <= 1e-12
+
+
+def _rf_loss(q, k, v, do, alpha, w, R, scale):
+    ds = [d for d, _ in oracle.frac_offset_table("fib", alpha, w, R)]
+    o, _ = oracle.rope_frac_forward(q, k, v, ds, w, scale)
+    return float(np.sum(o * do))
+
+
+def test_rope_frac_backward_matches_central_differences():
+    N, d, w, R, alpha, scale = 22, 8, 2, 32, 1.23, 0.6
+    q, k, v, do = (rand((N, d), s) for s in (34, 35, 36, 37))
+    tab = oracle.frac_offset_table("fib", alpha, w, R)
+    dq, dk, dv, dd = oracle.rope_frac_backward(q, k, v, do, [x for x, _ in tab], w, scale)
+    h = 1e-6
+    for X, G in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            old = X[idx]
+            X[idx] = old + h
+            lp = _rf_loss(q, k, v, do, alpha, w, R, scale)
+            X[idx] = old - h
+            lm = _rf_loss(q, k, v, do, alpha, w, R, scale)
+            X[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        assert np.max(np.abs(num - G)) / max(1.0, np.max(np.abs(G))) <= 1e-6
+    ga = oracle.frac_alpha_grad(dd, [f for _, f in tab])
+    num = (_rf_loss(q, k, v, do, alpha + h, w, R, scale) - _rf_loss(q, k, v, do, alpha - h, w, R, scale)) / (2 * h)
+    assert abs(num - ga) <= 1e-6 * max(1.0, abs(ga))
