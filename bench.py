@@ -335,10 +335,10 @@ def rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
                              for a in alphas))
     ws = torch.empty(max(b_bytes) // 4 + 1, dtype=torch.int32, device=dev)
 
-    def fwd(l):
+    def fwd(l, keep=False):  # inference: the rotated Q is not kept
         x = bufs[l]
         fsa.rope_forward(x["q"], x["k"], x["v"], table, alpha=alphas[l], w=W, R=R, base=BASE, scale=scale,
-                         out=x["o"], lse=x["lse"], ws=ws)
+                         out=x["o"], lse=x["lse"], ws=ws, keep_rotated=keep)
 
     def bwd(l):
         x = bufs[l]
@@ -346,7 +346,7 @@ def rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
                           base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], ws=ws)
 
     def step(l):  # a training step keeps the forward's rotated rows for its backward
-        fwd(l)
+        fwd(l, keep=True)
         x = bufs[l]
         fsa.rope_backward(x["q"], x["k"], x["v"], table, x["o"], x["lse"], x["do"], alpha=alphas[l], w=W, R=R,
                           base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], ws=ws, reuse_rotated=True)

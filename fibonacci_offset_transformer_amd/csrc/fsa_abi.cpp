@@ -665,8 +665,8 @@ fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int3
 
 fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
                               const float *rope, int32_t n_pos, void *o, float *lse, void *ws, uint64_t ws_bytes,
-                              int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
-                              int32_t w, int32_t R, void *stream) {
+                              int32_t keep_rotated, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                              fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream) {
     const Shape s{B, H, N, d};
     fsa_status_t st = check_common(dt, out_dt, s, scale);
     if (st != FSA_OK) return st;
@@ -685,22 +685,26 @@ fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
         return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
                     static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.fwd));
     char *wsb = static_cast<char *>(ws);
-    const void *xs[] = {q, k};
-    void *hats[] = {wsb + l.qhat, wsb + l.khat};
+    // K is rotated once per row by the rotation pass; the forward kernel rotates its own Q
+    // rows and leaves them in ws beside the rotated K (for the backward to reuse)
+    const void *xs[] = {k};
+    void *hats[] = {wsb + l.khat};
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const hipError_t e = rotate_rows(xs, hats, 2, rope, static_cast<int64_t>(B) * H * N, N, hs);
+    const hipError_t e = rotate_rows(xs, hats, 1, rope, static_cast<int64_t>(B) * H * N, N, hs);
     if (e != hipSuccess) return launched(e, "rotary rotation");
-    p.q = hats[0];
-    p.k = hats[1];
+    p.q = q;
+    p.k = hats[0];
     p.v = v;
     p.out = o;
     p.lse_out = lse;
+    p.rope = rope;
+    p.qhat = keep_rotated ? wsb + l.qhat : nullptr;
     p.bh = B * H;
     p.n = N;
     p.w = w;
     p.scale = scale;
     p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-    return launched(fsa::launch_forward(dt, out_dt, p, hs), "rotary forward");
+    return launched(fsa::launch_rope_forward(out_dt, p, hs), "rotary forward");
 }
 
 fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,

@@ -46,6 +46,7 @@ struct AttnParams {
     // Rotary embedding: when set, the backward kernels rotate dQ and dK of row r back by
     // its position's angles before storing them (table [n_pos, 32, 2] of cos, sin).
     const float *rope;
+    void *qhat;               // rotary forward: rotated Q rows written here [BH, N, 64]
 };
 
 // Rotary embedding of up to two [rows, 64] bf16 tensors (x[t] -> out[t]); rows come in
@@ -104,6 +105,9 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
 // backward (dQ with D, dK/dV, then the reduction of the alpha gradient).
 hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_rope(const RopeParams &p, hipStream_t stream);
+// Rotary forward on the bf16 window path: Q unrotated (rotated in the kernel and stored
+// to p.qhat), K already rotated.
+hipError_t launch_rope_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 
 }  // namespace fsa

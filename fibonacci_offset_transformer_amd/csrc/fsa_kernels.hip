@@ -721,6 +721,31 @@ __global__ void __launch_bounds__(kThreads) rope_kernel(const RopeParams p) {
     }
 }
 
+// Rotates the four channel pairs packed in a 16-byte bf16 chunk by the (cos, sin) table
+// entries t01 (pairs 0, 1) and t23 (pairs 2, 3), rounding the results to bf16 exactly as
+// rope_kernel does.
+__device__ __forceinline__ u32x4_t rope_chunk(const u32x4_t &xv, const f32x4_t &t01, const f32x4_t &t23) {
+    u32x4_t ov;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const f32x4_t &tt = k < 2 ? t01 : t23;
+        const int j = 2 * (k & 1);
+        float re, ro;
+        rope_pair(tt[j], tt[j + 1], bf16_lo(xv[k]), bf16_hi(xv[k]), re, ro);
+        ov[k] = pack_bf16(re, ro);
+    }
+    return ov;
+}
+
+// (cos, sin) table entries of channel pairs 4 c .. 4 c + 3 at position `row` through a
+// descriptor over the table (rows past its range read as zeros).
+__device__ __forceinline__ void rope_entries(__amdgpu_buffer_rsrc_t rt, int row, int c, f32x4_t &t01,
+                                             f32x4_t &t23) {
+    const int off = (row * 32 + 4 * c) * 8;
+    t01 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rt, off, 0, 0));
+    t23 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rt, off + 16, 0, 0));
+}
+
 // Rotates a slab-layout gradient chunk (channels 8 c8 .. 8 c8 + 7 of row `row`) back by
 // the row's angles: the transpose of the forward rotation, (e, o) -> (c e + s o, c o - s e).
 __device__ __forceinline__ void rope_back_chunk(const float *table, int row, int c8, f32x4_t a[2]) {
@@ -878,7 +903,10 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
 // With FRAC the table holds fractional entries (learned-alpha variant): entry t's key
 // and value for row i are (1 - phi) row(i - off[t]) + phi row(i - off[t] - 1), so each
 // entry reads two adjacent slabs (near and far); entries go two per softmax update.
-template <bool OUT_BF16, bool FRAC>
+// With ROPE, Q arrives unrotated (K, V as usual): the kernel rotates its own query rows
+// by the table p.rope and, when p.qhat is set, stores the rotated rows there (for a
+// backward to reuse).
+template <bool OUT_BF16, bool FRAC, bool ROPE = false>
 __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ks[kTileRows * 64];  // band K rows, then merge areas
@@ -909,6 +937,16 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     dma_tile(vs, V, i0 - 64, n, wave, lane);
     Frag<true> qf;
     buf_frag(qf, rq, i, g);
+    [[maybe_unused]] __amdgpu_buffer_rsrc_t rt;
+    if constexpr (ROPE) {
+        rt = head_rsrc(p.rope, n * 256);
+        f32x4_t a01, a23, b01, b23;
+        rope_entries(rt, i, g, a01, a23);      // chunk g: pairs 4g .. 4g + 3
+        rope_entries(rt, i, g + 4, b01, b23);  // chunk g + 4
+        wait_vm_all();
+        qf.c[0] = rope_chunk(qf.c[0], a01, a23);
+        qf.c[1] = rope_chunk(qf.c[1], b01, b23);
+    }
     wait_vm_all();
     __syncthreads();
     // the first slab rows are requested now and land while the band runs; most of them
@@ -999,7 +1037,23 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
 
     // ---- sparse slabs: keys row - off[t], four offsets per online-softmax update ----
     SFrag qs;
-    sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+    if constexpr (ROPE) {
+        // the rotated query rows, already in registers in the MFMA layout (row c16, chunks
+        // g and g + 4), move to the slab layout through this wave's 2 KB of the V tile,
+        // free since the barrier above
+        uint16_t *qa = vs + 1024 * wave + 512;
+        *reinterpret_cast<u32x4_t *>(qa + c16 * 64 + 8 * g) = qf.c[0];
+        *reinterpret_cast<u32x4_t *>(qa + c16 * 64 + 8 * (g + 4)) = qf.c[1];
+        uint16_t *QH = p.qhat ? static_cast<uint16_t *>(p.qhat) + head : nullptr;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            qs.r[h] = *reinterpret_cast<const u32x4_t *>(qa + (s8 + 8 * h) * 64 + 8 * c8);
+            if (p.qhat && row_s[h] < n)  // uniform test of the pointer
+                *reinterpret_cast<u32x4_t *>(QH + (int64_t)row_s[h] * 64 + 8 * c8) = qs.r[h];
+        }
+    } else {
+        sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+    }
     // moves the state to a new maximum; skipped (uniformly) when no row's maximum grew,
     // which the band's 64 keys make the common case
     auto rescale = [&](const float mn[2]) {
@@ -2210,6 +2264,11 @@ hipError_t launch_rope(const RopeParams &p, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_rope_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false, true>, tiles(p), p, s)
+                              : launch(&fwd_window_kernel<false, false, true>, tiles(p), p, s);
 }
 
 hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {

@@ -100,7 +100,7 @@ def library() -> ctypes.CDLL:
                                                    ctypes.POINTER(u64), ctypes.POINTER(u64)]
             L.fsa_rope_workspace_bytes.restype = ctypes.c_int
             L.fsa_rope_forward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, u64, i32, i32,
-                                           i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+                                           i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
             L.fsa_rope_forward.restype = ctypes.c_int
             L.fsa_rope_backward.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                             u64, i32, i32, i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
@@ -409,8 +409,10 @@ def _rope_ws(q, ws, which, alpha, w, R, base):
 
 
 def rope_forward(q, k, v, table, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None, out=None,
-                 lse=None, out_dtype=None, ws=None):
-    """Forward on rotated Q, K (unrotated inputs, rotary table on the device): (o, lse)."""
+                 lse=None, out_dtype=None, ws=None, keep_rotated: bool = True):
+    """Forward on rotated Q, K (unrotated inputs, rotary table on the device): (o, lse).
+    keep_rotated leaves the rotated Q in ws beside the rotated K for rope_backward's
+    reuse_rotated; inference can pass False."""
     B, H, N, d = _shape(q, k, v)
     o = _out(q, out, out_dtype)
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -418,8 +420,9 @@ def rope_forward(q, k, v, table, *, alpha: float = 1.0, w: int, R: int, base: st
     ws, ws_bytes = _rope_ws(q, ws, 0, alpha, w, R, base)
     with torch.cuda.device(q.device):
         _check(library().fsa_rope_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(table),
-                                          n_pos, _ptr(o), _ptr(l), _ptr(ws), ws_bytes, B, H, N, d, _scale(scale, d),
-                                          BASES[base], float(alpha), int(w), int(R), _stream(q.device)))
+                                          n_pos, _ptr(o), _ptr(l), _ptr(ws), ws_bytes, int(bool(keep_rotated)), B, H, N,
+                                          d, _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                                          _stream(q.device)))
     return o, l
 
 

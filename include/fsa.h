@@ -330,9 +330,11 @@ fsa_status_t fsa_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, 
  * rotated-row gradients rotated back by each row's angles (the transpose), with the
  * bf16 rounding passing gradients unchanged.
  *
- * Each key row is gathered by about |T| + 2 query tiles, so the calls rotate Q and
- * K once per row into a workspace (one memory-bound pass) instead of once per
- * gather; the backward's inverse rotation is fused into the store of dQ and dK.
+ * Each key row is gathered by about |T| + 2 query tiles, so the calls rotate K once
+ * per row into a workspace (one memory-bound pass) instead of once per gather; the
+ * forward kernel rotates its own Q rows, the backward rotates Q and K by the same
+ * pass (or reuses the forward's), and its inverse rotation is fused into the store
+ * of dQ and dK.
  * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64; other valid
  * arguments return FSA_E_UNSUPPORTED.
  */
@@ -381,13 +383,17 @@ fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int3
  *   o, lse          outputs as in fsa_forward
  *   ws, ws_bytes    caller-owned device workspace of at least the forward size of
  *                   fsa_rope_workspace_bytes, 16-byte aligned, overwritten (holds
- *                   the rotated Q and K)
+ *                   the rotated K, and the rotated Q when keep_rotated)
+ *   keep_rotated    nonzero: the rotated Q rows are also stored in ws, so that
+ *                   fsa_rope_backward can reuse them (reuse_rotated); 0 (inference)
+ *                   skips that store. K is rotated by a separate pass over its rows;
+ *                   the attention kernel rotates its own Q rows.
  *   other arguments as in fsa_forward
  */
 fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
                               const float *rope, int32_t n_pos, void *o, float *lse, void *ws, uint64_t ws_bytes,
-                              int32_t B, int32_t H, int32_t N, int32_t d, float scale, fsa_base_t base, double alpha,
-                              int32_t w, int32_t R, void *stream);
+                              int32_t keep_rotated, int32_t B, int32_t H, int32_t N, int32_t d, float scale,
+                              fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
 
 /*
  * fsa_rope_backward - gradients of sum(dO * O) of fsa_rope_forward with respect to
@@ -401,8 +407,8 @@ fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
  *                          of fsa_rope_workspace_bytes, 16-byte aligned, overwritten
  *   reuse_rotated          0: the call rotates q and k itself, and the contents of ws on
  *                          entry do not matter. Nonzero: ws's first forward-size bytes
- *                          still hold the rotated rows fsa_rope_forward wrote there for
- *                          these same q, k and table (the activations a training step
+ *                          still hold the rotated rows fsa_rope_forward wrote there, with
+ *                          keep_rotated, for these same q, k and table (the activations a training step
  *                          keeps for its backward); the rotation is skipped. Nothing
  *                          checks this: other contents give wrong gradients.
  *   other arguments as in fsa_backward

@@ -44,7 +44,7 @@ def rot(lib, dt=1, ptrs=None, n_pos=64, B=1, H=1, N=64, d=64):
 def rfwd(lib, dt=1, ptrs=None, n_pos=64, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=1.0, w=16, R=256,
          out_dt=1, ws_bytes=1 << 40):
     p = ptrs or FAKE[:7]  # q k v rope o lse ws
-    return lib.fsa_rope_forward(dt, out_dt, p[0], p[1], p[2], p[3], n_pos, p[4], p[5], p[6], ws_bytes,
+    return lib.fsa_rope_forward(dt, out_dt, p[0], p[1], p[2], p[3], n_pos, p[4], p[5], p[6], ws_bytes, 1,
                                 B, H, N, d, scale, base, alpha, w, R, None)
 
 

@@ -326,3 +326,13 @@ def test_rope_frac_reuse_and_full_size():
     check("dq[1,6]", g1[0][b, h], rq)
     check("dk[1,6]", g1[1][b, h], rk)
     check("dv[1,6]", g1[2][b, h], rv)
+
+
+def test_rope_forward_without_keeping_the_rotation_is_identical():
+    x = inputs(71, 0, (2, 2, 555, 64))
+    table = fsa.rope_table(555, device=dev())
+    kw = dict(alpha=1.4, w=64, R=1024, scale=0.125)
+    a = fsa.rope_forward(x["q"], x["k"], x["v"], table, keep_rotated=True, **kw)
+    b = fsa.rope_forward(x["q"], x["k"], x["v"], table, keep_rotated=False, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
