@@ -18,7 +18,7 @@ rotary-embedding variant (unrotated Q, K in) are timed on the same layers next t
 the static path.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--no-literal]
+                       [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--no-literal] [--no-long]
                        [--cold] [--copy-probe]
 """
 from __future__ import annotations
@@ -251,6 +251,61 @@ def decode_bench(fsa, torch, dev, stream):
     return res
 
 
+def long_context_bench(fsa, torch, dev, stream, scale, reps):
+    """One layer of the power-of-2 control at 8x the sequence length: bf16 [1, 8, 32768, 64],
+    table [64, 128, 256, 512] (w = 64, R = 1024), forward and backward, each timed as a HIP
+    graph of 10 launches."""
+    from fibonacci_offset_transformer_amd import synth
+    Bl, Hl, Nl = 1, 8, 32768
+    x = {k: t.to(dev) for k, t in synth.layer_inputs(5, 0, (Bl, Hl, Nl, D), torch.bfloat16, with_grad=True).items()}
+    kw = dict(alpha=1.0, w=W, R=R, base="pow2", scale=scale)
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((Bl, Hl, Nl), dtype=torch.float32, device=dev)
+    dl = torch.empty_like(lse)
+    g = [torch.empty_like(x["q"]) for _ in range(3)]
+    pw = torch.empty(max(fsa.workspace_bytes(torch.bfloat16, Bl, Hl, Nl, D, **{k: kw[k] for k in ("alpha", "w", "R",
+                                                                                                   "base")}), 16) // 4,
+                     dtype=torch.int32, device=dev)
+
+    def fwd():
+        fsa.forward(x["q"], x["k"], x["v"], out=o, lse=lse, **kw)
+
+    def bwd():
+        fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], dq=g[0], dk=g[1], dv=g[2], delta=dl, pair_ws=pw, **kw)
+
+    res = {}
+    for name, fn in (("fwd", fwd), ("bwd", bwd)):
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(10):
+                fn()
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) * 1e3 / (reps * 10)
+    rows = Bl * Hl * Nl
+    per_row = alg_bytes_per_row()
+    return {
+        "what": "power-of-2 control at 8x the length: bf16 [1,8,32768,64], table [64,128,256,512], one layer",
+        "fwd_us": round(res["fwd"], 2), "bwd_us": round(res["bwd"], 2),
+        "query_heads_per_s": round(rows / ((res["fwd"] + res["bwd"]) * 1e-6), 1),
+        "fwd_gb_s": round(per_row["fwd"] * rows / (res["fwd"] * 1e-6) / 1e9, 1),
+        "bwd_gb_s": round(per_row["bwd"] * rows / (res["bwd"] * 1e-6) / 1e9, 1),
+    }
+
+
 def stage_us(torch, dev, stream, fn, reps):
     """Average duration (us) of one layer's launches of fn: the 16 layers captured back to
     back in a HIP graph, replayed `reps` times (after ten untimed replays) between two
@@ -389,6 +444,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-frac", action="store_true", help="skip the learned-alpha (fractional) variant")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding variant")
+    ap.add_argument("--no-long", action="store_true", help="skip the [1,8,32768,64] power-of-2 layer")
     ap.add_argument("--no-literal", action="store_true",
                     help="skip the run with the literal stagger formula 0.5 + l*(1.5/15)")
     ap.add_argument("--cold", action="store_true",
@@ -674,6 +730,10 @@ def main():
         learned = frac_bench(fsa, torch, dev, stream, bufs, alphas, scale, dict(avg_us, step=static_step_us),
                              max(3, args.steps // 5))
 
+    long_ctx = None
+    if not args.no_long:
+        long_ctx = long_context_bench(fsa, torch, dev, stream, scale, 10)
+
     rope = None
     if not args.no_rope:
         rope = rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, dict(avg_us, step=static_step_us),
@@ -715,6 +775,7 @@ def main():
         "learned_alpha": learned,
         "rope": rope,
         "literal_stagger": literal,
+        "long_context": long_ctx,
         "cold": cold,
     }
     if cpu:
