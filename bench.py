@@ -148,10 +148,10 @@ def kernel_source_sha():
     return hashlib.sha256(open(p, "rb").read()).hexdigest()
 
 
-# Kernels that one launch of each stage runs (bf16, window path), under their short names.
-STAGE_KERNELS = {"fwd": ("fwd",), "bwd": ("dq", "dkdv")}
-KERNEL_NAMES = {"fwd": "fwd_window_kernel<bf16 out>", "dq": "bwd_dq_kernel<bf16 out, D formed>",
-                "dkdv": "bwd_dkdv_kernel<bf16 out>"}
+# Kernels that one launch of each stage runs (bf16, window path, B * H a multiple of 8:
+# the backward's dQ and dK/dV work in one launch), under their short names.
+STAGE_KERNELS = {"fwd": ("fwd",), "bwd": ("bwd",)}
+KERNEL_NAMES = {"fwd": "fwd_window_kernel<bf16 out>", "bwd": "bwd_fused_kernel<bf16 out, D formed>"}
 
 
 def measured_traffic(stage):

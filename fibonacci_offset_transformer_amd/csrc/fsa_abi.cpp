@@ -284,7 +284,8 @@ fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_d
     *empty = static_cast<int64_t>(B) * H * N == 0;
     if (*empty) return FSA_OK;
     p.n_off = trim_offsets(p.off, n_off, N);
-    const uint64_t need = 4ull * static_cast<uint64_t>(fsa::pair_words(dt, w, N, static_cast<int64_t>(B) * H, p.n_off));
+    const int64_t words = fsa::pair_words(dt, w, N, static_cast<int64_t>(B) * H, p.n_off);
+    const uint64_t need = fsa::pair_ws_bytes(dt, w, N, static_cast<int64_t>(B) * H, p.n_off);
     const int np = need > 0 ? 10 : 9;  // the pair workspace is checked only when it is used
     const char *names[] = {"q", "k", "v", "lse", "dout", "delta", "dq", "dk", "dv", "pair_ws"};
     const void *ptrs[] = {q, k, v, lse, dout, delta, dq, dk, dv, pair_ws};
@@ -303,6 +304,8 @@ fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_d
     p.dk = dk;
     p.dv = dv;
     p.pairs = need > 0 ? static_cast<uint32_t *>(pair_ws) : nullptr;
+    p.flags = need > 0 ? reinterpret_cast<uint64_t *>(static_cast<char *>(pair_ws) + fsa::pair_ws_flags_offset(words))
+                       : nullptr;
     p.bh = B * H;
     p.n = N;
     p.w = w;
@@ -323,8 +326,7 @@ fsa_status_t fsa_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, 
     int32_t tab[FSA_MAX_OFFSETS];
     const int n_off = build_table(base, alpha, w, R, tab, &st);
     if (n_off < 0) return st;
-    *bytes = 4ull * static_cast<uint64_t>(
-                        fsa::pair_words(dt, w, N, static_cast<int64_t>(B) * H, trim_offsets(tab, n_off, N)));
+    *bytes = fsa::pair_ws_bytes(dt, w, N, static_cast<int64_t>(B) * H, trim_offsets(tab, n_off, N));
     return ok();
 }
 
@@ -622,7 +624,7 @@ RopeLayout rope_layout(int64_t bh, int32_t n, int32_t n_off) {
     l.fwd = l.khat + fsa::align256(rows * 128);
     l.delta = l.fwd;
     l.pairs = l.delta + fsa::align256(rows * 4);
-    l.bwd = l.pairs + fsa::align256(4ull * fsa::pair_words(FSA_BF16, 64, n, bh, n_off));
+    l.bwd = l.pairs + fsa::align256(fsa::pair_ws_bytes(FSA_BF16, 64, n, bh, n_off));
     return l;
 }
 
@@ -748,6 +750,11 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     p.dv = dv;
     p.delta = reinterpret_cast<float *>(wsb + l.delta);
     p.pairs = p.n_off > 0 ? reinterpret_cast<uint32_t *>(wsb + l.pairs) : nullptr;
+    p.flags = p.n_off > 0 ? reinterpret_cast<uint64_t *>(
+                                wsb + l.pairs +
+                                fsa::pair_ws_flags_offset(fsa::pair_words(FSA_BF16, 64, N, static_cast<int64_t>(B) * H,
+                                                                          p.n_off)))
+                          : nullptr;
     p.rope = rope;
     p.bh = B * H;
     p.n = N;

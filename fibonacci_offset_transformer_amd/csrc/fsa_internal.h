@@ -47,6 +47,8 @@ struct AttnParams {
     // its position's angles before storing them (table [n_pos, 32, 2] of cos, sin).
     const float *rope;
     void *qhat;               // rotary forward: rotated Q rows written here [BH, N, 64]
+    // One-launch static backward: one 64-bit completion token per tile [BH * tiles per head].
+    uint64_t *flags;
 };
 
 // Rotary embedding of up to two [rows, 64] bf16 tensors (x[t] -> out[t]); rows come in
@@ -73,6 +75,17 @@ __host__ __device__ inline int32_t pair_slots(int32_t n_off) { return 8 * ((n_of
 inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
     return window_path(dt, w, n) ? static_cast<int64_t>(pair_slots(n_off)) * bh * n : 0;
 }
+inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// The static backward's workspace on the window path: the pair words, then (256-byte
+// aligned) one 64-bit completion token per 64-row tile, which the one-launch backward
+// uses. Empty when the table has no sparse offsets.
+inline uint64_t pair_ws_flags_offset(int64_t words) { return align256(4ull * static_cast<uint64_t>(words)); }
+inline uint64_t pair_ws_bytes(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
+    const int64_t words = pair_words(dt, w, n, bh, n_off);
+    if (words == 0) return 0;
+    return pair_ws_flags_offset(words) + 8ull * static_cast<uint64_t>(bh) * ((n + 63) / 64);
+}
 
 // Fractional-entry backward workspace on the window path: D [BH, N] floats, then the
 // pair words [BH, N, pair_slots(n_off), 2] (the near and far weights of every
@@ -80,7 +93,6 @@ inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int3
 struct FracWorkspace {
     uint64_t delta, pairs, partials, total;  // byte offsets of the parts, total size
 };
-inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
     FracWorkspace w;
     const uint64_t tiles = static_cast<uint64_t>(bh) * ((n + 63) / 64);

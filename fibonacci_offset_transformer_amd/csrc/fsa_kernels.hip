@@ -1491,6 +1491,44 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
 constexpr int kRingQ = 4, kPreQ = 2;    // dQ kernel: slab slots in the ring; slots requested before the band
 constexpr int kRingKV = 3, kPreKV = 1;  // dK/dV kernel
 
+// ---- one-launch backward: per-tile completion tokens ----
+//
+// A token names one launch: the dispatch id (the packet's index in its queue, which
+// grows by one per dispatch) mixed with the queue's address (each queue counts from
+// zero). The dQ work of a tile writes it to that tile's flag; a workspace's earlier
+// contents, earlier launches' tokens included, do not match it.
+extern "C" __device__ uint64_t fsa_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+__device__ __forceinline__ uint64_t launch_token() {
+    const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
+    return fsa_dispatch_id() ^ (q * 0x9E3779B97F4A7C15ull);
+}
+
+// Cache policy (sc0) for the pair words and D that another workgroup of the same launch
+// wrote, in the same XCD's L2. No CU reads them before their token is set, so no L1
+// holds an older copy.
+constexpr int kCachePastL1 = 1;
+
+// Polls before giving up; with the sleep below they span tens of milliseconds, far
+// beyond any real wait (the dQ work of a whole launch takes tens of microseconds).
+constexpr int kMaxSpins = 1 << 18;
+
+// Waits until flags[first .. last] all hold the token (one wave, 64 tiles per poll, one
+// per lane; device-scope loads, which miss this CU's L1). Returns false, uniformly over
+// the wave, if it gave up; the caller then stores NaN so that the failure shows.
+__device__ __forceinline__ bool poll_tiles(const uint64_t *flags, int first, int last, uint64_t token, int lane) {
+    for (int b = first; b <= last; b += 64) {
+        const int idx = b + lane;
+        for (int spin = 0;; ++spin) {
+            const bool ready =
+                idx > last || __hip_atomic_load(flags + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token;
+            if (__builtin_amdgcn_ballot_w64(!ready) == 0) break;
+            if (spin == kMaxSpins) return false;
+            __builtin_amdgcn_s_sleep(4);
+        }
+    }
+    return true;
+}
+
 // Descriptor over the pair-workspace words of head bh ([N, S] words, S = pair_slots):
 // rows past the sequence end read as zero words.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int bh) {
@@ -1509,18 +1547,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p,
 // stores two words per pair, the near and the far share of P and dS, and adds up, per
 // entry, the derivative of the loss with respect to the entry's distance over its rows
 // (one partial per workgroup and entry; see reduce_alpha_grad).
+//
+// The body works on logical tile lb with the caller's LDS: ta, tb (band K and V rows,
+// kTileRows * 64 each, then merge areas), d_s (64 floats: D of the tile's rows, WITH_D)
+// and dd_s (4 * FSA_MAX_OFFSETS floats, FRAC).
 template <bool OUT_BF16, bool WITH_D, bool FRAC>
-__global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
+__device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *d_s,
+                                        float *dd_s) {
     static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
     using OE = typename Elem<OUT_BF16>::T;
-    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // band K rows, then merge areas
-    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // band V rows
-    __shared__ float d_s[64];                                             // D of the tile's rows (WITH_D)
-    __shared__ float dd_s[FRAC ? 4 * FSA_MAX_OFFSETS : 1];                // per wave and entry (FRAC)
 
     const int n = p.n, w = p.w, n_off = p.n_off;
     const int nt = (n + 63) >> 6;
-    const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
     const int bh = lb / nt, tile = lb - bh * nt;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1757,6 +1795,15 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     }
 }
 
+template <bool OUT_BF16, bool WITH_D, bool FRAC>
+__global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
+    __shared__ float d_s[64];
+    __shared__ float dd_s[FRAC ? 4 * FSA_MAX_OFFSETS : 1];
+    dq_tile<OUT_BF16, WITH_D, FRAC>(p, xcd_logical_block(blockIdx.x, p.bh * ((p.n + 63) >> 6)), ta, tb, d_s, dd_s);
+}
+
 // Alpha gradient of the fractional backward, run by one whole workgroup: d(loss)/d(d_t)
 // is the sum of the dQ kernel's per-tile partials of entry t, and d(loss)/d(alpha) =
 // sum_t fbase[t] * d(loss)/d(d_t), since every target distance is alpha times its base
@@ -1793,17 +1840,21 @@ __device__ void reduce_alpha_grad(const AttnParams &p, double *red) {
 // With FRAC, key row j receives entry t from two queries: j + off[t], whose key mixes
 // row j with weight 1 - phi (its near word), and j + off[t] + 1, whose key mixes row j
 // with weight phi (its far word).
-template <bool OUT_BF16, bool FRAC>
-__global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) {
+//
+// The body works on logical tile lb with the caller's LDS: ta, tb (band Q and dO rows,
+// then merge areas), lse_s and del_s (log2-scaled LSE and D of the band queries,
+// kTileRows floats each). With FUSED the dQ work of the same call runs in the same
+// launch (bwd_fused_kernel): D and the pair words are read only once the tiles that
+// write them have published this launch's token (poll_tiles, while the band rows load).
+// FROM_DQ: D comes from that dQ work (otherwise the caller gave it).
+template <bool OUT_BF16, bool FRAC, bool FUSED = false, bool FROM_DQ = false>
+__device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *lse_s,
+                                          float *del_s, [[maybe_unused]] const uint64_t token = 0) {
+    static_assert(FUSED || !FROM_DQ, "D comes from the same launch only in the one-launch backward");
     using OE = typename Elem<OUT_BF16>::T;
-    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];  // band Q rows, then merge areas
-    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];  // band dO rows, then merge areas
-    __shared__ __attribute__((aligned(16))) float lse_s[kTileRows];       // log2-scaled LSE of band queries
-    __shared__ __attribute__((aligned(16))) float del_s[kTileRows];       // D of band queries
 
     const int n = p.n, w = p.w, n_off = p.n_off;
     const int nt = (n + 63) >> 6;
-    const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
     const int bh = lb / nt, tile = lb - bh * nt;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1831,13 +1882,43 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
     if (tid < kTileRows) {
         const int row = t0 + tid;
         lse_s[tid] = (row < n) ? LSE[row] * kLog2e : 0.f;
-        del_s[tid] = (row < n) ? DEL[row] : 0.f;
+        if constexpr (!FROM_DQ) del_s[tid] = (row < n) ? DEL[row] : 0.f;
     }
     Frag<true> kf, vf;
     buf_frag<kCacheNT>(kf, rk, j, g);  // read once by this kernel
     buf_frag<kCacheNT>(vf, rv, j, g);
-    wait_vm_all();
-    __syncthreads();
+    // scales of the stored dK and dV: NaN if the wait below gave up, so that it shows
+    float k_mul = p.scale, v_mul = 1.f;
+    if constexpr (FUSED) {
+        // D of the band queries (tiles tile and tile + 1) and the pair words of the slab
+        // queries (up to row + max offset) come from this launch's dQ work: wait for
+        // those tiles while the band rows are in flight
+        __shared__ int gave_up;
+        if (wave == 0) {
+            const int far = n_off > 0 ? t0 + 63 + p.off[n_off - 1] : t0;
+            const int last = min(nt - 1, max(FROM_DQ ? tile + 1 : tile, far >> 6));
+            const bool ok = poll_tiles(p.flags + (int64_t)bh * nt, tile, last, token, lane);
+            if (lane == 0) gave_up = ok ? 0 : 1;
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(gave_up)) {
+            k_mul = __builtin_nanf("");
+            v_mul = k_mul;
+        }
+        if constexpr (FROM_DQ) {
+            if (tid < kTileRows) {
+                const int row = t0 + tid;
+                del_s[tid] = (row < n) ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                             head_rsrc(DEL, n * 4), row * 4, 0, kCachePastL1))
+                                       : 0.f;
+            }
+        }
+        wait_vm_all();
+        __syncthreads();
+    } else {
+        wait_vm_all();
+        __syncthreads();
+    }
 
     // slot u: query rows row + off[t] (Q, dO) and their pair weights (word t of each row)
     // slot u of the ring. FRAC: the ring runs over half entries, 2t (the near queries
@@ -1848,18 +1929,26 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
     const int slots = pair_slots(n_off);
     const __amdgpu_buffer_rsrc_t rp =
         FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, n * slots * 8) : pair_rsrc(p, bh);
-    auto fill = [&](int u, int x) {
+    auto fill_words = [&](int u, int x) {
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
         const int iq0 = slab_row(p, t, row_s[0], 1) + far, iq1 = slab_row(p, t, row_s[1], 1) + far;
-        sfrag_load(sq[u], rq, iq0, iq1, c8);
-        sfrag_load(sd[u], rdo, iq0, iq1, c8);
         if constexpr (FRAC) {
             pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq0 * slots + t) * 2 + far) * 4, 0, 0);
             pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0, 0);
         } else {
-            pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, 0);
-            pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, 0);
+            pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, FUSED ? kCachePastL1 : 0);
+            pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, FUSED ? kCachePastL1 : 0);
         }
+    };
+    auto fill_rows = [&](int u, int x) {
+        const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
+        const int iq0 = slab_row(p, t, row_s[0], 1) + far, iq1 = slab_row(p, t, row_s[1], 1) + far;
+        sfrag_load(sq[u], rq, iq0, iq1, c8);
+        sfrag_load(sd[u], rdo, iq0, iq1, c8);
+    };
+    auto fill = [&](int u, int x) {
+        fill_rows(u, x);
+        fill_words(u, x);
     };
 #pragma unroll
     for (int u = 0; u < kPreKV; ++u) fill(u, u);
@@ -1963,8 +2052,8 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (row_s[h] < n) {
-            store_chunk<true>(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], p.scale);
-            store_chunk<true>(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], 1.f);
+            store_chunk<true>(static_cast<OE *>(p.dk) + head, row_s[h], c8, dk_s[h], k_mul);
+            store_chunk<true>(static_cast<OE *>(p.dv) + head, row_s[h], c8, dv_s[h], v_mul);
         }
     }
     // FRAC: the dQ kernel, which ran before this one on the stream, left the alpha
@@ -1975,6 +2064,45 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
             __syncthreads();              // the LDS tiles are free again
             reduce_alpha_grad(p, reinterpret_cast<double *>(ta));
         }
+    }
+}
+
+template <bool OUT_BF16, bool FRAC>
+__global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
+    __shared__ __attribute__((aligned(16))) float lse_s[kTileRows];
+    __shared__ __attribute__((aligned(16))) float del_s[kTileRows];
+    dkdv_tile<OUT_BF16, FRAC>(p, xcd_logical_block(blockIdx.x, p.bh * ((p.n + 63) >> 6)), ta, tb, lse_s, del_s);
+}
+
+// The static backward in one launch: blocks [0, tiles) do the dQ work of tile
+// xcd_logical_block(b), blocks [tiles, 2 tiles) the dK/dV work of tile
+// xcd_logical_block(b - tiles). A dQ tile publishes this launch's token in p.flags once
+// its pair words are in L2; a dK/dV tile waits for the tokens of the tiles whose pair
+// words it reads (D it forms itself, or reads from the caller).
+// Workgroups are dispatched in block order, so every dQ tile has been dispatched before
+// any dK/dV tile waits, and dQ tiles wait for nothing: the waits end. The host launches
+// this only when B * H is a multiple of 8: every XCD then holds whole heads, so a tile
+// and the tiles it waits for share one XCD and its L2.
+template <bool OUT_BF16, bool WITH_D>
+__global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
+    __shared__ __attribute__((aligned(16))) float fa[kTileRows];  // dQ: D of its rows; dK/dV: LSE of the band
+    __shared__ __attribute__((aligned(16))) float fb[kTileRows];  // dK/dV: D of the band
+    const int tiles = p.bh * ((p.n + 63) >> 6);
+    const uint64_t token = launch_token();
+    if (static_cast<int>(blockIdx.x) < tiles) {
+        const int lb = xcd_logical_block(blockIdx.x, tiles);
+        dq_tile<OUT_BF16, WITH_D, false>(p, lb, ta, tb, fa, fb);
+        // every wave's stores (pair words, D, dQ) have reached L2 before the token does
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        dkdv_tile<OUT_BF16, false, true, WITH_D>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb, fa, fb,
+                                                 token);
     }
 }
 
@@ -2228,6 +2356,15 @@ hipError_t launch_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnPara
 hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s,
                                  bool with_delta) {
     if (window_path(dt, p)) {
+        // one launch when every XCD holds whole heads (its waits stay within one L2)
+        if (p.flags && p.n_off > 0 && p.bh % 8 == 0) {
+            const unsigned grid = 2 * tiles(p);
+            if (with_delta)
+                return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true>, grid, p, s)
+                                          : launch(&bwd_fused_kernel<false, true>, grid, p, s);
+            return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, false>, grid, p, s)
+                                      : launch(&bwd_fused_kernel<false, false>, grid, p, s);
+        }
         hipError_t e;
         if (with_delta)
             e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, false>, tiles(p), p, s)

@@ -126,7 +126,8 @@ fsa_status_t fsa_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, cons
  *   pair_ws             caller-owned device workspace of at least
  *                       fsa_backward_workspace_bytes(...) bytes, 16-byte aligned,
  *                       overwritten; its contents on entry do not matter. It may
- *                       be NULL when that size is 0.
+ *                       be NULL when that size is 0. Two calls that overlap in
+ *                       time must not share one.
  *   pair_ws_bytes       size of pair_ws in bytes; FSA_E_ARG if smaller than needed
  */
 fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
@@ -139,12 +140,17 @@ fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, con
  * fsa_backward_workspace_bytes - bytes of pair workspace the backward needs.
  *
  * On the bf16 window path (dt = FSA_BF16, w <= 64, N <= 2^24) the gradient stage
- * runs as two kernels: the first stores, for every query row i and sparse offset
- * o of the table (offsets >= N dropped), the bf16 values of P and dS of the pair
- * (i, i - o) in one 32-bit word; the second reads them to form dK and dV. The
- * size is 4 * S * B * H * N bytes there, S = |T| rounded up to a multiple of 8
- * (words per query row), and 0 on every other path. Arguments as in
- * fsa_backward; *bytes receives the size.
+ * has two parts: the dQ part stores, for every query row i and sparse offset o of
+ * the table (offsets >= N dropped), the bf16 values of P and dS of the pair
+ * (i, i - o) in one 32-bit word; the dK/dV part reads them. When B * H is a
+ * multiple of 8 both parts run in one launch: each 64-row tile's dQ part then
+ * publishes a 64-bit token naming the launch (from the hardware dispatch id), and
+ * the dK/dV parts wait for the tokens of the tiles they read (a bounded wait; if
+ * it ever gave up, that tile's dK and dV would be NaN). Otherwise they run as two
+ * kernels. The size is 4 * S * B * H * N bytes of pair words, S = |T| rounded up
+ * to a multiple of 8 (words per query row), rounded up to a multiple of 256, plus
+ * 8 * B * H * ceil(N / 64) bytes of tokens; 0 on every other path or when no
+ * offset is below N. Arguments as in fsa_backward; *bytes receives the size.
  */
 fsa_status_t fsa_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                                           fsa_base_t base, double alpha, int32_t w, int32_t R,
@@ -369,7 +375,7 @@ fsa_status_t fsa_rope_rotate(fsa_dtype_t dt, const void *x, const float *rope, i
 /*
  * fsa_rope_workspace_bytes - bytes of ws the rotary forward and backward need:
  * forward 2 B H N d * 2 (the rotated Q and K, each part rounded up to 256 bytes);
- * backward that plus 4 B H N (D) plus fsa_backward_workspace_bytes' pair words.
+ * backward that plus 4 B H N (D) plus fsa_backward_workspace_bytes (pair words and tokens).
  * Arguments as in fsa_rope_forward; 0 and 0 for an empty problem.
  */
 fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d, fsa_base_t base,

@@ -207,14 +207,26 @@ def ws_bytes(lib, dt=1, B=2, H=8, N=4096, d=64, base=0, alpha=1.0, w=64, R=1024)
     return st, out.value
 
 
+def a256(x):
+    return (x + 255) // 256 * 256
+
+
+def pair_ws(words, bh, n):
+    # the pair words, then (256-byte aligned) one 64-bit completion token per 64-row tile
+    return a256(4 * words) + 8 * bh * ((n + 63) // 64)
+
+
 def test_backward_workspace_size(lib):
     # bf16, window 64: one 32-bit word per (head, row, offset slot), slots rounded up to
     # a multiple of 8; alpha = 1, R = 1024 gives the offsets 89, 144, 233, 377, 610, 987
-    assert ws_bytes(lib) == (fsa.FSA_OK, 4 * 8 * 16 * 4096)
+    assert ws_bytes(lib) == (fsa.FSA_OK, pair_ws(8 * 16 * 4096, 16, 4096))
+    assert pair_ws(8 * 16 * 4096, 16, 4096) == 4 * 8 * 16 * 4096 + 8 * 16 * 64
     # offsets >= N are dropped: at N = 600 only 89, 144, 233, 377 remain (still 8 slots)
-    assert ws_bytes(lib, N=600) == (fsa.FSA_OK, 4 * 8 * 16 * 600)
+    assert ws_bytes(lib, N=600) == (fsa.FSA_OK, pair_ws(8 * 16 * 600, 16, 600))
     # a table of 9 offsets takes 16 slots: w = 1, alpha = 1, R = 60 gives 1, 2, 3, 5, 8, 13, 21, 34, 55
-    assert ws_bytes(lib, w=1, R=60) == (fsa.FSA_OK, 4 * 16 * 16 * 4096)
+    assert ws_bytes(lib, w=1, R=60) == (fsa.FSA_OK, pair_ws(16 * 16 * 4096, 16, 4096))
+    # an odd row count (offset 89 only): the token area starts 256-byte aligned
+    assert ws_bytes(lib, B=1, H=3, N=101) == (fsa.FSA_OK, pair_ws(8 * 3 * 101, 3, 101))
     # no offset below N: no slots
     assert ws_bytes(lib, N=50, alpha=1.0, w=64) == (fsa.FSA_OK, 0)
     # paths without the pair workspace: fp32 inputs, wide windows
@@ -228,10 +240,11 @@ def test_backward_workspace_size(lib):
 
 @pytest.mark.parametrize("call", [bwd, grads])
 def test_backward_pair_workspace_checks(lib, call):
-    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 8 slots * 64 rows.
-    # Only failing validations are exercised here (the pointers are fake); the calls
-    # that pass NULL for an unneeded workspace run in the GPU tests (fp32 inputs).
-    need = 4 * 8 * 64
+    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 8 slots * 64 rows,
+    # then one token for the single tile. Only failing validations are exercised here
+    # (the pointers are fake); the calls that pass NULL for an unneeded workspace run in
+    # the GPU tests (fp32 inputs).
+    need = pair_ws(8 * 64, 1, 64)
     assert call(lib, pair_bytes=need - 1) == fsa.FSA_E_ARG
     assert b"pair_ws holds" in lib.fsa_last_error()
     assert call(lib, pair_bytes=0) == fsa.FSA_E_ARG

@@ -103,7 +103,8 @@ def test_rope_workspace_sizes(lib):
     rows = 2 * 8 * 4096
     fwd = 2 * a256(rows * 128)
     assert f.value == fwd
-    pair = 4 * 8 * rows  # six offsets at alpha = 1, w = 64, R = 1024 -> 8 slots
+    # six offsets at alpha = 1, w = 64, R = 1024 -> 8 slots, then one 64-bit token per tile
+    pair = a256(4 * 8 * rows) + 8 * 16 * 64
     assert b.value == fwd + a256(4 * rows) + a256(pair)
     assert lib.fsa_rope_workspace_bytes(1, 0, 8, 4096, 64, 0, 1.0, 64, 1024, ctypes.byref(f), ctypes.byref(b)) == 0
     assert f.value == 0 and b.value == 0

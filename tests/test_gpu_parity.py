@@ -300,12 +300,13 @@ def test_forward_any_scale(scale):
         check(f"lse[0,{h}] scale={scale}", lse[0, h], rl, TOL[torch.bfloat16])
 
 
-def test_pair_workspace_contents_do_not_matter():
-    # every word the dK/dV kernel reads was written by the dQ kernel of the same call
-    x = inputs(20, 0, (1, 2, 777, 64), torch.bfloat16, grad=True)
+@pytest.mark.parametrize("H", [2, 8], ids=["two_kernels", "one_launch"])
+def test_pair_workspace_contents_do_not_matter(H):
+    # every word the dK/dV work reads was written by the dQ work of the same call
+    x = inputs(20, 0, (1, H, 777, 64), torch.bfloat16, grad=True)
     kw = dict(alpha=0.75, w=64, R=1024, scale=0.125)
     o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
-    need = fsa.workspace_bytes(torch.bfloat16, 1, 2, 777, alpha=0.75, w=64, R=1024)
+    need = fsa.workspace_bytes(torch.bfloat16, 1, H, 777, alpha=0.75, w=64, R=1024)
     assert need > 0
     runs = []
     for fill in (0, 0x7FC07FC0, -1):  # zeros, NaN bit patterns, all ones
@@ -316,10 +317,55 @@ def test_pair_workspace_contents_do_not_matter():
         for a, b in zip(runs[0], other):
             assert torch.equal(a, b)
     T = oracle.offset_table("fib", 0.75, 64, 1024)
-    for h in range(2):
+    for h in range(H):
         q, k, v, do = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v", "do"))
         for name, got, want in zip(("dq", "dk", "dv"), runs[0], oracle.sparse_backward(q, k, v, do, T, 64, 0.125)):
             check(f"{name}[0,{h}]", got[0, h], want, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("N,alpha", [(65, 1.0), (777, 0.75), (1500, 1.4)])
+def test_one_launch_backward_equals_per_head_backward(N, alpha):
+    # B * H a multiple of 8 takes the one-launch backward (dK/dV tiles wait for the dQ
+    # tiles' tokens); one head at a time takes the two-kernel path: the same arithmetic
+    # per tile, so the results agree bit for bit
+    x = inputs(22, 0, (2, 4, N, 64), torch.bfloat16, grad=True)
+    kw = dict(alpha=alpha, w=64, R=1024, scale=0.125)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    note(f"one-launch backward N={N} alpha={alpha}")
+    whole = fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], out_dtype=torch.float32, **kw)
+    D = fsa.backward_delta(o, x["do"])
+    staged = fsa.backward_grads(x["q"], x["k"], x["v"], lse, x["do"], D, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    for b in range(2):
+        for h in range(4):
+            one = {t: x[t][b:b + 1, h:h + 1].clone() for t in ("q", "k", "v", "do")}
+            ref = fsa.backward(one["q"], one["k"], one["v"], o[b:b + 1, h:h + 1].clone(),
+                               lse[b:b + 1, h:h + 1].clone(), one["do"], out_dtype=torch.float32, **kw)
+            torch.cuda.synchronize()
+            for name, a, a2, r in zip(("dq", "dk", "dv"), whole, staged, ref):
+                assert torch.equal(a[b, h], r[0, 0]), (name, b, h)
+                assert torch.equal(a2[b, h], r[0, 0]), (name, b, h, "staged")
+
+
+def test_one_launch_backward_reused_workspace():
+    # consecutive calls on one workspace with different inputs, on two streams: each call
+    # waits for its own launch's tokens, never an earlier call's (whose pair words differ)
+    kw = dict(alpha=1.1, w=64, R=1024, scale=0.125)
+    need = fsa.workspace_bytes(torch.bfloat16, 1, 8, 900, alpha=1.1, w=64, R=1024)
+    pw = torch.full((need // 4,), -1, dtype=torch.int32, device=dev())
+    other = torch.cuda.Stream()
+    for seed in (23, 24, 25, 26):
+        x = inputs(seed, 0, (1, 8, 900, 64), torch.bfloat16, grad=True)
+        o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
+        fresh = fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], **kw)
+        torch.cuda.synchronize()
+        s = other if seed % 2 else torch.cuda.current_stream()
+        with torch.cuda.stream(s):
+            got = fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], pair_ws=pw, **kw)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv"), got, fresh):
+            assert torch.equal(a, b), (seed, name)
+            assert bool(torch.isfinite(a.float()).all()), (seed, name)
 
 
 def test_graph_replays_match_eager():
