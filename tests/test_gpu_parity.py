@@ -323,15 +323,16 @@ def test_pair_workspace_contents_do_not_matter(H):
             check(f"{name}[0,{h}]", got[0, h], want, TOL[torch.bfloat16])
 
 
-@pytest.mark.parametrize("N,alpha", [(65, 1.0), (777, 0.75), (1500, 1.4)])
-def test_one_launch_backward_equals_per_head_backward(N, alpha):
+@pytest.mark.parametrize("N,alpha,w", [(65, 1.0, 64), (777, 0.75, 64), (1500, 1.4, 64),
+                                       (1100, 1.0, 1)])  # the last: 15 offsets, 16 pair slots
+def test_one_launch_backward_equals_per_head_backward(N, alpha, w):
     # B * H a multiple of 8 takes the one-launch backward (dK/dV tiles wait for the dQ
     # tiles' tokens); one head at a time takes the two-kernel path: the same arithmetic
     # per tile, so the results agree bit for bit
     x = inputs(22, 0, (2, 4, N, 64), torch.bfloat16, grad=True)
-    kw = dict(alpha=alpha, w=64, R=1024, scale=0.125)
+    kw = dict(alpha=alpha, w=w, R=1024, scale=0.125)
     o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
-    note(f"one-launch backward N={N} alpha={alpha}")
+    note(f"one-launch backward N={N} alpha={alpha} w={w}")
     whole = fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], out_dtype=torch.float32, **kw)
     D = fsa.backward_delta(o, x["do"])
     staged = fsa.backward_grads(x["q"], x["k"], x["v"], lse, x["do"], D, out_dtype=torch.float32, **kw)
@@ -345,6 +346,11 @@ def test_one_launch_backward_equals_per_head_backward(N, alpha):
             for name, a, a2, r in zip(("dq", "dk", "dv"), whole, staged, ref):
                 assert torch.equal(a[b, h], r[0, 0]), (name, b, h)
                 assert torch.equal(a2[b, h], r[0, 0]), (name, b, h, "staged")
+    # and one head against the oracle
+    T = oracle.offset_table("fib", alpha, w, 1024)
+    q, k, v, do = (synth.as_f64(x[t][1, 3]) for t in ("q", "k", "v", "do"))
+    for name, got, want in zip(("dq", "dk", "dv"), whole, oracle.sparse_backward(q, k, v, do, T, w, 0.125)):
+        check(f"{name}[1,3]", got[1, 3], want, TOL[torch.bfloat16])
 
 
 def test_one_launch_backward_reused_workspace():

@@ -4,7 +4,8 @@ variant and the rotary variant (bf16, w <= 64).
 
 Sequence lengths, windows, alphas, reaches and bases are drawn from a fixed seed, so
 the sweep covers ragged tails, tables of 0 to 15 entries, windows wider than a tile
-and single-row sequences. Forward outputs are compared at the usual bars (1e-5 fp32,
+and single-row sequences; seeds 40 to 51 draw B * H = 8, whose bf16 backward runs as
+one launch. Forward outputs are compared at the usual bars (1e-5 fp32,
 1e-2 bf16). The backward is handed the oracle's own O (rounded to the input dtype)
 and LSE (rounded to fp32), and compared with the oracle's backward of those same
 inputs (P = exp(s - lse), D = <dO, o>); for the learned-alpha variant the alpha
@@ -41,7 +42,7 @@ def check(name, gpu, ref, tol):
     return err
 
 
-def draw(seed, wide_windows):
+def draw(seed, wide_windows, heads8=False):
     r = np.random.default_rng(seed)
     N = int(r.choice([1, 2, 63, 64, 65, int(r.integers(3, 400)), int(r.integers(400, 1500))]))
     w = int(r.integers(1, 130 if wide_windows else 65))
@@ -49,6 +50,10 @@ def draw(seed, wide_windows):
     R = int(r.choice([1, 2, 64, 200, 1024, 2048]))
     base = "pow2" if r.random() < 0.3 else "fib"
     B, H = int(r.integers(1, 3)), int(r.integers(1, 3))
+    if heads8:  # B * H = 8 with sparse offsets below N: the backward runs as one launch
+        B, H = [(1, 8), (2, 4), (4, 2), (8, 1)][int(r.integers(0, 4))]
+        N = int(r.choice([65, 130, 257, int(r.integers(66, 700))]))
+        R = int(r.choice([64, 200, 1024, 2048]))
     return B, H, N, w, alpha, R, base
 
 
@@ -63,11 +68,13 @@ def oracle_outputs(x, B, H, fwd):
 
 
 STATIC = [(s, dt) for s in range(12) for dt in (torch.float32, torch.bfloat16)]
+ONE_LAUNCH = [(s, torch.bfloat16) for s in range(40, 52)]
 
 
-@pytest.mark.parametrize("seed,dtype", STATIC, ids=[f"{s}-{'f32' if d == torch.float32 else 'bf16'}" for s, d in STATIC])
+@pytest.mark.parametrize("seed,dtype", STATIC + ONE_LAUNCH,
+                         ids=[f"{s}-{'f32' if d == torch.float32 else 'bf16'}" for s, d in STATIC + ONE_LAUNCH])
 def test_sweep_static(seed, dtype):
-    B, H, N, w, alpha, R, base = draw(100 + seed, wide_windows=True)
+    B, H, N, w, alpha, R, base = draw(100 + seed, wide_windows=seed < 40, heads8=seed >= 40)
     note(f"static {dtype} B={B} H={H} N={N} w={w} alpha={alpha:.4f} R={R} base={base}")
     x = {k: v.to(dev()) for k, v in synth.layer_inputs(80 + seed, 0, (B, H, N, 64), dtype, with_grad=True).items()}
     kw = dict(alpha=alpha, w=w, R=R, base=base, scale=0.125)
