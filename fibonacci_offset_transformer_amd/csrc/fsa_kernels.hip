@@ -418,14 +418,14 @@ __device__ __forceinline__ float buf_f32(__amdgpu_buffer_rsrc_t r, int idx) {
 // Row that sparse offset t pairs with row `row`: row - off[t] (sign -1) or row + off[t]
 // (sign +1); t beyond the table yields an offset of 0. Used as a buffer-load row only
 // (out-of-range rows read as zeros); the caller masks pairs outside the sequence.
-__device__ __forceinline__ int slab_row(const AttnParams &p, int t, int row, int sign) {
+__device__ __forceinline__ int slab_row(const AttnParams &p, int n_off, int t, int row, int sign) {
     const int o = p.off[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1];
-    return row + sign * (t < p.n_off ? o : 0);
+    return row + sign * (t < n_off ? o : 0);
 }
 
 // Offset t of the table, or a value no row can reach when t is past the table.
-__device__ __forceinline__ int table_off(const AttnParams &p, int t) {
-    return t < p.n_off ? p.off[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1] : 0x3fffffff;
+__device__ __forceinline__ int table_off(const AttnParams &p, int n_off, int t) {
+    return t < n_off ? p.off[t < FSA_MAX_OFFSETS ? t : FSA_MAX_OFFSETS - 1] : 0x3fffffff;
 }
 
 // Fractional entries: the weight phi[t] of the far row (row - off[t] - 1), 0 past the
@@ -906,13 +906,13 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
 // With ROPE, Q arrives unrotated (K, V as usual): the kernel rotates its own query rows
 // by the table p.rope and, when p.qhat is set, stores the rotated rows there (for a
 // backward to reuse).
-template <bool OUT_BF16, bool FRAC, bool ROPE = false>
+template <bool OUT_BF16, bool FRAC, bool ROPE = false, int NOFF = 0>
 __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p) {
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ks[kTileRows * 64];  // band K rows, then merge areas
     __shared__ __attribute__((aligned(16))) uint16_t vs[kTileRows * 64];  // band V rows, then band row stats
 
-    const int n = p.n, w = p.w, n_off = p.n_off;
+    const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
     const int nt = (n + 63) >> 6;
     const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
     const int bh = lb / nt, tile = lb - bh * nt;
@@ -953,7 +953,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     // are rows of neighbouring tiles whose band copies have just passed through L2
     SFrag sk[4], sv[4];  // FRAC: slot u of entries holds near rows in [2u], far rows in [2u + 1]
     auto frac_fill = [&](SFrag *f, __amdgpu_buffer_rsrc_t r, int u, int t) {
-        const int n0 = slab_row(p, t, row_s[0], -1), n1 = slab_row(p, t, row_s[1], -1);
+        const int n0 = slab_row(p, n_off, t, row_s[0], -1), n1 = slab_row(p, n_off, t, row_s[1], -1);
         sfrag_load(f[2 * u], r, n0, n1, c8);
         sfrag_load(f[2 * u + 1], r, n0 - 1, n1 - 1, c8);
     };
@@ -966,8 +966,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            sfrag_load(sk[u], rk, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
-            sfrag_load(sv[u], rv, slab_row(p, u, row_s[0], -1), slab_row(p, u, row_s[1], -1), c8);
+            sfrag_load(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+            sfrag_load(sv[u], rv, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
         }
     }
 
@@ -1114,7 +1114,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             float ss[4][2], gm[2] = {kNegInf, kNegInf};    // unscaled scores
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int o = table_off(p, t0 + u);
+                const int o = table_off(p, n_off, t0 + u);
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     ss[u][h] = kNegInf;
@@ -1126,7 +1126,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                     }
                 }
                 if (t0 == 0)
-                    sfrag_load(sk[u], rk, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+                    sfrag_load(sk[u], rk, slab_row(p, n_off, u + 4, row_s[0], -1), slab_row(p, n_off, u + 4, row_s[1], -1), c8);
             }
             const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
             rescale(mn);
@@ -1142,7 +1142,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                     }
                 }
                 if (t0 == 0)
-                    sfrag_load(sv[u], rv, slab_row(p, u + 4, row_s[0], -1), slab_row(p, u + 4, row_s[1], -1), c8);
+                    sfrag_load(sv[u], rv, slab_row(p, n_off, u + 4, row_s[0], -1), slab_row(p, n_off, u + 4, row_s[1], -1), c8);
             }
         }
         for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
@@ -1531,8 +1531,8 @@ __device__ __forceinline__ bool poll_tiles(const uint64_t *flags, int first, int
 
 // Descriptor over the pair-workspace words of head bh ([N, S] words, S = pair_slots):
 // rows past the sequence end read as zero words.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int bh) {
-    const int slots = pair_slots(p.n_off);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int n_off, int bh) {
+    const int slots = pair_slots(n_off);
     return head_rsrc(p.pairs + (int64_t)bh * p.n * slots, p.n * slots * 4);
 }
 
@@ -1551,13 +1551,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p,
 // The body works on logical tile lb with the caller's LDS: ta, tb (band K and V rows,
 // kTileRows * 64 each, then merge areas), d_s (64 floats: D of the tile's rows, WITH_D)
 // and dd_s (4 * FSA_MAX_OFFSETS floats, FRAC).
-template <bool OUT_BF16, bool WITH_D, bool FRAC>
+template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *d_s,
                                         float *dd_s) {
     static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
     using OE = typename Elem<OUT_BF16>::T;
 
-    const int n = p.n, w = p.w, n_off = p.n_off;
+    const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
     const int nt = (n + 63) >> 6;
     const int bh = lb / nt, tile = lb - bh * nt;
     const int lane = threadIdx.x & 63;
@@ -1612,19 +1612,19 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     // the first slab rows land while the band runs
     SFrag sk[kRingQ], sv[kRingQ];  // FRAC: entry slot u holds near rows in [2u], far rows in [2u + 1]
     auto fill = [&](int u, int t) {
-        sfrag_load(sk[u], rk, slab_row(p, t, row_s[0], -1), slab_row(p, t, row_s[1], -1), c8);
-        sfrag_load(sv[u], rv, slab_row(p, t, row_s[0], -1), slab_row(p, t, row_s[1], -1), c8);
+        sfrag_load(sk[u], rk, slab_row(p, n_off, t, row_s[0], -1), slab_row(p, n_off, t, row_s[1], -1), c8);
+        sfrag_load(sv[u], rv, slab_row(p, n_off, t, row_s[0], -1), slab_row(p, n_off, t, row_s[1], -1), c8);
     };
     // FRAC: K rows of two entries in flight (slot u: near rows in sk[2u], far rows in
     // sk[2u + 1]), V rows of one (sv[0] near, sv[1] far), requested as soon as the
     // previous entry's V rows have been used
     auto frac_load_k = [&](int u, int t) {
-        const int n0 = slab_row(p, t, row_s[0], -1), n1 = slab_row(p, t, row_s[1], -1);
+        const int n0 = slab_row(p, n_off, t, row_s[0], -1), n1 = slab_row(p, n_off, t, row_s[1], -1);
         sfrag_load(sk[2 * u], rk, n0, n1, c8);
         sfrag_load(sk[2 * u + 1], rk, n0 - 1, n1 - 1, c8);
     };
     auto frac_load_v = [&](int t) {
-        const int n0 = slab_row(p, t, row_s[0], -1), n1 = slab_row(p, t, row_s[1], -1);
+        const int n0 = slab_row(p, n_off, t, row_s[0], -1), n1 = slab_row(p, n_off, t, row_s[1], -1);
         sfrag_load(sv[0], rv, n0, n1, c8);
         sfrag_load(sv[1], rv, n0 - 1, n1 - 1, c8);
     };
@@ -1762,7 +1762,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
             if (s0 >= n_off || r0 + 15 < p.off[s0]) break;  // ascending offsets: no key left
 #pragma unroll
             for (int u = 0; u < kRingQ; ++u) {
-                if (s0 + u < n_off) slab(s0 + u, table_off(p, s0 + u), sk[u], sv[u]);  // uniform
+                if (s0 + u < n_off) slab(s0 + u, table_off(p, n_off, s0 + u), sk[u], sv[u]);  // uniform
                 if (s0 + kRingQ < unrolled_slabs(kRingQ)) fill(u, s0 + u + kRingQ);
             }
         }
@@ -1847,13 +1847,13 @@ __device__ void reduce_alpha_grad(const AttnParams &p, double *red) {
 // launch (bwd_fused_kernel): D and the pair words are read only once the tiles that
 // write them have published this launch's token (poll_tiles, while the band rows load).
 // FROM_DQ: D comes from that dQ work (otherwise the caller gave it).
-template <bool OUT_BF16, bool FRAC, bool FUSED = false, bool FROM_DQ = false>
+template <bool OUT_BF16, bool FRAC, bool FUSED = false, bool FROM_DQ = false, int NOFF = 0>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *lse_s,
                                           float *del_s, [[maybe_unused]] const uint64_t token = 0) {
     static_assert(FUSED || !FROM_DQ, "D comes from the same launch only in the one-launch backward");
     using OE = typename Elem<OUT_BF16>::T;
 
-    const int n = p.n, w = p.w, n_off = p.n_off;
+    const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
     const int nt = (n + 63) >> 6;
     const int bh = lb / nt, tile = lb - bh * nt;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1928,10 +1928,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     uint32_t pw[kRingKV][2];
     const int slots = pair_slots(n_off);
     const __amdgpu_buffer_rsrc_t rp =
-        FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, n * slots * 8) : pair_rsrc(p, bh);
+        FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, n * slots * 8) : pair_rsrc(p, n_off, bh);
     auto fill_words = [&](int u, int x) {
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
-        const int iq0 = slab_row(p, t, row_s[0], 1) + far, iq1 = slab_row(p, t, row_s[1], 1) + far;
+        const int iq0 = slab_row(p, n_off, t, row_s[0], 1) + far, iq1 = slab_row(p, n_off, t, row_s[1], 1) + far;
         if constexpr (FRAC) {
             pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq0 * slots + t) * 2 + far) * 4, 0, 0);
             pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0, 0);
@@ -1942,7 +1942,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     };
     auto fill_rows = [&](int u, int x) {
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
-        const int iq0 = slab_row(p, t, row_s[0], 1) + far, iq1 = slab_row(p, t, row_s[1], 1) + far;
+        const int iq0 = slab_row(p, n_off, t, row_s[0], 1) + far, iq1 = slab_row(p, n_off, t, row_s[1], 1) + far;
         sfrag_load(sq[u], rq, iq0, iq1, c8);
         sfrag_load(sd[u], rdo, iq0, iq1, c8);
     };
@@ -2085,7 +2085,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 // any dK/dV tile waits, and dQ tiles wait for nothing: the waits end. The host launches
 // this only when B * H is a multiple of 8: every XCD then holds whole heads, so a tile
 // and the tiles it waits for share one XCD and its L2.
-template <bool OUT_BF16, bool WITH_D>
+template <bool OUT_BF16, bool WITH_D, int NOFF = 0>
 __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
     __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
@@ -2095,14 +2095,14 @@ __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p)
     const uint64_t token = launch_token();
     if (static_cast<int>(blockIdx.x) < tiles) {
         const int lb = xcd_logical_block(blockIdx.x, tiles);
-        dq_tile<OUT_BF16, WITH_D, false>(p, lb, ta, tb, fa, fb);
+        dq_tile<OUT_BF16, WITH_D, false, NOFF>(p, lb, ta, tb, fa, fb);
         // every wave's stores (pair words, D, dQ) have reached L2 before the token does
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        dkdv_tile<OUT_BF16, false, true, WITH_D>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb, fa, fb,
-                                                 token);
+        dkdv_tile<OUT_BF16, false, true, WITH_D, NOFF>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb, fa,
+                                                       fb, token);
     }
 }
 
@@ -2301,6 +2301,26 @@ hipError_t launch(Kernel *kernel, unsigned grid, const AttnParams &p, hipStream_
 
 unsigned tiles(const AttnParams &p) { return (unsigned)(p.bh * ((p.n + 63) / 64)); }
 
+// Calls f(Len<k>{}) with the table length k fixed at compile time for the lengths the
+// window-64 tables usually have (4 to 8 offsets below N), Len<0> (length read at run
+// time) otherwise. A fixed length removes the uniform length tests from the unrolled
+// slab loops.
+template <int K>
+struct Len {
+    static constexpr int value = K;
+};
+template <typename F>
+hipError_t with_table_length(int n_off, F &&f) {
+    switch (n_off) {
+    case 4: return f(Len<4>{});
+    case 5: return f(Len<5>{});
+    case 6: return f(Len<6>{});
+    case 7: return f(Len<7>{});
+    case 8: return f(Len<8>{});
+    default: return f(Len<0>{});
+    }
+}
+
 template <int MODE>
 hipError_t launch_generic_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (dt == FSA_BF16)
@@ -2316,8 +2336,11 @@ bool window_path(fsa_dtype_t dt, const AttnParams &p) { return window_path(dt, p
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (window_path(dt, p) && p.scale_log2 > 0.f)  // the window kernel folds a positive scale into exponents
-        return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false>, tiles(p), p, s)
-                                  : launch(&fwd_window_kernel<false, false>, tiles(p), p, s);
+        return with_table_length(p.n_off, [&](auto len) {
+            constexpr int L = decltype(len)::value;
+            return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false, false, L>, tiles(p), p, s)
+                                      : launch(&fwd_window_kernel<false, false, false, L>, tiles(p), p, s);
+        });
     return launch_generic_forward<kWide>(dt, out_dt, p, s);
 }
 
@@ -2359,11 +2382,14 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
         // one launch when every XCD holds whole heads (its waits stay within one L2)
         if (p.flags && p.n_off > 0 && p.bh % 8 == 0) {
             const unsigned grid = 2 * tiles(p);
-            if (with_delta)
-                return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true>, grid, p, s)
-                                          : launch(&bwd_fused_kernel<false, true>, grid, p, s);
-            return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, false>, grid, p, s)
-                                      : launch(&bwd_fused_kernel<false, false>, grid, p, s);
+            return with_table_length(p.n_off, [&](auto len) {
+                constexpr int L = decltype(len)::value;
+                if (with_delta)
+                    return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, L>, grid, p, s)
+                                              : launch(&bwd_fused_kernel<false, true, L>, grid, p, s);
+                return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, false, L>, grid, p, s)
+                                          : launch(&bwd_fused_kernel<false, false, L>, grid, p, s);
+            });
         }
         hipError_t e;
         if (with_delta)
@@ -2404,8 +2430,11 @@ hipError_t launch_rope(const RopeParams &p, hipStream_t s) {
 }
 
 hipError_t launch_rope_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
-    return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false, true>, tiles(p), p, s)
-                              : launch(&fwd_window_kernel<false, false, true>, tiles(p), p, s);
+    return with_table_length(p.n_off, [&](auto len) {
+        constexpr int L = decltype(len)::value;
+        return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false, true, L>, tiles(p), p, s)
+                                  : launch(&fwd_window_kernel<false, false, true, L>, tiles(p), p, s);
+    });
 }
 
 hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
