@@ -36,6 +36,9 @@ def command(out: str = LIB) -> list[str]:
         "-Wall",
         # packed fp32 VALU ops are kept out of the generated code on purpose
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # no implicit multiply-add fusion: the kernels write every fma they use, so the
+        # rounding of each step is the same in every instantiation and call site
+        "-ffp-contract=off",
         # MFMA accumulators in ordinary VGPRs: the kernels also update them with VALU
         # ops, and the AGPR form would copy them back and forth around every MFMA
         "-mllvm", "-amdgpu-mfma-vgpr-form=1",

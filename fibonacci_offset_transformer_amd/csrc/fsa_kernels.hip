@@ -966,8 +966,10 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            sfrag_load(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
-            sfrag_load(sv[u], rv, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+            if (u < n_off) {  // uniform
+                sfrag_load(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+                sfrag_load(sv[u], rv, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+            }
         }
     }
 
@@ -1125,7 +1127,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                         gm[h] = fmaxf(gm[h], ss[u][h]);
                     }
                 }
-                if (t0 == 0)
+                if (t0 == 0 && u + 4 < n_off)  // uniform
                     sfrag_load(sk[u], rk, slab_row(p, n_off, u + 4, row_s[0], -1), slab_row(p, n_off, u + 4, row_s[1], -1), c8);
             }
             const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
@@ -1141,7 +1143,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                         chunk_axpy(acc_s[h], pt, sv[u].r[h]);
                     }
                 }
-                if (t0 == 0)
+                if (t0 == 0 && u + 4 < n_off)  // uniform
                     sfrag_load(sv[u], rv, slab_row(p, n_off, u + 4, row_s[0], -1), slab_row(p, n_off, u + 4, row_s[1], -1), c8);
             }
         }
@@ -1377,7 +1379,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
                 for (int r = 0; r < 4; ++r) {
                     const int j = kb0 + 4 * g + r;
                     const bool ok = row_ok && j <= i && j > i - w;
-                    const float pv = ok ? fast_exp2(st[r] * sl2 - lse2) : 0.f;
+                    const float pv = ok ? fast_exp2(__builtin_fmaf(st[r], sl2, -lse2)) : 0.f;
                     ds[r] = pv * (dpt[r] - di);
                 }
                 mma_over_rows(acc, t0s, kT64, 16 * kb, c16, g, ds);
@@ -1395,7 +1397,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
                 load_frag(vf, V, jc, g);
                 const float s = group_sum(frag_dot(qf, kf));
                 const float dp = group_sum(frag_dot(df, vf));
-                const float pv = ok ? fast_exp2(s * sl2 - lse2) : 0.f;
+                const float pv = ok ? fast_exp2(__builtin_fmaf(s, sl2, -lse2)) : 0.f;
                 frag_axpy(acc, pv * (dp - di), kf);
             }
         }
@@ -1446,7 +1448,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
                     const int qi = 16 * qb + 4 * g + r;  // row within the chunk
                     const int iq = c0 + qi;
                     const bool ok = key_ok && iq < n && iq >= j && iq - j < w;
-                    pr[r] = ok ? fast_exp2(sq[r] * sl2 - lse_s[qi]) : 0.f;
+                    pr[r] = ok ? fast_exp2(__builtin_fmaf(sq[r], sl2, -lse_s[qi])) : 0.f;
                     ds[r] = pr[r] * (dpq[r] - del_s[qi]);
                 }
                 mma_over_rows(dv, t1s, kT64, 16 * qb, c16, g, pr);
@@ -1466,7 +1468,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
                 load_frag(df, DO, ic, g);
                 const float s = group_sum(frag_dot(qf, kf));
                 const float dp = group_sum(frag_dot(df, vf));
-                const float pv = ok ? fast_exp2(s * sl2 - LSE[ic] * kLog2e) : 0.f;
+                const float pv = ok ? fast_exp2(__builtin_fmaf(s, sl2, -(LSE[ic] * kLog2e))) : 0.f;
                 const float dsv = pv * (dp - DEL[ic]);
                 frag_axpy(dv, pv, df);
                 frag_axpy(dk, dsv, qf);
@@ -1634,7 +1636,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
         if (threadIdx.x < 4 * FSA_MAX_OFFSETS) dd_s[threadIdx.x] = 0.f;  // read after the last barrier
     } else {
 #pragma unroll
-        for (int u = 0; u < kPreQ; ++u) fill(u, u);
+        for (int u = 0; u < kPreQ; ++u)
+            if (u < n_off) fill(u, u);  // uniform
     }
 
     // band on MFMA: query row i sees key blocks qb-4 .. qb (blocks outside the sequence
@@ -1652,7 +1655,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
         const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
         const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ds[r] = fast_exp2(st[r] * sl2 - lse2_i) * (dpt[r] - di_i);
+        for (int r = 0; r < 4; ++r) ds[r] = fast_exp2(__builtin_fmaf(st[r], sl2, -lse2_i)) * (dpt[r] - di_i);
         if (!full) {  // uniform: edge blocks only
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1677,7 +1680,8 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
         frac_load_k(1, 1);
     } else {
 #pragma unroll
-        for (int u = kPreQ; u < kRingQ; ++u) fill(u, u);
+        for (int u = kPreQ; u < kRingQ; ++u)
+            if (u < n_off) fill(u, u);  // uniform
     }
     __syncthreads();  // every wave is done with the band tiles
     f32x4_t dq_s[2][2];
@@ -1717,7 +1721,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
                 const float sn = row8_sum(chunk_dot(qs.r[h], kn.r[h]));
                 const float sd = row8_sum(chunk_dot(qs.r[h], kf.r[h])) - sn;
                 const float sc = __builtin_fmaf(ph, sd, sn), dp = __builtin_fmaf(ph, pd[h], pn[h]);
-                const float pv = ok ? fast_exp2(sc * sl2 - lse2[h]) : 0.f;
+                const float pv = ok ? fast_exp2(__builtin_fmaf(sc, sl2, -lse2[h])) : 0.f;
                 const float ds = pv * (dp - di[h]);
                 const float pf = pv * ph, dsf = ds * ph;
                 const uint2 pw = {pack_bf16(pv - pf, ds - dsf), pack_bf16(pf, dsf)};
@@ -1748,7 +1752,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
                 const bool ok = (row_s[h] < n) & (row_s[h] - o >= 0);
                 const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
                 const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
-                const float pv = ok ? fast_exp2(s * sl2 - lse2[h]) : 0.f;
+                const float pv = ok ? fast_exp2(__builtin_fmaf(s, sl2, -lse2[h])) : 0.f;
                 const uint32_t pw = pack_bf16(pv, pv * (dp - di[h]));
                 if (t < 8)
                     keep[h] = c8 == t ? pw : keep[h];
@@ -1763,7 +1767,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
 #pragma unroll
             for (int u = 0; u < kRingQ; ++u) {
                 if (s0 + u < n_off) slab(s0 + u, table_off(p, n_off, s0 + u), sk[u], sv[u]);  // uniform
-                if (s0 + kRingQ < unrolled_slabs(kRingQ)) fill(u, s0 + u + kRingQ);
+                if (s0 + u + kRingQ < min(n_off, unrolled_slabs(kRingQ))) fill(u, s0 + u + kRingQ);  // uniform
             }
         }
         static_assert(unrolled_slabs(kRingQ) == 8, "the kept pair words cover slots 0..7");
@@ -1951,7 +1955,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
         fill_words(u, x);
     };
 #pragma unroll
-    for (int u = 0; u < kPreKV; ++u) fill(u, u);
+    for (int u = 0; u < kPreKV; ++u)
+        if (u < (FRAC ? 2 * n_off : n_off)) fill(u, u);  // uniform; FRAC: half entries
 
     // band on MFMA: key row j sees query blocks r0 + 16 b (blocks past the sequence or
     // the window are masked like edge blocks)
@@ -1973,7 +1978,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
         const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(lse_s + 16 * wave + lr + 4 * g);
         const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(del_s + 16 * wave + lr + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sq4[r] * sl2 - l4[r]);
+        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(__builtin_fmaf(sq4[r], sl2, -l4[r]));
         if (!full) {  // uniform: edge blocks only
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -2002,7 +2007,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
         mma_over_rows_tr_exact(dk, ta_w, 64, tl, s0);
     }
 #pragma unroll
-    for (int u = kPreKV; u < kRingKV; ++u) fill(u, u);
+    for (int u = kPreKV; u < kRingKV; ++u)
+        if (u < (FRAC ? 2 * n_off : n_off)) fill(u, u);  // uniform; FRAC: half entries
     __syncthreads();  // every wave is done with the band tiles
     f32x4_t dk_s[2][2], dv_s[2][2];
     c_to_slab(reinterpret_cast<float *>(ta) + wave * 1024, dk, dk_s, c16, g, s8, c8);
@@ -2035,7 +2041,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
 #pragma unroll
             for (int u = 0; u < kRingKV; ++u) {
                 if (s0 + u < n_off) slab(pw[u], sq[u], sd[u]);  // uniform
-                if (s0 + kRingKV < unrolled_slabs(kRingKV)) fill(u, s0 + u + kRingKV);
+                if (s0 + u + kRingKV < min(n_off, unrolled_slabs(kRingKV))) fill(u, s0 + u + kRingKV);  // uniform
             }
         }
         for (int t = unrolled_slabs(kRingKV); t < n_off; ++t) {  // longer tables
@@ -2302,9 +2308,9 @@ hipError_t launch(Kernel *kernel, unsigned grid, const AttnParams &p, hipStream_
 unsigned tiles(const AttnParams &p) { return (unsigned)(p.bh * ((p.n + 63) / 64)); }
 
 // Calls f(Len<k>{}) with the table length k fixed at compile time for the lengths the
-// window-64 tables usually have (4 to 8 offsets below N), Len<0> (length read at run
+// window-64 tables usually have (4 to 7 offsets below N), Len<0> (length read at run
 // time) otherwise. A fixed length removes the uniform length tests from the unrolled
-// slab loops.
+// slab loops. (At 8 the one-launch backward would need more than 128 VGPRs.)
 template <int K>
 struct Len {
     static constexpr int value = K;
@@ -2316,7 +2322,6 @@ hipError_t with_table_length(int n_off, F &&f) {
     case 5: return f(Len<5>{});
     case 6: return f(Len<6>{});
     case 7: return f(Len<7>{});
-    case 8: return f(Len<8>{});
     default: return f(Len<0>{});
     }
 }
