@@ -560,6 +560,7 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
         p.delta = reinterpret_cast<float *>(base_ws + lay.delta);
         p.pairs = reinterpret_cast<uint32_t *>(base_ws + lay.pairs);
         p.dd_part = reinterpret_cast<float *>(base_ws + lay.partials);
+        p.flags = reinterpret_cast<uint64_t *>(base_ws + lay.flags);
     } else {
         p.bh = 0;  // no tiles: only the alpha reduction runs, writing zeros
     }
@@ -929,6 +930,7 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
     p.delta = reinterpret_cast<float *>(fw + fl.delta);
     p.pairs = reinterpret_cast<uint32_t *>(fw + fl.pairs);
     p.dd_part = reinterpret_cast<float *>(fw + fl.partials);
+    p.flags = reinterpret_cast<uint64_t *>(fw + fl.flags);
     p.rope = rope;
     return launched(fsa::launch_frac_backward(out_dt, p, hs), "rotary fractional backward");
 }

@@ -89,9 +89,10 @@ inline uint64_t pair_ws_bytes(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, 
 
 // Fractional-entry backward workspace on the window path: D [BH, N] floats, then the
 // pair words [BH, N, pair_slots(n_off), 2] (the near and far weights of every
-// entry), then the per-tile partials [tiles, n_off]; each part 256-byte aligned.
+// entry), then the per-tile partials [n_off, tiles], then one 64-bit completion token
+// per tile (the one-launch backward); each part 256-byte aligned.
 struct FracWorkspace {
-    uint64_t delta, pairs, partials, total;  // byte offsets of the parts, total size
+    uint64_t delta, pairs, partials, flags, total;  // byte offsets of the parts, total size
 };
 inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
     FracWorkspace w;
@@ -99,7 +100,8 @@ inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
     w.delta = 0;
     w.pairs = align256(4ull * bh * n);
     w.partials = w.pairs + align256(8ull * pair_slots(n_off) * bh * n);
-    w.total = w.partials + align256(4ull * tiles * n_off);
+    w.flags = w.partials + align256(4ull * tiles * n_off);
+    w.total = w.flags + align256(8ull * tiles);
     return w;
 }
 

@@ -1514,21 +1514,29 @@ constexpr int kCachePastL1 = 1;
 // beyond any real wait (the dQ work of a whole launch takes tens of microseconds).
 constexpr int kMaxSpins = 1 << 18;
 
-// Waits until flags[first .. last] all hold the token (one wave, 64 tiles per poll, one
-// per lane; device-scope loads, which miss this CU's L1). Returns false, uniformly over
-// the wave, if it gave up; the caller then stores NaN so that the failure shows.
+// Waits until flags[first .. last] all hold the token (one wave; lane l checks flags
+// first + l, first + l + 64, ...; device-scope loads, which miss this CU's L1). Each
+// poll requests up to 64 * BATCH flags before comparing any, so that it costs one
+// round trip for up to that many tiles. Returns false, uniformly over the wave, if it
+// gave up; the caller then stores NaN so that the failure shows.
+template <int BATCH = 1>
 __device__ __forceinline__ bool poll_tiles(const uint64_t *flags, int first, int last, uint64_t token, int lane) {
-    for (int b = first; b <= last; b += 64) {
-        const int idx = b + lane;
-        for (int spin = 0;; ++spin) {
-            const bool ready =
-                idx > last || __hip_atomic_load(flags + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token;
-            if (__builtin_amdgcn_ballot_w64(!ready) == 0) break;
-            if (spin == kMaxSpins) return false;
-            __builtin_amdgcn_s_sleep(4);
+    for (int spin = 0;; ++spin) {
+        bool ready = true;
+        for (int base = first + lane; base <= last; base += 64 * BATCH) {
+            // every lane loads (indices past `last` read `last` again), without branches,
+            // so that the loads leave back to back
+            uint64_t v[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k)
+                v[k] = __hip_atomic_load(flags + min(base + 64 * k, last), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) ready &= (base + 64 * k > last) | (v[k] == token);
         }
+        if (__builtin_amdgcn_ballot_w64(!ready) == 0) return true;
+        if (spin == kMaxSpins) return false;
+        __builtin_amdgcn_s_sleep(4);
     }
-    return true;
 }
 
 // Descriptor over the pair-workspace words of head bh ([N, S] words, S = pair_slots):
@@ -1553,7 +1561,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p,
 // The body works on logical tile lb with the caller's LDS: ta, tb (band K and V rows,
 // kTileRows * 64 each, then merge areas), d_s (64 floats: D of the tile's rows, WITH_D)
 // and dd_s (4 * FSA_MAX_OFFSETS floats, FRAC).
-template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0>
+template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0, bool PUBLISH = false>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *d_s,
                                         float *dd_s) {
     static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
@@ -1793,9 +1801,15 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     if constexpr (FRAC) {  // partials [n_off, tiles]: entry t's partials are contiguous
         __syncthreads();
         const int t = threadIdx.x;
-        if (t < n_off)
-            p.dd_part[(int64_t)t * (p.bh * nt) + lb] = (dd_s[t] + dd_s[FSA_MAX_OFFSETS + t]) +
-                                                       (dd_s[2 * FSA_MAX_OFFSETS + t] + dd_s[3 * FSA_MAX_OFFSETS + t]);
+        if (t < n_off) {
+            const float part = (dd_s[t] + dd_s[FSA_MAX_OFFSETS + t]) +
+                               (dd_s[2 * FSA_MAX_OFFSETS + t] + dd_s[3 * FSA_MAX_OFFSETS + t]);
+            float *dst = p.dd_part + (int64_t)t * (p.bh * nt) + lb;
+            if constexpr (PUBLISH)  // read in the same launch, possibly from another XCD
+                __hip_atomic_store(dst, part, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                *dst = part;
+        }
     }
 }
 
@@ -1814,13 +1828,15 @@ __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
 // value. Wave v sums entries v, v + 4, ... (lanes stride over the tiles, fp64), then one
 // thread forms the outputs in entry order: a fixed order, so the result is reproducible.
 // Entries that no row reaches (trimmed from the table) get 0. `red` holds 48 doubles.
+template <bool SAME_LAUNCH = false>
 __device__ void reduce_alpha_grad(const AttnParams &p, double *red) {
     const int n_tiles = p.bh * ((p.n + 63) >> 6);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int t = wave; t < p.n_off; t += kThreads / 64) {
         const float *part = p.dd_part + (int64_t)t * n_tiles;
         double x = 0.0;
-        for (int i = lane; i < n_tiles; i += 64) x += part[i];
+        for (int i = lane; i < n_tiles; i += 64)
+            x += SAME_LAUNCH ? __hip_atomic_load(part + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : part[i];
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
         if (lane == 0) red[t] = x;
@@ -1899,7 +1915,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
         // those tiles while the band rows are in flight
         __shared__ int gave_up;
         if (wave == 0) {
-            const int far = n_off > 0 ? t0 + 63 + p.off[n_off - 1] : t0;
+            const int far = n_off > 0 ? t0 + 63 + p.off[n_off - 1] + (FRAC ? 1 : 0) : t0;
             const int last = min(nt - 1, max(FROM_DQ ? tile + 1 : tile, far >> 6));
             const bool ok = poll_tiles(p.flags + (int64_t)bh * nt, tile, last, token, lane);
             if (lane == 0) gave_up = ok ? 0 : 1;
@@ -1937,8 +1953,10 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
         const int iq0 = slab_row(p, n_off, t, row_s[0], 1) + far, iq1 = slab_row(p, n_off, t, row_s[1], 1) + far;
         if constexpr (FRAC) {
-            pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq0 * slots + t) * 2 + far) * 4, 0, 0);
-            pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0, 0);
+            pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq0 * slots + t) * 2 + far) * 4, 0,
+                                                            FUSED ? kCachePastL1 : 0);
+            pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0,
+                                                            FUSED ? kCachePastL1 : 0);
         } else {
             pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, FUSED ? kCachePastL1 : 0);
             pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, FUSED ? kCachePastL1 : 0);
@@ -2067,8 +2085,23 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     // through the sparse entries, has the least work and reduces them
     if constexpr (FRAC) {
         if (bh == 0 && tile == nt - 1) {  // uniform over the workgroup
-            __syncthreads();              // the LDS tiles are free again
-            reduce_alpha_grad(p, reinterpret_cast<double *>(ta));
+            if constexpr (FUSED) {
+                // every tile's partials come from this launch's dQ work, on any XCD
+                __shared__ int all_ok;
+                if (wave == 0) {
+                    const bool ok = poll_tiles<16>(p.flags, 0, p.bh * nt - 1, token, lane);
+                    if (lane == 0) all_ok = ok ? 1 : 0;
+                }
+                __syncthreads();  // also: the LDS tiles are free again
+                if (!all_ok) {    // uniform: the wait gave up
+                    if (tid == 0) p.dalpha[0] = __builtin_nanf("");
+                    return;
+                }
+                reduce_alpha_grad<true>(p, reinterpret_cast<double *>(ta));
+            } else {
+                __syncthreads();  // the LDS tiles are free again
+                reduce_alpha_grad(p, reinterpret_cast<double *>(ta));
+            }
         }
     }
 }
@@ -2091,24 +2124,26 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 // any dK/dV tile waits, and dQ tiles wait for nothing: the waits end. The host launches
 // this only when B * H is a multiple of 8: every XCD then holds whole heads, so a tile
 // and the tiles it waits for share one XCD and its L2.
-template <bool OUT_BF16, bool WITH_D, int NOFF = 0>
+template <bool OUT_BF16, bool WITH_D, int NOFF = 0, bool FRAC = false>
 __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p) {
+    static_assert(!FRAC || (WITH_D && NOFF == 0), "the fractional form runs with D formed, any table length");
+    constexpr int kFb = FRAC ? 4 * FSA_MAX_OFFSETS : kTileRows;
     __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
     __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
     __shared__ __attribute__((aligned(16))) float fa[kTileRows];  // dQ: D of its rows; dK/dV: LSE of the band
-    __shared__ __attribute__((aligned(16))) float fb[kTileRows];  // dK/dV: D of the band
+    __shared__ __attribute__((aligned(16))) float fb[kFb];        // dQ: per-wave entry sums (FRAC); dK/dV: D of the band
     const int tiles = p.bh * ((p.n + 63) >> 6);
     const uint64_t token = launch_token();
     if (static_cast<int>(blockIdx.x) < tiles) {
         const int lb = xcd_logical_block(blockIdx.x, tiles);
-        dq_tile<OUT_BF16, WITH_D, false, NOFF>(p, lb, ta, tb, fa, fb);
+        dq_tile<OUT_BF16, WITH_D, FRAC, NOFF, true>(p, lb, ta, tb, fa, fb);
         // every wave's stores (pair words, D, dQ) have reached L2 before the token does
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        dkdv_tile<OUT_BF16, false, true, WITH_D, NOFF>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb, fa,
-                                                       fb, token);
+        dkdv_tile<OUT_BF16, FRAC, true, WITH_D, NOFF>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb, fa,
+                                                      fb, token);
     }
 }
 
@@ -2449,6 +2484,9 @@ hipError_t launch_frac_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStrea
 
 hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (tiles(p) == 0) return launch(&frac_alpha_kernel, 1, p, s);  // writes the zeros of an empty problem
+    if (p.flags && p.n_off > 0 && p.bh % 8 == 0)  // one launch, as for the static tables
+        return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, 0, true>, 2 * tiles(p), p, s)
+                                  : launch(&bwd_fused_kernel<false, true, 0, true>, 2 * tiles(p), p, s);
     const hipError_t e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, true>, tiles(p), p, s)
                                             : launch(&bwd_dq_kernel<false, true, true>, tiles(p), p, s);
     if (e != hipSuccess) return e;

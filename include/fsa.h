@@ -283,8 +283,11 @@ fsa_status_t fsa_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
  *   ws                  caller-owned device workspace of at least
  *                       fsa_frac_backward_workspace_bytes(...) bytes, 16-byte aligned,
  *                       overwritten; its contents on entry do not matter (it holds D,
- *                       the near and far bf16 weights of every pair and the per-tile
- *                       partials of the alpha gradient). May be NULL for an empty problem.
+ *                       the near and far bf16 weights of every pair, the per-tile
+ *                       partials of the alpha gradient and one 64-bit token per tile:
+ *                       with B * H a multiple of 8 the dQ and dK/dV parts run in one
+ *                       launch, as in fsa_backward). May be NULL for an empty problem.
+ *                       Two calls that overlap in time must not share one.
  *   ws_bytes            size of ws; FSA_E_ARG if smaller than needed
  */
 fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
@@ -297,7 +300,7 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
  * fsa_frac_backward_workspace_bytes - bytes of ws fsa_frac_backward needs:
  * 4 B H N (D) + 8 S B H N (two words per pair, S = number of entries some row
  * reaches, rounded up to a multiple of 8) + 4 B H ceil(N/64) S' (partials, S' the
- * unrounded count), each part rounded up to 256 bytes. Arguments as in
+ * unrounded count) + 8 B H ceil(N/64) (tokens), each part rounded up to 256 bytes. Arguments as in
  * fsa_frac_backward; *bytes receives the size.
  */
 fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,

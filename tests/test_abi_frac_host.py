@@ -144,19 +144,21 @@ def a256(x):
 
 
 def test_frac_workspace_size(lib):
+    # D, the pair words (two per pair), the per-tile partials, then one 64-bit token per
+    # tile (the one-launch backward), each part rounded up to 256 bytes.
     # alpha = 1.3, w = 64, R = 1024: d = 1.3 F >= 64 for F = 55 .. 987 (7 entries) -> 8 slots
     bh, N = 16, 4096
     n_ent = len(oracle.frac_offset_table("fib", 1.3, 64, 1024))
     assert n_ent == 7
-    want = a256(4 * bh * N) + a256(8 * 8 * bh * N) + a256(4 * bh * (N // 64) * n_ent)
+    want = a256(4 * bh * N) + a256(8 * 8 * bh * N) + a256(4 * bh * (N // 64) * n_ent) + a256(8 * bh * (N // 64))
     assert frac_ws(lib, alpha=1.3) == (fsa.FSA_OK, want)
     # entries whose first row (ceil d) is not below N are dropped: N = 200 keeps d = 71.5, 115.7, 187.2
     n = 200
-    want = a256(4 * bh * n) + a256(8 * 8 * bh * n) + a256(4 * bh * 4 * 3)
+    want = a256(4 * bh * n) + a256(8 * 8 * bh * n) + a256(4 * bh * 4 * 3) + a256(8 * bh * 4)
     assert frac_ws(lib, alpha=1.3, N=n) == (fsa.FSA_OK, want)
     # 9 entries (w = 1, alpha = 1.1, R = 60) take 16 slots
     assert len(oracle.frac_offset_table("fib", 1.1, 1, 60)) == 9
-    want = a256(4 * bh * N) + a256(8 * 16 * bh * N) + a256(4 * bh * (N // 64) * 9)
+    want = a256(4 * bh * N) + a256(8 * 16 * bh * N) + a256(4 * bh * (N // 64) * 9) + a256(8 * bh * (N // 64))
     assert frac_ws(lib, alpha=1.1, w=1, R=60) == (fsa.FSA_OK, want)
     assert frac_ws(lib, B=0) == (fsa.FSA_OK, 0)
     assert frac_ws(lib, dt=0)[0] == fsa.FSA_E_UNSUPPORTED

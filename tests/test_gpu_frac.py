@@ -199,11 +199,12 @@ def test_frac_integer_alpha_matches_static_path():
     assert float((lf - ls).abs().max()) <= 1e-5
 
 
-def test_frac_bitwise_deterministic_and_workspace_contents_do_not_matter():
-    x = inputs(44, 0, (1, 3, 999, 64), grad=True)
+@pytest.mark.parametrize("H", [3, 8], ids=["two_kernels", "one_launch"])
+def test_frac_bitwise_deterministic_and_workspace_contents_do_not_matter(H):
+    x = inputs(44, 0, (1, H, 999, 64), grad=True)
     kw = dict(alpha=1.17, w=64, R=1024, scale=0.125)
     o, lse = fsa.frac_forward(x["q"], x["k"], x["v"], **kw)
-    need = fsa.frac_workspace_bytes(torch.bfloat16, 1, 3, 999, alpha=1.17, w=64, R=1024)
+    need = fsa.frac_workspace_bytes(torch.bfloat16, 1, H, 999, alpha=1.17, w=64, R=1024)
     runs = []
     for fill in (0, 0x7FC07FC0, -1):  # zeros, NaN bit patterns, all ones
         ws = torch.full((need // 4 + 77,), fill, dtype=torch.int32, device=dev())
@@ -215,6 +216,34 @@ def test_frac_bitwise_deterministic_and_workspace_contents_do_not_matter():
         for a, b in zip(runs[0], other):
             assert torch.equal(a, b)
     assert bool(torch.isfinite(runs[0][3]).all())
+
+
+@pytest.mark.parametrize("B,H,N,alpha,w", [(2, 4, 777, 1.3, 64), (1, 8, 300, 1.1, 1), (8, 1, 130, 0.7, 16)])
+def test_frac_one_launch_equals_per_head(B, H, N, alpha, w):
+    # B * H = 8 runs the dQ and dK/dV work in one launch (the alpha reduction waits for
+    # every tile's token, on every XCD); one head at a time runs the two kernels. The
+    # gradients agree bit for bit; the alpha gradient is the same fp32 tile partials
+    # summed in another order (fp64), so it agrees to fp32 rounding of the per-head sums
+    x = inputs(50, 0, (B, H, N, 64), grad=True)
+    kw = dict(alpha=alpha, w=w, R=1024, scale=0.125)
+    o, lse = fsa.frac_forward(x["q"], x["k"], x["v"], **kw)
+    note(f"frac one-launch B={B} H={H} N={N} alpha={alpha} w={w}")
+    whole = fsa.frac_backward(x["q"], x["k"], x["v"], o, lse, x["do"], out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    da_sum, da_abs, dd_sum = 0.0, 0.0, None
+    for b in range(B):
+        for h in range(H):
+            one = {t: x[t][b:b + 1, h:h + 1].clone() for t in ("q", "k", "v", "do")}
+            ref = fsa.frac_backward(one["q"], one["k"], one["v"], o[b:b + 1, h:h + 1].clone(),
+                                    lse[b:b + 1, h:h + 1].clone(), one["do"], out_dtype=torch.float32, **kw)
+            torch.cuda.synchronize()
+            for name, a, r in zip(("dq", "dk", "dv"), whole[:3], ref[:3]):
+                assert torch.equal(a[b, h], r[0, 0]), (name, b, h)
+            da_sum += float(ref[3][0])
+            da_abs += abs(float(ref[3][0]))
+            dd_sum = ref[4].double() if dd_sum is None else dd_sum + ref[4].double()
+    assert abs(float(whole[3][0]) - da_sum) <= 1e-6 * da_abs + 1e-6, (float(whole[3][0]), da_sum)
+    assert float((whole[4].double() - dd_sum).abs().max()) <= 1e-6 * float(dd_sum.abs().max()) + 1e-6
 
 
 def test_frac_empty_problem_writes_zero_alpha_gradient():
@@ -352,17 +381,18 @@ def test_frac_decode_matches_frac_forward_last_row():
     assert float((ld - lse[:, :, -1]).abs().max()) <= 1e-5
 
 
-def test_frac_graph_replays_match_eager():
-    # forward + backward (with the alpha reduction inside the dK/dV kernel) and a decode step
+@pytest.mark.parametrize("H", [3, 4], ids=["two_kernels", "one_launch"])
+def test_frac_graph_replays_match_eager(H):
+    # forward + backward (with the alpha reduction inside the dK/dV work) and a decode step
     # captured in one HIP graph; every replay, with eager work and a clear in between,
     # reproduces the eager results bit for bit
-    x = inputs(49, 0, (2, 3, 700, 64), grad=True)
+    x = inputs(49, 0, (2, H, 700, 64), grad=True)
     kw = dict(alpha=1.13, w=64, R=1024, scale=0.125)
     bufs = {n: torch.empty_like(x["q"]) for n in ("o", "dq", "dk", "dv")}
     lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev())
     da = torch.empty(1, dtype=torch.float32, device=dev())
     dd = torch.empty(len(fsa.frac_offsets(1.13, 64, 1024)), dtype=torch.float32, device=dev())  # one per entry
-    ws = torch.empty(fsa.frac_workspace_bytes(torch.bfloat16, 2, 3, 700, alpha=1.13, w=64, R=1024) // 4 + 1,
+    ws = torch.empty(fsa.frac_workspace_bytes(torch.bfloat16, 2, H, 700, alpha=1.13, w=64, R=1024) // 4 + 1,
                      dtype=torch.int32, device=dev())
     qd = x["q"][:, :, -1].contiguous()
     sl = torch.tensor([700, 333], dtype=torch.int32, device=dev())
