@@ -472,6 +472,8 @@ fsa_status_t prepare_frac(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_dt
     if (!(scale > 0.f)) return fail(FSA_E_UNSUPPORTED, "fractional entries need a positive scale");
     int used = 0;
     while (used < n && p.off[used] + (p.phi[used] != 0.f ? 1 : 0) < N) ++used;
+    if (!fsa::pair_offsets_fit(N, used, 2))
+        return fail(FSA_E_UNSUPPORTED, "fractional entries: N = %d with %d entries exceeds 32-bit pair offsets", N, used);
     for (int t = 0; t < n; ++t) p.fbase[t] = static_cast<float>(fb[t]);
     p.n_entries = n;
     p.n_off = used;
@@ -604,10 +606,13 @@ hipError_t rotate_rows(const void *const *x, void *const *out, int count, const 
 
 
 // Path checks shared by the fused rotary calls.
-fsa_status_t check_rope_path(fsa_dtype_t dt, int32_t w, int32_t N, float scale, int32_t n_pos) {
+// n_off: the table's length before trimming to N.
+fsa_status_t check_rope_path(fsa_dtype_t dt, int32_t w, int32_t N, float scale, int32_t n_pos, int32_t n_off) {
     if (dt != FSA_BF16) return fail(FSA_E_UNSUPPORTED, "the rotary path stores rotated rows in bf16: bf16 inputs only");
     if (w > 64) return fail(FSA_E_UNSUPPORTED, "the rotary path needs a window w <= 64 (got %d)", w);
     if (N > (1 << 24)) return fail(FSA_E_UNSUPPORTED, "the rotary path needs N <= 2^24 (got %d)", N);
+    if (!fsa::pair_offsets_fit(N, n_off, 1))
+        return fail(FSA_E_UNSUPPORTED, "the rotary path: N = %d with %d offsets exceeds 32-bit pair offsets", N, n_off);
     if (!(scale > 0.f)) return fail(FSA_E_UNSUPPORTED, "the rotary path needs a positive scale");
     if (n_pos < N) return fail(FSA_E_ARG, "the rotary table has %d positions, the sequence %d", n_pos, N);
     return FSA_OK;
@@ -659,7 +664,7 @@ fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int3
     int32_t tab[FSA_MAX_OFFSETS];
     const int n_off = build_table(base, alpha, w, R, tab, &st);
     if (n_off < 0) return st;
-    if ((st = check_rope_path(dt, w, N, 1.0f, N)) != FSA_OK) return st;
+    if ((st = check_rope_path(dt, w, N, 1.0f, N, n_off)) != FSA_OK) return st;
     const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, trim_offsets(tab, n_off, N));
     *fwd_bytes = static_cast<int64_t>(B) * H * N == 0 ? 0 : l.fwd;
     *bwd_bytes = static_cast<int64_t>(B) * H * N == 0 ? 0 : l.bwd;
@@ -676,7 +681,7 @@ fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
     fsa::AttnParams p{};
     const int n_off = build_table(base, alpha, w, R, p.off, &st);
     if (n_off < 0) return st;
-    if ((st = check_rope_path(dt, w, N, scale, n_pos)) != FSA_OK) return st;
+    if ((st = check_rope_path(dt, w, N, scale, n_pos, n_off)) != FSA_OK) return st;
     if (static_cast<int64_t>(B) * H * N == 0) return ok();
     const char *names[] = {"q", "k", "v", "rope", "o", "lse", "ws"};
     const void *ptrs[] = {q, k, v, rope, o, lse, ws};
@@ -721,7 +726,7 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     fsa::AttnParams p{};
     const int n_off = build_table(base, alpha, w, R, p.off, &st);
     if (n_off < 0) return st;
-    if ((st = check_rope_path(dt, w, N, scale, n_pos)) != FSA_OK) return st;
+    if ((st = check_rope_path(dt, w, N, scale, n_pos, n_off)) != FSA_OK) return st;
     if (static_cast<int64_t>(B) * H * N == 0) return ok();
     const char *names[] = {"q", "k", "v", "rope", "o", "lse", "dout", "dq", "dk", "dv", "ws"};
     const void *ptrs[] = {q, k, v, rope, o, lse, dout, dq, dk, dv, ws};

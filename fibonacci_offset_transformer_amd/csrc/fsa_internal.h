@@ -72,8 +72,18 @@ inline bool window_path(fsa_dtype_t dt, int32_t w, int32_t n) { return dt == FSA
 // pair (row, row - off[t]). Slots come in groups of 8 so that one row's first eight
 // words are written by one 32-byte store. None elsewhere.
 __host__ __device__ inline int32_t pair_slots(int32_t n_off) { return 8 * ((n_off + 7) / 8); }
+// The window backward addresses one head's pair words with 32-bit offsets: [N, slots]
+// words on the static path (words_per_slot 1), [N, slots, 2] on the learned-alpha path.
+inline bool pair_offsets_fit(int32_t n, int32_t n_off, int words_per_slot) {
+    return static_cast<int64_t>(n) * pair_slots(n_off) * 4 * words_per_slot <= INT32_MAX;
+}
+// The static backward takes the window kernels (and their pair workspace) when the
+// window path applies and the pair words of a head fit 32-bit offsets.
+inline bool window_backward(fsa_dtype_t dt, int32_t w, int32_t n, int32_t n_off) {
+    return window_path(dt, w, n) && pair_offsets_fit(n, n_off, 1);
+}
 inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
-    return window_path(dt, w, n) ? static_cast<int64_t>(pair_slots(n_off)) * bh * n : 0;
+    return window_backward(dt, w, n, n_off) ? static_cast<int64_t>(pair_slots(n_off)) * bh * n : 0;
 }
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 

@@ -370,19 +370,6 @@ __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src, in
     }
 }
 
-// As dma_tile for a 64-row tile [row0, row0 + 64): two 1 KiB transfers per wave.
-__device__ __forceinline__ void dma_tile64(uint16_t *tile, const uint16_t *src, int row0, int n, int wave, int lane) {
-    const int rl = lane >> 3;
-    const int chunk = (lane & 7) ^ rl;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int rb = 8 * (2 * wave + k);
-        int r = row0 + rb + rl;
-        r = (r >= 0 && r < n) ? r : 0;
-        __builtin_amdgcn_global_load_lds(src + (int64_t)r * 64 + 8 * chunk, (lds_void_t *)(tile + rb * 64), 16, 0, 0);
-    }
-}
-
 // Element offset, within a swizzled tile, of the 16-byte chunk c of tile row r.
 __device__ __forceinline__ int tile_chunk(int r, int c) { return r * 64 + 8 * (c ^ (r & 7)); }
 
@@ -395,8 +382,15 @@ __device__ __forceinline__ int tile_chunk(int r, int c) { return r * 64 + 8 * (c
 
 constexpr int kBufferConfig = 0x00020000;  // descriptor word 3 for gfx9-family raw buffers
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufferConfig);
+// `bytes` is the range in bytes (at most 2^32 - 1; the callers' ranges are at most 2^31).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kBufferConfig);
+}
+
+// Byte range of `rows` rows of `row_bytes` bytes, formed in unsigned arithmetic (a head
+// of 2^24 rows of 128 bytes spans exactly 2^31 bytes).
+__device__ __forceinline__ uint32_t span_bytes(int rows, uint32_t row_bytes) {
+    return static_cast<uint32_t>(rows) * row_bytes;
 }
 
 // Row fragment of row `row` (lane group g's 16 elements) from a [n, 64] bf16 head.
@@ -540,6 +534,20 @@ __device__ __forceinline__ void mma_over_rows_tr2(f32x4_t acc[4], const uint16_t
     const u32x4_t b = {pack_bf16(bv0[0], bv0[1]), pack_bf16(bv0[2], bv0[3]), pack_bf16(bv1[0], bv1[1]),
                        pack_bf16(bv1[2], bv1[3])};
     const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr0 * 64 + tl.tr[db]));
+        const i16x4_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr1 * 64 + tl.tr[db]));
+        const i16x8_t a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), bb, acc[db], 0, 0, 0);
+    }
+}
+
+// As mma_over_rows_tr2 with the weights already packed as bf16 pairs: words 0-1 are
+// the four weights of rows lr0 + 4 g .. + 3, words 2-3 those of rows lr1 + 4 g .. + 3.
+__device__ __forceinline__ void mma_over_rows_tr2_packed(f32x4_t acc[4], const uint16_t *tile, int lr0, int lr1,
+                                                         const TileLanes &tl, const u32x4_t &w) {
+    const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, w);
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         const i16x4_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + lr0 * 64 + tl.tr[db]));
@@ -737,8 +745,8 @@ __device__ __forceinline__ u32x4_t rope_chunk(const u32x4_t &xv, const f32x4_t &
     return ov;
 }
 
-// (cos, sin) table entries of channel pairs 4 c .. 4 c + 3 at position `row` through a
-// descriptor over the table (rows past its range read as zeros).
+// (cos, sin) table entries of channel pairs 4 c .. 4 c + 3 of table row `row` through a
+// descriptor over table rows (rows past its range read as zeros).
 __device__ __forceinline__ void rope_entries(__amdgpu_buffer_rsrc_t rt, int row, int c, f32x4_t &t01,
                                              f32x4_t &t23) {
     const int off = (row * 32 + 4 * c) * 8;
@@ -928,7 +936,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + head;
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128), rv = head_rsrc(V, n * 128);
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, span_bytes(n, 128)), rk = head_rsrc(K, span_bytes(n, 128));
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, span_bytes(n, 128));
     const float sl2 = p.scale_log2;
     const int i = r0 + c16;  // MFMA-layout query row
     const bool row_ok = i < n;
@@ -939,10 +948,11 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     buf_frag(qf, rq, i, g);
     [[maybe_unused]] __amdgpu_buffer_rsrc_t rt;
     if constexpr (ROPE) {
-        rt = head_rsrc(p.rope, n * 256);
+        // the table rows of this tile's positions (the positions past n read as zeros)
+        rt = head_rsrc(p.rope + (int64_t)i0 * 64, span_bytes(min(64, n - i0), 256));
         f32x4_t a01, a23, b01, b23;
-        rope_entries(rt, i, g, a01, a23);      // chunk g: pairs 4g .. 4g + 3
-        rope_entries(rt, i, g + 4, b01, b23);  // chunk g + 4
+        rope_entries(rt, i - i0, g, a01, a23);      // chunk g: pairs 4g .. 4g + 3
+        rope_entries(rt, i - i0, g + 4, b01, b23);  // chunk g + 4
         wait_vm_all();
         qf.c[0] = rope_chunk(qf.c[0], a01, a23);
         qf.c[1] = rope_chunk(qf.c[1], b01, b23);
@@ -1179,11 +1189,42 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     }
 }
 
+// One thread's share of a 64-row K and V tile: the 16-byte chunks q = tid and
+// q = tid + 256 (tile row q / 8, chunk q % 8) of each.
+struct TileChunks {
+    u32x4_t k[2], v[2];
+};
+
+// Fetches key rows [row0, row0 + 64) into registers (rows past the sequence read as zeros).
+__device__ __forceinline__ void fetch_tile(TileChunks &c, __amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           int row0, int tid) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = tid + 256 * h;
+        const int off = (row0 + (q >> 3)) * 128 + 16 * (q & 7);
+        c.k[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        c.v[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+}
+
+// Writes fetched chunks into swizzled 64-row LDS tiles (chunk c of row r at c ^ (r & 7)).
+__device__ __forceinline__ void stage_tile(uint16_t *kt, uint16_t *vt, const TileChunks &c, int tid) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = tid + 256 * h;
+        const int e = tile_chunk(q >> 3, q & 7);
+        *reinterpret_cast<u32x4_t *>(kt + e) = c.k[h];
+        *reinterpret_cast<u32x4_t *>(vt + e) = c.v[h];
+    }
+}
+
 // Dense causal forward (the baseline), bf16 inputs, positive scale. One workgroup =
-// one 64-row query tile; it walks the key tiles 0 .. tile, each copied into LDS
-// (K and V, swizzled) one step ahead of its use, with an online softmax whose
-// accumulator is rescaled only when a row maximum grows. The tile order pairs light
-// and heavy tiles on a CU: within each head the upper half of the tiles runs in
+// one 64-row query tile; it walks the key tiles 0 .. tile with an online softmax whose
+// accumulator is rescaled only when a row maximum grows. Each key tile is fetched into
+// registers two tiles ahead of its use and written into one of two swizzled LDS stages
+// one tile ahead, so its fetch has two tiles of compute to land. Row sums are taken
+// over the bf16-rounded probabilities that the P.V product uses. The tile order pairs
+// light and heavy tiles on a CU: within each head the upper half of the tiles runs in
 // reverse, so the blocks that dispatch places on one CU (32 apart in an XCD's range)
 // hold tiles t and T - 1 - t.
 template <bool OUT_BF16>
@@ -1196,39 +1237,43 @@ __global__ void __launch_bounds__(kThreads) fwd_dense_kernel(const AttnParams p)
     const int lb = xcd_logical_block(blockIdx.x, p.bh * nt);
     const int bh = lb / nt, u = lb - bh * nt;
     const int tile = u < half ? u : nt - 1 + half - u;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
     const TileLanes tl = tile_lanes(c16, g);
     const int i0 = tile * 64, i = i0 + 16 * wave + c16;
     const bool row_ok = i < n;
     const int64_t head = (int64_t)bh * n * 64;
-    const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
-    const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
+    const __amdgpu_buffer_rsrc_t rk = head_rsrc(static_cast<const uint16_t *>(p.k) + head, span_bytes(n, 128));
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(static_cast<const uint16_t *>(p.v) + head, span_bytes(n, 128));
     const float sl2 = p.scale_log2;
 
     Frag<true> qf;
-    buf_frag(qf, head_rsrc(static_cast<const uint16_t *>(p.q) + head, n * 128), i, g);
-    dma_tile64(kt[0], K, 0, n, wave, lane);
-    dma_tile64(vt[0], V, 0, n, wave, lane);
+    buf_frag(qf, head_rsrc(static_cast<const uint16_t *>(p.q) + head, span_bytes(n, 128)), i, g);
+    // ring[x] holds the fetched key tile that is next staged at a step of parity x ^ 1.
+    // Fetches and stages run unconditionally, past the last tile on a copy of it, so that
+    // the wait before each stage counts exactly the loads issued after its fetch.
+    TileChunks ring[2];
+    fetch_tile(ring[0], rk, rv, 0, tid);
+    fetch_tile(ring[1], rk, rv, 64 * min(1, tile), tid);
+    stage_tile(kt[0], vt[0], ring[0], tid);
+    fetch_tile(ring[0], rk, rv, 64 * min(2, tile), tid);
 
     float m = kNegInf, lsum = 0.f;  // unscaled running maximum, running sum (lane partial)
     f32x4_t acc[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j <= tile; ++j) {
-        const int buf = j & 1;
-        wait_vm_all();
-        __syncthreads();  // key tile j has landed; every wave is done with tile j - 1
-        if (j < tile) {   // uniform: the next tile goes into the buffer tile j - 1 used
-            dma_tile64(kt[buf ^ 1], K, 64 * (j + 1), n, wave, lane);
-            dma_tile64(vt[buf ^ 1], V, 64 * (j + 1), n, wave, lane);
-        }
+    // step j: key tile j from stage b = j & 1; tile j + 1 goes from ring[b ^ 1] into the
+    // other stage, and ring[b ^ 1] then fetches tile j + 3
+    auto step = [&](int j, uint16_t *ks, uint16_t *vs, uint16_t *ks_next, uint16_t *vs_next, TileChunks &next) {
+        __syncthreads();  // key tile j is in its stage; every wave is done with tile j - 1
+        stage_tile(ks_next, vs_next, next, tid);
+        fetch_tile(next, rk, rv, 64 * min(j + 3, tile), tid);
         float sc[4][4], bm = kNegInf;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             Frag<true> kf;
-            lds_frag(kf, kt[buf], 16 * b, tl);
+            lds_frag(kf, ks, 16 * b, tl);
             f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
             if (j == tile) {  // uniform: the diagonal tile is causal-masked
 #pragma unroll
@@ -1250,17 +1295,30 @@ __global__ void __launch_bounds__(kThreads) fwd_dense_kernel(const AttnParams p)
             m = mn;
         }
         const float ms = m == kNegInf ? 0.f : m * sl2;
-        float pr[4][4];
+        // probabilities rounded to bf16 once: the P.V product and the row sum use the same values
+        u32x4_t pw[2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b) {
+            float pr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                pr[b][r] = fast_exp2(__builtin_fmaf(sc[b][r], sl2, -ms));
-                lsum += pr[b][r];
-            }
-        mma_over_rows_tr2(acc, vt[buf], 0, 16, tl, pr[0], pr[1]);
-        mma_over_rows_tr2(acc, vt[buf], 32, 48, tl, pr[2], pr[3]);
+            for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(__builtin_fmaf(sc[b][r], sl2, -ms));
+            pw[b >> 1][2 * (b & 1)] = pack_bf16(pr[0], pr[1]);
+            pw[b >> 1][2 * (b & 1) + 1] = pack_bf16(pr[2], pr[3]);
+        }
+        const bf16x2_t ones = as_bf16x2(0x3F803F80u);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) lsum = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pw[h][w]), ones, lsum, false);
+        mma_over_rows_tr2_packed(acc, vs, 0, 16, tl, pw[0]);
+        mma_over_rows_tr2_packed(acc, vs, 32, 48, tl, pw[1]);
+    };
+    int j = 0;
+    for (; j < tile; j += 2) {
+        step(j, kt[0], vt[0], kt[1], vt[1], ring[1]);
+        step(j + 1, kt[1], vt[1], kt[0], vt[0], ring[0]);
     }
+    if (j == tile) step(j, kt[0], vt[0], kt[1], vt[1], ring[1]);
     const float l = group_sum(lsum);
     if (row_ok) {
         store_row(static_cast<OE *>(p.out) + head, i, g, acc, 1.f / l);
@@ -1543,7 +1601,7 @@ __device__ __forceinline__ bool poll_tiles(const uint64_t *flags, int first, int
 // rows past the sequence end read as zero words.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int n_off, int bh) {
     const int slots = pair_slots(n_off);
-    return head_rsrc(p.pairs + (int64_t)bh * p.n * slots, p.n * slots * 4);
+    return head_rsrc(p.pairs + (int64_t)bh * p.n * slots, span_bytes(p.n, 4u * slots));
 }
 
 // dQ of query rows [t0, t0 + 64): the band keys [t0 - 64, t0 + 64) (K, V in LDS) on
@@ -1585,10 +1643,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
     const uint16_t *DO = static_cast<const uint16_t *>(p.dout) + head;
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128);
-    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, n * 128), rdo = head_rsrc(DO, n * 128);
-    const __amdgpu_buffer_rsrc_t rl = head_rsrc(p.lse_in + (int64_t)bh * n, n * 4);
-    const __amdgpu_buffer_rsrc_t rd = head_rsrc(p.delta + (int64_t)bh * n, n * 4);
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, span_bytes(n, 128)), rk = head_rsrc(K, span_bytes(n, 128));
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, span_bytes(n, 128)), rdo = head_rsrc(DO, span_bytes(n, 128));
+    const __amdgpu_buffer_rsrc_t rl = head_rsrc(p.lse_in + (int64_t)bh * n, span_bytes(n, 4));
+    const __amdgpu_buffer_rsrc_t rd = head_rsrc(p.delta + (int64_t)bh * n, span_bytes(n, 4));
     const float sl2 = p.scale_log2;
 
     dma_tile(ta, K, t0 - 64, n, wave, lane);
@@ -1602,7 +1660,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
         // D from the slab layout (whole rows per load); the band reads it back from LDS
         SFrag dos, os;
         sfrag_load(dos, rdo, row_s[0], row_s[1], c8);
-        sfrag_load<kCacheNT>(os, head_rsrc(static_cast<const uint16_t *>(p.o) + head, n * 128), row_s[0], row_s[1], c8);
+        sfrag_load<kCacheNT>(os, head_rsrc(static_cast<const uint16_t *>(p.o) + head, span_bytes(n, 128)), row_s[0], row_s[1], c8);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             di[h] = row8_sum(chunk_dot(dos.r[h], os.r[h]));
@@ -1893,8 +1951,8 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     const uint16_t *DO = static_cast<const uint16_t *>(p.dout) + head;
     const float *LSE = p.lse_in + (int64_t)bh * n;
     const float *DEL = p.delta + (int64_t)bh * n;
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, n * 128), rk = head_rsrc(K, n * 128);
-    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, n * 128), rdo = head_rsrc(DO, n * 128);
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, span_bytes(n, 128)), rk = head_rsrc(K, span_bytes(n, 128));
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, span_bytes(n, 128)), rdo = head_rsrc(DO, span_bytes(n, 128));
     const float sl2 = p.scale_log2;
 
     dma_tile(ta, Q, t0, n, wave, lane);
@@ -1929,7 +1987,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
             if (tid < kTileRows) {
                 const int row = t0 + tid;
                 del_s[tid] = (row < n) ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                             head_rsrc(DEL, n * 4), row * 4, 0, kCachePastL1))
+                                             head_rsrc(DEL, span_bytes(n, 4)), row * 4, 0, kCachePastL1))
                                        : 0.f;
             }
         }
@@ -1948,7 +2006,7 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     uint32_t pw[kRingKV][2];
     const int slots = pair_slots(n_off);
     const __amdgpu_buffer_rsrc_t rp =
-        FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, n * slots * 8) : pair_rsrc(p, n_off, bh);
+        FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, span_bytes(n, 8u * slots)) : pair_rsrc(p, n_off, bh);
     auto fill_words = [&](int u, int x) {
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
         const int iq0 = slab_row(p, n_off, t, row_s[0], 1) + far, iq1 = slab_row(p, n_off, t, row_s[1], 1) + far;
@@ -2418,7 +2476,7 @@ hipError_t launch_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnPara
 
 hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s,
                                  bool with_delta) {
-    if (window_path(dt, p)) {
+    if (window_backward(dt, p.w, p.n, p.n_off)) {
         // one launch when every XCD holds whole heads (its waits stay within one L2)
         if (p.flags && p.n_off > 0 && p.bh % 8 == 0) {
             const unsigned grid = 2 * tiles(p);

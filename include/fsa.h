@@ -139,10 +139,11 @@ fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, con
 /*
  * fsa_backward_workspace_bytes - bytes of pair workspace the backward needs.
  *
- * On the bf16 window path (dt = FSA_BF16, w <= 64, N <= 2^24) the gradient stage
- * has two parts: the dQ part stores, for every query row i and sparse offset o of
- * the table (offsets >= N dropped), the bf16 values of P and dS of the pair
- * (i, i - o) in one 32-bit word; the dK/dV part reads them. When B * H is a
+ * On the bf16 window path (dt = FSA_BF16, w <= 64, N <= 2^24, and 4 * S * N < 2^31
+ * with S below) the gradient stage has two parts: the dQ part stores, for every
+ * query row i and sparse offset o of the table (offsets >= N dropped), the bf16
+ * values of P and dS of the pair (i, i - o) in one 32-bit word; the dK/dV part
+ * reads them. When B * H is a
  * multiple of 8 both parts run in one launch: each 64-row tile's dQ part then
  * publishes a 64-bit token naming the launch (from the hardware dispatch id), and
  * the dK/dV parts wait for the tokens of the tiles they read (a bounded wait; if
@@ -231,8 +232,10 @@ fsa_status_t fsa_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
  *   - The derivative with respect to d is that of the piece [a, a + 1):
  *     k_{i-a-1} - k_{i-a} (and the same for v); rows without row i - a - 1
  *     contribute none. d(loss)/d(alpha) = sum_t F_t d(loss)/d(d_t).
- * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64; other valid
- * arguments return FSA_E_UNSUPPORTED.
+ * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64, and 8 * S * N <
+ * 2^31 (S: the entries some row reaches, rounded up to a multiple of 8; one head's
+ * pair words are addressed with 32-bit offsets); other valid arguments return
+ * FSA_E_UNSUPPORTED.
  */
 
 /*
@@ -344,8 +347,9 @@ fsa_status_t fsa_frac_decode(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, 
  * forward kernel rotates its own Q rows, the backward rotates Q and K by the same
  * pass (or reuses the forward's), and its inverse rotation is fused into the store
  * of dQ and dK.
- * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64; other valid
- * arguments return FSA_E_UNSUPPORTED.
+ * Supported for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64, and 4 * S * N <
+ * 2^31 (S: the table's offsets rounded up to a multiple of 8); other valid arguments
+ * return FSA_E_UNSUPPORTED.
  */
 
 /*
@@ -440,7 +444,8 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
  * fsa_rope_frac_forward / fsa_rope_frac_backward: arguments as in fsa_rope_forward /
  * fsa_rope_backward, plus dalpha and doffs as in fsa_frac_backward; reuse_rotated as
  * in fsa_rope_backward (ws then holds fsa_rope_frac_forward's rotated rows). Supported
- * for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64.
+ * for bf16 inputs, w <= 64, N <= 2^24, scale > 0, d = 64, within the pair-offset limit
+ * of the fractional calls.
  */
 fsa_status_t fsa_rope_frac_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                                            fsa_base_t base, double alpha, int32_t w, int32_t R, uint64_t *fwd_bytes,

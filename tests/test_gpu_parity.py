@@ -155,8 +155,9 @@ def test_wide_window_equals_dense_kernel_and_oracle(dtype):
         check(f"wide o[{h}]", o[0, h], ro, TOL[dtype])
 
 
-@pytest.mark.parametrize("N,scale", [(1, 0.125), (17, 0.125), (64, 0.125), (65, 0.125), (333, 0.125),
-                                     (1000, 0.125), (333, -0.125), (200, 0.0)])
+@pytest.mark.parametrize("N,scale", [(1, 0.125), (17, 0.125), (64, 0.125), (65, 0.125), (128, 0.125),
+                                     (129, 0.125), (191, 0.125), (256, 0.125), (333, 0.125), (1000, 0.125),
+                                     (333, -0.125), (200, 0.0)])
 def test_dense_forward_against_oracle(N, scale):
     # bf16 with a positive scale takes the dedicated dense kernel; other scales the general one
     x = inputs(15, 0, (1, 3, N, 64), torch.bfloat16)
