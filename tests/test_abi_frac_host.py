@@ -74,6 +74,17 @@ def fbwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=
 
 
 @pytest.mark.parametrize("call", [ffwd, fbwd])
+def test_frac_pair_words_need_32_bit_offsets(lib, call):
+    # w = 1, R = 2^30: 35 entries below N = 2^24 (40 slots of two words: 5.4 GB per head)
+    assert call(lib, N=1 << 24, w=1, R=1 << 30) == fsa.FSA_E_UNSUPPORTED
+    assert b"32-bit pair offsets" in lib.fsa_last_error()
+    # 12 entries (R = 300) at N = 2^23 (16 slots of two words: 1.1 GB per head) are accepted
+    ws = ctypes.c_uint64(0)
+    assert lib.fsa_frac_backward_workspace_bytes(1, 1, 1, 1 << 23, 64, 0, 1.0, 1, 300, ctypes.byref(ws)) == 0
+    assert ws.value > 16 * 8 << 23
+
+
+@pytest.mark.parametrize("call", [ffwd, fbwd])
 def test_frac_shape_dtype_and_path_errors(lib, call):
     assert call(lib, d=32) == fsa.FSA_E_UNSUPPORTED
     assert call(lib, d=0) == fsa.FSA_E_ARG

@@ -238,6 +238,16 @@ def test_backward_workspace_size(lib):
     assert lib.fsa_backward_workspace_bytes(1, 1, 1, 64, 64, 0, 1.0, 64, 1024, None) == fsa.FSA_E_ARG
 
 
+def test_backward_pair_words_need_32_bit_offsets(lib):
+    # w = 1, R = 2^30: the Fibonacci numbers below N are all offsets. At N = 2^23 there are
+    # 33 (40 slots, 160 bytes per row: 1.3 GB per head, within 32-bit offsets); at N = 2^24,
+    # 35 (40 slots: 2.7 GB per head), so the backward takes the general kernels, which need
+    # no pair words
+    n23 = 1 << 23
+    assert ws_bytes(lib, B=1, H=1, N=n23, w=1, R=1 << 30) == (fsa.FSA_OK, pair_ws(40 * n23, 1, n23))
+    assert ws_bytes(lib, B=1, H=1, N=1 << 24, w=1, R=1 << 30) == (fsa.FSA_OK, 0)
+
+
 @pytest.mark.parametrize("call", [bwd, grads])
 def test_backward_pair_workspace_checks(lib, call):
     # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 8 slots * 64 rows,

@@ -93,6 +93,13 @@ def test_rope_attention_checks(lib, call, n):
     assert call(lib, ws_bytes=0) == fsa.FSA_E_ARG and b"ws holds" in lib.fsa_last_error()
 
 
+@pytest.mark.parametrize("call,n", [(rfwd, 7), (rbwd, 11)])
+def test_rope_pair_words_need_32_bit_offsets(lib, call, n):
+    # w = 1, R = 2^30: 43 offsets (48 slots: 3.2 GB of pair words per head at N = 2^24)
+    assert call(lib, N=1 << 24, n_pos=1 << 24, w=1, R=1 << 30) == fsa.FSA_E_UNSUPPORTED
+    assert b"32-bit pair offsets" in lib.fsa_last_error()
+
+
 def a256(x):
     return (x + 255) // 256 * 256
 
