@@ -494,6 +494,27 @@ __device__ __forceinline__ void split_bf16(const float bv[4], u32x2_t &hi, u32x2
                  pack_bf16(bv[2] - bf16_lo(hi[1]), bv[3] - bf16_hi(hi[1]))};
 }
 
+// As mma_over_rows with the weights carried as bf16 high part plus bf16 remainder (two
+// MFMAs on one A operand), for unnormalised gradient weights; fp32 weights go through
+// the fp32 MFMA unrounded already.
+__device__ __forceinline__ void mma_over_rows_exact(f32x4_t acc[4], const uint16_t *At, int stride, int kk0, int c16,
+                                                    int g, const float bv[4]) {
+    u32x2_t h, l;
+    split_bf16(bv, h, l);
+    const i16x4_t bh = __builtin_bit_cast(i16x4_t, h), bl = __builtin_bit_cast(i16x4_t, l);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const i16x4_t a =
+            __builtin_bit_cast(i16x4_t, *reinterpret_cast<const u32x2_t *>(At + acc_row_d(db, c16) * stride + kk0 + 4 * g));
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bh, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bl, acc[db], 0, 0, 0);
+    }
+}
+__device__ __forceinline__ void mma_over_rows_exact(f32x4_t acc[4], const float *At, int stride, int kk0, int c16,
+                                                    int g, const float bv[4]) {
+    mma_over_rows(acc, At, stride, kk0, c16, g, bv);
+}
+
 // As mma_over_rows_tr2 and mma_over_rows_tr, with the weights carried as bf16 high
 // part plus remainder (two MFMAs on one A operand): for products whose weights are
 // large and unnormalised, where one bf16 rounding of each weight would add up.
@@ -1440,7 +1461,7 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
                     const float pv = ok ? fast_exp2(__builtin_fmaf(st[r], sl2, -lse2)) : 0.f;
                     ds[r] = pv * (dpt[r] - di);
                 }
-                mma_over_rows(acc, t0s, kT64, 16 * kb, c16, g, ds);
+                mma_over_rows_exact(acc, t0s, kT64, 16 * kb, c16, g, ds);
             }
         }
         if (r0 < n) {
@@ -1509,8 +1530,8 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
                     pr[r] = ok ? fast_exp2(__builtin_fmaf(sq[r], sl2, -lse_s[qi])) : 0.f;
                     ds[r] = pr[r] * (dpq[r] - del_s[qi]);
                 }
-                mma_over_rows(dv, t1s, kT64, 16 * qb, c16, g, pr);
-                mma_over_rows(dk, t0s, kT64, 16 * qb, c16, g, ds);
+                mma_over_rows_exact(dv, t1s, kT64, 16 * qb, c16, g, pr);
+                mma_over_rows_exact(dk, t0s, kT64, 16 * qb, c16, g, ds);
             }
         }
         // sparse offsets: queries i = j + o
