@@ -143,9 +143,16 @@ def cpu_baseline(cpu_inputs, alphas, heads_per_core=8):
 
 # ---------------------------------------------------------------- GPU part
 
+# The sources the kernels are compiled from, in a fixed order.
+KERNEL_SOURCES = ("fsa_internal.h", "fsa_device.h", "fsa_forward.hip", "fsa_backward.hip", "fsa_decode.hip",
+                  "fsa_rope.hip")
+
+
 def kernel_source_sha():
-    p = os.path.join(ROOT, "fibonacci_offset_transformer_amd", "csrc", "fsa_kernels.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "fibonacci_offset_transformer_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 # Kernels that one launch of each stage runs (bf16, window path, B * H a multiple of 8:

@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (fsa_abi.cpp) and the HIP kernels
-// (fsa_kernels.hip). Not installed; the public interface is include/fsa.h.
+// (fsa_*.hip). Not installed; the public interface is include/fsa.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
