@@ -28,6 +28,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -149,9 +150,15 @@ KERNEL_SOURCES = ("fsa_internal.h", "fsa_device.h", "fsa_forward.hip", "fsa_back
 
 
 def kernel_source_sha():
+    """Hash of the kernel sources' code, comments and blank lines left out (the sources
+    hold no string literal with a comment marker), so that a comment edit keeps the
+    counter readings taken on the same code."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, "fibonacci_offset_transformer_amd", "csrc", name), "rb").read())
+        text = open(os.path.join(ROOT, "fibonacci_offset_transformer_amd", "csrc", name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*", "", line).rstrip() for line in text.split("\n"))
+        h.update("\n".join(line for line in lines if line).encode())
     return h.hexdigest()
 
 

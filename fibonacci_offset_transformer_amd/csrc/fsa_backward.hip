@@ -219,14 +219,16 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
     }
 }
 
-// Backward on the window path (bf16 inputs, w <= 64) runs as two kernels over 64-row
-// tiles. The first forms dQ of its query rows and, for every sparse pair (query i,
-// key i - off[t]), stores P and dS rounded to bf16 (the weights the gradient products
-// use) in a pair workspace [BH, N, S] of 32-bit words (P in the low half). The
-// second forms dK and dV of its key rows from the window band, recomputed on MFMA, and
-// from the stored weights of the sparse pairs (key j, query j + off[t]), so no score is
-// formed twice on the vector units. Each kernel keeps one pair of operands resident
-// (K, V for dQ; Q, dO for dK and dV), which halves the data an XCD's L2 has to hold.
+// Backward on the window path (bf16 inputs, w <= 64) has two parts over 64-row tiles.
+// The dQ part forms dQ of its query rows and, for every sparse pair (query i, key
+// i - off[t]), stores P and dS rounded to bf16 (the weights the gradient products use)
+// in a pair workspace [BH, N, S] of 32-bit words (P in the low half). The dK/dV part
+// forms dK and dV of its key rows from the window band, recomputed on MFMA, and from
+// the stored weights of the sparse pairs (key j, query j + off[t]), so no score is
+// formed twice on the vector units. Each part keeps one pair of operands resident (K, V
+// for dQ; Q, dO for dK and dV), which halves the data an XCD's L2 has to hold. The two
+// parts run as two kernels (bwd_dq_kernel, bwd_dkdv_kernel) or, when B * H is a
+// multiple of 8, in one launch (bwd_fused_kernel) joined by per-tile tokens.
 
 constexpr int kRingQ = 4, kPreQ = 2;    // dQ kernel: slab slots in the ring; slots requested before the band
 constexpr int kRingKV = 3, kPreKV = 1;  // dK/dV kernel
