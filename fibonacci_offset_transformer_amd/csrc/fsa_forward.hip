@@ -301,18 +301,17 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     } else {
         sfrag_load(qs, rq, row_s[0], row_s[1], c8);
     }
-    // moves the state to a new maximum; skipped (uniformly) when no row's maximum grew,
-    // which the band's 64 keys make the common case
+    // moves the state to a new maximum. Unconditional: where no maximum grew the factor
+    // is 2^0 = 1. (Skipping it when no row's maximum grew, the common case after the
+    // band's 64 keys, made the compiler copy the whole state around the branch.)
     auto rescale = [&](const float mn[2]) {
-        if (__builtin_amdgcn_ballot_w64((mn[0] > m_s[0]) | (mn[1] > m_s[1])) != 0) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float al = fast_exp2(m_s[h] - (mn[h] == kNegInf ? 0.f : mn[h]));
-                acc_s[h][0] *= al;
-                acc_s[h][1] *= al;
-                l_s[h] *= al;
-                m_s[h] = mn[h];
-            }
+        for (int h = 0; h < 2; ++h) {
+            const float al = fast_exp2(m_s[h] - (mn[h] == kNegInf ? 0.f : mn[h]));
+            acc_s[h][0] *= al;
+            acc_s[h][1] *= al;
+            l_s[h] *= al;
+            m_s[h] = mn[h];
         }
     };
     if constexpr (FRAC) {
