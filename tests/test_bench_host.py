@@ -32,3 +32,21 @@ def test_algorithmic_bytes_match_the_stated_totals():
 def test_dense_flops():
     assert bench.dense_flops_per_layer() == 2 * 8 * 4 * 64 * (4096 * 4097 // 2)
     assert abs(bench.dense_flops_per_layer() / 1e9 - 34.4) < 0.1
+
+
+def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    # the counter readings stay keyed to the kernel code: a comment edit keeps the hash,
+    # a code edit changes it
+    csrc = os.path.join(ROOT, "fibonacci_offset_transformer_amd", "csrc")
+    pkg = tmp_path / "fibonacci_offset_transformer_amd" / "csrc"
+    pkg.mkdir(parents=True)
+    for name in bench.KERNEL_SOURCES:
+        (pkg / name).write_text(open(os.path.join(csrc, name)).read())
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    base = bench.kernel_source_sha()
+    f = pkg / "fsa_forward.hip"
+    text = f.read_text()
+    f.write_text("// an added comment line\n" + text.replace("\n", "  // trailing note\n", 1) + "\n/* block */\n")
+    assert bench.kernel_source_sha() == base
+    f.write_text(text.replace("kNegInf", "-kNegInf", 1))
+    assert bench.kernel_source_sha() != base
