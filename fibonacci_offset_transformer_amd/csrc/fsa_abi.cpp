@@ -12,6 +12,7 @@
 // This file must be compiled without -ffast-math: the table depends on exact
 // IEEE double rounding of alpha * F.
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -195,6 +196,16 @@ int trim_offsets(int32_t *off, int count, int32_t N) {
     return c;
 }
 
+// Set by fsa_debug_force_wait_timeout: the one-launch backward's waits then look for a
+// value no workgroup publishes and give up after a few polls.
+std::atomic<int> g_force_give_up{0};
+
+void set_wait_limits(fsa::AttnParams &p) {
+    const bool forced = g_force_give_up.load(std::memory_order_relaxed) != 0;
+    p.max_polls = forced ? 16 : fsa::kMaxPolls;
+    p.token_xor = forced ? 1u : 0u;
+}
+
 fsa_status_t launched(hipError_t e, const char *what) {
     if (e != hipSuccess)
         return fail(FSA_E_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
@@ -306,6 +317,10 @@ fsa_status_t prepare_grads(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_d
     p.pairs = need > 0 ? static_cast<uint32_t *>(pair_ws) : nullptr;
     p.flags = need > 0 ? reinterpret_cast<uint64_t *>(static_cast<char *>(pair_ws) + fsa::pair_ws_flags_offset(words))
                        : nullptr;
+    p.status = need > 0 ? reinterpret_cast<uint64_t *>(static_cast<char *>(pair_ws) +
+                                                       fsa::pair_ws_status_offset(words, static_cast<int64_t>(B) * H, N))
+                        : nullptr;
+    set_wait_limits(p);
     p.bh = B * H;
     p.n = N;
     p.w = w;
@@ -563,6 +578,8 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
         p.pairs = reinterpret_cast<uint32_t *>(base_ws + lay.pairs);
         p.dd_part = reinterpret_cast<float *>(base_ws + lay.partials);
         p.flags = reinterpret_cast<uint64_t *>(base_ws + lay.flags);
+        p.status = reinterpret_cast<uint64_t *>(base_ws + lay.status);
+        set_wait_limits(p);
     } else {
         p.bh = 0;  // no tiles: only the alpha reduction runs, writing zeros
     }
@@ -611,7 +628,7 @@ fsa_status_t check_rope_path(fsa_dtype_t dt, int32_t w, int32_t N, float scale, 
     if (dt != FSA_BF16) return fail(FSA_E_UNSUPPORTED, "the rotary path stores rotated rows in bf16: bf16 inputs only");
     if (w > 64) return fail(FSA_E_UNSUPPORTED, "the rotary path needs a window w <= 64 (got %d)", w);
     if (N > (1 << 24)) return fail(FSA_E_UNSUPPORTED, "the rotary path needs N <= 2^24 (got %d)", N);
-    if (!fsa::pair_offsets_fit(N, n_off, 1))
+    if (!fsa::pair_offsets_fit(N, n_off, fsa::pair_slot_words(w)))
         return fail(FSA_E_UNSUPPORTED, "the rotary path: N = %d with %d offsets exceeds 32-bit pair offsets", N, n_off);
     if (!(scale > 0.f)) return fail(FSA_E_UNSUPPORTED, "the rotary path needs a positive scale");
     if (n_pos < N) return fail(FSA_E_ARG, "the rotary table has %d positions, the sequence %d", n_pos, N);
@@ -620,9 +637,10 @@ fsa_status_t check_rope_path(fsa_dtype_t dt, int32_t w, int32_t N, float scale, 
 
 struct RopeLayout {
     uint64_t qhat, khat, delta, pairs, fwd, bwd;  // byte offsets into ws and the two sizes
+    int64_t words;                                // pair words of the static backward's workspace
 };
 
-RopeLayout rope_layout(int64_t bh, int32_t n, int32_t n_off) {
+RopeLayout rope_layout(int64_t bh, int32_t n, int32_t n_off, int32_t w) {
     RopeLayout l;
     const uint64_t rows = static_cast<uint64_t>(bh) * n;
     l.qhat = 0;
@@ -630,7 +648,8 @@ RopeLayout rope_layout(int64_t bh, int32_t n, int32_t n_off) {
     l.fwd = l.khat + fsa::align256(rows * 128);
     l.delta = l.fwd;
     l.pairs = l.delta + fsa::align256(rows * 4);
-    l.bwd = l.pairs + fsa::align256(fsa::pair_ws_bytes(FSA_BF16, 64, n, bh, n_off));
+    l.words = fsa::pair_words(FSA_BF16, w, n, bh, n_off);
+    l.bwd = l.pairs + fsa::align256(fsa::pair_ws_bytes(FSA_BF16, w, n, bh, n_off));
     return l;
 }
 
@@ -665,7 +684,7 @@ fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int3
     const int n_off = build_table(base, alpha, w, R, tab, &st);
     if (n_off < 0) return st;
     if ((st = check_rope_path(dt, w, N, 1.0f, N, n_off)) != FSA_OK) return st;
-    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, trim_offsets(tab, n_off, N));
+    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, trim_offsets(tab, n_off, N), w);
     *fwd_bytes = static_cast<int64_t>(B) * H * N == 0 ? 0 : l.fwd;
     *bwd_bytes = static_cast<int64_t>(B) * H * N == 0 ? 0 : l.bwd;
     return ok();
@@ -688,7 +707,7 @@ fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
     if ((st = check_ptrs(names, ptrs, 7)) != FSA_OK) return st;
     if ((st = check_no_alias(names, ptrs, 4, 7)) != FSA_OK) return st;
     p.n_off = trim_offsets(p.off, n_off, N);
-    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, p.n_off);
+    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, p.n_off, w);
     if (ws_bytes < l.fwd)
         return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
                     static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.fwd));
@@ -733,7 +752,7 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     if ((st = check_ptrs(names, ptrs, 11)) != FSA_OK) return st;
     if ((st = check_no_alias(names, ptrs, 7, 11)) != FSA_OK) return st;
     p.n_off = trim_offsets(p.off, n_off, N);
-    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, p.n_off);
+    const RopeLayout l = rope_layout(static_cast<int64_t>(B) * H, N, p.n_off, w);
     if (ws_bytes < l.bwd)
         return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
                     static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.bwd));
@@ -756,11 +775,11 @@ fsa_status_t fsa_rope_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     p.dv = dv;
     p.delta = reinterpret_cast<float *>(wsb + l.delta);
     p.pairs = p.n_off > 0 ? reinterpret_cast<uint32_t *>(wsb + l.pairs) : nullptr;
-    p.flags = p.n_off > 0 ? reinterpret_cast<uint64_t *>(
-                                wsb + l.pairs +
-                                fsa::pair_ws_flags_offset(fsa::pair_words(FSA_BF16, 64, N, static_cast<int64_t>(B) * H,
-                                                                          p.n_off)))
-                          : nullptr;
+    p.flags = p.n_off > 0 ? reinterpret_cast<uint64_t *>(wsb + l.pairs + fsa::pair_ws_flags_offset(l.words)) : nullptr;
+    p.status = p.n_off > 0 ? reinterpret_cast<uint64_t *>(
+                                 wsb + l.pairs + fsa::pair_ws_status_offset(l.words, static_cast<int64_t>(B) * H, N))
+                           : nullptr;
+    set_wait_limits(p);
     p.rope = rope;
     p.bh = B * H;
     p.n = N;
@@ -936,8 +955,77 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
     p.pairs = reinterpret_cast<uint32_t *>(fw + fl.pairs);
     p.dd_part = reinterpret_cast<float *>(fw + fl.partials);
     p.flags = reinterpret_cast<uint64_t *>(fw + fl.flags);
+    p.status = reinterpret_cast<uint64_t *>(fw + fl.status);
+    set_wait_limits(p);
     p.rope = rope;
     return launched(fsa::launch_frac_backward(out_dt, p, hs), "rotary fractional backward");
+}
+
+fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                             fsa_base_t base, double alpha, int32_t w, int32_t R, const void *ws,
+                             uint64_t ws_bytes, int32_t *gave_up, void *stream) {
+    if (!gave_up) return fail(FSA_E_ARG, "gave_up is NULL");
+    *gave_up = 0;
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    bool one_launch = false;
+    uint64_t flags = 0, status = 0, need = 0;  // byte offsets of the token array and status word, ws size
+    fsa_status_t st = FSA_OK;
+    if (kind == FSA_WS_BACKWARD || kind == FSA_WS_ROPE_BACKWARD) {
+        const Shape s{B, H, N, d};
+        if ((st = check_common(dt, dt, s, 1.0f)) != FSA_OK) return st;
+        int32_t tab[FSA_MAX_OFFSETS];
+        const int n_all = build_table(base, alpha, w, R, tab, &st);
+        if (n_all < 0) return st;
+        const int n_off = trim_offsets(tab, n_all, N);
+        uint64_t pairs = 0;  // start of the static backward's workspace within ws
+        if (kind == FSA_WS_ROPE_BACKWARD) {
+            if ((st = check_rope_path(dt, w, N, 1.0f, N, n_all)) != FSA_OK) return st;
+            const RopeLayout l = rope_layout(bh, N, n_off, w);
+            pairs = l.pairs;
+            need = l.bwd;
+        } else {
+            need = fsa::pair_ws_bytes(dt, w, N, bh, n_off);
+        }
+        const int64_t words = fsa::pair_words(dt, w, N, bh, n_off);
+        one_launch = words > 0 && n_off > 0 && bh % 8 == 0;
+        flags = pairs + fsa::pair_ws_flags_offset(words);
+        status = pairs + fsa::pair_ws_status_offset(words, bh, N);
+    } else if (kind == FSA_WS_FRAC_BACKWARD || kind == FSA_WS_ROPE_FRAC_BACKWARD) {
+        fsa::AttnParams p{};
+        if ((st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R)) != FSA_OK) return st;
+        const fsa::FracWorkspace fl = fsa::frac_workspace(bh, N, p.n_off);
+        uint64_t frac = 0;
+        need = fl.total;
+        if (kind == FSA_WS_ROPE_FRAC_BACKWARD) {
+            const RopeFracLayout l = rope_frac_layout(bh, N, p.n_off);
+            frac = l.frac;
+            need = l.bwd;
+        }
+        one_launch = bh * N > 0 && p.n_off > 0 && bh % 8 == 0;
+        flags = frac + fl.flags;
+        status = frac + fl.status;
+    } else {
+        return fail(FSA_E_ARG, "unknown workspace kind %d", static_cast<int>(kind));
+    }
+    if (!one_launch) return ok();  // no waits on this path
+    if (!ws) return fail(FSA_E_ARG, "ws is NULL");
+    if (ws_bytes < need)
+        return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
+                    static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(need));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    uint64_t words[2] = {0, 0};
+    const char *b = static_cast<const char *>(ws);
+    hipError_t e = hipMemcpyAsync(&words[0], b + flags, 8, hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipMemcpyAsync(&words[1], b + status, 8, hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return fail(FSA_E_HIP, "reading the wait status failed: %s", hipGetErrorString(e));
+    *gave_up = words[0] == words[1] ? 1 : 0;
+    return ok();
+}
+
+fsa_status_t fsa_debug_force_wait_timeout(int32_t enable) {
+    g_force_give_up.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
+    return ok();
 }
 
 const char *fsa_last_error(void) { return g_last_error.c_str(); }

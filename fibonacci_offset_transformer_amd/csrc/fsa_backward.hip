@@ -249,18 +249,18 @@ __device__ __forceinline__ uint64_t launch_token() {
 // wrote, in the same XCD's L2. No CU reads them before their token is set, so no L1
 // holds an older copy.
 constexpr int kCachePastL1 = 1;
-
-// Polls before giving up; with the sleep below they span tens of milliseconds, far
-// beyond any real wait (the dQ work of a whole launch takes tens of microseconds).
-constexpr int kMaxSpins = 1 << 18;
-
 // Waits until flags[first .. last] all hold the token (one wave; lane l checks flags
 // first + l, first + l + 64, ...; device-scope loads, which miss this CU's L1). Each
 // poll requests up to 64 * BATCH flags before comparing any, so that it costs one
-// round trip for up to that many tiles. Returns false, uniformly over the wave, if it
-// gave up; the caller then stores NaN so that the failure shows.
+// round trip for up to that many tiles. The wait is bounded (p.max_polls polls with a
+// short sleep between them) and looks for token ^ p.token_xor (the token itself unless
+// the host forces a give-up). Returns false, uniformly over the wave, if it gave up;
+// the caller then records the launch's token in p.status and stores NaN so that the
+// failure shows.
 template <int BATCH = 1>
-__device__ __forceinline__ bool poll_tiles(const uint64_t *flags, int first, int last, uint64_t token, int lane) {
+__device__ __forceinline__ bool poll_tiles(const AttnParams &p, const uint64_t *flags, int first, int last,
+                                           uint64_t token, int lane) {
+    const uint64_t want = token ^ p.token_xor;
     for (int spin = 0;; ++spin) {
         bool ready = true;
         for (int base = first + lane; base <= last; base += 64 * BATCH) {
@@ -271,19 +271,26 @@ __device__ __forceinline__ bool poll_tiles(const uint64_t *flags, int first, int
             for (int k = 0; k < BATCH; ++k)
                 v[k] = __hip_atomic_load(flags + min(base + 64 * k, last), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int k = 0; k < BATCH; ++k) ready &= (base + 64 * k > last) | (v[k] == token);
+            for (int k = 0; k < BATCH; ++k) ready &= (base + 64 * k > last) | (v[k] == want);
         }
         if (__builtin_amdgcn_ballot_w64(!ready) == 0) return true;
-        if (spin == kMaxSpins) return false;
+        if (spin >= p.max_polls) return false;
         __builtin_amdgcn_s_sleep(4);
     }
 }
 
-// Descriptor over the pair-workspace words of head bh ([N, S] words, S = pair_slots):
-// rows past the sequence end read as zero words.
+// Records that a wait of this launch gave up: the status word takes the launch's token
+// (read back by the host, see fsa_wait_status).
+__device__ __forceinline__ void record_give_up(const AttnParams &p, uint64_t token) {
+    __hip_atomic_store(p.status, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Descriptor over the pair-workspace words of head bh ([N, S, WORDS] words, S =
+// pair_slots): rows past the sequence end read as zero words.
+template <int WORDS>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p, int n_off, int bh) {
     const int slots = pair_slots(n_off);
-    return head_rsrc(p.pairs + (int64_t)bh * p.n * slots, span_bytes(p.n, 4u * slots));
+    return head_rsrc(p.pairs + (int64_t)bh * p.n * slots * WORDS, span_bytes(p.n, 4u * slots * WORDS));
 }
 
 // dQ of query rows [t0, t0 + 64): the band keys [t0 - 64, t0 + 64) (K, V in LDS) on
@@ -298,13 +305,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p,
 // entry, the derivative of the loss with respect to the entry's distance over its rows
 // (one partial per workgroup and entry; see reduce_alpha_grad).
 //
+// With EXACT (windows narrower than 64, static tables) each pair slot holds P and dS as
+// two fp32 words, and the sparse part of dQ takes dS unrounded.
+//
 // The body works on logical tile lb with the caller's LDS: ta, tb (band K and V rows,
 // kTileRows * 64 each, then merge areas), d_s (64 floats: D of the tile's rows, WITH_D)
 // and dd_s (4 * FSA_MAX_OFFSETS floats, FRAC).
-template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0, bool PUBLISH = false>
+template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0, bool PUBLISH = false, bool EXACT = false>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *d_s,
                                         float *dd_s) {
     static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
+    static_assert(!(FRAC && EXACT), "fractional entries keep their own pair format");
     using OE = typename Elem<OUT_BF16>::T;
 
     const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
@@ -442,10 +453,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     float lse2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
-    // pair words of this head's rows: [n, slots]; lane c8 of a row keeps the word of
-    // slot c8 of the unrolled part and the eight lanes store them with one 32-byte write
     const int slots = pair_slots(n_off);
-    uint32_t *pairs = p.pairs + (int64_t)bh * n * slots;
     if constexpr (FRAC) {
         // pair words [n, slots, 2]: the near word {(1 - phi) P, (1 - phi) dS} and the far
         // word {phi P, phi dS} of every entry, each rounded once to bf16, stored by the lane
@@ -493,7 +501,11 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
             }
         }
     } else {
-        uint32_t keep[2] = {0u, 0u};
+        // pair slots of this head's rows: [n, slots]; lane c8 of a row keeps slot c8 of the
+        // unrolled part and the eight lanes store them with one 32-byte (EXACT: 64-byte) write
+        using PairT = typename PairSlot<EXACT>::T;
+        PairT *pairs = reinterpret_cast<PairT *>(p.pairs) + (int64_t)bh * n * slots;
+        PairT keep[2] = {PairT{}, PairT{}};
         auto slab = [&](int t, int o, const SFrag &kt, const SFrag &vt) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -501,12 +513,19 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
                 const float s = row8_sum(chunk_dot(qs.r[h], kt.r[h]));
                 const float dp = row8_sum(chunk_dot(dos.r[h], vt.r[h]));
                 const float pv = ok ? fast_exp2(__builtin_fmaf(s, sl2, -lse2[h])) : 0.f;
-                const uint32_t pw = pack_bf16(pv, pv * (dp - di[h]));
+                const float ds = pv * (dp - di[h]);
+                PairT pw;
+                if constexpr (EXACT) {
+                    pw = PairT{__float_as_uint(pv), __float_as_uint(ds)};
+                    chunk_axpy_f32(dq_s[h], ds, kt.r[h]);
+                } else {
+                    pw = pack_bf16(pv, ds);
+                    chunk_axpy_words(dq_s[h], pw >> 16, pw & 0xffff0000u, kt.r[h]);
+                }
                 if (t < 8)
-                    keep[h] = c8 == t ? pw : keep[h];
+                    keep[h] = select(c8 == t, pw, keep[h]);
                 else if (c8 == 0 && row_s[h] < n)
                     pairs[(int64_t)row_s[h] * slots + t] = pw;
-                chunk_axpy_words(dq_s[h], pw >> 16, pw & 0xffff0000u, kt.r[h]);
             }
         };
 #pragma unroll
@@ -553,13 +572,14 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     }
 }
 
-template <bool OUT_BF16, bool WITH_D, bool FRAC>
+template <bool OUT_BF16, bool WITH_D, bool FRAC, bool EXACT = false>
 __global__ void __launch_bounds__(kThreads) bwd_dq_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
     __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
     __shared__ float d_s[64];
     __shared__ float dd_s[FRAC ? 4 * FSA_MAX_OFFSETS : 1];
-    dq_tile<OUT_BF16, WITH_D, FRAC>(p, xcd_logical_block(blockIdx.x, p.bh * ((p.n + 63) >> 6)), ta, tb, d_s, dd_s);
+    dq_tile<OUT_BF16, WITH_D, FRAC, 0, false, EXACT>(p, xcd_logical_block(blockIdx.x, p.bh * ((p.n + 63) >> 6)), ta,
+                                                     tb, d_s, dd_s);
 }
 
 // Alpha gradient of the fractional backward, run by one whole workgroup: d(loss)/d(d_t)
@@ -606,11 +626,13 @@ __device__ void reduce_alpha_grad(const AttnParams &p, double *red) {
 // kTileRows floats each). With FUSED the dQ work of the same call runs in the same
 // launch (bwd_fused_kernel): D and the pair words are read only once the tiles that
 // write them have published this launch's token (poll_tiles, while the band rows load).
-// FROM_DQ: D comes from that dQ work (otherwise the caller gave it).
-template <bool OUT_BF16, bool FRAC, bool FUSED = false, bool FROM_DQ = false, int NOFF = 0>
+// FROM_DQ: D comes from that dQ work (otherwise the caller gave it). EXACT: the pair
+// slots hold P and dS as fp32 words (see dq_tile), which weight the rows unrounded.
+template <bool OUT_BF16, bool FRAC, bool FUSED = false, bool FROM_DQ = false, int NOFF = 0, bool EXACT = false>
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *lse_s,
                                           float *del_s, [[maybe_unused]] const uint64_t token = 0) {
     static_assert(FUSED || !FROM_DQ, "D comes from the same launch only in the one-launch backward");
+    static_assert(!(FRAC && EXACT), "fractional entries keep their own pair format");
     using OE = typename Elem<OUT_BF16>::T;
 
     const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
@@ -657,8 +679,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
         if (wave == 0) {
             const int far = n_off > 0 ? t0 + 63 + p.off[n_off - 1] + (FRAC ? 1 : 0) : t0;
             const int last = min(nt - 1, max(FROM_DQ ? tile + 1 : tile, far >> 6));
-            const bool ok = poll_tiles(p.flags + (int64_t)bh * nt, tile, last, token, lane);
-            if (lane == 0) gave_up = ok ? 0 : 1;
+            const bool ok = poll_tiles(p, p.flags + (int64_t)bh * nt, tile, last, token, lane);
+            if (lane == 0) {
+                gave_up = ok ? 0 : 1;
+                if (!ok) record_give_up(p, token);
+            }
         }
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(gave_up)) {
@@ -684,11 +709,13 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     // slot u of the ring. FRAC: the ring runs over half entries, 2t (the near queries
     // j + off[t] with their near words) and 2t + 1 (the far queries j + off[t] + 1 with
     // their far words)
+    using PairT = typename PairSlot<EXACT>::T;
     SFrag sq[kRingKV], sd[kRingKV];
-    uint32_t pw[kRingKV][2];
+    PairT pw[kRingKV][2];
     const int slots = pair_slots(n_off);
-    const __amdgpu_buffer_rsrc_t rp =
-        FRAC ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, span_bytes(n, 8u * slots)) : pair_rsrc(p, n_off, bh);
+    const __amdgpu_buffer_rsrc_t rp = FRAC    ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, span_bytes(n, 8u * slots))
+                                      : EXACT ? pair_rsrc<2>(p, n_off, bh)
+                                              : pair_rsrc<1>(p, n_off, bh);
     auto fill_words = [&](int u, int x) {
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
         const int iq0 = slab_row(p, n_off, t, row_s[0], 1) + far, iq1 = slab_row(p, n_off, t, row_s[1], 1) + far;
@@ -697,6 +724,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
                                                             FUSED ? kCachePastL1 : 0);
             pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0,
                                                             FUSED ? kCachePastL1 : 0);
+        } else if constexpr (EXACT) {
+            pw[u][0] = __builtin_bit_cast(
+                PairT, __builtin_amdgcn_raw_buffer_load_b64(rp, (iq0 * slots + t) * 8, 0, FUSED ? kCachePastL1 : 0));
+            pw[u][1] = __builtin_bit_cast(
+                PairT, __builtin_amdgcn_raw_buffer_load_b64(rp, (iq1 * slots + t) * 8, 0, FUSED ? kCachePastL1 : 0));
         } else {
             pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq0 * slots + t) * 4, 0, FUSED ? kCachePastL1 : 0);
             pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, (iq1 * slots + t) * 4, 0, FUSED ? kCachePastL1 : 0);
@@ -772,14 +804,19 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     c_to_slab(reinterpret_cast<float *>(ta) + wave * 1024, dk, dk_s, c16, g, s8, c8);
     c_to_slab(reinterpret_cast<float *>(tb) + wave * 1024, dv, dv_s, c16, g, s8, c8);
 
-    // sparse offsets: queries j + o, weights P (low half) and dS (high half) as stored;
-    // pairs past the sequence end read as zero words
-    auto slab = [&](const uint32_t pwt[2], const SFrag &qt, const SFrag &dt) {
+    // sparse offsets: queries j + o, weights P (low half, or first word) and dS (high
+    // half, or second word) as stored; pairs past the sequence end read as zero words
+    auto slab = [&](const PairT pwt[2], const SFrag &qt, const SFrag &dt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t x = pwt[h];
-            chunk_axpy_words(dv_s[h], x & 0xffffu, x << 16, dt.r[h]);
-            chunk_axpy_words(dk_s[h], x >> 16, x & 0xffff0000u, qt.r[h]);
+            if constexpr (EXACT) {
+                chunk_axpy_f32(dv_s[h], __uint_as_float(pwt[h][0]), dt.r[h]);
+                chunk_axpy_f32(dk_s[h], __uint_as_float(pwt[h][1]), qt.r[h]);
+            } else {
+                const uint32_t x = pwt[h];
+                chunk_axpy_words(dv_s[h], x & 0xffffu, x << 16, dt.r[h]);
+                chunk_axpy_words(dk_s[h], x >> 16, x & 0xffff0000u, qt.r[h]);
+            }
         }
     };
     if constexpr (FRAC) {
@@ -829,8 +866,11 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
                 // every tile's partials come from this launch's dQ work, on any XCD
                 __shared__ int all_ok;
                 if (wave == 0) {
-                    const bool ok = poll_tiles<16>(p.flags, 0, p.bh * nt - 1, token, lane);
-                    if (lane == 0) all_ok = ok ? 1 : 0;
+                    const bool ok = poll_tiles<16>(p, p.flags, 0, p.bh * nt - 1, token, lane);
+                    if (lane == 0) {
+                        all_ok = ok ? 1 : 0;
+                        if (!ok) record_give_up(p, token);
+                    }
                 }
                 __syncthreads();  // also: the LDS tiles are free again
                 if (!all_ok) {    // uniform: the wait gave up
@@ -846,13 +886,14 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     }
 }
 
-template <bool OUT_BF16, bool FRAC>
+template <bool OUT_BF16, bool FRAC, bool EXACT = false>
 __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t ta[kTileRows * 64];
     __shared__ __attribute__((aligned(16))) uint16_t tb[kTileRows * 64];
     __shared__ __attribute__((aligned(16))) float lse_s[kTileRows];
     __shared__ __attribute__((aligned(16))) float del_s[kTileRows];
-    dkdv_tile<OUT_BF16, FRAC>(p, xcd_logical_block(blockIdx.x, p.bh * ((p.n + 63) >> 6)), ta, tb, lse_s, del_s);
+    dkdv_tile<OUT_BF16, FRAC, false, false, 0, EXACT>(p, xcd_logical_block(blockIdx.x, p.bh * ((p.n + 63) >> 6)), ta,
+                                                      tb, lse_s, del_s);
 }
 
 // The static backward in one launch: blocks [0, tiles) do the dQ work of tile
@@ -864,7 +905,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 // any dK/dV tile waits, and dQ tiles wait for nothing: the waits end. The host launches
 // this only when B * H is a multiple of 8: every XCD then holds whole heads, so a tile
 // and the tiles it waits for share one XCD and its L2.
-template <bool OUT_BF16, bool WITH_D, int NOFF = 0, bool FRAC = false>
+template <bool OUT_BF16, bool WITH_D, int NOFF = 0, bool FRAC = false, bool EXACT = false>
 __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p) {
     static_assert(!FRAC || (WITH_D && NOFF == 0), "the fractional form runs with D formed, any table length");
     constexpr int kFb = FRAC ? 4 * FSA_MAX_OFFSETS : kTileRows;
@@ -876,14 +917,14 @@ __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p)
     const uint64_t token = launch_token();
     if (static_cast<int>(blockIdx.x) < tiles) {
         const int lb = xcd_logical_block(blockIdx.x, tiles);
-        dq_tile<OUT_BF16, WITH_D, FRAC, NOFF, true>(p, lb, ta, tb, fa, fb);
+        dq_tile<OUT_BF16, WITH_D, FRAC, NOFF, true, EXACT>(p, lb, ta, tb, fa, fb);
         // every wave's stores (pair words, D, dQ) have reached L2 before the token does
         __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
-        dkdv_tile<OUT_BF16, FRAC, true, WITH_D, NOFF>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb, fa,
-                                                      fb, token);
+        dkdv_tile<OUT_BF16, FRAC, true, WITH_D, NOFF, EXACT>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb,
+                                                             fa, fb, token);
     }
 }
 
@@ -891,6 +932,36 @@ __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p)
 __global__ void __launch_bounds__(kThreads) frac_alpha_kernel(const AttnParams p) {
     __shared__ double red[FSA_MAX_OFFSETS];
     reduce_alpha_grad(p, red);
+}
+
+// Static window backward with pair slots of one format (EXACT: fp32 P and dS).
+template <bool EXACT>
+hipError_t launch_window_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s, bool with_delta) {
+    // one launch when every XCD holds whole heads (its waits stay within one L2)
+    if (one_launch_backward(p)) {
+        const unsigned grid = 2 * tiles(p);
+        auto fused = [&](auto len) {
+            constexpr int L = decltype(len)::value;
+            if (with_delta)
+                return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, L, false, EXACT>, grid, p, s)
+                                          : launch(&bwd_fused_kernel<false, true, L, false, EXACT>, grid, p, s);
+            return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, false, L, false, EXACT>, grid, p, s)
+                                      : launch(&bwd_fused_kernel<false, false, L, false, EXACT>, grid, p, s);
+        };
+        // the narrow windows that take EXACT slots have long tables: the run-time length only
+        if constexpr (EXACT) return fused(Len<0>{});
+        else return with_table_length(p.n_off, fused);
+    }
+    hipError_t e;
+    if (with_delta)
+        e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, false, EXACT>, tiles(p), p, s)
+                               : launch(&bwd_dq_kernel<false, true, false, EXACT>, tiles(p), p, s);
+    else
+        e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, false, false, EXACT>, tiles(p), p, s)
+                               : launch(&bwd_dq_kernel<false, false, false, EXACT>, tiles(p), p, s);
+    if (e != hipSuccess) return e;
+    return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true, false, EXACT>, tiles(p), p, s)
+                              : launch(&bwd_dkdv_kernel<false, false, EXACT>, tiles(p), p, s);
 }
 
 }  // namespace
@@ -905,28 +976,8 @@ hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_
 hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s,
                                  bool with_delta) {
     if (window_backward(dt, p.w, p.n, p.n_off)) {
-        // one launch when every XCD holds whole heads (its waits stay within one L2)
-        if (p.flags && p.n_off > 0 && p.bh % 8 == 0) {
-            const unsigned grid = 2 * tiles(p);
-            return with_table_length(p.n_off, [&](auto len) {
-                constexpr int L = decltype(len)::value;
-                if (with_delta)
-                    return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, L>, grid, p, s)
-                                              : launch(&bwd_fused_kernel<false, true, L>, grid, p, s);
-                return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, false, L>, grid, p, s)
-                                          : launch(&bwd_fused_kernel<false, false, L>, grid, p, s);
-            });
-        }
-        hipError_t e;
-        if (with_delta)
-            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, false>, tiles(p), p, s)
-                                   : launch(&bwd_dq_kernel<false, true, false>, tiles(p), p, s);
-        else
-            e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, false, false>, tiles(p), p, s)
-                                   : launch(&bwd_dq_kernel<false, false, false>, tiles(p), p, s);
-        if (e != hipSuccess) return e;
-        return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true, false>, tiles(p), p, s)
-                                  : launch(&bwd_dkdv_kernel<false, false>, tiles(p), p, s);
+        if (pair_slot_words(p.w) == 2) return launch_window_backward<true>(out_dt, p, s, with_delta);
+        return launch_window_backward<false>(out_dt, p, s, with_delta);
     }
     if (with_delta) {  // the generic kernel reads D: form it first
         const hipError_t e = launch_backward_delta(dt, p, s);
@@ -941,7 +992,7 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
 
 hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (tiles(p) == 0) return launch(&frac_alpha_kernel, 1, p, s);  // writes the zeros of an empty problem
-    if (p.flags && p.n_off > 0 && p.bh % 8 == 0)  // one launch, as for the static tables
+    if (one_launch_backward(p))  // one launch, as for the static tables
         return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, 0, true>, 2 * tiles(p), p, s)
                                   : launch(&bwd_fused_kernel<false, true, 0, true>, 2 * tiles(p), p, s);
     const hipError_t e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, true>, tiles(p), p, s)

@@ -633,6 +633,35 @@ __device__ __forceinline__ void chunk_axpy(f32x4_t acc[2], float x, const u32x4_
     chunk_axpy_words(acc, xb, xb << 16, c);
 }
 
+// acc[0..1] += x * chunk in fp32: the bf16 values widened (exactly) to fp32 and the
+// weight x taken unrounded.
+__device__ __forceinline__ void chunk_axpy_f32(f32x4_t acc[2], float x, const u32x4_t &c) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        f32x4_t &a = acc[w >> 1];
+        const int r = 2 * (w & 1);
+        a[r] = __builtin_fmaf(bf16_lo(c[w]), x, a[r]);
+        a[r + 1] = __builtin_fmaf(bf16_hi(c[w]), x, a[r + 1]);
+    }
+}
+
+// One slot of the backward's pair workspace: P and dS as two bf16 in one word, or (EXACT)
+// as two fp32 words.
+template <bool EXACT>
+struct PairSlot {
+    using T = uint32_t;
+};
+template <>
+struct PairSlot<true> {
+    using T = u32x2_t;
+};
+
+// c ? a : b for a pair slot (one or two words).
+__device__ __forceinline__ uint32_t select(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
+__device__ __forceinline__ u32x2_t select(bool c, const u32x2_t &a, const u32x2_t &b) {
+    return u32x2_t{c ? a[0] : b[0], c ? a[1] : b[1]};
+}
+
 // DPP controls: quad_perm [1,0,3,2], quad_perm [2,3,0,1], and the mirror of each half row.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
 

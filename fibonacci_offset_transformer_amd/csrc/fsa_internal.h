@@ -47,8 +47,12 @@ struct AttnParams {
     // its position's angles before storing them (table [n_pos, 32, 2] of cos, sin).
     const float *rope;
     void *qhat;               // rotary forward: rotated Q rows written here [BH, N, 64]
-    // One-launch static backward: one 64-bit completion token per tile [BH * tiles per head].
+    // One-launch backward: one 64-bit completion token per tile [BH * tiles per head], and
+    // the status word a waiting workgroup that gave up sets to the launch's token.
     uint64_t *flags;
+    uint64_t *status;
+    int32_t max_polls;        // polls a wait makes before it gives up
+    uint32_t token_xor;       // waits look for token ^ token_xor (0; nonzero only to force a give-up)
 };
 
 // Rotary embedding of up to two [rows, 64] bf16 tensors (x[t] -> out[t]); rows come in
@@ -67,42 +71,59 @@ struct RopeParams {
 // The bf16 window kernels (w <= 64) address each head with 32-bit byte offsets.
 inline bool window_path(fsa_dtype_t dt, int32_t w, int32_t n) { return dt == FSA_BF16 && w <= 64 && n <= (1 << 24); }
 
-// Backward pair workspace on the window path: [BH, N, pair_slots(n_off)] 32-bit words,
-// word t of a query row holding bf16 P (low half) and bf16 dS (high half) of the
-// pair (row, row - off[t]). Slots come in groups of 8 so that one row's first eight
-// words are written by one 32-byte store. None elsewhere.
+// Backward pair workspace on the window path: [BH, N, pair_slots(n_off)] slots, slot t of a
+// query row holding P and dS of the pair (row, row - off[t]). Slots come in groups of 8 so
+// that one row's first eight slots are written by one store. None elsewhere.
 __host__ __device__ inline int32_t pair_slots(int32_t n_off) { return 8 * ((n_off + 7) / 8); }
-// The window backward addresses one head's pair words with 32-bit offsets: [N, slots]
-// words on the static path (words_per_slot 1), [N, slots, 2] on the learned-alpha path.
+
+// Format of a slot. With a window of 64 keys or more every query that has a sparse pair
+// also has at least 64 window keys, and one 32-bit word of two bf16 (P in the low half,
+// dS in the high half) carries the pair. With a narrower window a row's few keys can each
+// hold most of its probability: a bf16 rounding of such a weight (up to 2^-8 of it)
+// times an upstream gradient of a few units would take most of a 1e-2 error budget, so
+// P and dS travel unrounded as two fp32 words.
+constexpr int32_t kCompactPairWindow = 64;
+__host__ __device__ inline int32_t pair_slot_words(int32_t w) { return w >= kCompactPairWindow ? 1 : 2; }
+
+// The window backward addresses one head's pair words with 32-bit offsets: [N, slots,
+// words_per_slot] words (the learned-alpha path stores two words per slot).
 inline bool pair_offsets_fit(int32_t n, int32_t n_off, int words_per_slot) {
     return static_cast<int64_t>(n) * pair_slots(n_off) * 4 * words_per_slot <= INT32_MAX;
 }
 // The static backward takes the window kernels (and their pair workspace) when the
 // window path applies and the pair words of a head fit 32-bit offsets.
 inline bool window_backward(fsa_dtype_t dt, int32_t w, int32_t n, int32_t n_off) {
-    return window_path(dt, w, n) && pair_offsets_fit(n, n_off, 1);
+    return window_path(dt, w, n) && pair_offsets_fit(n, n_off, pair_slot_words(w));
 }
 inline int64_t pair_words(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
-    return window_backward(dt, w, n, n_off) ? static_cast<int64_t>(pair_slots(n_off)) * bh * n : 0;
+    return window_backward(dt, w, n, n_off)
+               ? static_cast<int64_t>(pair_slots(n_off)) * pair_slot_words(w) * bh * n
+               : 0;
 }
 inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 // The static backward's workspace on the window path: the pair words, then (256-byte
 // aligned) one 64-bit completion token per 64-row tile, which the one-launch backward
-// uses. Empty when the table has no sparse offsets.
+// uses, then one 64-bit status word (the token of a one-launch backward whose dK/dV
+// work gave up waiting; see fsa_backward_status). Empty when the table has no sparse
+// offsets.
 inline uint64_t pair_ws_flags_offset(int64_t words) { return align256(4ull * static_cast<uint64_t>(words)); }
+inline uint64_t pair_ws_status_offset(int64_t words, int64_t bh, int32_t n) {
+    return pair_ws_flags_offset(words) + 8ull * static_cast<uint64_t>(bh) * ((n + 63) / 64);
+}
 inline uint64_t pair_ws_bytes(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, int32_t n_off) {
     const int64_t words = pair_words(dt, w, n, bh, n_off);
     if (words == 0) return 0;
-    return pair_ws_flags_offset(words) + 8ull * static_cast<uint64_t>(bh) * ((n + 63) / 64);
+    return pair_ws_status_offset(words, bh, n) + 8;
 }
 
 // Fractional-entry backward workspace on the window path: D [BH, N] floats, then the
 // pair words [BH, N, pair_slots(n_off), 2] (the near and far weights of every
 // entry), then the per-tile partials [n_off, tiles], then one 64-bit completion token
-// per tile (the one-launch backward); each part 256-byte aligned.
+// per tile (the one-launch backward), then the 64-bit status word; each part 256-byte
+// aligned.
 struct FracWorkspace {
-    uint64_t delta, pairs, partials, flags, total;  // byte offsets of the parts, total size
+    uint64_t delta, pairs, partials, flags, status, total;  // byte offsets of the parts, total size
 };
 inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
     FracWorkspace w;
@@ -111,9 +132,19 @@ inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
     w.pairs = align256(4ull * bh * n);
     w.partials = w.pairs + align256(8ull * pair_slots(n_off) * bh * n);
     w.flags = w.partials + align256(4ull * tiles * n_off);
-    w.total = w.flags + align256(8ull * tiles);
+    w.status = w.flags + align256(8ull * tiles);
+    w.total = w.status + (tiles > 0 ? 256 : 0);
     return w;
 }
+
+// Polls of a bounded wait before it gives up: with the sleep between polls they span
+// tens of milliseconds, far beyond any real wait (the dQ work of a whole launch takes
+// tens of microseconds).
+constexpr int32_t kMaxPolls = 1 << 18;
+
+// The one-launch backward runs when it has sparse offsets, a token array and B * H a
+// multiple of 8 (every XCD then holds whole heads).
+inline bool one_launch_backward(const AttnParams &p) { return p.flags && p.n_off > 0 && p.bh % 8 == 0; }
 
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);

@@ -31,7 +31,9 @@ EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_wor
            "fsa_frac_offsets", "fsa_frac_forward", "fsa_frac_backward", "fsa_frac_backward_workspace_bytes",
            "fsa_frac_decode",
            "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
-           "fsa_rope_frac_workspace_bytes", "fsa_rope_frac_forward", "fsa_rope_frac_backward", "fsa_last_error")
+           "fsa_rope_frac_workspace_bytes", "fsa_rope_frac_forward", "fsa_rope_frac_backward", "fsa_wait_status",
+           "fsa_debug_force_wait_timeout", "fsa_last_error")
+WS_KINDS = {"backward": 0, "frac_backward": 1, "rope_backward": 2, "rope_frac_backward": 3}
 
 
 class FsaError(RuntimeError):
@@ -115,6 +117,11 @@ def library() -> ctypes.CDLL:
                                                  vp, vp, vp, vp, u64, i32, i32, i32, i32, i32, f32, ctypes.c_int, f64,
                                                  i32, i32, vp]
             L.fsa_rope_frac_backward.restype = ctypes.c_int
+            L.fsa_wait_status.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64, i32, i32,
+                                          vp, u64, ctypes.POINTER(i32), vp]
+            L.fsa_wait_status.restype = ctypes.c_int
+            L.fsa_debug_force_wait_timeout.argtypes = [i32]
+            L.fsa_debug_force_wait_timeout.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
             L.fsa_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -171,12 +178,30 @@ def _out(like, out, out_dtype):
     return out
 
 
+def _rows(like, t, name, shape=None):
+    """Per-row float32 buffer (LSE or D): the caller's tensor, checked, or a new one.
+    shape defaults to like's [B, H, N]."""
+    shape = tuple(like.shape[:3]) if shape is None else tuple(shape)
+    if t is None:
+        return torch.empty(shape, dtype=torch.float32, device=like.device)
+    if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() or t.device != like.device:
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {list(shape)} on the inputs' device")
+    return t
+
+
+def _rows_in(like, t, name):
+    """A per-row float32 input (LSE, or D): must be given, [B, H, N], contiguous, on the inputs' device."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    return _rows(like, t, name)
+
+
 def forward(q, k, v, *, alpha: float = 1.0, w: int, R: int, base: str = "fib", scale=None,
             out=None, lse=None, out_dtype=None):
     """Sparse forward: returns (o [B,H,N,d] in out_dtype (default q.dtype), lse [B,H,N] float32)."""
     B, H, N, d = _shape(q, k, v)
     o = _out(q, out, out_dtype)
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    l = _rows(q, lse, "lse")
     with torch.cuda.device(q.device):
         _check(library().fsa_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
                                      B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
@@ -214,7 +239,8 @@ def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base:
     dq = _out(q, dq, out_dtype)
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
-    ws = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    lse = _rows_in(q, lse, "lse")
+    ws = _rows(q, delta, "delta")
     pw, pw_bytes = _pair_ws(q, pair_ws, alpha, w, R, base)
     with torch.cuda.device(q.device):
         _check(library().fsa_backward(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -227,7 +253,7 @@ def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base:
 def backward_delta(o, dout, *, delta=None):
     """First backward stage: D = rowsum(dout * o), float32 [B, H, N]."""
     B, H, N, d = _shape(o, dout)
-    ws = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if delta is None else delta
+    ws = _rows(o, delta, "delta")
     with torch.cuda.device(o.device):
         _check(library().fsa_backward_delta(DTYPES[o.dtype], _ptr(o), _ptr(dout), _ptr(ws), B, H, N, d,
                                             _stream(o.device)))
@@ -238,6 +264,8 @@ def backward_grads(q, k, v, lse, dout, delta, *, alpha: float = 1.0, w: int, R: 
                    scale=None, dq=None, dk=None, dv=None, pair_ws=None, out_dtype=None):
     """Second backward stage: (dq, dk, dv) from a D computed by backward_delta."""
     B, H, N, d = _shape(q, k, v, dout)
+    lse = _rows_in(q, lse, "lse")
+    delta = _rows_in(q, delta, "delta")
     dq = _out(q, dq, out_dtype)
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
@@ -267,8 +295,8 @@ def decode(q, k_cache, v_cache, seq_lens, *, alpha: float = 1.0, w: int, R: int,
         raise ValueError("q must be a contiguous float32 or bfloat16 device tensor")
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or seq_lens.device != q.device:
         raise ValueError("seq_lens must be an int32 [B] tensor on q's device")
-    o = torch.empty_like(q, dtype=out_dtype or q.dtype) if out is None else out
-    l = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(q, out, out_dtype)
+    l = _rows(q, lse, "lse", (B, H))
     fn = library().fsa_frac_decode if fractional else library().fsa_decode
     with torch.cuda.device(q.device):
         _check(fn(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(o),
@@ -281,7 +309,7 @@ def dense_forward(q, k, v, *, scale=None, out=None, lse=None, out_dtype=None):
     """Dense causal baseline: returns (o, lse)."""
     B, H, N, d = _shape(q, k, v)
     o = _out(q, out, out_dtype)
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    l = _rows(q, lse, "lse")
     with torch.cuda.device(q.device):
         _check(library().fsa_dense_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l),
                                            B, H, N, d, _scale(scale, d), _stream(q.device)))
@@ -310,7 +338,7 @@ def frac_forward(q, k, v, *, alpha: float, w: int, R: int, base: str = "fib", sc
     """Learned-alpha forward (interpolated entries): returns (o, lse) like forward()."""
     B, H, N, d = _shape(q, k, v)
     o = _out(q, out, out_dtype)
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    l = _rows(q, lse, "lse")
     with torch.cuda.device(q.device):
         _check(library().fsa_frac_forward(DTYPES[q.dtype], DTYPES[o.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                           _ptr(l), B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w),
@@ -333,6 +361,7 @@ def frac_backward(q, k, v, o, lse, dout, *, alpha: float, w: int, R: int, base: 
     """Learned-alpha backward: returns (dq, dk, dv, dalpha float32 [1], doffs float32 [entries]).
     ws is the device workspace (allocated here when not given)."""
     B, H, N, d = _shape(q, k, v, o, dout)
+    lse = _rows_in(q, lse, "lse")
     dq = _out(q, dq, out_dtype)
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
@@ -415,7 +444,7 @@ def rope_forward(q, k, v, table, *, alpha: float = 1.0, w: int, R: int, base: st
     reuse_rotated; inference can pass False."""
     B, H, N, d = _shape(q, k, v)
     o = _out(q, out, out_dtype)
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    l = _rows(q, lse, "lse")
     n_pos = _table(table, N)
     ws, ws_bytes = _rope_ws(q, ws, 0, alpha, w, R, base)
     with torch.cuda.device(q.device):
@@ -433,6 +462,7 @@ def rope_backward(q, k, v, table, o, lse, dout, *, alpha: float = 1.0, w: int, R
     if reuse_rotated and ws is None:
         raise ValueError("reuse_rotated needs the forward's workspace")
     B, H, N, d = _shape(q, k, v, o, dout)
+    lse = _rows_in(q, lse, "lse")
     dq = _out(q, dq, out_dtype)
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
@@ -463,7 +493,7 @@ def rope_frac_forward(q, k, v, table, *, alpha: float, w: int, R: int, base: str
     """Learned-alpha forward over rotated Q, K (unrotated inputs): (o, lse)."""
     B, H, N, d = _shape(q, k, v)
     o = _out(q, out, out_dtype)
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    l = _rows(q, lse, "lse")
     n_pos = _table(table, N)
     if ws is None:
         need = rope_frac_workspace_bytes(q.dtype, B, H, N, d, alpha=alpha, w=w, R=R, base=base)[0]
@@ -481,6 +511,7 @@ def rope_frac_backward(q, k, v, table, o, lse, dout, *, alpha: float, w: int, R:
                        reuse_rotated: bool = False):
     """Backward of rope_frac_forward: (dq, dk, dv, dalpha [1], doffs [entries])."""
     B, H, N, d = _shape(q, k, v, o, dout)
+    lse = _rows_in(q, lse, "lse")
     dq = _out(q, dq, out_dtype)
     dk = _out(q, dk, dq.dtype)
     dv = _out(q, dv, dq.dtype)
@@ -501,3 +532,27 @@ def rope_frac_backward(q, k, v, table, o, lse, dout, *, alpha: float, w: int, R:
                                                 _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
                                                 _stream(q.device)))
     return dq, dk, dv, dalpha, doffs[:n_entries]
+
+
+# ----------------------------------------------------------------------------
+# the one-launch backward's bounded waits
+# ----------------------------------------------------------------------------
+
+
+def wait_status(kind: str, q, ws, *, alpha: float = 1.0, w: int, R: int, base: str = "fib") -> bool:
+    """True if the last one-launch backward of `kind` ("backward", "frac_backward",
+    "rope_backward", "rope_frac_backward") that ran with workspace `ws` on q's shape gave
+    up one of its bounded waits (it then stored NaN gradients). Synchronises the current
+    stream (see fsa_wait_status)."""
+    B, H, N, d = q.shape
+    out = ctypes.c_int32(0)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    with torch.cuda.device(q.device):
+        _check(library().fsa_wait_status(WS_KINDS[kind], DTYPES[q.dtype], B, H, N, d, BASES[base], float(alpha),
+                                         int(w), int(R), _ptr(ws), nbytes, ctypes.byref(out), _stream(q.device)))
+    return bool(out.value)
+
+
+def debug_force_wait_timeout(enable: bool) -> None:
+    """Diagnostic hook: makes later one-launch backward waits give up (see fsa_debug_force_wait_timeout)."""
+    _check(library().fsa_debug_force_wait_timeout(int(bool(enable))))

@@ -139,19 +139,22 @@ fsa_status_t fsa_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, con
 /*
  * fsa_backward_workspace_bytes - bytes of pair workspace the backward needs.
  *
- * On the bf16 window path (dt = FSA_BF16, w <= 64, N <= 2^24, and 4 * S * N < 2^31
- * with S below) the gradient stage has two parts: the dQ part stores, for every
- * query row i and sparse offset o of the table (offsets >= N dropped), the bf16
- * values of P and dS of the pair (i, i - o) in one 32-bit word; the dK/dV part
- * reads them. When B * H is a
- * multiple of 8 both parts run in one launch: each 64-row tile's dQ part then
- * publishes a 64-bit token naming the launch (from the hardware dispatch id), and
- * the dK/dV parts wait for the tokens of the tiles they read (a bounded wait; if
- * it ever gave up, that tile's dK and dV would be NaN). Otherwise they run as two
- * kernels. The size is 4 * S * B * H * N bytes of pair words, S = |T| rounded up
- * to a multiple of 8 (words per query row), rounded up to a multiple of 256, plus
- * 8 * B * H * ceil(N / 64) bytes of tokens; 0 on every other path or when no
- * offset is below N. Arguments as in fsa_backward; *bytes receives the size.
+ * On the bf16 window path (dt = FSA_BF16, w <= 64, N <= 2^24, and 4 * S * W * N < 2^31
+ * with S and W below) the gradient stage has two parts: the dQ part stores, for every
+ * query row i and sparse offset o of the table (offsets >= N dropped), P and dS of the
+ * pair (i, i - o); the dK/dV part reads them. A pair takes W 32-bit words: W = 1 (two
+ * bf16) when w >= 64, W = 2 (two fp32) for narrower windows, where a query's few keys
+ * can each carry most of its probability and one bf16 rounding of such a weight would
+ * weigh on the gradients. When B * H is a multiple of 8 both parts run in one launch:
+ * each 64-row tile's dQ part then publishes a 64-bit token naming the launch (from the
+ * hardware dispatch id), and the dK/dV parts wait for the tokens of the tiles they read.
+ * That wait is bounded: if it ever gave up, the tile's dK and dV would be NaN and a
+ * status word in the workspace would name the launch (fsa_wait_status reads it).
+ * Otherwise the parts run as two kernels. The size is 4 * S * W * B * H * N bytes of pair
+ * words, S = |T| rounded up to a multiple of 8 (slots per query row), rounded up to a
+ * multiple of 256, plus 8 * B * H * ceil(N / 64) bytes of tokens and 8 bytes of status;
+ * 0 on every other path or when no offset is below N. Arguments as in fsa_backward;
+ * *bytes receives the size.
  */
 fsa_status_t fsa_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                                           fsa_base_t base, double alpha, int32_t w, int32_t R,
@@ -303,8 +306,9 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
  * fsa_frac_backward_workspace_bytes - bytes of ws fsa_frac_backward needs:
  * 4 B H N (D) + 8 S B H N (two words per pair, S = number of entries some row
  * reaches, rounded up to a multiple of 8) + 4 B H ceil(N/64) S' (partials, S' the
- * unrounded count) + 8 B H ceil(N/64) (tokens), each part rounded up to 256 bytes. Arguments as in
- * fsa_frac_backward; *bytes receives the size.
+ * unrounded count) + 8 B H ceil(N/64) (tokens) + 8 (status word, see fsa_wait_status),
+ * each part rounded up to 256 bytes. Arguments as in fsa_frac_backward; *bytes receives
+ * the size.
  */
 fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                                                fsa_base_t base, double alpha, int32_t w, int32_t R,
@@ -382,7 +386,8 @@ fsa_status_t fsa_rope_rotate(fsa_dtype_t dt, const void *x, const float *rope, i
 /*
  * fsa_rope_workspace_bytes - bytes of ws the rotary forward and backward need:
  * forward 2 B H N d * 2 (the rotated Q and K, each part rounded up to 256 bytes);
- * backward that plus 4 B H N (D) plus fsa_backward_workspace_bytes (pair words and tokens).
+ * backward that plus 4 B H N (D) plus fsa_backward_workspace_bytes for the same window
+ * (pair words, tokens and status word).
  * Arguments as in fsa_rope_forward; 0 and 0 for an empty problem.
  */
 fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d, fsa_base_t base,
@@ -460,6 +465,50 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
                                     void *ws, uint64_t ws_bytes, int32_t reuse_rotated, int32_t B, int32_t H,
                                     int32_t N, int32_t d, float scale, fsa_base_t base, double alpha, int32_t w,
                                     int32_t R, void *stream);
+
+/*
+ * fsa_wait_status - whether the last one-launch backward that ran with a workspace
+ * gave up one of its bounded waits.
+ *
+ * The one-launch backward (B * H a multiple of 8, sparse offsets below N) is correct
+ * only if the GPU dispatches its workgroups in block order and places block b on XCD
+ * b mod 8; its dK/dV workgroups then never wait for a workgroup that has not started.
+ * Each wait is bounded nonetheless: a workgroup that gives up stores NaN dK and dV
+ * (and the learned-alpha reduction NaN dalpha) instead of hanging, and writes the
+ * launch's token into the workspace's status word. This call reads that word and the
+ * token of the workspace's most recent launch (published by its first tile, whose
+ * work never waits) and reports whether they match. It synchronises `stream` and
+ * copies 16 bytes to the host (the one call of the library that waits). Call it after
+ * the backward, with the same arguments, before the workspace is reused.
+ *
+ *   kind        which call's workspace: FSA_WS_BACKWARD (fsa_backward,
+ *               fsa_backward_grads: pair_ws), FSA_WS_FRAC_BACKWARD (fsa_frac_backward:
+ *               ws), FSA_WS_ROPE_BACKWARD (fsa_rope_backward: ws),
+ *               FSA_WS_ROPE_FRAC_BACKWARD (fsa_rope_frac_backward: ws)
+ *   dt, B, H, N, d, base, alpha, w, R   the arguments the backward ran with
+ *   ws, ws_bytes   that workspace and its size
+ *   gave_up     receives 1 if a wait of that launch gave up, else 0 (also 0 when the
+ *               problem does not take the one-launch path)
+ *   stream      the stream the backward ran on
+ */
+typedef enum {
+    FSA_WS_BACKWARD = 0,
+    FSA_WS_FRAC_BACKWARD = 1,
+    FSA_WS_ROPE_BACKWARD = 2,
+    FSA_WS_ROPE_FRAC_BACKWARD = 3
+} fsa_ws_kind_t;
+fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
+                             fsa_base_t base, double alpha, int32_t w, int32_t R, const void *ws,
+                             uint64_t ws_bytes, int32_t *gave_up, void *stream);
+
+/*
+ * fsa_debug_force_wait_timeout - diagnostic hook for tests of the failure path (not
+ * part of the method). With enable != 0, later one-launch backward calls of this
+ * process wait for a value no workgroup publishes and give up after 16 polls, so every
+ * kernel still exits and fsa_wait_status then reports the give-up; enable = 0 restores
+ * normal waits. Process-wide; returns FSA_OK.
+ */
+fsa_status_t fsa_debug_force_wait_timeout(int32_t enable);
 
 /* Text describing the calling thread's last non-OK status ("" if none). */
 const char *fsa_last_error(void);

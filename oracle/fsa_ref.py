@@ -631,10 +631,10 @@ def frac_backward_rows(q, k, v, dout, entries, w, scale, rows):
 #   * values are not rotated; the backward returns gradients with respect to the
 #     unrotated Q and K.
 # The rotated rows are handed to the attention in the input's storage type, as a
-# separate rotation step would store them (rope_store_bf16): that rounding is a
-# decision of the method's data path, so the oracle takes it in the same precision
-# as the library (an fp32 table of cos/sin, two fp32 operations per channel, round
-# to nearest even).
+# separate rotation step would store them (rope_store_bf16): the exact rotation
+# (fp64 cos and sin of the fp64 angle) rounded once to bfloat16, nearest with ties to
+# even. A library that computes the rotation in fp32 before that rounding may land
+# one bf16 step away from it where the exact value sits next to a rounding boundary.
 
 
 def rope_angles(n_pos: int, d: int, base: float = 10000.0):
@@ -673,40 +673,36 @@ def rope_table_f32(n_pos: int, d: int, base: float = 10000.0):
     return out
 
 
-def rope_store_bf16(x, base: float = 10000.0, table=None):
-    """Rotated rows of x [..., N, d] as a rotation step that stores bf16 produces them:
-    with c, s the float32 table entries, channel 2m becomes fl(c x_2m - fl(s x_2m+1))
-    and channel 2m + 1 becomes fl(s x_2m + fl(c x_2m+1)) (fl = float32 rounding), then
-    each value is rounded to bfloat16 (nearest, ties to even; torch's conversion).
-    Every product of a float32 and a bf16 value and every difference here is exact in
-    fp64 before its single rounding, so fp64 arithmetic with explicit float32 casts
-    reproduces the float32 steps. Returns the bf16 values as float64."""
-    import torch
-
+def bf16_round(x):
+    """Rounds float64 values to the nearest bfloat16 value (8 significant bits, fp32's
+    exponent range), ties to even, in one step from the fp64 value (no intermediate
+    float32). Returns float64. Written out: x = m * 2^e with 1/2 <= |m| < 1, so
+    m * 2^8 holds the 8 kept bits in its integer part; numpy's rint rounds that to
+    nearest, ties to even, exactly in fp64. Below 2^-126 (bf16 subnormals) the quantum
+    is fixed at 2^-133."""
     x = np.asarray(x, dtype=np.float64)
-    N, d = x.shape[-2], x.shape[-1]
-    tab = rope_table_f32(N, d, base) if table is None else table[:N]
-    c = tab[..., 0].astype(np.float64)
-    s = tab[..., 1].astype(np.float64)
-    xe, xo = x[..., 0::2], x[..., 1::2]
-    f32 = lambda a: np.asarray(a, dtype=np.float32).astype(np.float64)
-    re = f32(c * xe - f32(s * xo))
-    ro = f32(s * xe + f32(c * xo))
-    out = np.empty_like(x)
-    out[..., 0::2] = re
-    out[..., 1::2] = ro
-    return torch.from_numpy(out.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    m, e = np.frexp(x)
+    normal = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    sub = np.ldexp(np.rint(np.ldexp(x, 133)), -133)
+    return np.where(np.abs(x) < 2.0 ** -126, sub, normal)
 
 
-def rope_sparse_forward(q, k, v, T, w, scale, base: float = 10000.0, stored: bool = False, table=None):
+def rope_store_bf16(x, base: float = 10000.0):
+    """Rotated rows of x [..., N, d] as a rotation step that stores bf16 hands them to the
+    attention: the exact fp64 rotation (rope_rotate) rounded once to bfloat16
+    (bf16_round). Returns the bf16 values as float64."""
+    return bf16_round(rope_rotate(x, base))
+
+
+def rope_sparse_forward(q, k, v, T, w, scale, base: float = 10000.0, stored: bool = False):
     """sparse_forward on rotated queries and keys (rounded to bf16 as stored when
     `stored`, exact otherwise)."""
     if stored:
-        return sparse_forward(rope_store_bf16(q, base, table), rope_store_bf16(k, base, table), v, T, w, scale)
+        return sparse_forward(rope_store_bf16(q, base), rope_store_bf16(k, base), v, T, w, scale)
     return sparse_forward(rope_rotate(q, base), rope_rotate(k, base), v, T, w, scale)
 
 
-def rope_sparse_backward(q, k, v, dout, T, w, scale, base: float = 10000.0, stored: bool = False, table=None,
+def rope_sparse_backward(q, k, v, dout, T, w, scale, base: float = 10000.0, stored: bool = False,
                          o=None, lse=None):
     """Gradients of sum(dout * o) of rope_sparse_forward with respect to the unrotated
     q, k and v: the rotated-input gradients carried back through the transposed
@@ -715,7 +711,7 @@ def rope_sparse_backward(q, k, v, dout, T, w, scale, base: float = 10000.0, stor
     o and lse, when given, are the forward outputs handed to the backward (see
     sparse_backward)."""
     if stored:
-        qr, kr = rope_store_bf16(q, base, table), rope_store_bf16(k, base, table)
+        qr, kr = rope_store_bf16(q, base), rope_store_bf16(k, base)
     else:
         qr, kr = rope_rotate(q, base), rope_rotate(k, base)
     dq, dk, dv = sparse_backward(qr, kr, v, dout, T, w, scale, o=o, lse=lse)
@@ -731,38 +727,36 @@ def _rotate_rows_back(x, rows, N, d, base):
     return out
 
 
-def rope_sparse_forward_rows(q, k, v, T, w, scale, rows, base: float = 10000.0, stored: bool = False,
-                             table=None):
+def rope_sparse_forward_rows(q, k, v, T, w, scale, rows, base: float = 10000.0, stored: bool = False):
     """Rows of rope_sparse_forward."""
-    rot = (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
+    rot = _rope_rot(base, stored)
     return sparse_forward_rows(rot(q), rot(k), v, T, w, scale, rows)
 
 
-def rope_sparse_backward_rows(q, k, v, dout, T, w, scale, rows, base: float = 10000.0, stored: bool = False,
-                              table=None):
+def rope_sparse_backward_rows(q, k, v, dout, T, w, scale, rows, base: float = 10000.0, stored: bool = False):
     """Rows of rope_sparse_backward."""
     N, d = np.asarray(q).shape[-2], np.asarray(q).shape[-1]
-    rot = (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
+    rot = _rope_rot(base, stored)
     dq, dk, dv = sparse_backward_rows(rot(q), rot(k), v, dout, T, w, scale, rows)
     return _rotate_rows_back(dq, rows, N, d, base), _rotate_rows_back(dk, rows, N, d, base), dv
 
 
-def _rope_rot(base, stored, table):
-    return (lambda x: rope_store_bf16(x, base, table)) if stored else (lambda x: rope_rotate(x, base))
+def _rope_rot(base, stored):
+    return (lambda x: rope_store_bf16(x, base)) if stored else (lambda x: rope_rotate(x, base))
 
 
-def rope_frac_forward(q, k, v, entries, w, scale, base: float = 10000.0, stored: bool = False, table=None):
+def rope_frac_forward(q, k, v, entries, w, scale, base: float = 10000.0, stored: bool = False):
     """The learned-alpha variant as the pages run it: queries and keys rotated first
     ([EXPL-pt] Metodologia / Arquitetura, item "Implementação"), then frac_forward, so
     each entry interpolates rotated key rows (values are not rotated)."""
-    rot = _rope_rot(base, stored, table)
+    rot = _rope_rot(base, stored)
     return frac_forward(rot(q), rot(k), v, entries, w, scale)
 
 
-def rope_frac_backward(q, k, v, dout, entries, w, scale, base: float = 10000.0, stored: bool = False, table=None,
+def rope_frac_backward(q, k, v, dout, entries, w, scale, base: float = 10000.0, stored: bool = False,
                        o=None, lse=None):
     """Gradients of rope_frac_forward: frac_backward on the rotated rows, dq and dk
     rotated back (the transpose), dv and the per-entry derivative unchanged."""
-    rot = _rope_rot(base, stored, table)
+    rot = _rope_rot(base, stored)
     dq, dk, dv, dd = frac_backward(rot(q), rot(k), v, dout, entries, w, scale, o=o, lse=lse)
     return rope_rotate(dq, base, inverse=True), rope_rotate(dk, base, inverse=True), dv, dd

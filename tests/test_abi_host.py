@@ -212,19 +212,22 @@ def a256(x):
 
 
 def pair_ws(words, bh, n):
-    # the pair words, then (256-byte aligned) one 64-bit completion token per 64-row tile
-    return a256(4 * words) + 8 * bh * ((n + 63) // 64)
+    # the pair words, then (256-byte aligned) one 64-bit completion token per 64-row tile,
+    # then the 8-byte status word
+    return a256(4 * words) + 8 * bh * ((n + 63) // 64) + 8
 
 
 def test_backward_workspace_size(lib):
     # bf16, window 64: one 32-bit word per (head, row, offset slot), slots rounded up to
     # a multiple of 8; alpha = 1, R = 1024 gives the offsets 89, 144, 233, 377, 610, 987
     assert ws_bytes(lib) == (fsa.FSA_OK, pair_ws(8 * 16 * 4096, 16, 4096))
-    assert pair_ws(8 * 16 * 4096, 16, 4096) == 4 * 8 * 16 * 4096 + 8 * 16 * 64
+    assert pair_ws(8 * 16 * 4096, 16, 4096) == 4 * 8 * 16 * 4096 + 8 * 16 * 64 + 8
     # offsets >= N are dropped: at N = 600 only 89, 144, 233, 377 remain (still 8 slots)
     assert ws_bytes(lib, N=600) == (fsa.FSA_OK, pair_ws(8 * 16 * 600, 16, 600))
-    # a table of 9 offsets takes 16 slots: w = 1, alpha = 1, R = 60 gives 1, 2, 3, 5, 8, 13, 21, 34, 55
-    assert ws_bytes(lib, w=1, R=60) == (fsa.FSA_OK, pair_ws(16 * 16 * 4096, 16, 4096))
+    # narrower windows carry each pair as two fp32 words: a table of 9 offsets takes 16
+    # slots (w = 1, alpha = 1, R = 60 gives 1, 2, 3, 5, 8, 13, 21, 34, 55)
+    assert ws_bytes(lib, w=1, R=60) == (fsa.FSA_OK, pair_ws(2 * 16 * 16 * 4096, 16, 4096))
+    assert ws_bytes(lib, w=63) == (fsa.FSA_OK, pair_ws(2 * 8 * 16 * 4096, 16, 4096))
     # an odd row count (offset 89 only): the token area starts 256-byte aligned
     assert ws_bytes(lib, B=1, H=3, N=101) == (fsa.FSA_OK, pair_ws(8 * 3 * 101, 3, 101))
     # no offset below N: no slots
@@ -239,22 +242,25 @@ def test_backward_workspace_size(lib):
 
 
 def test_backward_pair_words_need_32_bit_offsets(lib):
-    # w = 1, R = 2^30: the Fibonacci numbers below N are all offsets. At N = 2^23 there are
-    # 33 (40 slots, 160 bytes per row: 1.3 GB per head, within 32-bit offsets); at N = 2^24,
-    # 35 (40 slots: 2.7 GB per head), so the backward takes the general kernels, which need
-    # no pair words
-    n23 = 1 << 23
-    assert ws_bytes(lib, B=1, H=1, N=n23, w=1, R=1 << 30) == (fsa.FSA_OK, pair_ws(40 * n23, 1, n23))
-    assert ws_bytes(lib, B=1, H=1, N=1 << 24, w=1, R=1 << 30) == (fsa.FSA_OK, 0)
+    # w = 1, R = 2^30: the Fibonacci numbers below N are all offsets, each pair two words.
+    # At N = 2^22 there are 31 (32 slots, 256 bytes per row: 1 GiB per head, within
+    # 32-bit offsets); at N = 2^23, 33 (40 slots: 2.7 GB per head), so the backward takes
+    # the general kernels, which need no pair words
+    n22 = 1 << 22
+    assert ws_bytes(lib, B=1, H=1, N=n22, w=1, R=1 << 30) == (fsa.FSA_OK, pair_ws(2 * 32 * n22, 1, n22))
+    assert ws_bytes(lib, B=1, H=1, N=1 << 23, w=1, R=1 << 30) == (fsa.FSA_OK, 0)
+    # with w = 64 (one word per pair) 2^24 rows of 8 slots still fit
+    n24 = 1 << 24
+    assert ws_bytes(lib, B=1, H=1, N=n24, w=64, R=1 << 16) == (fsa.FSA_OK, pair_ws(16 * n24, 1, n24))
 
 
 @pytest.mark.parametrize("call", [bwd, grads])
 def test_backward_pair_workspace_checks(lib, call):
-    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 8 slots * 64 rows,
-    # then one token for the single tile. Only failing validations are exercised here
-    # (the pointers are fake); the calls that pass NULL for an unneeded workspace run in
-    # the GPU tests (fp32 inputs).
-    need = pair_ws(8 * 64, 1, 64)
+    # bf16, w = 16, N = 64, alpha = 1, R = 256: offsets 21, 34, 55 -> 8 slots of two words
+    # * 64 rows, then one token for the single tile and the status word. Only failing
+    # validations are exercised here (the pointers are fake); the calls that pass NULL for
+    # an unneeded workspace run in the GPU tests (fp32 inputs).
+    need = pair_ws(2 * 8 * 64, 1, 64)
     assert call(lib, pair_bytes=need - 1) == fsa.FSA_E_ARG
     assert b"pair_ws holds" in lib.fsa_last_error()
     assert call(lib, pair_bytes=0) == fsa.FSA_E_ARG
@@ -294,3 +300,35 @@ def test_literal_stagger_tables(lib):
     tabs = [build(lib, "fib", a, 64, 1024)[1] for a in al]
     assert tabs == [oracle.offset_table("fib", a, 64, 1024) for a in al]
     assert [len(t) for t in tabs][-2:] == [8, 8] and max(max(t) for t in tabs) == 1974
+
+
+# ---- the wait-status call: argument checks and the paths without waits (no HIP call) ----
+
+def wait_status(lib, kind=0, dt=1, B=2, H=4, N=300, d=64, base=0, alpha=1.0, w=64, R=1024, ws=None,
+                ws_bytes=1 << 40, flag=True):
+    out = ctypes.c_int32(7)
+    st = lib.fsa_wait_status(kind, dt, B, H, N, d, base, alpha, w, R, ws if ws is not None else FAKE[0], ws_bytes,
+                             ctypes.byref(out) if flag else None, None)
+    return st, out.value
+
+
+def test_wait_status_checks(lib):
+    assert wait_status(lib, flag=False)[0] == fsa.FSA_E_ARG
+    assert wait_status(lib, kind=9)[0] == fsa.FSA_E_ARG
+    assert wait_status(lib, d=32)[0] == fsa.FSA_E_UNSUPPORTED
+    assert wait_status(lib, alpha=0.0)[0] == fsa.FSA_E_ARG
+    # one-launch shapes (B * H a multiple of 8) check the workspace before reading it
+    assert wait_status(lib, ws=P(0))[0] == fsa.FSA_E_ARG
+    assert wait_status(lib, ws_bytes=16)[0] == fsa.FSA_E_ARG and b"ws holds" in lib.fsa_last_error()
+    # shapes that run without waits report 0 and read nothing
+    assert wait_status(lib, B=1, H=3, ws=P(0)) == (fsa.FSA_OK, 0)        # two kernels
+    assert wait_status(lib, N=50, ws=P(0)) == (fsa.FSA_OK, 0)            # no offset below N
+    assert wait_status(lib, dt=0, ws=P(0)) == (fsa.FSA_OK, 0)            # fp32: general kernel
+    assert wait_status(lib, kind=1, B=1, H=3, alpha=1.3, ws=P(0)) == (fsa.FSA_OK, 0)
+    assert wait_status(lib, kind=2, B=1, H=3, ws=P(0)) == (fsa.FSA_OK, 0)
+    assert wait_status(lib, kind=3, B=1, H=3, alpha=1.3, ws=P(0)) == (fsa.FSA_OK, 0)
+
+
+def test_debug_force_wait_timeout_toggles(lib):
+    assert lib.fsa_debug_force_wait_timeout(1) == fsa.FSA_OK
+    assert lib.fsa_debug_force_wait_timeout(0) == fsa.FSA_OK

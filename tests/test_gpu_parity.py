@@ -495,3 +495,71 @@ def test_literal_stagger_formula_layers(layer):
     b, h = int(rng.integers(0, 2)), int(rng.integers(0, 8))
     fwd_case(7, 2, 8, 4096, torch.bfloat16, "fib", a, 64, 1024, heads=[(b, h)], layer=layer)
     bwd_case(7, 2, 8, 4096, torch.bfloat16, "fib", a, 64, 1024, heads=[(b, h)], layer=layer)
+
+
+def test_pow2_reach_at_evaluation_length():
+    # the power-of-2 control with its reach at the evaluation length (R = N = 4096): the
+    # table gains 1024 and 2048, the large offsets that control brought in at 4x length
+    T = oracle.offset_table("pow2", 1.0, 64, 4096)
+    assert T == [64, 128, 256, 512, 1024, 2048] and fsa.build_offsets(1.0, 64, 4096, "pow2") == T
+    fwd_case(35, 2, 8, 4096, torch.bfloat16, "pow2", 1.0, 64, 4096, heads=[(0, 2), (1, 7)])
+    bwd_case(35, 2, 8, 4096, torch.bfloat16, "pow2", 1.0, 64, 4096, heads=[(1, 5)])
+
+
+@pytest.mark.parametrize("layer", [0, 9, 15])
+def test_workload4_edge_tiles_of_every_head(layer):
+    # the first and last 64-row tiles of all 16 heads of a training-step layer (the
+    # sequence start and end, where masks and buffer ranges cut the tiles), row by row
+    alpha = schedules.linear_stagger(16)[layer]
+    x = inputs(4, layer, (2, 8, 4096, 64), torch.bfloat16, grad=True)
+    kw = dict(alpha=alpha, w=64, R=1024, scale=0.125)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    o32, _ = fsa.forward(x["q"], x["k"], x["v"], out_dtype=torch.float32, **kw)
+    g = fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    T = oracle.offset_table("fib", alpha, 64, 1024)
+    rows = np.concatenate([np.arange(0, 64), np.arange(4096 - 64, 4096)])
+    note(f"edge tiles of every head, layer {layer} alpha={alpha:.4f}")
+    worst = 0.0
+    for b in range(2):
+        for h in range(8):
+            q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
+            ro, rl = oracle.sparse_forward_rows(q, k, v, T, 64, 0.125, rows)
+            rq, rk, rv = oracle.sparse_backward_rows(q, k, v, do, T, 64, 0.125, rows)
+            for name, got, want in (("o", o32[b, h][rows], ro), ("lse", lse[b, h][rows], rl),
+                                    ("dq", g[0][b, h][rows], rq), ("dk", g[1][b, h][rows], rk),
+                                    ("dv", g[2][b, h][rows], rv)):
+                err = maxabs(got, want)
+                worst = max(worst, err)
+                assert err <= 1e-2, (b, h, name, err)
+    note(f"  worst max|err| over all heads' edge tiles: {worst:.3e}")
+
+
+def test_binding_rejects_bad_row_buffers():
+    # LSE and D are float32 [B, H, N] on the inputs' device, contiguous; anything else is
+    # refused before any kernel runs
+    x = inputs(36, 0, (1, 2, 100, 64), torch.bfloat16, grad=True)
+    kw = dict(alpha=1.0, w=64, R=1024)
+    o, lse = fsa.forward(x["q"], x["k"], x["v"], **kw)
+    bad = [lse[:, :1], lse.to(torch.bfloat16), lse.cpu(), torch.empty(1, 100, 2, device=dev()).transpose(1, 2),
+           torch.empty(2, 100, device=dev())]
+    for b in bad:
+        with pytest.raises(ValueError):
+            fsa.forward(x["q"], x["k"], x["v"], lse=b, **kw)
+        with pytest.raises(ValueError):
+            fsa.backward(x["q"], x["k"], x["v"], o, b, x["do"], **kw)
+        with pytest.raises(ValueError):
+            fsa.backward(x["q"], x["k"], x["v"], o, lse, x["do"], delta=b, **kw)
+        with pytest.raises(ValueError):
+            fsa.backward_grads(x["q"], x["k"], x["v"], b, x["do"], lse, **kw)
+        with pytest.raises(ValueError):
+            fsa.frac_backward(x["q"], x["k"], x["v"], o, b, x["do"], **kw)
+    with pytest.raises(ValueError):
+        fsa.backward(x["q"], x["k"], x["v"], o, None, x["do"], **kw)
+    # decode: LSE is [B, H]
+    q1 = x["q"][:, :, -1].contiguous()
+    sl = torch.full((1,), 100, dtype=torch.int32, device=dev())
+    with pytest.raises(ValueError):
+        fsa.decode(q1, x["k"], x["v"], sl, lse=torch.empty((1, 2, 1), device=dev()), **kw)
+    with pytest.raises(ValueError):
+        fsa.decode(q1, x["k"], x["v"], sl, out=torch.empty((1, 2, 32), device=dev(), dtype=torch.bfloat16), **kw)

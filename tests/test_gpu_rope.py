@@ -1,9 +1,12 @@
 """GPU parity of the rotary path (Q and K rotated before the attention) through the
 C ABI, against the fp64 oracle.
 
-Bars: the rotation step bit-exact (it is a rounding to bf16 that both sides take
-in the same float32 steps from the same table); O, LSE, dQ, dK, dV within max-abs
-1e-2 of the oracle's attention over the same stored rotated rows, with gradients
+The oracle's rotated rows are the exact rotation (fp64 cos and sin) rounded once to
+bf16. The library computes the rotation in fp32 from an fp32 table before rounding
+to bf16, so a stored value may sit one bf16 step from the oracle's where the exact
+value lies next to a rounding boundary: the rotation step is checked to within one
+bf16 step, with the count of differing values reported. O, LSE, dQ, dK, dV are checked
+within max-abs 1e-2 of the oracle's attention over its rotated rows, with gradients
 carried back to the unrotated rows.
 
 The backward is a function of (q, k, v, o, lse, dO). The exhaustive small cases
@@ -50,17 +53,34 @@ def check(name, gpu, ref, tol=TOL):
     assert err <= tol, (name, err)
 
 
+def bf16_step(x):
+    """Spacing of the bf16 grid at |x| (the step up from |x|): 2^(e - 8) for |x| = m 2^e,
+    1/2 <= m < 1; 2^-133 among the subnormals."""
+    _, e = np.frexp(np.abs(x))
+    return np.where(np.abs(x) < 2.0 ** -126, 2.0 ** -133, np.ldexp(1.0, e - 8))
+
+
 @pytest.mark.parametrize("B,H,N,n_pos", [(1, 1, 1, 1), (2, 3, 77, 100), (1, 2, 4096, 4096), (2, 1, 1000, 5000)])
-def test_rotation_bit_exact(B, H, N, n_pos):
+def test_rotation_within_one_bf16_step(B, H, N, n_pos):
     x = inputs(60, 0, (B, H, N, 64))["q"]
     table = fsa.rope_table(n_pos, device=dev())
     y = fsa.rope_rotate(x, table)
     torch.cuda.synchronize()
-    want = oracle.rope_store_bf16(synth.as_f64(x), table=oracle.rope_table_f32(n_pos, 64))
+    want = oracle.rope_store_bf16(synth.as_f64(x))
     got = synth.as_f64(y)
-    bad = int(np.sum(got != want))
-    note(f"rotation B={B} H={H} N={N}: {bad} of {got.size} values differ")
-    assert bad == 0
+    diff = np.abs(got - want)
+    bad = int(np.sum(diff != 0))
+    note(f"rotation B={B} H={H} N={N}: {bad} of {got.size} values differ from the exact rounding "
+         f"(max difference {float(diff.max()) if diff.size else 0:.3e})")
+    # one step of the grid on either side of the oracle's value (the step below a power of
+    # two is half the step above, so the larger one bounds both), plus the fp32 steps'
+    # own error where the pair's two terms cancel: the table's rounding and the two fp32
+    # roundings stay below 2^-22 (|x_2m| + |x_2m+1|)
+    xf = synth.as_f64(x)
+    floor = 2.0 ** -21 * np.repeat(np.abs(xf[..., 0::2]) + np.abs(xf[..., 1::2]), 2, axis=-1)
+    assert np.all(diff <= np.maximum(bf16_step(want), bf16_step(got)) + floor)
+    # a wrong table or formula would move most values, not a few near rounding ties
+    assert bad <= max(8, got.size // 1000)
 
 
 def rope_fwd_case(workload, B, H, N, base, alpha, w, R, heads=None, layer=0, scale=0.125, n_pos=None):

@@ -38,6 +38,7 @@ def note(msg):
 
 def check(name, gpu, ref, tol):
     err = float(np.max(np.abs(synth.as_f64(gpu) - ref))) if ref.size else 0.0
+    note(f"  {name}: max|err|={err:.3e} tol={tol}")
     assert err <= tol, (name, err, tol)
     return err
 
@@ -74,8 +75,30 @@ ONE_LAUNCH = [(s, torch.bfloat16) for s in range(40, 52)]
 @pytest.mark.parametrize("seed,dtype", STATIC + ONE_LAUNCH,
                          ids=[f"{s}-{'f32' if d == torch.float32 else 'bf16'}" for s, d in STATIC + ONE_LAUNCH])
 def test_sweep_static(seed, dtype):
-    B, H, N, w, alpha, R, base = draw(100 + seed, wide_windows=seed < 40, heads8=seed >= 40)
-    note(f"static {dtype} B={B} H={H} N={N} w={w} alpha={alpha:.4f} R={R} base={base}")
+    static_case(seed, dtype, wide_windows=seed < 40, heads8=seed >= 40)
+
+
+# Narrow windows (w <= 5) drawn the same way, where a query's one to five keys each carry
+# a large share of its probability. On these draws a single bf16 rounding of each sparse
+# pair's P and dS moves some gradient by 1.0e-2 to 1.4e-2 (a CPU search over seeds 0-4499
+# with that one rounding put into the oracle's backward); the window backward carries
+# those weights as fp32 words for windows below 64, and these cases pin it. heads8 draws
+# B * H = 8 (one-launch backward), the others the two-kernel backward.
+SMALL_WINDOW = [(1332, True), (3675, True), (2437, True), (3120, True), (2477, True), (2591, True),
+                (1864, True), (547, True), (2723, True), (2834, True), (4180, True), (419, True),
+                (1332, False), (737, False), (885, False), (1864, False)]
+
+
+@pytest.mark.parametrize("seed,heads8", SMALL_WINDOW, ids=[f"{s}-{'one' if h else 'two'}" for s, h in SMALL_WINDOW])
+def test_small_window_backward(seed, heads8):
+    B, H, N, w, alpha, R, base = draw(100 + seed, wide_windows=False, heads8=heads8)
+    assert w <= 5 and (B * H == 8) == heads8
+    static_case(seed, torch.bfloat16, wide_windows=False, heads8=heads8)
+
+
+def static_case(seed, dtype, wide_windows, heads8):
+    B, H, N, w, alpha, R, base = draw(100 + seed, wide_windows=wide_windows, heads8=heads8)
+    note(f"static {dtype} seed={seed} B={B} H={H} N={N} w={w} alpha={alpha:.4f} R={R} base={base}")
     x = {k: v.to(dev()) for k, v in synth.layer_inputs(80 + seed, 0, (B, H, N, 64), dtype, with_grad=True).items()}
     kw = dict(alpha=alpha, w=w, R=R, base=base, scale=0.125)
     T = oracle.offset_table(base, alpha, w, R)
