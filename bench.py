@@ -7,11 +7,15 @@ with the static linear stagger alpha_l = 0.5 + l/15 (Fibonacci base, window
 w = 64, reach R = 1024; tables built at R = 1024 and used unchanged at 4096).
 Inputs are seeded N(0, 1) synthetic tensors resident in HBM before timing.
 
-One step = the 16 layers' fsa_forward and fsa_backward (the whole backward: D,
-dQ and the pair weights, dK and dV), launched as one HIP graph. Prints one JSON line:
-query-heads/s (value), algorithmic HBM GB/s of the step, a roofline entry for
-the dominant kernel, the dense causal baseline, and the fp64 CPU oracle timed
-on a bounded sample of the same workload.
+One step = a training step's attention work: the 16 layers' fsa_forward in layer
+order, then their fsa_backward (the whole backward: D, dQ and the pair weights, dK
+and dV) in reverse layer order, launched as one HIP graph. Prints one JSON line:
+query-heads/s (value), algorithmic HBM GB/s of the step, a roofline entry for the
+dominant kernel, the step in per-layer order (forward then backward of each layer)
+and after writing 1 GiB of scratch (cold caches), the forward at the training length
+N = 1024 (one layer of bf16 [8,8,1024,64], and the 16-layer stagger), the dense
+causal baseline, and the fp64 CPU oracle timed on a bounded sample of the same
+workload.
 
 The learned-alpha variant (fractional targets, interpolated K/V rows) and the
 rotary-embedding variant (unrotated Q, K in) are timed on the same layers next to
@@ -19,7 +23,7 @@ the static path.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--no-literal] [--no-long]
-                       [--cold] [--copy-probe]
+                       [--no-cold] [--no-short] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -39,6 +43,9 @@ METRIC = "sparse-attn fwd+bwd query-heads/s and achieved HBM GB/s at N=1024/4096
 B, H, N, D, LAYERS, W, R, BASE = 2, 8, 4096, 64, 16, 64, 1024, "fib"
 WORKLOAD_ID = 4
 HBM_PEAK_GBS = 8000.0
+# worker processes of the CPU baseline: the host's CPU share per GPU on the measurement
+# boxes (16 cores for one GPU), whatever the process can see
+HOST_CPU_SHARE = 16
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 ELEM = 2  # bf16 bytes
 
@@ -109,7 +116,8 @@ def cpu_baseline(cpu_inputs, alphas, heads_per_core=8):
 
     import oracle
 
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    visible = len(os.sched_getaffinity(0))
+    cores = max(1, min(HOST_CPU_SHARE, visible))
     n_heads = cores * heads_per_core
     rng = np.random.default_rng(7)
     _SAMPLE.clear()
@@ -137,8 +145,10 @@ def cpu_baseline(cpu_inputs, alphas, heads_per_core=8):
         "cores": cores,
         "kind": "oracle",
         "sample": f"{n_heads} of {LAYERS * B * H} (layer, b, h) heads of the same workload, fp64 numpy "
-                  f"sparse forward + backward at N={N}, {cores} single-threaded worker processes, "
+                  f"sparse forward + backward at N={N}, {cores} single-threaded worker processes "
+                  f"(the host's CPU share per GPU; {visible} cores visible to the process), "
                   f"{wall:.2f} s wall ({wall * cores:.1f} core-seconds); CPU: {model}",
+        "cores_visible": visible,
     }
 
 
@@ -320,6 +330,90 @@ def long_context_bench(fsa, torch, dev, stream, scale, reps):
     }
 
 
+def short_context_bench(fsa, torch, dev, stream, reps):
+    """The forward at the training length N = 1024 (bf16 [8,8,1024,64], w = 64, R = 1024):
+    the one-layer workload (alpha = 1) and the 16-layer linear stagger, each timed as the
+    average launch over 16 layers' own seeded inputs (541 MB, more than the 256 MB
+    last-level cache, so every launch reads its inputs from HBM); and the fp32
+    single-head workload (fp32 [1,1,256,64], w = 16, R = 256), which is launch-bound."""
+    from fibonacci_offset_transformer_amd import schedules, synth
+    Bs, Hs, Ns = 8, 8, 1024
+    shape = (Bs, Hs, Ns, D)
+    bufs = []
+    for l in range(LAYERS):
+        x = {k: t.to(dev) for k, t in synth.layer_inputs(3, l, shape, torch.bfloat16, with_grad=False).items()}
+        x["o"] = torch.empty_like(x["q"])
+        x["lse"] = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+        bufs.append(x)
+    alphas = schedules.linear_stagger(LAYERS)
+    scale = 1.0 / math.sqrt(D)
+
+    def fwd(alpha_of):
+        def run(l):
+            x = bufs[l]
+            fsa.forward(x["q"], x["k"], x["v"], alpha=alpha_of(l), w=W, R=R, base=BASE, scale=scale, out=x["o"],
+                        lse=x["lse"])
+        return run
+
+    us_one = stage_us(torch, dev, stream, fwd(lambda l: 1.0), reps)
+    us_stagger = stage_us(torch, dev, stream, fwd(lambda l: alphas[l]), reps)
+    rows = Bs * Hs * Ns
+    nbytes = alg_bytes_per_row()["fwd"] * rows
+
+    def line(us, layers):
+        achieved = nbytes / (us * 1e-6) / 1e9
+        return {
+            "us_per_layer": round(us, 3),
+            "us_per_pass": round(us * layers, 3),
+            "query_heads_per_s": round(rows / (us * 1e-6), 1),
+            "gb_s": round(achieved, 1),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "kernel": KERNEL_NAMES["fwd"],
+                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": round(us, 3)},
+        }
+
+    del bufs
+    # fp32 single head: 100 launches captured in one graph
+    x1 = {k: t.to(dev) for k, t in synth.layer_inputs(1, 0, (1, 1, 256, D), torch.float32, with_grad=False).items()}
+    o1 = torch.empty_like(x1["q"])
+    l1 = torch.empty((1, 1, 256), dtype=torch.float32, device=dev)
+
+    def one():
+        fsa.forward(x1["q"], x1["k"], x1["v"], alpha=1.0, w=16, R=256, base=BASE, scale=scale, out=o1, lse=l1)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        one()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(100):
+            one()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us1 = e0.elapsed_time(e1) * 1e3 / 500
+    del g
+    return {
+        "what": "forward at the training length N = 1024: bf16 [8,8,1024,64], w = 64, R = 1024; each figure the "
+                "average launch over 16 layers' own seeded inputs (read from HBM)",
+        "one_layer_alpha1": line(us_one, 1),
+        "sixteen_layer_stagger": line(us_stagger, LAYERS),
+        "fp32_single_head": {"what": "fp32 [1,1,256,64], w = 16, alpha = 1, R = 256, forward (general kernel; "
+                                     "launch-bound: 4 workgroups)",
+                             "us_per_launch": round(us1, 3),
+                             "query_heads_per_s": round(256 / (us1 * 1e-6), 1)},
+    }
+
+
 def stage_us(torch, dev, stream, fn, reps):
     """Average duration (us) of one layer's launches of fn: the 16 layers captured back to
     back in a HIP graph, replayed `reps` times (after ten untimed replays) between two
@@ -461,8 +555,11 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the [1,8,32768,64] power-of-2 layer")
     ap.add_argument("--no-literal", action="store_true",
                     help="skip the run with the literal stagger formula 0.5 + l*(1.5/15)")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time single steps after writing 1 GiB of scratch (cold caches); median reported")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the single steps timed after writing 1 GiB of scratch (cold caches)")
+    ap.add_argument("--no-short", action="store_true",
+                    help="skip the forward at the training length N = 1024 (bf16 [8,8,1024,64], one layer and "
+                         "the 16-layer stagger) and the fp32 single-head case")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter scale reference) and exit")
     args = ap.parse_args()
@@ -526,6 +623,16 @@ def main():
                      scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], delta=x["delta"], pair_ws=pair_ws)
 
     def step():
+        # a training step: every layer's forward in layer order, then the backward from
+        # the last layer down, so each backward finds its layer's rows long evicted
+        for l in range(LAYERS):
+            layer_fwd(l)
+        for l in reversed(range(LAYERS)):
+            layer_bwd(l)
+
+    def step_per_layer():
+        # forward then backward of each layer in turn (each backward finds its layer's
+        # rows still in the last-level cache): reported beside the training step
         for l in range(LAYERS):
             layer_fwd(l)
             layer_bwd(l)
@@ -537,17 +644,22 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    # capture one step as a HIP graph
-    side = torch.cuda.Stream(device=dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        step()
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
+    def capture(fn):
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    # one step captured as a HIP graph
+    graph = capture(step)
+    graph_per_layer = capture(step_per_layer)
 
     # bring the GPU to steady clocks before anything is timed (untimed replays for at
     # least half a second), then the requested warmup steps
@@ -559,13 +671,17 @@ def main():
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for _ in range(args.steps):
-        graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    def timed(g, n):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(n):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    ms_per_step = timed(graph, args.steps)
 
     # graph replays must reproduce the eager results bit for bit (deterministic kernels)
     for l in range(LAYERS):
@@ -585,9 +701,19 @@ def main():
         layer_fwd(l)
         layer_bwd(l)
 
-    # forward + backward of one layer back to back (the order of a training step, which
-    # finds the layer's rows still in cache): the reference for the variants' steps
+    # forward + backward of one layer back to back (which finds the layer's rows still
+    # in cache): the reference for the variants' steps
     static_step_us = stage_us(torch, dev, stream, layer_step, reps)
+
+    # the whole step in per-layer order, for comparison with the training order
+    for _ in range(3):
+        graph_per_layer.replay()
+    per_layer_ms = timed(graph_per_layer, max(5, args.steps // 2))
+    del graph_per_layer
+    for l in range(LAYERS):
+        for name, a in zip(("o", "lse", "dq", "dk", "dv"), ref[l]):
+            if not torch.equal(bufs[l][name], a):
+                raise SystemExit(f"per-layer order differs from the training-order result: layer {l} {name}")
 
     # eager step time for context
     step()
@@ -601,7 +727,7 @@ def main():
     eager_ms = e0.elapsed_time(e1) / max(3, args.steps // 5)
 
     cold = None
-    if args.cold:
+    if not args.no_cold:
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         times = []
         for _ in range(max(5, min(args.steps, 20))):
@@ -748,6 +874,10 @@ def main():
     if not args.no_long:
         long_ctx = long_context_bench(fsa, torch, dev, stream, scale, 10)
 
+    short = None
+    if not args.no_short:
+        short = short_context_bench(fsa, torch, dev, stream, max(20, args.steps // 5))
+
     rope = None
     if not args.no_rope:
         rope = rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, dict(avg_us, step=static_step_us),
@@ -771,8 +901,12 @@ def main():
                         f"[B={B},H={H},N={N},d={D}], linear stagger alpha_l=0.5+l/15, fib base, w={W}, "
                         f"R={R} (tables reused at N={N}), Q/K/V/dO ~ N(0,1) seeded",
             "layers": LAYERS, "batch": B, "heads": H, "seq_len": N, "head_dim": D,
-            "launch": "one HIP graph per step (3 kernels per layer)",
+            "launch": "one HIP graph per step: 16 forwards in layer order, then 16 backwards in reverse "
+                      "layer order (2 kernels per layer: the forward and the one-launch backward)",
         },
+        "per_layer_order_ms_per_step": round(per_layer_ms, 5),
+        "per_layer_order_note": "the same kernels with each layer's backward right after its forward "
+                                "(its rows still cached); value and ms_per_step use the training order",
         "hbm_gb_s": round(gbs, 1),
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "copy_gb_s": round(copy_gbs, 1),
@@ -789,6 +923,7 @@ def main():
         "learned_alpha": learned,
         "rope": rope,
         "literal_stagger": literal,
+        "short_context": short,
         "long_context": long_ctx,
         "cold": cold,
     }
