@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfsa.so")
 
-SOURCES = ["fsa_abi.cpp", "fsa_forward.hip", "fsa_backward.hip", "fsa_decode.hip", "fsa_rope.hip"]
+SOURCES = ["fsa_abi.cpp", "fsa_forward.hip", "fsa_backward.hip", "fsa_decode.hip", "fsa_rope.hip", "fsa_noalloc.hip"]
 ARCH = "gfx950"
 
 

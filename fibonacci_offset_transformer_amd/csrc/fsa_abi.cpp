@@ -214,6 +214,11 @@ fsa_status_t launched(hipError_t e, const char *what) {
 
 }  // namespace
 
+namespace fsa {
+// Sets the calling thread's error text (for the C-ABI functions of other sources).
+fsa_status_t set_error(fsa_status_t st, const char *msg) { return fail(st, "%s", msg); }
+}  // namespace fsa
+
 extern "C" {
 
 fsa_status_t fsa_build_offsets(fsa_base_t base, double alpha, int32_t w, int32_t R,
@@ -970,6 +975,20 @@ fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int3
     bool one_launch = false;
     uint64_t flags = 0, status = 0, need = 0;  // byte offsets of the token array and status word, ws size
     fsa_status_t st = FSA_OK;
+    if (kind == FSA_WS_BACKWARD_NOALLOC) {
+        // the library's scratch on the current device: D, then the static backward's workspace
+        if (bh * N == 0) return ok();
+        uint64_t pair_bytes = 0;
+        if ((st = fsa_backward_workspace_bytes(dt, B, H, N, d, base, alpha, w, R, &pair_bytes)) != FSA_OK) return st;
+        const uint64_t delta_bytes = fsa::align256(4ull * static_cast<uint64_t>(bh) * N);
+        if (delta_bytes + pair_bytes > fsa::kScratchBytes) return ok();  // the call refused this size
+        void *p = nullptr;
+        const hipError_t e = fsa::scratch_address(&p);
+        if (e != hipSuccess) return fail(FSA_E_HIP, "looking up the scratch array failed: %s", hipGetErrorString(e));
+        ws = static_cast<const char *>(p) + delta_bytes;
+        ws_bytes = pair_bytes;
+        kind = FSA_WS_BACKWARD;
+    }
     if (kind == FSA_WS_BACKWARD || kind == FSA_WS_ROPE_BACKWARD) {
         const Shape s{B, H, N, d};
         if ((st = check_common(dt, dt, s, 1.0f)) != FSA_OK) return st;

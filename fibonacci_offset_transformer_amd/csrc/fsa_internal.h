@@ -146,6 +146,13 @@ constexpr int32_t kMaxPolls = 1 << 18;
 // multiple of 8 (every XCD then holds whole heads).
 inline bool one_launch_backward(const AttnParams &p) { return p.flags && p.n_off > 0 && p.bh % 8 == 0; }
 
+// Sets the calling thread's error text, returns st (fsa_abi.cpp).
+fsa_status_t set_error(fsa_status_t st, const char *msg);
+// Device address of the library's static scratch array on the current device, looked up
+// once per device (fsa_noalloc.hip); its size in bytes.
+extern const uint64_t kScratchBytes;
+hipError_t scratch_address(void **ptr);
+
 hipError_t launch_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnParams &p, hipStream_t stream);
 hipError_t launch_backward_delta(fsa_dtype_t dt, const AttnParams &p, hipStream_t stream);

@@ -32,8 +32,8 @@ EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_wor
            "fsa_frac_decode",
            "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
            "fsa_rope_frac_workspace_bytes", "fsa_rope_frac_forward", "fsa_rope_frac_backward", "fsa_wait_status",
-           "fsa_debug_force_wait_timeout", "fsa_last_error")
-WS_KINDS = {"backward": 0, "frac_backward": 1, "rope_backward": 2, "rope_frac_backward": 3}
+           "fsa_backward_noalloc", "fsa_debug_force_wait_timeout", "fsa_last_error")
+WS_KINDS = {"backward": 0, "frac_backward": 1, "rope_backward": 2, "rope_frac_backward": 3, "backward_noalloc": 4}
 
 
 class FsaError(RuntimeError):
@@ -120,6 +120,9 @@ def library() -> ctypes.CDLL:
             L.fsa_wait_status.argtypes = [ctypes.c_int, ctypes.c_int, i32, i32, i32, i32, ctypes.c_int, f64, i32, i32,
                                           vp, u64, ctypes.POINTER(i32), vp]
             L.fsa_wait_status.restype = ctypes.c_int
+            L.fsa_backward_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                               i32, i32, i32, f32, ctypes.c_int, f64, i32, i32, vp]
+            L.fsa_backward_noalloc.restype = ctypes.c_int
             L.fsa_debug_force_wait_timeout.argtypes = [i32]
             L.fsa_debug_force_wait_timeout.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
@@ -247,6 +250,24 @@ def backward(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base:
                                       _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _ptr(pw), pw_bytes,
                                       B, H, N, d, _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
                                       _stream(q.device)))
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, dout, *, alpha: float = 1.0, w: int, R: int, base: str = "fib",
+                     scale=None, dq=None, dk=None, dv=None, out_dtype=None):
+    """backward() with the workspaces in the library's static device scratch (see
+    fsa_backward_noalloc): the C call allocates nothing. Outputs are allocated here only
+    when not given."""
+    B, H, N, d = _shape(q, k, v, o, dout)
+    lse = _rows_in(q, lse, "lse")
+    dq = _out(q, dq, out_dtype)
+    dk = _out(q, dk, dq.dtype)
+    dv = _out(q, dv, dq.dtype)
+    with torch.cuda.device(q.device):
+        _check(library().fsa_backward_noalloc(DTYPES[q.dtype], DTYPES[dq.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                              _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d,
+                                              _scale(scale, d), BASES[base], float(alpha), int(w), int(R),
+                                              _stream(q.device)))
     return dq, dk, dv
 
 

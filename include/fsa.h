@@ -467,6 +467,29 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
                                     int32_t R, void *stream);
 
 /*
+ * fsa_backward_noalloc - fsa_backward for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Computes exactly what fsa_backward computes (the same kernels, bitwise the same
+ * results), with its two workspaces (D, and the pair weights, tokens and status word of
+ * fsa_backward_workspace_bytes) taken from a static device array of the library: 32 MiB
+ * per GPU, held by every GPU the library runs on until the process ends. The caller
+ * passes inputs and outputs only; the call allocates nothing and makes no allocating
+ * library call. Problems whose D (4 B H N bytes, rounded up to 256) plus pair workspace
+ * exceed 32 MiB are refused with FSA_E_CAPACITY (fsa_backward with caller workspaces
+ * takes them). Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (nothing in it has to start at zero): two calls that overlap in time on one
+ * GPU, on different streams or threads, race and must not be issued. fsa_wait_status
+ * with FSA_WS_BACKWARD_NOALLOC reads this array's status word.
+ *
+ * Arguments as in fsa_backward, without delta_ws, pair_ws and pair_ws_bytes.
+ */
+fsa_status_t fsa_backward_noalloc(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k,
+                                  const void *v, const void *o, const float *lse, const void *dout,
+                                  void *dq, void *dk, void *dv, int32_t B, int32_t H, int32_t N, int32_t d,
+                                  float scale, fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
+
+/*
  * fsa_wait_status - whether the last one-launch backward that ran with a workspace
  * gave up one of its bounded waits.
  *
@@ -484,7 +507,9 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
  *   kind        which call's workspace: FSA_WS_BACKWARD (fsa_backward,
  *               fsa_backward_grads: pair_ws), FSA_WS_FRAC_BACKWARD (fsa_frac_backward:
  *               ws), FSA_WS_ROPE_BACKWARD (fsa_rope_backward: ws),
- *               FSA_WS_ROPE_FRAC_BACKWARD (fsa_rope_frac_backward: ws)
+ *               FSA_WS_ROPE_FRAC_BACKWARD (fsa_rope_frac_backward: ws),
+ *               FSA_WS_BACKWARD_NOALLOC (fsa_backward_noalloc: the library's scratch
+ *               on the current device; ws and ws_bytes are ignored)
  *   dt, B, H, N, d, base, alpha, w, R   the arguments the backward ran with
  *   ws, ws_bytes   that workspace and its size
  *   gave_up     receives 1 if a wait of that launch gave up, else 0 (also 0 when the
@@ -495,7 +520,8 @@ typedef enum {
     FSA_WS_BACKWARD = 0,
     FSA_WS_FRAC_BACKWARD = 1,
     FSA_WS_ROPE_BACKWARD = 2,
-    FSA_WS_ROPE_FRAC_BACKWARD = 3
+    FSA_WS_ROPE_FRAC_BACKWARD = 3,
+    FSA_WS_BACKWARD_NOALLOC = 4
 } fsa_ws_kind_t;
 fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                              fsa_base_t base, double alpha, int32_t w, int32_t R, const void *ws,
