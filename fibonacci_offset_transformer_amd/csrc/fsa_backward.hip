@@ -423,7 +423,36 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
             }
         }
     };
-    {
+    if (w == 64 && r0 >= 64 && r0 + 15 < n) {  // uniform: a full window of 64 keys for every row
+        // only the oldest block and the newest are cut, at the same lane position: key
+        // 4 g + r of the block against row c16 (no branch, so the blocks' LDS reads and
+        // MFMAs interleave)
+        auto fast_ds = [&](auto bc, float ds[4]) {
+            constexpr int b = decltype(bc)::value;
+            Frag<true> kf, vf;
+            lds_frag(kf, ta_w, 16 * b, tl);
+            lds_frag(vf, tb_w, 16 * b, tl);
+            const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const f32x4_t dpt = mma_over_d(vf, df, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool newer = 4 * g + r > c16;
+                const float x = fast_exp2(__builtin_fmaf(st[r], sl2, -lse2_i)) * (dpt[r] - di_i);
+                ds[r] = (b == 0 && !newer) || (b == 4 && newer) ? 0.f : x;
+            }
+        };
+        float d0[4], d1[4];
+        fast_ds(Len<0>{}, d0);
+        fast_ds(Len<1>{}, d1);
+        mma_over_rows_tr2_exact(acc, ta_w, 0, 16, tl, d0, d1);
+        __builtin_amdgcn_sched_barrier(0);  // keeps the next pair's reads from piling up registers
+        fast_ds(Len<2>{}, d0);
+        fast_ds(Len<3>{}, d1);
+        mma_over_rows_tr2_exact(acc, ta_w, 32, 48, tl, d0, d1);
+        __builtin_amdgcn_sched_barrier(0);
+        fast_ds(Len<4>{}, d0);
+        mma_over_rows_tr_exact(acc, ta_w, 64, tl, d0);
+    } else {
         float d0[4], d1[4];
         // the band's dS weights go in as bf16 high part plus remainder (see bwd_dkdv_kernel)
         block_ds(0, d0);

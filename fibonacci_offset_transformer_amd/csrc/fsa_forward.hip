@@ -177,10 +177,13 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const int i = r0 + c16;  // MFMA-layout query row
     const bool row_ok = i < n;
 
+    // K and Q first, V after them: the scores start once K and Q have landed, while V
+    // is still in flight (static tables; the variants wait for everything)
+    constexpr bool kSplit = !FRAC && !ROPE;
     dma_tile(ks, K, i0 - 64, n, wave, lane);
-    dma_tile(vs, V, i0 - 64, n, wave, lane);
     Frag<true> qf;
     buf_frag(qf, rq, i, g);
+    dma_tile(vs, V, i0 - 64, n, wave, lane);
     [[maybe_unused]] __amdgpu_buffer_rsrc_t rt;
     if constexpr (ROPE) {
         // the table rows of this tile's positions (the positions past n read as zeros)
@@ -192,8 +195,15 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         qf.c[0] = rope_chunk(qf.c[0], a01, a23);
         qf.c[1] = rope_chunk(qf.c[1], b01, b23);
     }
-    wait_vm_all();
-    __syncthreads();
+    if constexpr (kSplit) {
+        wait_vm<4>();  // the four V copies of this wave may still be in flight
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    } else {
+        wait_vm_all();
+        __syncthreads();
+    }
     // the first slab rows are requested now and land while the band runs; most of them
     // are rows of neighbouring tiles whose band copies have just passed through L2
     SFrag sk[4], sv[4];  // FRAC: slot u of entries holds near rows in [2u], far rows in [2u + 1]
@@ -226,6 +236,22 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const int qb = r0 >> 4;
     float sc[5][4];
     float bm = kNegInf;
+    if (w == 64 && r0 >= 64 && r0 + 15 < n) {  // uniform: a full window of 64 keys for every row
+        // only the oldest block (keys older than the window) and the newest (keys after the
+        // row) are cut, at the same lane position: key 4 g + r of the block against row c16
+#pragma unroll
+        for (int b = 0; b < 5; ++b) {
+            Frag<true> kf;
+            lds_frag(kf, ks_w, 16 * b, tl);
+            const f32x4_t st = mma_over_d(kf, qf, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool newer = 4 * g + r > c16;
+                sc[b][r] = (b == 0 && !newer) || (b == 4 && newer) ? kNegInf : st[r];
+                bm = fmaxf(bm, sc[b][r]);
+            }
+        }
+    } else {
 #pragma unroll
     for (int b = 0; b < 5; ++b) {
         const int kb0 = 16 * (qb - 4 + b);
@@ -246,6 +272,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             bm = fmaxf(bm, st[r]);
         }
     }
+    }
     // scaled row maximum; a valid row always attends itself, so it is finite there
     const float m_b = row_ok ? group_max(bm) * sl2 : kNegInf;
     const float msb = row_ok ? m_b : 0.f;
@@ -260,6 +287,14 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             pr[b][r] = fast_exp2(__builtin_fmaf(sc[b][r], sl2, -msb));
             lsum_b += pr[b][r];
         }
+    if constexpr (kSplit) {
+        // the V copies were issued before the slab loads (at most 4 x 4 of them per wave)
+        if (n_off >= 4) wait_vm<16>();
+        else wait_vm_all();
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+    }
     mma_over_rows_tr2(acc_b, vs_w, 0, 16, tl, pr[0], pr[1]);
     mma_over_rows_tr2(acc_b, vs_w, 32, 48, tl, pr[2], pr[3]);
     mma_over_rows_tr(acc_b, vs_w, 64, tl, pr[4]);
@@ -417,8 +452,9 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (row_s[h] < n) {
-            store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], 1.f / l_s[h]);
-            if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = m_s[h] * kLn2 + logf(l_s[h]);
+            // hardware reciprocal and log2 (1 ulp): l >= 1, since the row maximum's term is 1
+            store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], __builtin_amdgcn_rcpf(l_s[h]));
+            if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = (m_s[h] + __builtin_amdgcn_logf(l_s[h])) * kLn2;
         }
     }
 }
