@@ -14,8 +14,9 @@ query-heads/s (value), algorithmic HBM GB/s of the step, a roofline entry for th
 dominant kernel, the step in per-layer order (forward then backward of each layer)
 and after writing 1 GiB of scratch (cold caches), the forward at the training length
 N = 1024 (one layer of bf16 [8,8,1024,64], and the 16-layer stagger), the dense
-causal baseline, and the fp64 CPU oracle timed on a bounded sample of the same
-workload.
+causal baseline, device-copy rates on buffers the last-level cache cannot hold (a
+1 GiB copy, and per stage copies moving its bytes per launch) for reference, and the
+fp64 CPU oracle timed on a bounded sample of the same workload.
 
 The learned-alpha variant (fractional targets, interpolated K/V rows) and the
 rotary-embedding variant (unrotated Q, K in) are timed on the same layers next to
@@ -414,6 +415,42 @@ def short_context_bench(fsa, torch, dev, stream, reps):
     }
 
 
+def copy_reference(torch, dev, stream, stage_bytes):
+    """Device-copy rates (bytes read + written per second) for reference, always on buffers
+    that the 256 MB last-level cache cannot hold from one pass to the next: a 1 GiB to
+    1 GiB copy (the sustained rate), and for each stage copies that move its algorithmic
+    bytes per launch (half read, half written), rotated over 16 distinct buffer pairs
+    like the layers of the step."""
+    def rate(pairs, reps):
+        for s, d in pairs:
+            d.copy_(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for s, d in pairs:
+                d.copy_(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        moved = 2 * reps * sum(s.numel() * s.element_size() for s, _ in pairs)
+        return moved / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    src = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out = {"large_gb_s": round(rate([(src, dst)], 5), 1)}
+    del src, dst
+    for k, nbytes in stage_bytes.items():
+        elems = int(nbytes) // 2 // 4
+        pairs = [(torch.ones(elems, dtype=torch.float32, device=dev), torch.empty(elems, dtype=torch.float32, device=dev))
+                 for _ in range(LAYERS)]
+        out[f"{k}_sized_gb_s"] = round(rate(pairs, 5), 1)
+        del pairs
+    out["what"] = ("torch device-to-device copies (the HIP runtime's copy kernel); large: 1 GiB to 1 GiB; "
+                   "<stage>_sized: 16 distinct buffer pairs, each copy moving that stage's algorithmic bytes per launch "
+                   "(at the forward's 34 MB a copy launch does not reach the sustained rate)")
+    return out
+
+
 def stage_us(torch, dev, stream, fn, reps):
     """Average duration (us) of one layer's launches of fn: the 16 layers captured back to
     back in a HIP graph, replayed `reps` times (after ten untimed replays) between two
@@ -743,20 +780,8 @@ def main():
         cold = {"ms_per_step_median": round(times[len(times) // 2], 5), "steps": len(times),
                 "what": "one graph step after writing 1 GiB of scratch, per step"}
 
-    # device-copy bandwidth at the size of one layer's step traffic, for reference
-    cbytes = 128 << 20
-    src = torch.ones(cbytes // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 2 * cbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    copy_ref = copy_reference(torch, dev, stream, {k: alg_bytes_per_row()[k] * rows_per_layer() for k in avg_us})
+    copy_gbs = copy_ref["large_gb_s"]
 
     literal = None
     if not args.no_literal:
@@ -832,6 +857,8 @@ def main():
                          "useful flops, and the backward recomputes scores and dP in both kernels)")
     stages = {k: {"avg_us": round(v, 3), "algorithmic_bytes": per_row[k] * rows,
                   "gb_s": round(per_row[k] * rows / (v * 1e-6) / 1e9, 1),
+                  "frac_of_runtime_copy_same_bytes": round(per_row[k] * rows / (v * 1e-6) / 1e9
+                                                   / copy_ref[f"{k}_sized_gb_s"], 4),
                   "kernels": [KERNEL_NAMES[n] for n in STAGE_KERNELS[k]]} for k, v in avg_us.items()}
 
     dense = None
@@ -911,6 +938,7 @@ def main():
         "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "copy_gb_s": round(copy_gbs, 1),
         "hbm_frac_of_copy": round(gbs / copy_gbs, 4),
+        "copy_reference": copy_ref,
         "algorithmic_bytes_per_step": step_bytes,
         "query_heads_per_step": qh_per_step,
         "eager_ms_per_step": round(eager_ms, 4),
