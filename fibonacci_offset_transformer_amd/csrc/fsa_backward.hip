@@ -310,10 +310,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pair_rsrc(const AttnParams &p,
 //
 // The body works on logical tile lb with the caller's LDS: ta, tb (band K and V rows,
 // kTileRows * 64 each, then merge areas), d_s (64 floats: D of the tile's rows, WITH_D)
-// and dd_s (4 * FSA_MAX_OFFSETS floats, FRAC).
+// and dd_s (4 * FSA_MAX_OFFSETS floats, FRAC). With PUBLISH (one-launch backward) the
+// tile sets its flag to `token` once its D, pair words and partials are in L2, before
+// it stores dQ, which nothing in the launch reads.
 template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0, bool PUBLISH = false, bool EXACT = false>
 __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *d_s,
-                                        float *dd_s) {
+                                        float *dd_s, [[maybe_unused]] const uint64_t token = 0) {
     static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
     static_assert(!(FRAC && EXACT), "fractional entries keep their own pair format");
     using OE = typename Elem<OUT_BF16>::T;
@@ -476,9 +478,24 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     c_to_slab(reinterpret_cast<float *>(ta) + wave * 1024, acc, dq_s, c16, g, s8, c8);
 
     // sparse offsets: keys i - o, in the slab layout
+    // Q and dO rows move from the MFMA layout (row c16, chunks g and g + 4) to the slab
+    // layout through this wave's 4 KB of the V tile, free since the barrier above (chunk
+    // c of row r at position c ^ (r & 7), so that neither side conflicts on banks)
     SFrag qs, dos;
-    sfrag_load<kCacheNT>(qs, rq, row_s[0], row_s[1], c8);  // second and last read of these rows
-    sfrag_load<kCacheNT>(dos, rdo, row_s[0], row_s[1], c8);
+    {
+        uint16_t *qa = tb + 2048 * wave, *da = qa + 1024;
+        const int w0 = c16 * 64 + 8 * (g ^ (c16 & 7)), w1 = c16 * 64 + 8 * ((g + 4) ^ (c16 & 7));
+        *reinterpret_cast<u32x4_t *>(qa + w0) = qf.c[0];
+        *reinterpret_cast<u32x4_t *>(qa + w1) = qf.c[1];
+        *reinterpret_cast<u32x4_t *>(da + w0) = df.c[0];
+        *reinterpret_cast<u32x4_t *>(da + w1) = df.c[1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int r = (s8 + 8 * h) * 64 + 8 * (c8 ^ s8);
+            qs.r[h] = *reinterpret_cast<const u32x4_t *>(qa + r);
+            dos.r[h] = *reinterpret_cast<const u32x4_t *>(da + r);
+        }
+    }
     float lse2[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) lse2[h] = buf_f32(rl, row_s[h]) * kLog2e;
@@ -583,9 +600,6 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
         for (int h = 0; h < 2; ++h)
             if (row_s[h] < n) rope_back_chunk(p.rope, row_s[h], c8, dq_s[h]);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-        if (row_s[h] < n) store_chunk<true>(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
     if constexpr (FRAC) {  // partials [n_off, tiles]: entry t's partials are contiguous
         __syncthreads();
         const int t = threadIdx.x;
@@ -599,6 +613,16 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
                 *dst = part;
         }
     }
+    if constexpr (PUBLISH) {
+        // every wave's stores of the words others read (pair words, D, the partials) have
+        // reached L2 before the token does; dQ, read by no one in the launch, follows it
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (row_s[h] < n) store_chunk<true>(static_cast<OE *>(p.dq) + head, row_s[h], c8, dq_s[h], p.scale);
 }
 
 template <bool OUT_BF16, bool WITH_D, bool FRAC, bool EXACT = false>
@@ -928,7 +952,7 @@ __global__ void __launch_bounds__(kThreads) bwd_dkdv_kernel(const AttnParams p) 
 // The static backward in one launch: blocks [0, tiles) do the dQ work of tile
 // xcd_logical_block(b), blocks [tiles, 2 tiles) the dK/dV work of tile
 // xcd_logical_block(b - tiles). A dQ tile publishes this launch's token in p.flags once
-// its pair words are in L2; a dK/dV tile waits for the tokens of the tiles whose pair
+// its D and pair words are in L2 (before its dQ store); a dK/dV tile waits for the tokens of the tiles whose pair
 // words it reads (D it forms itself, or reads from the caller).
 // Workgroups are dispatched in block order, so every dQ tile has been dispatched before
 // any dK/dV tile waits, and dQ tiles wait for nothing: the waits end. The host launches
@@ -946,11 +970,7 @@ __global__ void __launch_bounds__(kThreads) bwd_fused_kernel(const AttnParams p)
     const uint64_t token = launch_token();
     if (static_cast<int>(blockIdx.x) < tiles) {
         const int lb = xcd_logical_block(blockIdx.x, tiles);
-        dq_tile<OUT_BF16, WITH_D, FRAC, NOFF, true, EXACT>(p, lb, ta, tb, fa, fb);
-        // every wave's stores (pair words, D, dQ) have reached L2 before the token does
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dq_tile<OUT_BF16, WITH_D, FRAC, NOFF, true, EXACT>(p, lb, ta, tb, fa, fb, token);
     } else {
         dkdv_tile<OUT_BF16, FRAC, true, WITH_D, NOFF, EXACT>(p, xcd_logical_block(blockIdx.x - tiles, tiles), ta, tb,
                                                              fa, fb, token);
