@@ -506,6 +506,16 @@ def test_pow2_reach_at_evaluation_length():
     bwd_case(35, 2, 8, 4096, torch.bfloat16, "pow2", 1.0, 64, 4096, heads=[(1, 5)])
 
 
+def test_fibonacci_reach_at_evaluation_length():
+    # the Fibonacci table with its reach at the evaluation length (R = N = 4096) at the
+    # stagger's largest alpha: base values up to 2584 give offsets up to 3876, nine
+    # entries (one past the kernels' unrolled slab groups)
+    T = oracle.offset_table("fib", 1.5, 64, 4096)
+    assert len(T) == 9 and T[-1] == 3876 and fsa.build_offsets(1.5, 64, 4096, "fib") == T
+    fwd_case(36, 2, 8, 4096, torch.bfloat16, "fib", 1.5, 64, 4096, heads=[(0, 3), (1, 6)])
+    bwd_case(36, 2, 8, 4096, torch.bfloat16, "fib", 1.5, 64, 4096, heads=[(0, 1)])
+
+
 @pytest.mark.parametrize("layer", [0, 9, 15])
 def test_workload4_edge_tiles_of_every_head(layer):
     # the first and last 64-row tiles of all 16 heads of a training-step layer (the
