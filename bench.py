@@ -787,11 +787,13 @@ def main():
     if not args.no_literal:
         lit_alphas = schedules.literal_stagger(LAYERS)
 
-        def lit_step():
+        def lit_step():  # training order, as the main step
             for l in range(LAYERS):
                 x = bufs[l]
                 fsa.forward(x["q"], x["k"], x["v"], alpha=lit_alphas[l], w=W, R=R, base=BASE, scale=scale,
                             out=x["o"], lse=x["lse"])
+            for l in reversed(range(LAYERS)):
+                x = bufs[l]
                 fsa.backward(x["q"], x["k"], x["v"], x["o"], x["lse"], x["do"], alpha=lit_alphas[l], w=W, R=R,
                              base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], delta=x["delta"],
                              pair_ws=lit_ws)
