@@ -177,26 +177,27 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const int i = r0 + c16;  // MFMA-layout query row
     const bool row_ok = i < n;
 
-    // K and Q first, V after them: the scores start once K and Q have landed, while V
-    // is still in flight (static tables; the variants wait for everything)
-    constexpr bool kSplit = !FRAC && !ROPE;
+    // K and Q first, V after them: the scores start once K and Q (and, with ROPE, the
+    // table rows that rotate Q) have landed, while V is still in flight (the learned-alpha
+    // variant waits for everything)
+    constexpr bool kSplit = !FRAC;
+    [[maybe_unused]] f32x4_t a01, a23, b01, b23;
+    if constexpr (ROPE) {
+        // the table rows of this tile's positions (the positions past n read as zeros)
+        const __amdgpu_buffer_rsrc_t rt = head_rsrc(p.rope + (int64_t)i0 * 64, span_bytes(min(64, n - i0), 256));
+        rope_entries(rt, i - i0, g, a01, a23);      // chunk g: pairs 4g .. 4g + 3
+        rope_entries(rt, i - i0, g + 4, b01, b23);  // chunk g + 4
+    }
     dma_tile(ks, K, i0 - 64, n, wave, lane);
     Frag<true> qf;
     buf_frag(qf, rq, i, g);
     dma_tile(vs, V, i0 - 64, n, wave, lane);
-    [[maybe_unused]] __amdgpu_buffer_rsrc_t rt;
-    if constexpr (ROPE) {
-        // the table rows of this tile's positions (the positions past n read as zeros)
-        rt = head_rsrc(p.rope + (int64_t)i0 * 64, span_bytes(min(64, n - i0), 256));
-        f32x4_t a01, a23, b01, b23;
-        rope_entries(rt, i - i0, g, a01, a23);      // chunk g: pairs 4g .. 4g + 3
-        rope_entries(rt, i - i0, g + 4, b01, b23);  // chunk g + 4
-        wait_vm_all();
-        qf.c[0] = rope_chunk(qf.c[0], a01, a23);
-        qf.c[1] = rope_chunk(qf.c[1], b01, b23);
-    }
     if constexpr (kSplit) {
         wait_vm<4>();  // the four V copies of this wave may still be in flight
+        if constexpr (ROPE) {
+            qf.c[0] = rope_chunk(qf.c[0], a01, a23);
+            qf.c[1] = rope_chunk(qf.c[1], b01, b23);
+        }
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");
