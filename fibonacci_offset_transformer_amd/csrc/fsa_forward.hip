@@ -453,8 +453,10 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         if (row_s[h] < n) {
-            // hardware reciprocal and log2 (1 ulp): l >= 1, since the row maximum's term is 1
-            store_chunk(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], __builtin_amdgcn_rcpf(l_s[h]));
+            // hardware reciprocal and log2 (1 ulp): l >= 1, since the row maximum's term is 1.
+            // O goes out with non-temporal stores, which keep it from evicting the K and V
+            // rows that other workgroups' slabs still gather from L2
+            store_chunk<true>(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], __builtin_amdgcn_rcpf(l_s[h]));
             if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = (m_s[h] + __builtin_amdgcn_logf(l_s[h])) * kLn2;
         }
     }
