@@ -178,9 +178,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const bool row_ok = i < n;
 
     // K and Q first, V after them: the scores start once K and Q (and, with ROPE, the
-    // table rows that rotate Q) have landed, while V is still in flight (the learned-alpha
-    // variant waits for everything)
-    constexpr bool kSplit = !FRAC;
+    // table rows that rotate Q) have landed, while V is still in flight
     [[maybe_unused]] f32x4_t a01, a23, b01, b23;
     if constexpr (ROPE) {
         // the table rows of this tile's positions (the positions past n read as zeros)
@@ -192,19 +190,15 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     Frag<true> qf;
     buf_frag(qf, rq, i, g);
     dma_tile(vs, V, i0 - 64, n, wave, lane);
-    if constexpr (kSplit) {
-        wait_vm<4>();  // the four V copies of this wave may still be in flight
-        if constexpr (ROPE) {
-            qf.c[0] = rope_chunk(qf.c[0], a01, a23);
-            qf.c[1] = rope_chunk(qf.c[1], b01, b23);
-        }
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        __asm__ volatile("" ::: "memory");
-    } else {
-        wait_vm_all();
-        __syncthreads();
+    // a bare barrier (the compiler's __syncthreads would first wait for every copy into LDS)
+    wait_vm<4>();  // the four V copies of this wave may still be in flight
+    if constexpr (ROPE) {
+        qf.c[0] = rope_chunk(qf.c[0], a01, a23);
+        qf.c[1] = rope_chunk(qf.c[1], b01, b23);
     }
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
     // the first slab rows are requested now and land while the band runs; most of them
     // are rows of neighbouring tiles whose band copies have just passed through L2
     SFrag sk[4], sv[4];  // FRAC: slot u of entries holds near rows in [2u], far rows in [2u + 1]
@@ -288,14 +282,13 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             pr[b][r] = fast_exp2(__builtin_fmaf(sc[b][r], sl2, -msb));
             lsum_b += pr[b][r];
         }
-    if constexpr (kSplit) {
-        // the V copies were issued before the slab loads (at most 4 x 4 of them per wave)
-        if (n_off >= 4) wait_vm<16>();
-        else wait_vm_all();
-        __asm__ volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        __asm__ volatile("" ::: "memory");
-    }
+    // the V copies were issued before the slab loads (at most 4 x 4 of them per wave; the
+    // learned-alpha ring always requests its 16)
+    if (FRAC || n_off >= 4) wait_vm<16>();
+    else wait_vm_all();
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
     mma_over_rows_tr2(acc_b, vs_w, 0, 16, tl, pr[0], pr[1]);
     mma_over_rows_tr2(acc_b, vs_w, 32, 48, tl, pr[2], pr[3]);
     mma_over_rows_tr(acc_b, vs_w, 64, tl, pr[4]);
