@@ -20,11 +20,12 @@ fp64 CPU oracle timed on a bounded sample of the same workload.
 
 The learned-alpha variant (fractional targets, interpolated K/V rows) and the
 rotary-embedding variant (unrotated Q, K in) are timed on the same layers next to
-the static path.
+the static path, and so are the pages' other schedules (the coprime reassignment,
+the power-of-2 base with the stagger, the window sweep).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-dense] [--no-decode] [--no-frac] [--no-rope] [--no-literal] [--no-long]
-                       [--no-cold] [--no-short] [--copy-probe]
+                       [--no-schedules] [--no-cold] [--no-short] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -592,6 +593,8 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the [1,8,32768,64] power-of-2 layer")
     ap.add_argument("--no-literal", action="store_true",
                     help="skip the run with the literal stagger formula 0.5 + l*(1.5/15)")
+    ap.add_argument("--no-schedules", action="store_true",
+                    help="skip the steps under the coprime, power-of-2 stagger and window-sweep schedules")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the single steps timed after writing 1 GiB of scratch (cold caches)")
     ap.add_argument("--no-short", action="store_true",
@@ -783,51 +786,51 @@ def main():
     copy_ref = copy_reference(torch, dev, stream, {k: alg_bytes_per_row()[k] * rows_per_layer() for k in avg_us})
     copy_gbs = copy_ref["large_gb_s"]
 
-    literal = None
-    if not args.no_literal:
-        lit_alphas = schedules.literal_stagger(LAYERS)
+    def schedule_step(sched_alphas, base, w, reps):
+        """ms per training-order step (16 forwards, then 16 backwards in reverse) of the
+        same layers' inputs under another schedule, captured as one HIP graph."""
+        nbytes = max(fsa.workspace_bytes(torch.bfloat16, B, H, N, D, alpha=a, w=w, R=R, base=base)
+                     for a in sched_alphas)
+        ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.int32, device=dev)
 
-        def lit_step():  # training order, as the main step
+        def run():
             for l in range(LAYERS):
                 x = bufs[l]
-                fsa.forward(x["q"], x["k"], x["v"], alpha=lit_alphas[l], w=W, R=R, base=BASE, scale=scale,
+                fsa.forward(x["q"], x["k"], x["v"], alpha=sched_alphas[l], w=w, R=R, base=base, scale=scale,
                             out=x["o"], lse=x["lse"])
             for l in reversed(range(LAYERS)):
                 x = bufs[l]
-                fsa.backward(x["q"], x["k"], x["v"], x["o"], x["lse"], x["do"], alpha=lit_alphas[l], w=W, R=R,
-                             base=BASE, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], delta=x["delta"],
-                             pair_ws=lit_ws)
+                fsa.backward(x["q"], x["k"], x["v"], x["o"], x["lse"], x["do"], alpha=sched_alphas[l], w=w, R=R,
+                             base=base, scale=scale, dq=x["dq"], dk=x["dk"], dv=x["dv"], delta=x["delta"],
+                             pair_ws=ws)
 
-        lit_bytes = max(fsa.workspace_bytes(torch.bfloat16, B, H, N, D, alpha=a, w=W, R=R, base=BASE)
-                        for a in lit_alphas)
-        lit_ws = torch.empty(max(lit_bytes, 16) // 4, dtype=torch.int32, device=dev)
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            lit_step()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        lg = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(lg):
-            lit_step()
-        lg.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(max(3, args.steps // 5)):
-            lg.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        lit_ms = e0.elapsed_time(e1) / max(3, args.steps // 5)
-        del lg
-        literal = {
-            "what": "the same 16-layer step with alpha_l = 0.5 + l*(1.5/15) as one workload description writes "
-                    "it (reaches 2.0 at layer 15; the main run uses the pages' ramp 0.5 + l/15)",
-            "tables_per_layer": [len(fsa.build_offsets(a, W, R, BASE)) for a in lit_alphas],
-            "max_offset": max(max(fsa.build_offsets(a, W, R, BASE) or [0]) for a in lit_alphas),
-            "ms_per_step": round(lit_ms, 5),
-            "query_heads_per_s": round(rows_per_layer() * LAYERS / (lit_ms * 1e-3), 1),
+        g = capture(run)
+        for _ in range(3):
+            g.replay()
+        ms = timed(g, reps)
+        del g, ws
+        tabs = [fsa.build_offsets(a, w, R, base) for a in sched_alphas]
+        return {"ms_per_step": round(ms, 5), "query_heads_per_s": round(rows_per_layer() * LAYERS / (ms * 1e-3), 1),
+                "tables_per_layer": [len(t) for t in tabs], "max_offset": max(max(t or [0]) for t in tabs)}
+
+    literal = None
+    if not args.no_literal:
+        literal = dict(what="the same 16-layer step with alpha_l = 0.5 + l*(1.5/15) as one workload description "
+                            "writes it (reaches 2.0 at layer 15; the main run uses the pages' ramp 0.5 + l/15)",
+                       **schedule_step(schedules.literal_stagger(LAYERS), BASE, W, max(3, args.steps // 5)))
+
+    other_schedules = None
+    if not args.no_schedules:
+        reps = max(3, args.steps // 5)
+        other_schedules = {
+            "what": "the training-order step of the same inputs under the pages' other schedules: the stagger "
+                    "reassigned layer -> 7 layer mod 16 (coprime), the power-of-2 base with the linear stagger, and "
+                    "the window sweep w = 6, 8, 10, 12 with the Fibonacci stagger (R = 1024 throughout)",
+            "coprime": schedule_step(schedules.coprime_stagger(LAYERS), BASE, W, reps),
+            "pow2_stagger": schedule_step(alphas, "pow2", W, reps),
         }
+        for w_s in (6, 8, 10, 12):
+            other_schedules[f"window_{w_s}"] = schedule_step(alphas, BASE, w_s, reps)
 
     per_row = alg_bytes_per_row()
     rows = rows_per_layer()
@@ -953,6 +956,7 @@ def main():
         "learned_alpha": learned,
         "rope": rope,
         "literal_stagger": literal,
+        "schedules": other_schedules,
         "short_context": short,
         "long_context": long_ctx,
         "cold": cold,
