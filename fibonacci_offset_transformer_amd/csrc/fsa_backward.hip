@@ -583,7 +583,7 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
                 if (s0 + u + kRingQ < min(n_off, unrolled_slabs(kRingQ))) fill(u, s0 + u + kRingQ);  // uniform
             }
         }
-        static_assert(unrolled_slabs(kRingQ) == 8, "the kept pair words cover slots 0..7");
+        static_assert(unrolled_slabs(kRingQ) >= 8, "the kept pair words cover slots 0..7");
         if (n_off > 0) {  // uniform
 #pragma unroll
             for (int h = 0; h < 2; ++h)

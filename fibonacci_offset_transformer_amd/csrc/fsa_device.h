@@ -352,9 +352,10 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kTileRows = 128;  // rows per LDS tile: the 64-row tile and its 64-row neighbour
 
-// Offsets handled by the unrolled, prefetching slab code for a ring of r slots:
-// whole groups of r covering at least the eight offsets of a window-64 table.
-constexpr int unrolled_slabs(int r) { return ((8 + r - 1) / r) * r; }
+// Offsets handled by the unrolled, prefetching slab code of the backward for a ring of
+// r slots: whole groups of r covering at least twelve offsets (a window-64 table has
+// up to eight; the narrow windows of the pages' sweep, 6 to 12, have 8 to 12).
+constexpr int unrolled_slabs(int r) { return ((12 + r - 1) / r) * r; }
 
 // Copies rows [row0, row0 + 128) of a [n, 64] bf16 matrix into an LDS tile of 128
 // rows of 128 bytes. The eight 16-byte chunks of tile row r are stored XOR-swizzled:
