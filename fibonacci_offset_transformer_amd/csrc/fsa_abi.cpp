@@ -641,16 +641,20 @@ fsa_status_t check_rope_path(fsa_dtype_t dt, int32_t w, int32_t N, float scale, 
 }
 
 struct RopeLayout {
-    uint64_t qhat, khat, delta, pairs, fwd, bwd;  // byte offsets into ws and the two sizes
-    int64_t words;                                // pair words of the static backward's workspace
+    uint64_t qhat, khat, fflags, fstatus, delta, pairs, fwd, bwd;  // byte offsets into ws and the two sizes
+    int64_t words;                                                // pair words of the static backward's workspace
 };
 
+// The forward's part: rotated Q rows, rotated K rows, then the forward's per-tile tokens
+// and status word (the forward that rotates K itself, B * H a multiple of 8).
 RopeLayout rope_layout(int64_t bh, int32_t n, int32_t n_off, int32_t w) {
     RopeLayout l;
     const uint64_t rows = static_cast<uint64_t>(bh) * n;
     l.qhat = 0;
     l.khat = fsa::align256(rows * 128);
-    l.fwd = l.khat + fsa::align256(rows * 128);
+    l.fflags = l.khat + fsa::align256(rows * 128);
+    l.fstatus = l.fflags + 8ull * static_cast<uint64_t>(bh) * ((n + 63) / 64);
+    l.fwd = fsa::align256(l.fstatus + 8);
     l.delta = l.fwd;
     l.pairs = l.delta + fsa::align256(rows * 4);
     l.words = fsa::pair_words(FSA_BF16, w, n, bh, n_off);
@@ -717,15 +721,25 @@ fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
         return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
                     static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.fwd));
     char *wsb = static_cast<char *>(ws);
-    // K is rotated once per row by the rotation pass; the forward kernel rotates its own Q
-    // rows and leaves them in ws beside the rotated K (for the backward to reuse)
-    const void *xs[] = {k};
-    void *hats[] = {wsb + l.khat};
     const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const hipError_t e = rotate_rows(xs, hats, 1, rope, static_cast<int64_t>(B) * H * N, N, hs);
-    if (e != hipSuccess) return launched(e, "rotary rotation");
+    // The forward kernel rotates its own Q rows (and leaves them in ws with keep_rotated).
+    // With B * H a multiple of 8 (each XCD holds whole heads) it also rotates K: every tile
+    // rotates the band rows it copies and stores its own rows in ws, where the other tiles'
+    // slabs read them once its token is set. Otherwise a rotation pass rotates K first.
     p.q = q;
-    p.k = hats[0];
+    if (static_cast<int64_t>(B) * H % 8 == 0) {
+        p.k = k;
+        p.khat = wsb + l.khat;
+        p.flags = reinterpret_cast<uint64_t *>(wsb + l.fflags);
+        p.status = reinterpret_cast<uint64_t *>(wsb + l.fstatus);
+        set_wait_limits(p);
+    } else {
+        const void *xs[] = {k};
+        void *hats[] = {wsb + l.khat};
+        const hipError_t e = rotate_rows(xs, hats, 1, rope, static_cast<int64_t>(B) * H * N, N, hs);
+        if (e != hipSuccess) return launched(e, "rotary rotation");
+        p.k = hats[0];
+    }
     p.v = v;
     p.out = o;
     p.lse_out = lse;
@@ -1009,6 +1023,18 @@ fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int3
         one_launch = words > 0 && n_off > 0 && bh % 8 == 0;
         flags = pairs + fsa::pair_ws_flags_offset(words);
         status = pairs + fsa::pair_ws_status_offset(words, bh, N);
+    } else if (kind == FSA_WS_ROPE_FORWARD) {
+        const Shape s{B, H, N, d};
+        if ((st = check_common(dt, dt, s, 1.0f)) != FSA_OK) return st;
+        int32_t tab[FSA_MAX_OFFSETS];
+        const int n_all = build_table(base, alpha, w, R, tab, &st);
+        if (n_all < 0) return st;
+        if ((st = check_rope_path(dt, w, N, 1.0f, N, n_all)) != FSA_OK) return st;
+        const RopeLayout l = rope_layout(bh, N, trim_offsets(tab, n_all, N), w);
+        need = l.fwd;
+        one_launch = bh * N > 0 && bh % 8 == 0;
+        flags = l.fflags;
+        status = l.fstatus;
     } else if (kind == FSA_WS_FRAC_BACKWARD || kind == FSA_WS_ROPE_FRAC_BACKWARD) {
         fsa::AttnParams p{};
         if ((st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R)) != FSA_OK) return st;

@@ -233,58 +233,6 @@ __global__ void __launch_bounds__(kThreads) bwd_generic_kernel(const AttnParams 
 constexpr int kRingQ = 4, kPreQ = 2;    // dQ kernel: slab slots in the ring; slots requested before the band
 constexpr int kRingKV = 3, kPreKV = 1;  // dK/dV kernel
 
-// ---- one-launch backward: per-tile completion tokens ----
-//
-// A token names one launch: the dispatch id (the packet's index in its queue, which
-// grows by one per dispatch) mixed with the queue's address (each queue counts from
-// zero). The dQ work of a tile writes it to that tile's flag; a workspace's earlier
-// contents, earlier launches' tokens included, do not match it.
-extern "C" __device__ uint64_t fsa_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
-__device__ __forceinline__ uint64_t launch_token() {
-    const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
-    return fsa_dispatch_id() ^ (q * 0x9E3779B97F4A7C15ull);
-}
-
-// Cache policy (sc0) for the pair words and D that another workgroup of the same launch
-// wrote, in the same XCD's L2. No CU reads them before their token is set, so no L1
-// holds an older copy.
-constexpr int kCachePastL1 = 1;
-// Waits until flags[first .. last] all hold the token (one wave; lane l checks flags
-// first + l, first + l + 64, ...; device-scope loads, which miss this CU's L1). Each
-// poll requests up to 64 * BATCH flags before comparing any, so that it costs one
-// round trip for up to that many tiles. The wait is bounded (p.max_polls polls with a
-// short sleep between them) and looks for token ^ p.token_xor (the token itself unless
-// the host forces a give-up). Returns false, uniformly over the wave, if it gave up;
-// the caller then records the launch's token in p.status and stores NaN so that the
-// failure shows.
-template <int BATCH = 1>
-__device__ __forceinline__ bool poll_tiles(const AttnParams &p, const uint64_t *flags, int first, int last,
-                                           uint64_t token, int lane) {
-    const uint64_t want = token ^ p.token_xor;
-    for (int spin = 0;; ++spin) {
-        bool ready = true;
-        for (int base = first + lane; base <= last; base += 64 * BATCH) {
-            // every lane loads (indices past `last` read `last` again), without branches,
-            // so that the loads leave back to back
-            uint64_t v[BATCH];
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k)
-                v[k] = __hip_atomic_load(flags + min(base + 64 * k, last), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-            for (int k = 0; k < BATCH; ++k) ready &= (base + 64 * k > last) | (v[k] == want);
-        }
-        if (__builtin_amdgcn_ballot_w64(!ready) == 0) return true;
-        if (spin >= p.max_polls) return false;
-        __builtin_amdgcn_s_sleep(4);
-    }
-}
-
-// Records that a wait of this launch gave up: the status word takes the launch's token
-// (read back by the host, see fsa_wait_status).
-__device__ __forceinline__ void record_give_up(const AttnParams &p, uint64_t token) {
-    __hip_atomic_store(p.status, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Descriptor over the pair-workspace words of head bh ([N, S, WORDS] words, S =
 // pair_slots): rows past the sequence end read as zero words.
 template <int WORDS>

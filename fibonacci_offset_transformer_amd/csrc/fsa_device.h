@@ -452,6 +452,9 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Waits until the wave's LDS operations have completed (vector memory counter left alone).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Per-lane element offsets into a swizzled tile, for blocks of 16 rows starting at a
 // multiple of 8 (the swizzle then depends on the lane only, so a block's rows add a
 // constant that the LDS instructions take as an immediate).
@@ -827,6 +830,61 @@ hipError_t with_table_length(int n_off, F &&f) {
     default: return f(Len<0>{});
     }
 }
+
+// ----------------------------------------------------------------------------
+// Per-tile completion tokens within one launch (one-launch backward, rotary forward)
+// ----------------------------------------------------------------------------
+//
+// A token names one launch: the dispatch id (the packet's index in its queue, which
+// grows by one per dispatch) mixed with the queue's address (each queue counts from
+// zero). A tile whose words others read writes it to that tile's flag once they are in
+// L2; a workspace's earlier contents, earlier launches' tokens included, do not match it.
+extern "C" __device__ uint64_t fsa_dispatch_id() __asm("llvm.amdgcn.dispatch.id");
+__device__ __forceinline__ uint64_t launch_token() {
+    const uint64_t q = reinterpret_cast<uint64_t>(__builtin_amdgcn_queue_ptr());
+    return fsa_dispatch_id() ^ (q * 0x9E3779B97F4A7C15ull);
+}
+
+// Cache policy (sc0) for words that another workgroup of the same launch wrote, in the
+// same XCD's L2 (pair words, D, rotated K rows). No CU reads them before their token is
+// set, and this one bypasses the L1, so no older copy is read.
+constexpr int kCachePastL1 = 1;
+// Waits until flags[first .. last] all hold the token (one wave; lane l checks flags
+// first + l, first + l + 64, ...; device-scope loads, which miss this CU's L1). Each
+// poll requests up to 64 * BATCH flags before comparing any, so that it costs one
+// round trip for up to that many tiles. The wait is bounded (p.max_polls polls with a
+// short sleep between them) and looks for token ^ p.token_xor (the token itself unless
+// the host forces a give-up). Returns false, uniformly over the wave, if it gave up;
+// the caller then records the launch's token in p.status and stores NaN so that the
+// failure shows.
+template <int BATCH = 1>
+__device__ __forceinline__ bool poll_tiles(const AttnParams &p, const uint64_t *flags, int first, int last,
+                                           uint64_t token, int lane) {
+    const uint64_t want = token ^ p.token_xor;
+    for (int spin = 0;; ++spin) {
+        bool ready = true;
+        for (int base = first + lane; base <= last; base += 64 * BATCH) {
+            // every lane loads (indices past `last` read `last` again), without branches,
+            // so that the loads leave back to back
+            uint64_t v[BATCH];
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k)
+                v[k] = __hip_atomic_load(flags + min(base + 64 * k, last), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int k = 0; k < BATCH; ++k) ready &= (base + 64 * k > last) | (v[k] == want);
+        }
+        if (__builtin_amdgcn_ballot_w64(!ready) == 0) return true;
+        if (spin >= p.max_polls) return false;
+        __builtin_amdgcn_s_sleep(4);
+    }
+}
+
+// Records that a wait of this launch gave up: the status word takes the launch's token
+// (read back by the host, see fsa_wait_status).
+__device__ __forceinline__ void record_give_up(const AttnParams &p, uint64_t token) {
+    __hip_atomic_store(p.status, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 
 }  // namespace
 }  // namespace fsa

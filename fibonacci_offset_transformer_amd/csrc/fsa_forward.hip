@@ -146,11 +146,17 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
 // With FRAC the table holds fractional entries (learned-alpha variant): entry t's key
 // and value for row i are (1 - phi) row(i - off[t]) + phi row(i - off[t] - 1), so each
 // entry reads two adjacent slabs (near and far); entries go two per softmax update.
-// With ROPE, Q arrives unrotated (K, V as usual): the kernel rotates its own query rows
-// by the table p.rope and, when p.qhat is set, stores the rotated rows there (for a
-// backward to reuse).
-template <bool OUT_BF16, bool FRAC, bool ROPE = false, int NOFF = 0>
+// With ROPE, Q arrives unrotated: the kernel rotates its own query rows by the table
+// p.rope and, when p.qhat is set, stores the rotated rows there (for a backward to
+// reuse). K arrives rotated (a rotation pass ran first), or, with FUSEK, unrotated: then
+// each tile rotates the band rows it copied into LDS, stores its own 64 rows to p.khat,
+// publishes this launch's token in its flag once they are in L2, and reads its slab K
+// rows from p.khat after the tiles that hold them have published (earlier tiles of the
+// same head, dispatched before it on the same XCD, so the waits end; bounded, as in the
+// one-launch backward, with NaN output and the status word if a wait gives up).
+template <bool OUT_BF16, bool FRAC, bool ROPE = false, int NOFF = 0, bool FUSEK = false>
 __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p) {
+    static_assert(!FUSEK || (ROPE && !FRAC), "the in-kernel K rotation belongs to the static rotary forward");
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ks[kTileRows * 64];  // band K rows, then merge areas
     __shared__ __attribute__((aligned(16))) uint16_t vs[kTileRows * 64];  // band V rows, then band row stats
@@ -171,8 +177,11 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + head;
     const uint16_t *K = static_cast<const uint16_t *>(p.k) + head;
     const uint16_t *V = static_cast<const uint16_t *>(p.v) + head;
-    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, span_bytes(n, 128)), rk = head_rsrc(K, span_bytes(n, 128));
+    // slab K rows: the caller's (pre-rotated) K, or with FUSEK the rotated rows the tiles store
+    const uint16_t *KS = FUSEK ? static_cast<const uint16_t *>(p.khat) + head : K;
+    const __amdgpu_buffer_rsrc_t rq = head_rsrc(Q, span_bytes(n, 128)), rk = head_rsrc(KS, span_bytes(n, 128));
     const __amdgpu_buffer_rsrc_t rv = head_rsrc(V, span_bytes(n, 128));
+    constexpr int kSlabK = FUSEK ? kCachePastL1 : kCacheNormal;  // rows other tiles wrote in this launch
     const float sl2 = p.scale_log2;
     const int i = r0 + c16;  // MFMA-layout query row
     const bool row_ok = i < n;
@@ -186,19 +195,70 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         rope_entries(rt, i - i0, g, a01, a23);      // chunk g: pairs 4g .. 4g + 3
         rope_entries(rt, i - i0, g + 4, b01, b23);  // chunk g + 4
     }
+    // FUSEK: the band's K rows are rotated in LDS once they have all landed. The tile's own
+    // rows (tile rows 64..127, positions i0 ..) take the query rows' table entries (lane
+    // (c16, g) of wave w: row 16 w + c16, chunks g and g + 4); the rows before it (tile
+    // rows 0..63) take entries of their own, two chunks per lane (positions before 0
+    // read as zeros)
+    [[maybe_unused]] f32x4_t ktab[2][2];
+    if constexpr (FUSEK) {
+        const int pos0 = max(i0 - 64, 0);
+        const __amdgpu_buffer_rsrc_t rb = head_rsrc(p.rope + (int64_t)pos0 * 64, span_bytes(min(64, n - pos0), 256));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int idx = threadIdx.x + 256 * j;  // chunk idx & 7 of tile row idx >> 3
+            rope_entries(rb, i0 - 64 + (idx >> 3) - pos0, idx & 7, ktab[j][0], ktab[j][1]);
+        }
+    }
     dma_tile(ks, K, i0 - 64, n, wave, lane);
     Frag<true> qf;
     buf_frag(qf, rq, i, g);
-    dma_tile(vs, V, i0 - 64, n, wave, lane);
+    // FUSEK: V follows the rotated K rows' stores, so that the wait for those stores (and
+    // with it the tile's token) does not wait for V
+    if constexpr (!FUSEK) dma_tile(vs, V, i0 - 64, n, wave, lane);
     // a bare barrier (the compiler's __syncthreads would first wait for every copy into LDS)
-    wait_vm<4>();  // the four V copies of this wave may still be in flight
+    if constexpr (FUSEK) wait_vm_all();
+    else wait_vm<4>();  // the four V copies of this wave may still be in flight
+    __asm__ volatile("" ::: "memory");
     if constexpr (ROPE) {
         qf.c[0] = rope_chunk(qf.c[0], a01, a23);
         qf.c[1] = rope_chunk(qf.c[1], b01, b23);
     }
+    if constexpr (FUSEK) {
+        // every wave's K copies have landed; rotate in place with the rotation pass's
+        // arithmetic, and store the tile's own rows for the other tiles' slabs and for a
+        // backward
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int idx = threadIdx.x + 256 * j, r = idx >> 3, c = idx & 7;
+            u32x4_t *slot = reinterpret_cast<u32x4_t *>(ks + r * 64 + 8 * (c ^ (r & 7)));
+            *slot = rope_chunk(*slot, ktab[j][0], ktab[j][1]);
+        }
+        uint16_t *KH = static_cast<uint16_t *>(p.khat) + head;
+        const int r = 64 + 16 * wave + c16, pos = i0 + 16 * wave + c16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int c = g + 4 * h;
+            u32x4_t *slot = reinterpret_cast<u32x4_t *>(ks + r * 64 + 8 * (c ^ (r & 7)));
+            const u32x4_t x = rope_chunk(*slot, h == 0 ? a01 : b01, h == 0 ? a23 : b23);
+            *slot = x;
+            if (pos < n) *reinterpret_cast<u32x4_t *>(KH + (int64_t)pos * 64 + 8 * c) = x;
+        }
+        dma_tile(vs, V, i0 - 64, n, wave, lane);
+        wait_vm<4>();  // the stores have reached L2; the four V copies may still be in flight
+        wait_lds();    // the rotated rows are in LDS before the barrier lets the other waves read them
+    }
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
+    [[maybe_unused]] uint64_t token = 0;
+    if constexpr (FUSEK) {
+        // every wave's rotated rows are in L2: this tile's token goes out
+        token = launch_token();
+        if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // the first slab rows are requested now and land while the band runs; most of them
     // are rows of neighbouring tiles whose band copies have just passed through L2
     SFrag sk[4], sv[4];  // FRAC: slot u of entries holds near rows in [2u], far rows in [2u + 1]
@@ -217,7 +277,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (u < n_off) {  // uniform
-                sfrag_load(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+                if constexpr (!FUSEK)  // with FUSEK the K rows follow the wait for their tiles
+                    sfrag_load(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
                 sfrag_load(sv[u], rv, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
             }
         }
@@ -283,9 +344,14 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             lsum_b += pr[b][r];
         }
     // the V copies were issued before the slab loads (at most 4 x 4 of them per wave; the
-    // learned-alpha ring always requests its 16)
-    if (FRAC || n_off >= 4) wait_vm<16>();
-    else wait_vm_all();
+    // learned-alpha ring always requests its 16; with FUSEK 4 x 2, the V rows only)
+    if constexpr (FUSEK) {
+        if (n_off >= 4) wait_vm<8>();
+        else wait_vm_all();
+    } else {
+        if (FRAC || n_off >= 4) wait_vm<16>();
+        else wait_vm_all();
+    }
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
@@ -293,6 +359,30 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     mma_over_rows_tr2(acc_b, vs_w, 32, 48, tl, pr[2], pr[3]);
     mma_over_rows_tr(acc_b, vs_w, 64, tl, pr[4]);
     const float l_b = group_sum(lsum_b);
+
+    // FUSEK: wait for the tiles whose rotated rows the slabs read, then request them
+    [[maybe_unused]] float o_mul = 1.f;  // NaN if the wait gave up, so that it shows
+    if constexpr (FUSEK) {
+        __shared__ int gave_up;
+        if (wave == 0) {
+            // key rows row - off[t] of rows [i0, i0 + 64): tiles (i0 - max off) / 64 .. this
+            // one (its own rows it stored itself); earlier tiles only
+            const int first = max(0, i0 - p.off[n_off > 0 ? n_off - 1 : 0]) >> 6;
+            bool ok = true;
+            if (n_off > 0 && first < tile)  // uniform
+                ok = poll_tiles(p, p.flags + (int64_t)bh * nt, first, tile - 1, token, lane);
+            if (lane == 0) {
+                gave_up = ok ? 0 : 1;
+                if (!ok) record_give_up(p, token);
+            }
+        }
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(gave_up)) o_mul = __builtin_nanf("");
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (u < n_off)  // uniform
+                sfrag_load<kSlabK>(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+    }
 
     // ---- the band state, moved into the slab layout, starts the slabs' online softmax ----
     __syncthreads();  // every wave is done with the band tiles
@@ -401,7 +491,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                     }
                 }
                 if (t0 == 0 && u + 4 < n_off)  // uniform
-                    sfrag_load(sk[u], rk, slab_row(p, n_off, u + 4, row_s[0], -1), slab_row(p, n_off, u + 4, row_s[1], -1), c8);
+                    sfrag_load<kSlabK>(sk[u], rk, slab_row(p, n_off, u + 4, row_s[0], -1), slab_row(p, n_off, u + 4, row_s[1], -1), c8);
             }
             const float mn[2] = {fmaxf(m_s[0], gm[0] * sl2), fmaxf(m_s[1], gm[1] * sl2)};
             rescale(mn);
@@ -423,7 +513,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
         for (int t = 8; t < n_off; ++t) {  // tables longer than eight offsets
             if (r0 + 15 < p.off[t]) break;
             SFrag kt, vt;
-            sfrag_load(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
+            sfrag_load<kSlabK>(kt, rk, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
             sfrag_load(vt, rv, row_s[0] - p.off[t], row_s[1] - p.off[t], c8);
             float sv1[2];
 #pragma unroll
@@ -449,8 +539,11 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             // hardware reciprocal and log2 (1 ulp): l >= 1, since the row maximum's term is 1.
             // O goes out with non-temporal stores, which keep it from evicting the K and V
             // rows that other workgroups' slabs still gather from L2
-            store_chunk<true>(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], __builtin_amdgcn_rcpf(l_s[h]));
-            if (c8 == 0) p.lse_out[(int64_t)bh * n + row_s[h]] = (m_s[h] + __builtin_amdgcn_logf(l_s[h])) * kLn2;
+            const float rl = FUSEK ? __builtin_amdgcn_rcpf(l_s[h]) * o_mul : __builtin_amdgcn_rcpf(l_s[h]);
+            store_chunk<true>(static_cast<OE *>(p.out) + head, row_s[h], c8, acc_s[h], rl);
+            if (c8 == 0)
+                p.lse_out[(int64_t)bh * n + row_s[h]] =
+                    FUSEK ? (m_s[h] + __builtin_amdgcn_logf(l_s[h])) * kLn2 * o_mul : (m_s[h] + __builtin_amdgcn_logf(l_s[h])) * kLn2;
         }
     }
 }
@@ -623,6 +716,9 @@ hipError_t launch_dense_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnPa
 hipError_t launch_rope_forward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     return with_table_length(p.n_off, [&](auto len) {
         constexpr int L = decltype(len)::value;
+        if (p.khat)  // K rotated in the kernel (the caller set the flags and the status word)
+            return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false, true, L, true>, tiles(p), p, s)
+                                      : launch(&fwd_window_kernel<false, false, true, L, true>, tiles(p), p, s);
         return out_dt == FSA_BF16 ? launch(&fwd_window_kernel<true, false, true, L>, tiles(p), p, s)
                                   : launch(&fwd_window_kernel<false, false, true, L>, tiles(p), p, s);
     });

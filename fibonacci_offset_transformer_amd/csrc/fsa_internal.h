@@ -47,6 +47,8 @@ struct AttnParams {
     // its position's angles before storing them (table [n_pos, 32, 2] of cos, sin).
     const float *rope;
     void *qhat;               // rotary forward: rotated Q rows written here [BH, N, 64]
+    void *khat;               // rotary forward with the K rotation in the kernel: the rotated K
+                              // rows [BH, N, 64], written by their tile and read by the slabs
     // One-launch backward: one 64-bit completion token per tile [BH * tiles per head], and
     // the status word a waiting workgroup that gave up sets to the launch's token.
     uint64_t *flags;

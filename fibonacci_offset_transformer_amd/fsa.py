@@ -33,7 +33,8 @@ EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_wor
            "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
            "fsa_rope_frac_workspace_bytes", "fsa_rope_frac_forward", "fsa_rope_frac_backward", "fsa_wait_status",
            "fsa_backward_noalloc", "fsa_debug_force_wait_timeout", "fsa_last_error")
-WS_KINDS = {"backward": 0, "frac_backward": 1, "rope_backward": 2, "rope_frac_backward": 3, "backward_noalloc": 4}
+WS_KINDS = {"backward": 0, "frac_backward": 1, "rope_backward": 2, "rope_frac_backward": 3, "backward_noalloc": 4,
+            "rope_forward": 5}
 
 
 class FsaError(RuntimeError):

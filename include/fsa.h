@@ -385,7 +385,8 @@ fsa_status_t fsa_rope_rotate(fsa_dtype_t dt, const void *x, const float *rope, i
 
 /*
  * fsa_rope_workspace_bytes - bytes of ws the rotary forward and backward need:
- * forward 2 B H N d * 2 (the rotated Q and K, each part rounded up to 256 bytes);
+ * forward 2 B H N d * 2 (the rotated Q and K, each part rounded up to 256 bytes) plus
+ * 8 bytes per 64-row tile and an 8-byte status word (rounded up to 256);
  * backward that plus 4 B H N (D) plus fsa_backward_workspace_bytes for the same window
  * (pair words, tokens and status word).
  * Arguments as in fsa_rope_forward; 0 and 0 for an empty problem.
@@ -401,11 +402,19 @@ fsa_status_t fsa_rope_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H, int3
  *   o, lse          outputs as in fsa_forward
  *   ws, ws_bytes    caller-owned device workspace of at least the forward size of
  *                   fsa_rope_workspace_bytes, 16-byte aligned, overwritten (holds
- *                   the rotated K, and the rotated Q when keep_rotated)
+ *                   the rotated K, the rotated Q when keep_rotated, and per-tile
+ *                   tokens); its contents on entry do not matter
  *   keep_rotated    nonzero: the rotated Q rows are also stored in ws, so that
  *                   fsa_rope_backward can reuse them (reuse_rotated); 0 (inference)
- *                   skips that store. K is rotated by a separate pass over its rows;
- *                   the attention kernel rotates its own Q rows.
+ *                   skips that store. The attention kernel rotates its own Q rows.
+ *                   With B * H a multiple of 8 it rotates K as well: each 64-row tile
+ *                   rotates the K rows it copies for its window, stores its own rows
+ *                   in ws and publishes a token, and the tiles whose sparse offsets
+ *                   reach those rows read them there after a bounded wait for the
+ *                   token (as in fsa_backward's one-launch path: a wait that gives up
+ *                   stores NaN O and LSE for its tile and sets the status word that
+ *                   fsa_wait_status reads with FSA_WS_ROPE_FORWARD). Otherwise a
+ *                   separate pass rotates K first.
  *   other arguments as in fsa_forward
  */
 fsa_status_t fsa_rope_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q, const void *k, const void *v,
@@ -490,26 +499,30 @@ fsa_status_t fsa_backward_noalloc(fsa_dtype_t dt, fsa_dtype_t out_dt, const void
                                   float scale, fsa_base_t base, double alpha, int32_t w, int32_t R, void *stream);
 
 /*
- * fsa_wait_status - whether the last one-launch backward that ran with a workspace
- * gave up one of its bounded waits.
+ * fsa_wait_status - whether the last one-launch backward (or rotary forward that
+ * rotates K itself) that ran with a workspace gave up one of its bounded waits.
  *
  * The one-launch backward (B * H a multiple of 8, sparse offsets below N) is correct
  * only if the GPU dispatches its workgroups in block order and places block b on XCD
  * b mod 8; its dK/dV workgroups then never wait for a workgroup that has not started.
- * Each wait is bounded nonetheless: a workgroup that gives up stores NaN dK and dV
- * (and the learned-alpha reduction NaN dalpha) instead of hanging, and writes the
- * launch's token into the workspace's status word. This call reads that word and the
- * token of the workspace's most recent launch (published by its first tile, whose
- * work never waits) and reports whether they match. It synchronises `stream` and
- * copies 16 bytes to the host (the one call of the library that waits). Call it after
- * the backward, with the same arguments, before the workspace is reused.
+ * The rotary forward with B * H a multiple of 8 rests on the same two facts (its tiles
+ * wait only for earlier tiles of their head). Each wait is bounded nonetheless: a
+ * workgroup that gives up stores NaN results (dK and dV; the learned-alpha reduction's
+ * dalpha; the rotary forward's O and LSE) instead of hanging, and writes the launch's
+ * token into the workspace's status word. This call reads that word and the token of
+ * the workspace's most recent launch (published by its first tile, whose work never
+ * waits) and reports whether they match. It synchronises `stream` and copies 16 bytes
+ * to the host (the one call of the library that waits). Call it after the backward or
+ * forward, with the same arguments, before the workspace is reused.
  *
  *   kind        which call's workspace: FSA_WS_BACKWARD (fsa_backward,
  *               fsa_backward_grads: pair_ws), FSA_WS_FRAC_BACKWARD (fsa_frac_backward:
  *               ws), FSA_WS_ROPE_BACKWARD (fsa_rope_backward: ws),
  *               FSA_WS_ROPE_FRAC_BACKWARD (fsa_rope_frac_backward: ws),
  *               FSA_WS_BACKWARD_NOALLOC (fsa_backward_noalloc: the library's scratch
- *               on the current device; ws and ws_bytes are ignored)
+ *               on the current device; ws and ws_bytes are ignored),
+ *               FSA_WS_ROPE_FORWARD (fsa_rope_forward: ws; its waits are those of the
+ *               tiles that read rotated K rows other tiles stored)
  *   dt, B, H, N, d, base, alpha, w, R   the arguments the backward ran with
  *   ws, ws_bytes   that workspace and its size
  *   gave_up     receives 1 if a wait of that launch gave up, else 0 (also 0 when the
@@ -521,7 +534,8 @@ typedef enum {
     FSA_WS_FRAC_BACKWARD = 1,
     FSA_WS_ROPE_BACKWARD = 2,
     FSA_WS_ROPE_FRAC_BACKWARD = 3,
-    FSA_WS_BACKWARD_NOALLOC = 4
+    FSA_WS_BACKWARD_NOALLOC = 4,
+    FSA_WS_ROPE_FORWARD = 5
 } fsa_ws_kind_t;
 fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int32_t H, int32_t N, int32_t d,
                              fsa_base_t base, double alpha, int32_t w, int32_t R, const void *ws,
@@ -529,10 +543,10 @@ fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int3
 
 /*
  * fsa_debug_force_wait_timeout - diagnostic hook for tests of the failure path (not
- * part of the method). With enable != 0, later one-launch backward calls of this
- * process wait for a value no workgroup publishes and give up after 16 polls, so every
- * kernel still exits and fsa_wait_status then reports the give-up; enable = 0 restores
- * normal waits. Process-wide; returns FSA_OK.
+ * part of the method). With enable != 0, later one-launch backward and rotary forward
+ * calls of this process wait for a value no workgroup publishes and give up after 16
+ * polls, so every kernel still exits and fsa_wait_status then reports the give-up;
+ * enable = 0 restores normal waits. Process-wide; returns FSA_OK.
  */
 fsa_status_t fsa_debug_force_wait_timeout(int32_t enable);
 

@@ -108,7 +108,9 @@ def test_rope_workspace_sizes(lib):
     f, b = ctypes.c_uint64(1), ctypes.c_uint64(1)
     assert lib.fsa_rope_workspace_bytes(1, 2, 8, 4096, 64, 0, 1.0, 64, 1024, ctypes.byref(f), ctypes.byref(b)) == 0
     rows = 2 * 8 * 4096
-    fwd = 2 * a256(rows * 128)
+    # rotated Q and K, then one 64-bit token per 64-row tile and the status word (the
+    # forward that rotates K itself)
+    fwd = 2 * a256(rows * 128) + a256(8 * 16 * 64 + 8)
     assert f.value == fwd
     # six offsets at alpha = 1, w = 64, R = 1024 -> 8 slots, then one 64-bit token per tile
     # and the status word
@@ -117,7 +119,7 @@ def test_rope_workspace_sizes(lib):
     # a narrower window carries each pair as two words: w = 16 at N = 64 (offsets 21, 34, 55)
     assert lib.fsa_rope_workspace_bytes(1, 1, 2, 64, 64, 0, 1.0, 16, 256, ctypes.byref(f), ctypes.byref(b)) == 0
     rows = 2 * 64
-    assert b.value == 2 * a256(rows * 128) + a256(4 * rows) + a256(a256(8 * 8 * rows) + 8 * 2 + 8)
+    assert b.value == 2 * a256(rows * 128) + a256(8 * 2 + 8) + a256(4 * rows) + a256(a256(8 * 8 * rows) + 8 * 2 + 8)
     assert lib.fsa_rope_workspace_bytes(1, 0, 8, 4096, 64, 0, 1.0, 64, 1024, ctypes.byref(f), ctypes.byref(b)) == 0
     assert f.value == 0 and b.value == 0
     assert lib.fsa_rope_workspace_bytes(0, 1, 1, 64, 64, 0, 1.0, 64, 1024, ctypes.byref(f), ctypes.byref(b)) \

@@ -168,9 +168,11 @@ def test_rope_full_size_stagger_layers():
         rope_bwd_case(63, 2, 8, 4096, "fib", alphas[l], 64, 1024, heads=[(b, h)], layer=l, given=False)
 
 
-def test_fused_forward_equals_rotate_then_forward():
-    # the rotated rows the fused call hands to the attention are the rotation step's
-    x = inputs(64, 0, (2, 4, 900, 64), grad=True)
+@pytest.mark.parametrize("H", [3, 4], ids=["rotation_pass", "rotation_in_kernel"])
+def test_fused_forward_equals_rotate_then_forward(H):
+    # the rotated rows the fused call hands to the attention are the rotation step's, bit
+    # for bit, whether a pass rotates K first or the attention kernel's tiles do (B * H = 8)
+    x = inputs(64, 0, (2, H, 900, 64), grad=True)
     table = fsa.rope_table(900, device=dev())
     kw = dict(alpha=1.3, w=64, R=1024, scale=0.125)
     o1, l1 = fsa.rope_forward(x["q"], x["k"], x["v"], table, **kw)
@@ -198,11 +200,13 @@ def test_rope_workspace_contents_do_not_matter_and_deterministic():
     assert all(bool(torch.isfinite(t).all()) for t in runs[0])
 
 
-def test_backward_reusing_the_forward_rotation_is_identical():
-    x = inputs(66, 0, (2, 3, 1234, 64), grad=True)
+@pytest.mark.parametrize("H", [3, 4], ids=["rotation_pass", "rotation_in_kernel"])
+def test_backward_reusing_the_forward_rotation_is_identical(H):
+    # B * H = 8: the forward rotates K in the kernel and stores the tiles' rows; else a pass
+    x = inputs(66, 0, (2, H, 1234, 64), grad=True)
     table = fsa.rope_table(1234, device=dev())
     kw = dict(alpha=1.17, w=64, R=1024, scale=0.125)
-    need = fsa.rope_workspace_bytes(torch.bfloat16, 2, 3, 1234, alpha=1.17, w=64, R=1024)[1]
+    need = fsa.rope_workspace_bytes(torch.bfloat16, 2, H, 1234, alpha=1.17, w=64, R=1024)[1]
     ws = torch.empty(need // 4 + 1, dtype=torch.int32, device=dev())
     o, lse = fsa.rope_forward(x["q"], x["k"], x["v"], table, ws=ws, **kw)
     g1 = fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], ws=ws, reuse_rotated=True, **kw)

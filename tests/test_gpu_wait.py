@@ -120,3 +120,28 @@ def test_rope_give_up_is_reported():
     assert gave_up and bool(torch.isnan(g[1].float()).all())
     fsa.rope_backward(x["q"], x["k"], x["v"], table, o, lse, x["do"], ws=ws, **kw)
     assert not fsa.wait_status("rope_backward", x["q"], ws, alpha=1.2, w=64, R=1024)
+
+
+def test_rope_forward_give_up_is_reported():
+    # B * H = 8: the rotary forward rotates K in the kernel; tiles read the rotated rows of
+    # earlier tiles after waiting for their tokens. Tile 0 of each head waits for none.
+    x = inputs(124, (2, 4, 300, 64))
+    table = fsa.rope_table(300, device=dev())
+    kw = dict(alpha=1.2, w=64, R=1024, scale=0.125)
+    need = fsa.rope_workspace_bytes(torch.bfloat16, 2, 4, 300, alpha=1.2, w=64, R=1024)[0]
+    ws = torch.empty(need // 4 + 1, dtype=torch.int32, device=dev())
+    o0, l0 = fsa.rope_forward(x["q"], x["k"], x["v"], table, ws=ws, **kw)
+    assert not fsa.wait_status("rope_forward", x["q"], ws, alpha=1.2, w=64, R=1024)
+    fsa.debug_force_wait_timeout(True)
+    try:
+        o1, l1 = fsa.rope_forward(x["q"], x["k"], x["v"], table, ws=ws, **kw)
+        gave_up = fsa.wait_status("rope_forward", x["q"], ws, alpha=1.2, w=64, R=1024)
+    finally:
+        fsa.debug_force_wait_timeout(False)
+    note(f"rope forward forced give-up reported: {gave_up}")
+    assert gave_up
+    assert torch.equal(o1[:, :, :64], o0[:, :, :64]) and torch.equal(l1[:, :, :64], l0[:, :, :64])
+    assert bool(torch.isnan(o1[:, :, 64:].float()).all()) and bool(torch.isnan(l1[:, :, 64:]).all())
+    o2, l2 = fsa.rope_forward(x["q"], x["k"], x["v"], table, ws=ws, **kw)
+    assert not fsa.wait_status("rope_forward", x["q"], ws, alpha=1.2, w=64, R=1024)
+    assert torch.equal(o2, o0) and torch.equal(l2, l0)
