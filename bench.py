@@ -562,9 +562,10 @@ def rope_bench(fsa, torch, dev, stream, bufs, alphas, scale, static_us, reps):
     rot_us = stage_us(torch, dev, stream, rot, reps)
     rot_bytes = B * H * N * (2 * D * ELEM)  # one tensor: read and write each row (the table stays in L2)
     return {
-        "what": "rotary embedding before the attention: Q and K rotated once per row into a workspace "
-                "(bf16, as a separate rotation step stores them), the static attention kernels on the "
-                "rotated rows, dQ and dK rotated back in the backward's store",
+        "what": "rotary embedding before the attention: the forward kernel rotates its query rows and its "
+                "tiles' K rows (bf16, as a separate rotation step stores them; each tile stores its own rotated "
+                "K rows for the other tiles' slabs and for the backward), the backward reuses the forward's "
+                "rotated rows or rotates them in a pass, and rotates dQ and dK back in its store",
         "fwd_us_per_layer": round(fwd_us, 3),
         "bwd_us_per_layer": round(bwd_us, 3),
         "static_fwd_us_per_layer": round(static_us["fwd"], 3),
