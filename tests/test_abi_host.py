@@ -327,6 +327,11 @@ def test_wait_status_checks(lib):
     assert wait_status(lib, kind=1, B=1, H=3, alpha=1.3, ws=P(0)) == (fsa.FSA_OK, 0)
     assert wait_status(lib, kind=2, B=1, H=3, ws=P(0)) == (fsa.FSA_OK, 0)
     assert wait_status(lib, kind=3, B=1, H=3, alpha=1.3, ws=P(0)) == (fsa.FSA_OK, 0)
+    # the rotary forward waits (it rotates K in the kernel) only with B * H a multiple of 8
+    assert wait_status(lib, kind=5, B=1, H=3, ws=P(0)) == (fsa.FSA_OK, 0)
+    assert wait_status(lib, kind=5, ws=P(0))[0] == fsa.FSA_E_ARG
+    assert wait_status(lib, kind=5, ws_bytes=16)[0] == fsa.FSA_E_ARG and b"ws holds" in lib.fsa_last_error()
+    assert wait_status(lib, kind=5, d=32)[0] == fsa.FSA_E_UNSUPPORTED
 
 
 def test_debug_force_wait_timeout_toggles(lib):
