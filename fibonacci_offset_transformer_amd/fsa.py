@@ -562,10 +562,11 @@ def rope_frac_backward(q, k, v, table, o, lse, dout, *, alpha: float, w: int, R:
 
 
 def wait_status(kind: str, q, ws, *, alpha: float = 1.0, w: int, R: int, base: str = "fib") -> bool:
-    """True if the last one-launch backward of `kind` ("backward", "frac_backward",
-    "rope_backward", "rope_frac_backward") that ran with workspace `ws` on q's shape gave
-    up one of its bounded waits (it then stored NaN gradients). Synchronises the current
-    stream (see fsa_wait_status)."""
+    """True if the last one-launch call of `kind` ("backward", "frac_backward",
+    "rope_backward", "rope_frac_backward", "backward_noalloc", or "rope_forward", the
+    rotary forward that rotates K in the kernel) that ran with workspace `ws` on q's shape
+    gave up one of its bounded waits (it then stored NaN results). Synchronises the
+    current stream (see fsa_wait_status)."""
     B, H, N, d = q.shape
     out = ctypes.c_int32(0)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
@@ -576,5 +577,5 @@ def wait_status(kind: str, q, ws, *, alpha: float = 1.0, w: int, R: int, base: s
 
 
 def debug_force_wait_timeout(enable: bool) -> None:
-    """Diagnostic hook: makes later one-launch backward waits give up (see fsa_debug_force_wait_timeout)."""
+    """Diagnostic hook: makes later one-launch waits give up (see fsa_debug_force_wait_timeout)."""
     _check(library().fsa_debug_force_wait_timeout(int(bool(enable))))
