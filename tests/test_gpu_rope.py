@@ -149,9 +149,33 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("H", [2, 4], ids=["rotation_pass", "rotation_in_kernel"])
 @pytest.mark.parametrize("N,base,alpha,w,R", SMALL)
-def test_rope_forward_small(N, base, alpha, w, R):
-    rope_fwd_case(61, 2, 2, N, base, alpha, w, R)
+def test_rope_forward_small(N, base, alpha, w, R, H):
+    # B * H = 8 takes the forward that rotates K in the kernel (tiles wait for the earlier
+    # tiles' rotated rows); B * H = 4 a rotation pass first
+    rope_fwd_case(61, 2, H, N, base, alpha, w, R)
+
+
+@pytest.mark.parametrize("base,alpha", [("pow2", 1.0), ("fib", 1.5)])
+def test_rope_forward_long_context_in_kernel_rotation(base, alpha):
+    # [1, 8, 32768]: 4096 tiles, more than the GPU holds at once, so tiles wait for tiles
+    # that may have finished long before; sampled rows of two heads against the oracle
+    B, H, N, w, R, scale = 1, 8, 32768, 64, 1024, 0.125
+    x = inputs(65 if base == "pow2" else 66, 0, (B, H, N, 64))
+    table = fsa.rope_table(N, device=dev())
+    note(f"rope forward long context {base} alpha={alpha} B={B} H={H} N={N}")
+    o, lse = fsa.rope_forward(x["q"], x["k"], x["v"], table, alpha=alpha, w=w, R=R, base=base, scale=scale,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    T = oracle.offset_table(base, alpha, w, R)
+    rng = np.random.default_rng(67)
+    rows = np.unique(np.concatenate([np.arange(70), np.arange(N - 70, N), rng.integers(0, N, 200)]))
+    for h in (0, 5):
+        q, k, v = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v"))
+        ro, rl = oracle.rope_sparse_forward_rows(q, k, v, T, w, scale, rows, stored=True)
+        check(f"o[0,{h}] sampled", o[0, h].cpu()[rows], ro)
+        check(f"lse[0,{h}] sampled", lse[0, h].cpu()[rows], rl)
 
 
 @pytest.mark.parametrize("N,base,alpha,w,R", SMALL)
