@@ -24,6 +24,7 @@ import pytest
 import torch
 
 import oracle
+import rope_rounding
 from fibonacci_offset_transformer_amd import fsa, schedules, synth
 
 pytestmark = pytest.mark.gpu
@@ -306,7 +307,8 @@ def _entry_l1(q, k, v, do, o_given, tab, w, scale):
 def test_rope_frac_against_oracle(N, alpha, w, R):
     """Forward against the oracle over the stored rotated rows; backward handed the oracle's
     O (bf16) and LSE (fp32), dQ/dK/dV at 1e-2 and the alpha gradient within 1e-5 of its
-    terms' absolute sum (as in the unrotated learned-alpha tests)."""
+    terms' absolute sum (as in the unrotated learned-alpha tests), plus the allowance of
+    rope_rounding for rotated elements next to a bf16 rounding boundary."""
     B, H, scale = 2, 2, 0.125
     x = inputs(68, 0, (B, H, N, 64), grad=True)
     table = fsa.rope_table(N, device=dev())
@@ -331,6 +333,7 @@ def test_rope_frac_against_oracle(N, alpha, w, R):
     o_g, lse_g = synth.as_f64(o_c), synth.as_f64(lse_c)
     dd = np.zeros(len(tab))
     l1 = np.zeros(len(tab))
+    allow = np.zeros(len(tab))
     for b in range(B):
         for h in range(H):
             q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
@@ -341,7 +344,8 @@ def test_rope_frac_against_oracle(N, alpha, w, R):
             check(f"dv[{b},{h}]", g[2][b, h], rv)
             dd += rdd
             l1 += _entry_l1(oracle.rope_store_bf16(q), oracle.rope_store_bf16(k), v, do, o_g[b, h], tab, w, scale)
-    tol = 1e-5 * l1 + 1e-6
+            allow += rope_rounding.entry_grad_allowance(q, k, v, do, ds, w, scale, o_g[b, h], lse_g[b, h])[0]
+    tol = 1e-5 * l1 + 1e-6 + allow
     err = np.abs(synth.as_f64(g[4]) - dd)
     note(f"  doffs: max|err|/tol={float(np.max(err / tol)) if len(tab) else 0:.4f}")
     assert np.all(err <= tol)

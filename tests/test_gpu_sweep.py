@@ -9,7 +9,8 @@ one launch. Forward outputs are compared at the usual bars (1e-5 fp32,
 1e-2 bf16). The backward is handed the oracle's own O (rounded to the input dtype)
 and LSE (rounded to fp32), and compared with the oracle's backward of those same
 inputs (P = exp(s - lse), D = <dO, o>); for the learned-alpha variant the alpha
-gradient must agree within 1e-5 of the sum of its terms' absolute values."""
+gradient must agree within 1e-5 of the sum of its terms' absolute values (over rotated
+rows, plus the allowance of rope_rounding for elements next to a rounding boundary)."""
 import math
 import sys
 
@@ -18,6 +19,7 @@ import pytest
 import torch
 
 import oracle
+import rope_rounding
 from fibonacci_offset_transformer_amd import fsa, synth
 
 pytestmark = pytest.mark.gpu
@@ -174,6 +176,7 @@ def test_sweep_learned_alpha(seed, rope):
     og, lg = synth.as_f64(o_in), synth.as_f64(lse_in)
     dd = np.zeros(len(tab))
     l1 = np.zeros(len(tab))
+    allow = np.zeros(len(tab))
     for b in range(B):
         for h in range(H):
             q, k, v, do = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v", "do"))
@@ -185,10 +188,13 @@ def test_sweep_learned_alpha(seed, rope):
                 check(f"{name}[{b},{h}]", got[b, h], want, 1e-2)
             dd += ref[3]
             l1 += _entry_l1(rot(q), rot(k), v, do, og[b, h], tab, w, 0.125)
+            if rope:  # rotated elements next to a bf16 rounding boundary may hold either neighbour
+                allow += rope_rounding.entry_grad_allowance(q, k, v, do, ds, w, 0.125, og[b, h], lg[b, h])[0]
+    tol = 1e-5 * l1 + 1e-6 + allow
     got = synth.as_f64(g[4])
-    assert np.all(np.abs(got - dd) <= 1e-5 * l1 + 1e-6), (got, dd)
+    assert np.all(np.abs(got - dd) <= tol), (got, dd, tol)
     fs = np.array([f for _, f in tab], dtype=np.float64)
-    assert abs(float(g[3].item()) - oracle.frac_alpha_grad(dd, fs)) <= float(np.sum(fs * (1e-5 * l1 + 1e-6)))
+    assert abs(float(g[3].item()) - oracle.frac_alpha_grad(dd, fs)) <= float(np.sum(fs * tol))
 
 
 @pytest.mark.parametrize("seed", range(12))
