@@ -213,8 +213,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     dma_tile(ks, K, i0 - 64, n, wave, lane);
     Frag<true> qf;
     buf_frag(qf, rq, i, g);
-    // FUSEK: V follows the rotated K rows' stores, so that the wait for those stores (and
-    // with it the tile's token) does not wait for V
+    // FUSEK: V is requested once the rotated K rows' stores have completed and the tile's
+    // token is out, so that the wait for those stores does not wait for V
     if constexpr (!FUSEK) dma_tile(vs, V, i0 - 64, n, wave, lane);
     // a bare barrier (the compiler's __syncthreads would first wait for every copy into LDS)
     if constexpr (FUSEK) wait_vm_all();
@@ -246,18 +246,20 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
             *slot = x;
             if (pos < n) *reinterpret_cast<u32x4_t *>(KH + (int64_t)pos * 64 + 8 * c) = x;
         }
-        dma_tile(vs, V, i0 - 64, n, wave, lane);
-        wait_vm<4>();  // the stores have reached L2; the four V copies may still be in flight
-        wait_lds();    // the rotated rows are in LDS before the barrier lets the other waves read them
+        // the load counter counts stores too: with nothing else outstanding, waiting for
+        // zero waits for exactly these stores to reach L2 (V is requested after the token)
+        wait_vm_all();
+        wait_lds();  // the rotated rows are in LDS before the barrier lets the other waves read them
     }
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
     [[maybe_unused]] uint64_t token = 0;
     if constexpr (FUSEK) {
-        // every wave's rotated rows are in L2: this tile's token goes out
+        // every wave's rotated rows are in L2: this tile's token goes out, then V is requested
         token = launch_token();
         if (threadIdx.x == 0) __hip_atomic_store(p.flags + lb, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dma_tile(vs, V, i0 - 64, n, wave, lane);
     }
     // the first slab rows are requested now and land while the band runs; most of them
     // are rows of neighbouring tiles whose band copies have just passed through L2
