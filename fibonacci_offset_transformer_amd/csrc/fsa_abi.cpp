@@ -1068,6 +1068,13 @@ fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int3
     return ok();
 }
 
+fsa_status_t fsa_debug_tile_order(int32_t nb, int32_t *tile_of_block) {
+    if (nb < 0) return fail(FSA_E_ARG, "nb must be >= 0 (got %d)", nb);
+    if (nb > 0 && !tile_of_block) return fail(FSA_E_ARG, "tile_of_block is NULL");
+    for (int32_t b = 0; b < nb; ++b) tile_of_block[b] = fsa::xcd_logical_block(b, nb);
+    return ok();
+}
+
 fsa_status_t fsa_debug_force_wait_timeout(int32_t enable) {
     g_force_give_up.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
     return ok();

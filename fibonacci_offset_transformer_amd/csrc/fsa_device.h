@@ -334,14 +334,6 @@ __device__ __forceinline__ void stage_tile(typename Elem<BF16>::T *lds, int stri
     }
 }
 
-// Hardware dispatch places workgroup b on XCD b % 8. Returns the logical tile
-// index so that each XCD receives one contiguous range of logical tiles, which
-// it processes in increasing order.
-__device__ __forceinline__ int xcd_logical_block(int b, int nb) {
-    const int x = b & 7, idx = b >> 3;
-    const int per = nb >> 3, extra = nb & 7;
-    return x * per + (x < extra ? x : extra) + idx;
-}
 
 // ----------------------------------------------------------------------------
 // Row-major LDS tiles filled by direct global -> LDS loads (bf16 window kernels)

@@ -13,6 +13,16 @@ constexpr int kHeadDim = 64;   // head size supported by the kernels
 constexpr int kTile = 64;      // query (or key) rows owned by one workgroup
 constexpr int kThreads = 256;  // four wave64 per workgroup, 16 rows each
 
+// Hardware dispatch places workgroup b on XCD b % 8. Returns the logical tile of
+// workgroup b of a grid of nb so that each XCD receives one contiguous range of
+// logical tiles, which it processes in increasing order (shared with the host, which
+// exports it for tests: fsa_debug_tile_order).
+__host__ __device__ inline int xcd_logical_block(int b, int nb) {
+    const int x = b & 7, idx = b >> 3;
+    const int per = nb >> 3, extra = nb & 7;
+    return x * per + (x < extra ? x : extra) + idx;
+}
+
 // Kernel arguments, passed by value. Offsets are the sparse table T after the
 // host dropped entries >= N (they attend nothing); all entries are >= w.
 struct AttnParams {

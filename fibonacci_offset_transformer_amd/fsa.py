@@ -32,7 +32,7 @@ EXPORTS = ("fsa_build_offsets", "fsa_forward", "fsa_backward", "fsa_backward_wor
            "fsa_frac_decode",
            "fsa_rope_table", "fsa_rope_rotate", "fsa_rope_workspace_bytes", "fsa_rope_forward", "fsa_rope_backward",
            "fsa_rope_frac_workspace_bytes", "fsa_rope_frac_forward", "fsa_rope_frac_backward", "fsa_wait_status",
-           "fsa_backward_noalloc", "fsa_debug_force_wait_timeout", "fsa_last_error")
+           "fsa_backward_noalloc", "fsa_debug_force_wait_timeout", "fsa_debug_tile_order", "fsa_last_error")
 WS_KINDS = {"backward": 0, "frac_backward": 1, "rope_backward": 2, "rope_frac_backward": 3, "backward_noalloc": 4,
             "rope_forward": 5}
 
@@ -126,6 +126,8 @@ def library() -> ctypes.CDLL:
             L.fsa_backward_noalloc.restype = ctypes.c_int
             L.fsa_debug_force_wait_timeout.argtypes = [i32]
             L.fsa_debug_force_wait_timeout.restype = ctypes.c_int
+            L.fsa_debug_tile_order.argtypes = [i32, ctypes.POINTER(i32)]
+            L.fsa_debug_tile_order.restype = ctypes.c_int
             L.fsa_last_error.argtypes = []
             L.fsa_last_error.restype = ctypes.c_char_p
             _lib = L
@@ -579,3 +581,11 @@ def wait_status(kind: str, q, ws, *, alpha: float = 1.0, w: int, R: int, base: s
 def debug_force_wait_timeout(enable: bool) -> None:
     """Diagnostic hook: makes later one-launch waits give up (see fsa_debug_force_wait_timeout)."""
     _check(library().fsa_debug_force_wait_timeout(int(bool(enable))))
+
+
+def debug_tile_order(nb: int):
+    """Diagnostic hook: the logical tile each workgroup of a window-kernel grid of nb
+    workgroups processes (see fsa_debug_tile_order), as a list."""
+    out = (ctypes.c_int32 * max(nb, 1))()
+    _check(library().fsa_debug_tile_order(int(nb), out))
+    return [out[b] for b in range(nb)]

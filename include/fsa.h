@@ -550,6 +550,19 @@ fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int3
  */
 fsa_status_t fsa_debug_force_wait_timeout(int32_t enable);
 
+/*
+ * fsa_debug_tile_order - diagnostic hook for tests of the dispatch assumptions (not part
+ * of the method). Writes, for each workgroup b of a window-kernel grid of nb workgroups
+ * (nb = B * H * ceil(N / 64); the one-launch backward runs two such grids back to back),
+ * the logical tile it processes (head b_h = tile / ceil(N / 64), row tile = tile mod
+ * ceil(N / 64)) into tile_of_block[b] (host memory, nb entries, caller-owned). The
+ * kernels rely on the hardware placing workgroup b on XCD b mod 8 and dispatching in
+ * increasing b; this order gives each XCD one contiguous range of tiles (whole heads
+ * when B * H is a multiple of 8), taken in increasing order. Returns FSA_E_ARG for
+ * nb < 0 or a NULL array with nb > 0.
+ */
+fsa_status_t fsa_debug_tile_order(int32_t nb, int32_t *tile_of_block);
+
 /* Text describing the calling thread's last non-OK status ("" if none). */
 const char *fsa_last_error(void);
 

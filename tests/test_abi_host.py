@@ -337,3 +337,47 @@ def test_wait_status_checks(lib):
 def test_debug_force_wait_timeout_toggles(lib):
     assert lib.fsa_debug_force_wait_timeout(1) == fsa.FSA_OK
     assert lib.fsa_debug_force_wait_timeout(0) == fsa.FSA_OK
+
+
+# ------------------------------------------------------------- workgroup order of the window kernels
+
+def test_tile_order_rejects_bad_arguments(lib):
+    assert lib.fsa_debug_tile_order(-1, None) == 1
+    assert lib.fsa_debug_tile_order(5, None) == 1
+    assert lib.fsa_debug_tile_order(0, None) == 0
+
+
+@pytest.mark.parametrize("bh,N", [(16, 4096), (8, 4096), (64, 1024), (8, 32768), (8, 65), (24, 300),
+                                  (3, 4096), (1, 100), (5, 257), (12, 1000)])
+def test_tile_order_properties(bh, N):
+    """The dispatch assumptions the one-launch waits rest on, checked on the order the
+    kernels use: workgroup b (on XCD b mod 8, dispatched in increasing b) takes the
+    logical tile order[b]. Every XCD gets one contiguous range of tiles in increasing
+    order; with B * H a multiple of 8 that range is whole heads, so every tile a
+    workgroup waits for (its own head's earlier tiles in the rotary forward; its head's
+    dQ tiles in the one-launch backward, whose dK/dV grid follows the dQ grid) was
+    dispatched earlier on the same XCD."""
+    nt = (N + 63) // 64
+    tiles = bh * nt
+    order = fsa.debug_tile_order(tiles)
+    assert sorted(order) == list(range(tiles))  # a permutation
+    block_of = {t: b for b, t in enumerate(order)}
+    for x in range(8):
+        mine = [order[b] for b in range(x, tiles, 8)]
+        if mine:
+            assert mine == list(range(mine[0], mine[0] + len(mine)))  # contiguous, increasing
+    if bh % 8:
+        return
+    for h in range(bh):
+        xcds = {block_of[h * nt + t] % 8 for t in range(nt)}
+        assert len(xcds) == 1  # whole heads per XCD
+        blocks = [block_of[h * nt + t] for t in range(nt)]
+        assert blocks == sorted(blocks)  # earlier tiles dispatched earlier
+    # one-launch backward: dK/dV block tiles + b' takes tile order[b'] and waits for dQ
+    # tiles of the same head; those sit on the same XCD and come earlier in the grid
+    assert tiles % 8 == 0
+    for b2 in range(tiles):
+        t = order[b2]
+        h = t // nt
+        for t2 in range(t - t % nt, (h + 1) * nt):
+            assert block_of[t2] % 8 == (tiles + b2) % 8 and block_of[t2] < tiles + b2
