@@ -392,10 +392,12 @@ def test_rope_forward_without_keeping_the_rotation_is_identical():
 
 # ---------------------------------------------------------------- decoding with RoPE
 
-def test_rope_decode_from_a_rotated_cache():
+@pytest.mark.parametrize("fractional", [False, True], ids=["static", "learned_alpha"])
+def test_rope_decode_from_a_rotated_cache(fractional):
     """Decoding with rotary embedding needs no kernel of its own: the cache keeps K rows
     rotated by their positions (the rotation step), the newest query is rotated by its
-    position i = L - 1, and the static decode runs on those rows. Checked against the
+    position i = L - 1, and the decode (static, or the learned-alpha variant's, whose
+    entries then interpolate rotated rows) runs on those rows. Checked against the
     oracle's rotary forward, row L - 1, over the stored rotated rows."""
     B, H, Lmax, w, alpha, R = 3, 4, 700, 64, 1.2, 1024
     x = inputs(69, 0, (B, H, Lmax, 64))
@@ -405,13 +407,20 @@ def test_rope_decode_from_a_rotated_cache():
     q_rot = fsa.rope_rotate(x["q"], table)  # row r rotated by position r
     q_new = torch.stack([q_rot[b, :, lens[b] - 1] for b in range(B)]).contiguous()  # [B, H, 64]
     sl = torch.tensor(lens, dtype=torch.int32, device=dev())
-    o, lse = fsa.decode(q_new, k_rot, x["v"], sl, alpha=alpha, w=w, R=R, scale=0.125, out_dtype=torch.float32)
+    o, lse = fsa.decode(q_new, k_rot, x["v"], sl, alpha=alpha, w=w, R=R, scale=0.125, out_dtype=torch.float32,
+                        fractional=fractional)
     torch.cuda.synchronize()
     T = oracle.offset_table("fib", alpha, w, R)
-    note(f"rotary decode B={B} H={H} Lmax={Lmax} lens={lens}")
+    ds = [d for d, _ in oracle.frac_offset_table("fib", alpha, w, R)]
+    note(f"rotary decode fractional={fractional} B={B} H={H} Lmax={Lmax} lens={lens}")
     for b in range(B):
         for h in range(H):
             q, k, v = (synth.as_f64(x[t][b, h]) for t in ("q", "k", "v"))
-            ro, rl = oracle.rope_sparse_forward_rows(q, k, v, T, w, 0.125, [lens[b] - 1], stored=True)
+            i = lens[b] - 1
+            if fractional:
+                ro, rl = oracle.rope_frac_forward(q[: i + 1], k[: i + 1], v[: i + 1], ds, w, 0.125, stored=True)
+                ro, rl = ro[i:], rl[i:]
+            else:
+                ro, rl = oracle.rope_sparse_forward_rows(q, k, v, T, w, 0.125, [i], stored=True)
             check(f"o[{b},{h}]", o[b, h][None], ro)
             check(f"lse[{b},{h}]", lse[b, h][None], rl)
