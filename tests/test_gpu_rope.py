@@ -241,13 +241,16 @@ def test_backward_reusing_the_forward_rotation_is_identical(H):
         assert torch.equal(a, b)
 
 
-def test_rope_graph_replays_match_eager():
-    x = inputs(67, 0, (2, 3, 700, 64), grad=True)
+@pytest.mark.parametrize("H", [3, 4], ids=["rotation_pass", "rotation_in_kernel"])
+def test_rope_graph_replays_match_eager(H):
+    # B * H = 8: the forward's tiles publish per-launch tokens for their rotated rows; a
+    # replayed graph must make new ones (the workspace is refilled with -1 in between)
+    x = inputs(67, 0, (2, H, 700, 64), grad=True)
     table = fsa.rope_table(700, device=dev())
     kw = dict(alpha=1.2, w=64, R=1024, scale=0.125)
     bufs = {n: torch.empty_like(x["q"]) for n in ("o", "dq", "dk", "dv")}
     lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device=dev())
-    ws = torch.empty(fsa.rope_workspace_bytes(torch.bfloat16, 2, 3, 700, alpha=1.2, w=64, R=1024)[1] // 4 + 1,
+    ws = torch.empty(fsa.rope_workspace_bytes(torch.bfloat16, 2, H, 700, alpha=1.2, w=64, R=1024)[1] // 4 + 1,
                      dtype=torch.int32, device=dev())
 
     def step():
