@@ -492,7 +492,7 @@ fsa_status_t prepare_frac(fsa::AttnParams &p, fsa_dtype_t dt, fsa_dtype_t out_dt
     if (!(scale > 0.f)) return fail(FSA_E_UNSUPPORTED, "fractional entries need a positive scale");
     int used = 0;
     while (used < n && p.off[used] + (p.phi[used] != 0.f ? 1 : 0) < N) ++used;
-    if (!fsa::pair_offsets_fit(N, used, 2))
+    if (!fsa::pair_offsets_fit(N, used, fsa::frac_pair_words(w)))
         return fail(FSA_E_UNSUPPORTED, "fractional entries: N = %d with %d entries exceeds 32-bit pair offsets", N, used);
     for (int t = 0; t < n; ++t) p.fbase[t] = static_cast<float>(fb[t]);
     p.n_entries = n;
@@ -533,7 +533,7 @@ fsa_status_t fsa_frac_backward_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_
     fsa::AttnParams p{};
     const fsa_status_t st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R);
     if (st != FSA_OK) return st;
-    *bytes = fsa::frac_workspace(static_cast<int64_t>(B) * H, N, p.n_off).total;
+    *bytes = fsa::frac_workspace(static_cast<int64_t>(B) * H, N, p.n_off, w).total;
     return ok();
 }
 
@@ -550,7 +550,7 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     if (doffs && (reinterpret_cast<uintptr_t>(doffs) & 3u)) return fail(FSA_E_ARG, "doffs is not 4-byte aligned");
     const bool empty = static_cast<int64_t>(B) * H * N == 0;
     if (!empty) {
-        const uint64_t need = fsa::frac_workspace(static_cast<int64_t>(B) * H, N, p.n_off).total;
+        const uint64_t need = fsa::frac_workspace(static_cast<int64_t>(B) * H, N, p.n_off, w).total;
         const char *names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv", "ws"};
         const void *ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv, ws};
         if ((st = check_ptrs(names, ptrs, 10)) != FSA_OK) return st;
@@ -568,7 +568,7 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
     p.dalpha = dalpha;
     p.doffs = doffs;
     if (!empty) {
-        const fsa::FracWorkspace lay = fsa::frac_workspace(p.bh, N, p.n_off);
+        const fsa::FracWorkspace lay = fsa::frac_workspace(p.bh, N, p.n_off, w);
         char *base_ws = static_cast<char *>(ws);
         p.q = q;
         p.k = k;
@@ -857,14 +857,14 @@ struct RopeFracLayout {
     uint64_t qhat, khat, frac, fwd, bwd;  // byte offsets into ws (frac: the fractional workspace) and sizes
 };
 
-RopeFracLayout rope_frac_layout(int64_t bh, int32_t n, int32_t n_off) {
+RopeFracLayout rope_frac_layout(int64_t bh, int32_t n, int32_t n_off, int32_t w) {
     RopeFracLayout l;
     const uint64_t rows = static_cast<uint64_t>(bh) * n;
     l.qhat = 0;
     l.khat = fsa::align256(rows * 128);
     l.fwd = l.khat + fsa::align256(rows * 128);
     l.frac = l.fwd;
-    l.bwd = l.frac + fsa::frac_workspace(bh, n, n_off).total;
+    l.bwd = l.frac + fsa::frac_workspace(bh, n, n_off, w).total;
     return l;
 }
 
@@ -878,7 +878,7 @@ fsa_status_t fsa_rope_frac_workspace_bytes(fsa_dtype_t dt, int32_t B, int32_t H,
     const fsa_status_t st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R);
     if (st != FSA_OK) return st;
     const bool empty = static_cast<int64_t>(B) * H * N == 0;
-    const RopeFracLayout l = rope_frac_layout(static_cast<int64_t>(B) * H, N, p.n_off);
+    const RopeFracLayout l = rope_frac_layout(static_cast<int64_t>(B) * H, N, p.n_off, w);
     *fwd_bytes = empty ? 0 : l.fwd;
     *bwd_bytes = empty ? 0 : l.bwd;
     return ok();
@@ -897,7 +897,7 @@ fsa_status_t fsa_rope_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const voi
     const void *ptrs[] = {q, k, v, rope, o, lse, ws};
     if ((st = check_ptrs(names, ptrs, 7)) != FSA_OK) return st;
     if ((st = check_no_alias(names, ptrs, 4, 7)) != FSA_OK) return st;
-    const RopeFracLayout l = rope_frac_layout(p.bh, N, p.n_off);
+    const RopeFracLayout l = rope_frac_layout(p.bh, N, p.n_off, w);
     if (ws_bytes < l.fwd)
         return fail(FSA_E_ARG, "ws holds %llu bytes, this problem needs %llu",
                     static_cast<unsigned long long>(ws_bytes), static_cast<unsigned long long>(l.fwd));
@@ -931,7 +931,7 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
     const bool empty = static_cast<int64_t>(B) * H * N == 0;
     RopeFracLayout l{};
     if (!empty) {
-        l = rope_frac_layout(p.bh, N, p.n_off);
+        l = rope_frac_layout(p.bh, N, p.n_off, w);
         const char *names[] = {"q", "k", "v", "rope", "o", "lse", "dout", "dq", "dk", "dv", "ws"};
         const void *ptrs[] = {q, k, v, rope, o, lse, dout, dq, dk, dv, ws};
         if ((st = check_ptrs(names, ptrs, 11)) != FSA_OK) return st;
@@ -959,7 +959,7 @@ fsa_status_t fsa_rope_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const vo
         const hipError_t e = rotate_rows(xs, hats, 2, rope, static_cast<int64_t>(B) * H * N, N, hs);
         if (e != hipSuccess) return launched(e, "rotary rotation");
     }
-    const fsa::FracWorkspace fl = fsa::frac_workspace(p.bh, N, p.n_off);
+    const fsa::FracWorkspace fl = fsa::frac_workspace(p.bh, N, p.n_off, w);
     char *fw = wsb + l.frac;
     p.q = hats[0];
     p.k = hats[1];
@@ -1038,11 +1038,11 @@ fsa_status_t fsa_wait_status(fsa_ws_kind_t kind, fsa_dtype_t dt, int32_t B, int3
     } else if (kind == FSA_WS_FRAC_BACKWARD || kind == FSA_WS_ROPE_FRAC_BACKWARD) {
         fsa::AttnParams p{};
         if ((st = prepare_frac(p, dt, dt, B, H, N, d, 1.0f, base, alpha, w, R)) != FSA_OK) return st;
-        const fsa::FracWorkspace fl = fsa::frac_workspace(bh, N, p.n_off);
+        const fsa::FracWorkspace fl = fsa::frac_workspace(bh, N, p.n_off, w);
         uint64_t frac = 0;
         need = fl.total;
         if (kind == FSA_WS_ROPE_FRAC_BACKWARD) {
-            const RopeFracLayout l = rope_frac_layout(bh, N, p.n_off);
+            const RopeFracLayout l = rope_frac_layout(bh, N, p.n_off, w);
             frac = l.frac;
             need = l.bwd;
         }

@@ -265,7 +265,6 @@ template <bool OUT_BF16, bool WITH_D, bool FRAC, int NOFF = 0, bool PUBLISH = fa
 __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *d_s,
                                         float *dd_s, [[maybe_unused]] const uint64_t token = 0) {
     static_assert(!FRAC || WITH_D, "the fractional backward forms D in the dQ kernel");
-    static_assert(!(FRAC && EXACT), "fractional entries keep their own pair format");
     using OE = typename Elem<OUT_BF16>::T;
 
     const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
@@ -450,9 +449,10 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
     const int slots = pair_slots(n_off);
     if constexpr (FRAC) {
         // pair words [n, slots, 2]: the near word {(1 - phi) P, (1 - phi) dS} and the far
-        // word {phi P, phi dS} of every entry, each rounded once to bf16, stored by the lane
-        // c8 = t mod 8 of each row
+        // word {phi P, phi dS} of every entry, each rounded once to bf16 (EXACT: [n, slots,
+        // 4], the same four values as fp32 words), stored by the lane c8 = t mod 8 of each row
         uint2 *pairs2 = reinterpret_cast<uint2 *>(p.pairs) + (int64_t)bh * n * slots;
+        uint4 *pairs4 = reinterpret_cast<uint4 *>(p.pairs) + (int64_t)bh * n * slots;
         auto entry = [&](int t, const SFrag &kn, const SFrag &kf) {
             const int a = p.off[t], first = table_first(p, t);
             const float ph = table_phi(p, t);
@@ -474,10 +474,18 @@ __device__ __forceinline__ void dq_tile(const AttnParams &p, const int lb, uint1
                 const float pv = ok ? fast_exp2(__builtin_fmaf(sc, sl2, -lse2[h])) : 0.f;
                 const float ds = pv * (dp - di[h]);
                 const float pf = pv * ph, dsf = ds * ph;
-                const uint2 pw = {pack_bf16(pv - pf, ds - dsf), pack_bf16(pf, dsf)};
-                if (c8 == (t & 7) && row < n) pairs2[(int64_t)row * slots + t] = pw;
-                chunk_axpy_words(dq_s[h], pw.x >> 16, pw.x & 0xffff0000u, kn.r[h]);
-                chunk_axpy_words(dq_s[h], pw.y >> 16, pw.y & 0xffff0000u, kf.r[h]);
+                if constexpr (EXACT) {
+                    if (c8 == (t & 7) && row < n)
+                        pairs4[(int64_t)row * slots + t] = uint4{__float_as_uint(pv - pf), __float_as_uint(ds - dsf),
+                                                                 __float_as_uint(pf), __float_as_uint(dsf)};
+                    chunk_axpy_f32(dq_s[h], ds - dsf, kn.r[h]);
+                    chunk_axpy_f32(dq_s[h], dsf, kf.r[h]);
+                } else {
+                    const uint2 pw = {pack_bf16(pv - pf, ds - dsf), pack_bf16(pf, dsf)};
+                    if (c8 == (t & 7) && row < n) pairs2[(int64_t)row * slots + t] = pw;
+                    chunk_axpy_words(dq_s[h], pw.x >> 16, pw.x & 0xffff0000u, kn.r[h]);
+                    chunk_axpy_words(dq_s[h], pw.y >> 16, pw.y & 0xffff0000u, kf.r[h]);
+                }
                 // moving the target distance moves the key and value along far - near
                 // (the piece [a, a + 1)); rows without the far row contribute nothing
                 if (ok & (row - a - 1 >= 0)) ddl += __builtin_fmaf(p.scale * ds, sd, pv * pd[h]);
@@ -633,7 +641,6 @@ template <bool OUT_BF16, bool FRAC, bool FUSED = false, bool FROM_DQ = false, in
 __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uint16_t *ta, uint16_t *tb, float *lse_s,
                                           float *del_s, [[maybe_unused]] const uint64_t token = 0) {
     static_assert(FUSED || !FROM_DQ, "D comes from the same launch only in the one-launch backward");
-    static_assert(!(FRAC && EXACT), "fractional entries keep their own pair format");
     using OE = typename Elem<OUT_BF16>::T;
 
     const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
@@ -714,13 +721,20 @@ __device__ __forceinline__ void dkdv_tile(const AttnParams &p, const int lb, uin
     SFrag sq[kRingKV], sd[kRingKV];
     PairT pw[kRingKV][2];
     const int slots = pair_slots(n_off);
-    const __amdgpu_buffer_rsrc_t rp = FRAC    ? head_rsrc(p.pairs + (int64_t)bh * n * slots * 2, span_bytes(n, 8u * slots))
+    constexpr int kFracWords = EXACT ? 4 : 2;  // FRAC: words per slot (near and far share)
+    const __amdgpu_buffer_rsrc_t rp = FRAC    ? head_rsrc(p.pairs + (int64_t)bh * n * slots * kFracWords,
+                                                          span_bytes(n, 4u * kFracWords * slots))
                                       : EXACT ? pair_rsrc<2>(p, n_off, bh)
                                               : pair_rsrc<1>(p, n_off, bh);
     auto fill_words = [&](int u, int x) {
         const int t = FRAC ? x >> 1 : x, far = FRAC ? x & 1 : 0;
         const int iq0 = slab_row(p, n_off, t, row_s[0], 1) + far, iq1 = slab_row(p, n_off, t, row_s[1], 1) + far;
-        if constexpr (FRAC) {
+        if constexpr (FRAC && EXACT) {  // the share's two fp32 words
+            pw[u][0] = __builtin_bit_cast(PairT, __builtin_amdgcn_raw_buffer_load_b64(rp, ((iq0 * slots + t) * 2 + far) * 8,
+                                                                                      0, FUSED ? kCachePastL1 : 0));
+            pw[u][1] = __builtin_bit_cast(PairT, __builtin_amdgcn_raw_buffer_load_b64(rp, ((iq1 * slots + t) * 2 + far) * 8,
+                                                                                      0, FUSED ? kCachePastL1 : 0));
+        } else if constexpr (FRAC) {
             pw[u][0] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq0 * slots + t) * 2 + far) * 4, 0,
                                                             FUSED ? kCachePastL1 : 0);
             pw[u][1] = __builtin_amdgcn_raw_buffer_load_b32(rp, ((iq1 * slots + t) * 2 + far) * 4, 0,
@@ -987,17 +1001,24 @@ hipError_t launch_backward_grads(fsa_dtype_t dt, fsa_dtype_t out_dt, const AttnP
                               : launch(&bwd_generic_kernel<false, false>, tiles(p), p, s);
 }
 
-hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
-    if (tiles(p) == 0) return launch(&frac_alpha_kernel, 1, p, s);  // writes the zeros of an empty problem
+// Learned-alpha backward with pair slots of one format (EXACT: fp32 shares, below w = 64).
+template <bool EXACT>
+hipError_t launch_frac_window_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
     if (one_launch_backward(p))  // one launch, as for the static tables
-        return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, 0, true>, 2 * tiles(p), p, s)
-                                  : launch(&bwd_fused_kernel<false, true, 0, true>, 2 * tiles(p), p, s);
-    const hipError_t e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, true>, tiles(p), p, s)
-                                            : launch(&bwd_dq_kernel<false, true, true>, tiles(p), p, s);
+        return out_dt == FSA_BF16 ? launch(&bwd_fused_kernel<true, true, 0, true, EXACT>, 2 * tiles(p), p, s)
+                                  : launch(&bwd_fused_kernel<false, true, 0, true, EXACT>, 2 * tiles(p), p, s);
+    const hipError_t e = out_dt == FSA_BF16 ? launch(&bwd_dq_kernel<true, true, true, EXACT>, tiles(p), p, s)
+                                            : launch(&bwd_dq_kernel<false, true, true, EXACT>, tiles(p), p, s);
     if (e != hipSuccess) return e;
     // the dK/dV kernel also reduces the alpha gradient
-    return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true, true>, tiles(p), p, s)
-                              : launch(&bwd_dkdv_kernel<false, true>, tiles(p), p, s);
+    return out_dt == FSA_BF16 ? launch(&bwd_dkdv_kernel<true, true, EXACT>, tiles(p), p, s)
+                              : launch(&bwd_dkdv_kernel<false, true, EXACT>, tiles(p), p, s);
+}
+
+hipError_t launch_frac_backward(fsa_dtype_t out_dt, const AttnParams &p, hipStream_t s) {
+    if (tiles(p) == 0) return launch(&frac_alpha_kernel, 1, p, s);  // writes the zeros of an empty problem
+    if (frac_pair_words(p.w) == 4) return launch_frac_window_backward<true>(out_dt, p, s);
+    return launch_frac_window_backward<false>(out_dt, p, s);
 }
 
 }  // namespace fsa

@@ -137,12 +137,16 @@ inline uint64_t pair_ws_bytes(fsa_dtype_t dt, int32_t w, int32_t n, int64_t bh, 
 struct FracWorkspace {
     uint64_t delta, pairs, partials, flags, status, total;  // byte offsets of the parts, total size
 };
-inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off) {
+// Words per pair slot of the learned-alpha backward: the near and the far share, each
+// P and dS as two bf16 in one word at w >= 64, as four fp32 words below (the same
+// reading as the static slots).
+__host__ __device__ inline int32_t frac_pair_words(int32_t window) { return 2 * pair_slot_words(window); }
+inline FracWorkspace frac_workspace(int64_t bh, int32_t n, int32_t n_off, int32_t window) {
     FracWorkspace w;
     const uint64_t tiles = static_cast<uint64_t>(bh) * ((n + 63) / 64);
     w.delta = 0;
     w.pairs = align256(4ull * bh * n);
-    w.partials = w.pairs + align256(8ull * pair_slots(n_off) * bh * n);
+    w.partials = w.pairs + align256(4ull * frac_pair_words(window) * pair_slots(n_off) * bh * n);
     w.flags = w.partials + align256(4ull * tiles * n_off);
     w.status = w.flags + align256(8ull * tiles);
     w.total = w.status + (tiles > 0 ? 256 : 0);

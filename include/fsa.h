@@ -289,7 +289,8 @@ fsa_status_t fsa_frac_forward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q,
  *   ws                  caller-owned device workspace of at least
  *                       fsa_frac_backward_workspace_bytes(...) bytes, 16-byte aligned,
  *                       overwritten; its contents on entry do not matter (it holds D,
- *                       the near and far bf16 weights of every pair, the per-tile
+ *                       the near and far weights of every pair (bf16 at w = 64, fp32
+ *                       below, as fsa_backward's pair slots), the per-tile
  *                       partials of the alpha gradient and one 64-bit token per tile:
  *                       with B * H a multiple of 8 the dQ and dK/dV parts run in one
  *                       launch, as in fsa_backward). May be NULL for an empty problem.
@@ -304,8 +305,9 @@ fsa_status_t fsa_frac_backward(fsa_dtype_t dt, fsa_dtype_t out_dt, const void *q
 
 /*
  * fsa_frac_backward_workspace_bytes - bytes of ws fsa_frac_backward needs:
- * 4 B H N (D) + 8 S B H N (two words per pair, S = number of entries some row
- * reaches, rounded up to a multiple of 8) + 4 B H ceil(N/64) S' (partials, S' the
+ * 4 B H N (D) + 4 W S B H N (W words per pair: 2 at w = 64, the near and far
+ * shares' P and dS as bf16 pairs, and 4 below, as fp32 words; S = number of entries
+ * some row reaches, rounded up to a multiple of 8) + 4 B H ceil(N/64) S' (partials, S' the
  * unrounded count) + 8 B H ceil(N/64) (tokens) + 8 (status word, see fsa_wait_status),
  * each part rounded up to 256 bytes. Arguments as in fsa_frac_backward; *bytes receives
  * the size.

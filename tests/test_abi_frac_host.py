@@ -75,13 +75,17 @@ def fbwd(lib, dt=1, ptrs=None, B=1, H=1, N=64, d=64, scale=0.125, base=0, alpha=
 
 @pytest.mark.parametrize("call", [ffwd, fbwd])
 def test_frac_pair_words_need_32_bit_offsets(lib, call):
-    # w = 1, R = 2^30: 35 entries below N = 2^24 (40 slots of two words: 5.4 GB per head)
+    # w = 1, R = 2^30: 35 entries below N = 2^24 (40 slots of four fp32 words below w = 64:
+    # 10.7 GB per head)
     assert call(lib, N=1 << 24, w=1, R=1 << 30) == fsa.FSA_E_UNSUPPORTED
     assert b"32-bit pair offsets" in lib.fsa_last_error()
-    # 12 entries (R = 300) at N = 2^23 (16 slots of two words: 1.1 GB per head) are accepted
+    # 12 entries (R = 300) take 16 slots: at N = 2^22 (1.07 GB per head) they are accepted,
+    # at N = 2^23 (2.1 GB) not; at w = 64 (two words per slot) N = 2^23 fits
     ws = ctypes.c_uint64(0)
-    assert lib.fsa_frac_backward_workspace_bytes(1, 1, 1, 1 << 23, 64, 0, 1.0, 1, 300, ctypes.byref(ws)) == 0
-    assert ws.value > 16 * 8 << 23
+    assert lib.fsa_frac_backward_workspace_bytes(1, 1, 1, 1 << 22, 64, 0, 1.0, 1, 300, ctypes.byref(ws)) == 0
+    assert ws.value > 16 * 16 << 22
+    assert call(lib, N=1 << 23, w=1, R=300) == fsa.FSA_E_UNSUPPORTED
+    assert lib.fsa_frac_backward_workspace_bytes(1, 1, 1, 1 << 23, 64, 0, 20.0, 64, 300, ctypes.byref(ws)) == 0
 
 
 @pytest.mark.parametrize("call", [ffwd, fbwd])
@@ -155,7 +159,7 @@ def a256(x):
 
 
 def test_frac_workspace_size(lib):
-    # D, the pair words (two per pair), the per-tile partials, then one 64-bit token per
+    # D, the pair words (two per pair at w = 64, four below), the per-tile partials, then one 64-bit token per
     # tile (the one-launch backward) and the status word, each part rounded up to 256 bytes.
     # alpha = 1.3, w = 64, R = 1024: d = 1.3 F >= 64 for F = 55 .. 987 (7 entries) -> 8 slots
     bh, N = 16, 4096
@@ -167,9 +171,9 @@ def test_frac_workspace_size(lib):
     n = 200
     want = a256(4 * bh * n) + a256(8 * 8 * bh * n) + a256(4 * bh * 4 * 3) + a256(8 * bh * 4) + 256
     assert frac_ws(lib, alpha=1.3, N=n) == (fsa.FSA_OK, want)
-    # 9 entries (w = 1, alpha = 1.1, R = 60) take 16 slots
+    # 9 entries (w = 1, alpha = 1.1, R = 60) take 16 slots, of four fp32 words below w = 64
     assert len(oracle.frac_offset_table("fib", 1.1, 1, 60)) == 9
-    want = a256(4 * bh * N) + a256(8 * 16 * bh * N) + a256(4 * bh * (N // 64) * 9) + a256(8 * bh * (N // 64)) + 256
+    want = a256(4 * bh * N) + a256(16 * 16 * bh * N) + a256(4 * bh * (N // 64) * 9) + a256(8 * bh * (N // 64)) + 256
     assert frac_ws(lib, alpha=1.1, w=1, R=60) == (fsa.FSA_OK, want)
     assert frac_ws(lib, B=0) == (fsa.FSA_OK, 0)
     assert frac_ws(lib, dt=0)[0] == fsa.FSA_E_UNSUPPORTED
