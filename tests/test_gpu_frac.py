@@ -426,3 +426,29 @@ def test_frac_graph_replays_match_eager(H):
         torch.cuda.synchronize()
         for n in outs:
             assert torch.equal(outs[n], ref[n]), (rep, n)
+
+
+@pytest.mark.parametrize("H", [3, 8], ids=["two_kernels", "one_launch"])
+def test_small_window_backward_with_sharp_attention(H):
+    # as the static test of the same name: scale 1/2 at w = 8, where bf16 shares of P and
+    # dS would move a gradient by up to about 0.02 and the fp32 shares below w = 64 keep it
+    # within 1e-2; the backward is handed the oracle's own O (bf16) and LSE
+    B, N, w, alpha, R, scale = 1, 400, 8, 1.3, 1024, 0.5
+    x = inputs(42, 0, (B, H, N, 64), grad=True)
+    ds = [d for d, _ in oracle.frac_offset_table("fib", alpha, w, R)]
+    o_ref, lse_ref = np.zeros((B, H, N, 64)), np.zeros((B, H, N))
+    for h in range(H):
+        q, k, v = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v"))
+        o_ref[0, h], lse_ref[0, h] = oracle.frac_forward(q, k, v, ds, w, scale)
+    o_in = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse_in = torch.from_numpy(lse_ref).to(torch.float32)
+    g = fsa.frac_backward(x["q"], x["k"], x["v"], o_in.to(dev()), lse_in.to(dev()), x["do"], alpha=alpha, w=w, R=R,
+                          scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    note(f"sharp attention learned-alpha backward B={B} H={H} N={N} w={w} scale={scale}")
+    og, lg = synth.as_f64(o_in), synth.as_f64(lse_in)
+    for h in range(H):
+        q, k, v, do = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v", "do"))
+        ref = oracle.frac_backward(q, k, v, do, ds, w, scale, o=og[0, h], lse=lg[0, h])
+        for name, got, want in zip(("dq", "dk", "dv"), g[:3], ref[:3]):
+            check(f"{name}[{h}]", got[0, h], want, 1e-2)

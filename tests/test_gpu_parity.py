@@ -573,3 +573,32 @@ def test_binding_rejects_bad_row_buffers():
         fsa.decode(q1, x["k"], x["v"], sl, lse=torch.empty((1, 2, 1), device=dev()), **kw)
     with pytest.raises(ValueError):
         fsa.decode(q1, x["k"], x["v"], sl, out=torch.empty((1, 2, 32), device=dev(), dtype=torch.bfloat16), **kw)
+
+
+# ---------------------------------------------------------------- sharp attention, small windows
+
+@pytest.mark.parametrize("H", [3, 8], ids=["two_kernels", "one_launch"])
+def test_small_window_backward_with_sharp_attention(H):
+    # scale 1/2 (attention logits of standard deviation about 4) at w = 8: single keys take
+    # most of a row's weight, where one bf16 rounding of a pair's P and dS would move a
+    # gradient by up to about 0.02; the fp32 pair slots below w = 64 keep it within 1e-2.
+    # The backward is handed the oracle's own O (bf16) and LSE, as in the sweep
+    B, N, w, alpha, R, scale = 1, 400, 8, 1.0, 1024, 0.5
+    x = inputs(41, 0, (B, H, N, 64), torch.bfloat16, grad=True)
+    T = oracle.offset_table("fib", alpha, w, R)
+    o_ref, lse_ref = np.zeros((B, H, N, 64)), np.zeros((B, H, N))
+    for h in range(H):
+        q, k, v = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v"))
+        o_ref[0, h], lse_ref[0, h] = oracle.sparse_forward(q, k, v, T, w, scale)
+    o_in = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse_in = torch.from_numpy(lse_ref).to(torch.float32)
+    g = fsa.backward(x["q"], x["k"], x["v"], o_in.to(dev()), lse_in.to(dev()), x["do"], alpha=alpha, w=w, R=R,
+                     scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    note(f"sharp attention backward B={B} H={H} N={N} w={w} scale={scale}")
+    og, lg = synth.as_f64(o_in), synth.as_f64(lse_in)
+    for h in range(H):
+        q, k, v, do = (synth.as_f64(x[t][0, h]) for t in ("q", "k", "v", "do"))
+        ref = oracle.sparse_backward(q, k, v, do, T, w, scale, o=og[0, h], lse=lg[0, h])
+        for name, got, want in zip(("dq", "dk", "dv"), g, ref):
+            check(f"{name}[{h}]", got[0, h], want, 1e-2)
