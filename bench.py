@@ -337,7 +337,8 @@ def short_context_bench(fsa, torch, dev, stream, reps):
     the one-layer workload (alpha = 1) and the 16-layer linear stagger, each timed as the
     average launch over 16 layers' own seeded inputs (541 MB, more than the 256 MB
     last-level cache, so every launch reads its inputs from HBM); and the fp32
-    single-head workload (fp32 [1,1,256,64], w = 16, R = 256), which is launch-bound."""
+    single-head workload (fp32 [1,1,256,64], w = 16, R = 256): four workgroups, whose
+    time is the latency of one workgroup's chain of dependent loads, not bandwidth."""
     from fibonacci_offset_transformer_amd import schedules, synth
     Bs, Hs, Ns = 8, 8, 1024
     shape = (Bs, Hs, Ns, D)
@@ -410,7 +411,7 @@ def short_context_bench(fsa, torch, dev, stream, reps):
         "one_layer_alpha1": line(us_one, 1),
         "sixteen_layer_stagger": line(us_stagger, LAYERS),
         "fp32_single_head": {"what": "fp32 [1,1,256,64], w = 16, alpha = 1, R = 256, forward (general kernel; "
-                                     "launch-bound: 4 workgroups)",
+                                     "latency-bound: 4 workgroups)",
                              "us_per_launch": round(us1, 3),
                              "query_heads_per_s": round(256 / (us1 * 1e-6), 1)},
     }
