@@ -137,6 +137,15 @@ __global__ void __launch_bounds__(kThreads) fwd_kernel(const AttnParams p) {
     }
 }
 
+// Key row row - off[t] of a slab, or -1 (a row the buffer loads return as zeros without
+// touching memory) when BAND and the row lies in the band tiles, which hold rows
+// i0 - 64 .. i0 + 63: such rows are read from LDS after the band instead.
+template <bool BAND>
+__device__ __forceinline__ int band_slab_row(const AttnParams &p, int n_off, int t, int row, int i0) {
+    const int x = slab_row(p, n_off, t, row, -1);
+    return BAND && x >= i0 - 64 ? -1 : x;
+}
+
 // Forward, bf16 inputs, window w <= 64. The workgroup's band keys [i0 - 64, i0 + 64)
 // are copied into LDS (K and V row-major) first. Once they have landed, the first
 // sparse slabs are requested, in the slab layout, into a ring of four row pairs per
@@ -279,9 +288,12 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (u < n_off) {  // uniform
+                // rows the band tiles hold are read from LDS after the band instead
+                const int a = band_slab_row<!FUSEK>(p, n_off, u, row_s[0], i0);
+                const int b = band_slab_row<!FUSEK>(p, n_off, u, row_s[1], i0);
                 if constexpr (!FUSEK)  // with FUSEK the K rows follow the wait for their tiles
-                    sfrag_load(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
-                sfrag_load(sv[u], rv, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
+                    sfrag_load(sk[u], rk, a, b, c8);
+                sfrag_load(sv[u], rv, a, b, c8);
             }
         }
     }
@@ -386,6 +398,24 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                 sfrag_load<kSlabK>(sk[u], rk, slab_row(p, n_off, u, row_s[0], -1), slab_row(p, n_off, u, row_s[1], -1), c8);
     }
 
+    if constexpr (!FRAC && !FUSEK) {
+        // the ring's rows that lie in the band tiles (tile row r = row - i0 + 64 >= 0; r <
+        // 128 since every offset is >= 1) come from LDS: offsets below 128 at w = 64, most
+        // of the ring at the narrow windows
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (u < n_off) {  // uniform
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = slab_row(p, n_off, u, row_s[h], -1) - i0 + 64;
+                    if (r >= 0) {
+                        sk[u].r[h] = *reinterpret_cast<const u32x4_t *>(ks + tile_chunk(r, c8));
+                        sv[u].r[h] = *reinterpret_cast<const u32x4_t *>(vs + tile_chunk(r, c8));
+                    }
+                }
+            }
+        }
+    }
     // ---- the band state, moved into the slab layout, starts the slabs' online softmax ----
     __syncthreads();  // every wave is done with the band tiles
     float *area = reinterpret_cast<float *>(ks) + wave * 1024;
