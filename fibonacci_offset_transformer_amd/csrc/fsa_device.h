@@ -370,6 +370,19 @@ __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src, in
     }
 }
 
+// As dma_tile for a 64-row tile (rows [row0, row0 + 64)): two transfers per wave.
+__device__ __forceinline__ void dma_tile64(uint16_t *tile, const uint16_t *src, int row0, int n, int wave, int lane) {
+    const int rl = lane >> 3;
+    const int chunk = (lane & 7) ^ rl;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int rb = 8 * (2 * wave + k);
+        int r = row0 + rb + rl;
+        r = (r >= 0 && r < n) ? r : 0;
+        __builtin_amdgcn_global_load_lds(src + (int64_t)r * 64 + 8 * chunk, (lds_void_t *)(tile + rb * 64), 16, 0, 0);
+    }
+}
+
 // Element offset, within a swizzled tile, of the 16-byte chunk c of tile row r.
 __device__ __forceinline__ int tile_chunk(int r, int c) { return r * 64 + 8 * (c ^ (r & 7)); }
 

@@ -147,9 +147,11 @@ __device__ __forceinline__ int band_slab_row(const AttnParams &p, int n_off, int
 }
 
 // Forward, bf16 inputs, window w <= 64. The workgroup's band keys [i0 - 64, i0 + 64)
-// are copied into LDS (K and V row-major) first. Once they have landed, the first
-// sparse slabs are requested, in the slab layout, into a ring of four row pairs per
-// lane, and the band runs on MFMA while those loads are in flight; its softmax state
+// are copied into LDS (K and V row-major) first, with its query rows (read from there
+// in the MFMA and in the slab layout; with ROPE they go to registers, to be rotated).
+// Once they have landed, the first sparse slabs are requested, in the slab layout, into
+// a ring of four row pairs per lane (rows the band tiles hold are read from LDS after
+// the band), and the band runs on MFMA while those loads are in flight; its softmax state
 // then moves into the slab layout and the slabs continue it as an online softmax, one
 // group of four offsets at a time. The slab layout stores O and the LSE.
 // With FRAC the table holds fractional entries (learned-alpha variant): entry t's key
@@ -169,6 +171,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     using OE = typename Elem<OUT_BF16>::T;
     __shared__ __attribute__((aligned(16))) uint16_t ks[kTileRows * 64];  // band K rows, then merge areas
     __shared__ __attribute__((aligned(16))) uint16_t vs[kTileRows * 64];  // band V rows, then band row stats
+    __shared__ __attribute__((aligned(16))) uint16_t qt[ROPE ? 8 : 64 * 64];  // the tile's query rows
 
     const int n = p.n, w = p.w, n_off = NOFF > 0 ? NOFF : p.n_off;
     const int nt = (n + 63) >> 6;
@@ -221,7 +224,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     }
     dma_tile(ks, K, i0 - 64, n, wave, lane);
     Frag<true> qf;
-    buf_frag(qf, rq, i, g);
+    if constexpr (ROPE) buf_frag(qf, rq, i, g);
+    else dma_tile64(qt, Q, i0, n, wave, lane);  // read in both layouts from LDS
     // FUSEK: V is requested once the rotated K rows' stores have completed and the tile's
     // token is out, so that the wait for those stores does not wait for V
     if constexpr (!FUSEK) dma_tile(vs, V, i0 - 64, n, wave, lane);
@@ -263,6 +267,7 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
     __asm__ volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
+    if constexpr (!ROPE) lds_frag(qf, qt, 16 * wave, tl);
     [[maybe_unused]] uint64_t token = 0;
     if constexpr (FUSEK) {
         // every wave's rotated rows are in L2: this tile's token goes out, then V is requested
@@ -450,7 +455,8 @@ __global__ void __launch_bounds__(kThreads) fwd_window_kernel(const AttnParams p
                 *reinterpret_cast<u32x4_t *>(QH + (int64_t)row_s[h] * 64 + 8 * c8) = qs.r[h];
         }
     } else {
-        sfrag_load(qs, rq, row_s[0], row_s[1], c8);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) qs.r[h] = *reinterpret_cast<const u32x4_t *>(qt + tile_chunk(16 * wave + s8 + 8 * h, c8));
     }
     // moves the state to a new maximum. Unconditional: where no maximum grew the factor
     // is 2^0 = 1. (Skipping it when no row's maximum grew, the common case after the
